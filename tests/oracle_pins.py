@@ -1,0 +1,371 @@
+"""Pins that tie the fp64 oracle to what the pages and the mathematics fix.
+
+Each ``check_*`` raises AssertionError when the oracle disagrees with a value
+that does not come from the oracle itself: a hand-derived worked example, a
+closed form, an exact special case, torch's scaled-dot-product attention in
+float64, autograd of torch's MSE, or brute force on tiny inputs. The tests in
+test_oracle.py run them; test_oracle_mutations.py plants plausible mistakes in
+the oracle and checks that some pin fails for each.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import oracle.ssa_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- pooling
+
+def check_pool_closed_form():
+    """x[t, d] = t + d/2 -> the mean of block b is b*bs + (bs-1)/2 + d/2."""
+    bs, nb, D = 8, 5, 3
+    t = np.arange(nb * bs, dtype=np.float64)[:, None]
+    d = np.arange(D, dtype=np.float64)[None, :]
+    x = (t + 0.5 * d).astype(np.float32)
+    got = O.pool_blocks(x, bs)
+    want = np.array([[b * bs + (bs - 1) / 2 + 0.5 * dd for dd in range(D)] for b in range(nb)])
+    assert got.dtype == np.float32 and got.shape == (nb, D)
+    assert np.array_equal(got.astype(np.float64), want), (got, want)
+
+
+def check_pool_mean_identity():
+    """Mean(q K^T) = q Mean(K)^T over a block pair ("SSA: Achieving Sparser
+    Attention ...", "Practical Implementation of SSA"), in both indices:
+    mean_{i in qb, j in kb} q_i . k_j equals pooled(Q)[qb] . pooled(K)[kb]
+    up to the float32 rounding of the pooled vectors."""
+    r = _rng(1)
+    bs, nb, D = 4, 3, 5
+    q = r.standard_normal((nb * bs, D)).astype(np.float32)
+    k = r.standard_normal((nb * bs, D)).astype(np.float32)
+    qbar, kbar = O.pool_blocks(q, bs), O.pool_blocks(k, bs)
+    s = O.block_score_matrix(qbar, kbar)
+    for a in range(nb):
+        for b in range(nb):
+            brute = 0.0
+            for i in range(a * bs, (a + 1) * bs):
+                for j in range(b * bs, (b + 1) * bs):
+                    brute += sum(float(q[i, dd]) * float(k[j, dd]) for dd in range(D))
+            brute /= bs * bs
+            tol = 1e-6 * (np.linalg.norm(qbar[a]) * np.linalg.norm(kbar[b]) + 1e-30)
+            assert abs(s[a, b] - brute) <= tol, (a, b, s[a, b], brute)
+
+
+def check_scores_exact_integers():
+    """Small integer vectors: every summation order is exact, so the scores
+    must equal the integer dot products exactly (pins operand order)."""
+    r = _rng(2)
+    qbar = r.integers(-8, 9, size=(4, 6)).astype(np.float32)
+    kbar = r.integers(-8, 9, size=(7, 6)).astype(np.float32)
+    s = O.block_score_matrix(qbar, kbar)
+    want = qbar.astype(np.int64) @ kbar.astype(np.int64).T
+    assert s.shape == (4, 7)
+    assert np.array_equal(s, want.astype(np.float64))
+
+
+# ---------------------------------------------------------------- selection
+
+def check_select_constant_scores():
+    """All scores equal: the free slots go to the lowest candidate indices."""
+    s = np.zeros(20)
+    got = O.select_row(s, diag=19, budget=6, n_sink=1, n_local=1)
+    assert got == [0, 1, 2, 3, 4, 19], got
+    got = O.select_row(s, diag=19, budget=6, n_sink=2, n_local=2)
+    assert got == [0, 1, 2, 3, 18, 19], got
+
+
+def check_select_duplicate_lower_index():
+    """Two blocks with the same score compete for one slot: lower index wins,
+    also between +0.0 and -0.0."""
+    s = np.array([0.0, 1.0, 5.0, 3.0, 5.0, 2.0, 0.0])
+    assert O.select_row(s, diag=6, budget=3, n_sink=1, n_local=1) == [0, 2, 6]
+    s = np.array([9.0, -0.0, 0.0, -1.0, 0.0])
+    assert O.select_row(s, diag=4, budget=3, n_sink=1, n_local=1) == [0, 1, 4]
+
+
+def check_select_known_ranking():
+    """Distinct scores: the top-`free` candidates by value, forced blocks
+    kept even when they score lowest."""
+    s = np.array([-100.0, 3.0, 9.0, 1.0, 7.0, 8.0, 2.0, -50.0])
+    assert O.select_row(s, diag=7, budget=5, n_sink=1, n_local=1) == [0, 2, 4, 5, 7]
+    # diag below the end of the score row: later blocks are not candidates
+    assert O.select_row(s, diag=4, budget=3, n_sink=1, n_local=1) == [0, 2, 4]
+    # fewer candidates than slots: every causal block
+    assert O.select_row(s, diag=3, budget=8, n_sink=1, n_local=1) == [0, 1, 2, 3]
+
+
+def check_select_invariants(seed=3, trials=200):
+    """Brute-force property check on random rows: forced blocks present, list
+    ascending and of size min(budget, diag+1), and every picked candidate
+    ranks (score desc, index asc) above every candidate left out."""
+    r = _rng(seed)
+    for _ in range(trials):
+        diag = int(r.integers(0, 40))
+        n_sink, n_local = int(r.integers(0, 3)), int(r.integers(0, 3))
+        budget = n_sink + n_local + int(r.integers(0, 10))
+        s = np.round(r.standard_normal(diag + 1), 1)   # rounding makes ties
+        sel = O.select_row(s, diag, budget, n_sink, n_local)
+        forced = set(range(min(n_sink, diag + 1))) | set(range(max(0, diag - n_local + 1), diag + 1))
+        assert sel == sorted(set(sel))
+        assert forced <= set(sel)
+        assert len(sel) == min(max(budget, len(forced)), diag + 1)
+        picked = [x for x in sel if x not in forced]
+        left = [x for x in range(diag + 1) if x not in sel]
+        for p in picked:
+            for o in left:
+                assert (s[p] > s[o]) or (s[p] == s[o] and p < o), (s, sel, p, o)
+
+
+# ---------------------------------------------------------------- attention
+
+def _sdpa(q, k, v, mask, scale):
+    """torch scaled-dot-product attention in float64 on the CPU."""
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        t(q)[None, None], t(k)[None, None], t(v)[None, None],
+        attn_mask=torch.from_numpy(mask)[None, None], scale=scale)
+    return out[0, 0].numpy()
+
+
+def _random_problem(r, nb, bs, D, budget, n_sink, n_local, nq=None):
+    n = nb * bs
+    q = r.standard_normal((n if nq is None else nq, D))
+    k = r.standard_normal((n, D)) * 1.5
+    v = r.standard_normal((n, D))
+    return q, k, v
+
+
+def _sel_masks(q, k, bs, budget, n_sink, n_local):
+    """Selected-block masks of each query row via the oracle's selection."""
+    nq, n = q.shape[0], k.shape[0]
+    idx, cnt = O.select_blocks(q[None, None], k[None, None], block=bs, budget=budget,
+                               n_sink=n_sink, n_local=n_local, head_map=[0])
+    nkb = n // bs
+    rows_blocks = (np.arange(nq) // bs) if nq == n else np.zeros(nq, dtype=int)
+    sel = np.stack([O.selected_mask(idx[0, 0, x], nkb) for x in rows_blocks])
+    return idx[0, 0], sel
+
+
+def check_attention_vs_sdpa(seed=4, trials=12):
+    """Full stream == causal SDPA; sparse stream == SDPA under the boolean
+    mask of the selected blocks' causal tokens; delta == full-softmax weight
+    outside that mask."""
+    r = _rng(seed)
+    for _ in range(trials):
+        bs = int(r.choice([2, 4, 8])); nb = int(r.integers(1, 7)); D = int(r.integers(1, 9))
+        n_sink, n_local = int(r.integers(0, 2)), int(r.integers(1, 3))
+        budget = n_sink + n_local + int(r.integers(0, 3))
+        scale = float(r.uniform(0.2, 1.5))
+        q, k, v = _random_problem(r, nb, bs, D, budget, n_sink, n_local)
+        n = nb * bs
+        _, sel = _sel_masks(q, k, bs, budget, n_sink, n_local)
+        pos = np.arange(n)
+        hf, hs, dl = O.dual_attention_rows(q, pos, k, v, sel, block=bs, scale=scale)
+        causal = np.tril(np.ones((n, n), dtype=bool))
+        smask = causal & sel[:, np.arange(n) // bs]
+        assert np.allclose(hf, _sdpa(q, k, v, causal, scale), atol=1e-12, rtol=1e-12)
+        assert np.allclose(hs, _sdpa(q, k, v, smask, scale), atol=1e-12, rtol=1e-12)
+        z = scale * q @ k.T
+        p = np.where(causal, np.exp(z - np.where(causal, z, -np.inf).max(1, keepdims=True)), 0)
+        p /= p.sum(1, keepdims=True)
+        assert np.allclose(dl, np.where(causal & ~smask, p, 0).sum(1), atol=1e-13)
+
+
+def check_attention_constant_keys():
+    """All keys equal: uniform weights. h_full[t] = mean(v[0..t]); h_sparse[t]
+    = mean of v over the selected causal tokens; delta = dropped/(t+1)."""
+    r = _rng(5)
+    bs, nb, D = 4, 6, 3
+    n = bs * nb
+    q = r.standard_normal((n, D))
+    k = np.tile(r.standard_normal((1, D)), (n, 1))
+    v = r.standard_normal((n, D))
+    idx, sel = _sel_masks(q, k, bs, 3, 1, 1)
+    hf, hs, dl = O.dual_attention_rows(q, np.arange(n), k, v, sel, block=bs, scale=0.7)
+    for t in range(n):
+        toks = [j for j in range(t + 1) if sel[t, j // bs]]
+        assert np.allclose(hf[t], v[:t + 1].mean(0), atol=1e-13)
+        assert np.allclose(hs[t], v[toks].mean(0), atol=1e-13)
+        assert abs(dl[t] - (t + 1 - len(toks)) / (t + 1)) < 1e-14
+
+
+def check_attention_graded_logits():
+    """Keys chosen so that the scaled logit of key j is ln(j+1): weights are
+    (j+1)/sum. Pins the 1/sqrt(D) default scale and the exponential."""
+    n, D = 12, 4
+    scale = 1.0 / math.sqrt(D)
+    q = np.zeros((n, D)); q[:, 0] = 1.0
+    k = np.zeros((n, D)); k[:, 0] = np.log(np.arange(1, n + 1)) / scale
+    v = np.stack([np.arange(n, dtype=np.float64), np.arange(n) ** 2.0, np.ones(n), -np.arange(n, dtype=np.float64)], 1)
+    sel = np.ones((n, 3), dtype=bool)  # block 4, every block selected
+    res = O.ssa_forward(q[None, None], k[None, None], v[None, None], block=4, budget=3,
+                        n_sink=1, n_local=1)
+    for t in range(n):
+        w = np.arange(1, t + 2, dtype=np.float64); w /= w.sum()
+        assert np.allclose(res["h_full"][0, 0, t], w @ v[:t + 1], atol=1e-12)
+    hf, hs, dl = O.dual_attention_rows(q, np.arange(n), k, v, sel, block=4, scale=scale)
+    assert np.allclose(hf, res["h_full"][0, 0], atol=1e-14)
+
+
+def check_full_budget_equals_full(seed=6):
+    """Budget covering every causal block: h_sparse == h_full, delta == 0,
+    losses 0 (the decomposition's delta = 0 case)."""
+    r = _rng(seed)
+    bs, nb, D = 4, 5, 6
+    q, k, v = _random_problem(r, nb, bs, D, nb, 1, 1)
+    res = O.ssa_forward(q[None, None], k[None, None], v[None, None], block=bs,
+                        budget=nb, n_sink=1, n_local=1)
+    assert np.array_equal(res["idx"][0, 0, -1], np.arange(nb))
+    assert np.allclose(res["h_sparse"], res["h_full"], atol=1e-14)
+    assert np.all(res["delta"] == 0.0)
+    assert res["loss_sparsity"] < 1e-28
+
+
+def check_decomposition_and_bound(seed=7):
+    """h_full = (1-delta) h_sparse + delta h_dropped, with h_dropped the
+    attention over the dropped causal tokens alone (torch SDPA), and the
+    linear bound ||h_full - h_sparse|| <= 2 delta max_j ||v_j|| (abstract of
+    'SSA: Sparse Sparse Attention by Aligning ...': the error scales linearly
+    with the dropped mass)."""
+    r = _rng(seed)
+    bs, nb, D = 4, 8, 5
+    q, k, v = _random_problem(r, nb, bs, D, 3, 1, 1)
+    n = bs * nb
+    _, sel = _sel_masks(q, k, bs, 3, 1, 1)
+    hf, hs, dl = O.dual_attention_rows(q, np.arange(n), k, v, sel, block=bs, scale=0.5)
+    causal = np.tril(np.ones((n, n), dtype=bool))
+    dmask = causal & ~sel[:, np.arange(n) // bs]
+    vmax = np.linalg.norm(v, axis=1).max()
+    checked = 0
+    for t in range(n):
+        err = np.linalg.norm(hf[t] - hs[t])
+        assert err <= 2 * dl[t] * vmax + 1e-12
+        if dmask[t].any():
+            hd = _sdpa(q[t:t + 1], k, v, dmask[t:t + 1], 0.5)[0]
+            assert np.allclose(hf[t], (1 - dl[t]) * hs[t] + dl[t] * hd, atol=1e-12)
+            checked += 1
+        else:
+            assert dl[t] == 0.0
+    assert checked > 0
+
+
+def check_nested_budgets(seed=8):
+    """Growing budgets select nested block sets and drop no more mass."""
+    r = _rng(seed)
+    bs, nb, D = 4, 12, 6
+    q, k, v = _random_problem(r, nb, bs, D, 4, 1, 1)
+    prev_idx, prev_delta = None, None
+    for budget in (2, 4, 6, 12):
+        res = O.ssa_forward(q[None, None], k[None, None], v[None, None], block=bs,
+                            budget=budget, n_sink=1, n_local=1)
+        if prev_idx is not None:
+            for qb in range(nb):
+                a = set(prev_idx[0, 0, qb][prev_idx[0, 0, qb] >= 0].tolist())
+                b = set(res["idx"][0, 0, qb][res["idx"][0, 0, qb] >= 0].tolist())
+                assert a <= b
+            assert np.all(res["delta"] <= prev_delta + 1e-15)
+        prev_idx, prev_delta = res["idx"], res["delta"]
+    assert np.all(prev_delta == 0.0)
+
+
+def check_gqa_equals_replicated(seed=9):
+    """GQA with a head map equals MHA over K/V replicated per q head."""
+    r = _rng(seed)
+    B, Hq, Hkv, bs, nb, D = 2, 4, 2, 4, 4, 3
+    n = bs * nb
+    q = r.standard_normal((B, Hq, n, D)); k = r.standard_normal((B, Hkv, n, D)); v = r.standard_normal((B, Hkv, n, D))
+    hm = [1, 0, 1, 0]
+    a = O.ssa_forward(q, k, v, block=bs, budget=2, n_sink=1, n_local=1, head_map=hm)
+    kr, vr = k[:, hm], v[:, hm]
+    b = O.ssa_forward(q, kr, vr, block=bs, budget=2, n_sink=1, n_local=1)
+    for key in ("idx", "cnt"):
+        assert np.array_equal(a[key], b[key])
+    for key in ("h_full", "h_sparse", "delta"):
+        assert np.allclose(a[key], b[key], atol=1e-14)
+
+
+def check_decode_vs_sdpa(seed=10):
+    """Decode: one query at the last position, its own block representation,
+    diag = last block; streams equal SDPA on that single row."""
+    r = _rng(seed)
+    bs, nb, D = 4, 10, 5
+    n = bs * nb
+    k = r.standard_normal((n, D)); v = r.standard_normal((n, D)); q = r.standard_normal((1, D))
+    res = O.ssa_forward(q[None, None], k[None, None], v[None, None], block=bs, budget=4,
+                        n_sink=1, n_local=1)
+    sel = O.selected_mask(res["idx"][0, 0, 0], nb)
+    assert sel[0] and sel[nb - 1] and sel.sum() == 4
+    # the free picks are the two best pooled scores among blocks 1..nb-2
+    kbar = O.pool_blocks(k.astype(np.float32), bs).astype(np.float64)
+    s = kbar @ q[0].astype(np.float32).astype(np.float64)
+    best = sorted(range(1, nb - 1), key=lambda j: -s[j])[:2]
+    assert set(np.nonzero(sel)[0].tolist()) == {0, nb - 1, *best}
+    mask = sel[np.arange(n) // bs][None]
+    scale = 1 / math.sqrt(D)
+    assert np.allclose(res["h_full"][0, 0], _sdpa(q, k, v, np.ones((1, n), bool), scale), atol=1e-12)
+    assert np.allclose(res["h_sparse"][0, 0], _sdpa(q, k, v, mask, scale), atol=1e-12)
+
+
+# ---------------------------------------------------------------- losses
+
+def check_loss_vs_torch(seed=11):
+    """Loss values equal torch's MSE; gradient seeds equal autograd through
+    MSE with the stop-gradient side detached."""
+    r = _rng(seed)
+    hf = r.standard_normal((2, 3, 5, 4)); hs = r.standard_normal((2, 3, 5, 4))
+    ls, lc, gf, gs = O.align_loss(hf, hs)
+    tf = torch.tensor(hf, requires_grad=True); ts = torch.tensor(hs, requires_grad=True)
+    l_sparsity = torch.nn.functional.mse_loss(tf, ts.detach())
+    l_commit = torch.nn.functional.mse_loss(ts, tf.detach())
+    (l_sparsity + l_commit).backward()
+    assert abs(ls - l_sparsity.item()) < 1e-15 and abs(lc - l_commit.item()) < 1e-15
+    assert np.allclose(gf, tf.grad.numpy(), atol=1e-16)
+    assert np.allclose(gs, ts.grad.numpy(), atol=1e-16)
+    # constant shift c -> loss c^2
+    ls2, _, _, _ = O.align_loss(hf, hf + 0.25)
+    assert abs(ls2 - 0.0625) < 1e-15
+
+
+# ---------------------------------------------------------------- worked example
+
+def check_worked_example():
+    with open(os.path.join(GOLDEN, "worked_example_6tok.json")) as f:
+        ex = json.load(f)
+    inp, exp = ex["inputs"], ex["expected"]
+    n, D = inp["N"], inp["D"]
+    q = np.zeros((n, D)); q[:, 0] = 1.0
+    k = np.zeros((n, D)); k[:, 0] = np.log(np.array(inp["a"], dtype=np.float64))
+    v = np.array(inp["v"], dtype=np.float64)
+    res = O.ssa_forward(q[None, None], k[None, None], v[None, None], block=inp["block"],
+                        budget=inp["budget"], n_sink=inp["n_sink"], n_local=inp["n_local"],
+                        scale=inp["scale"])
+    fr = lambda a: np.array([[float(Fraction(x)) for x in row] for row in a])
+    assert res["idx"][0, 0].tolist() == exp["idx"]
+    assert res["cnt"][0, 0].tolist() == exp["cnt"]
+    assert np.allclose(res["h_full"][0, 0], fr(exp["h_full"]), atol=1e-13)
+    assert np.allclose(res["h_sparse"][0, 0], fr(exp["h_sparse"]), atol=1e-13)
+    assert np.allclose(res["delta"][0, 0], [float(Fraction(x)) for x in exp["delta"]], atol=1e-14)
+    assert abs(res["loss_sparsity"] - float(Fraction(exp["loss"]))) < 1e-14
+    assert res["loss_commitment"] == res["loss_sparsity"]
+
+
+ALL_CHECKS = [
+    check_pool_closed_form, check_pool_mean_identity, check_scores_exact_integers,
+    check_select_constant_scores, check_select_duplicate_lower_index,
+    check_select_known_ranking, check_select_invariants, check_attention_vs_sdpa,
+    check_attention_constant_keys, check_attention_graded_logits,
+    check_full_budget_equals_full, check_decomposition_and_bound, check_nested_budgets,
+    check_gqa_equals_replicated, check_decode_vs_sdpa, check_loss_vs_torch,
+    check_worked_example,
+]

@@ -1,0 +1,90 @@
+"""Plants plausible mistakes in the oracle (on the CPU, by monkeypatching) and
+checks that at least one pin catches each of them."""
+import numpy as np
+import pytest
+
+import oracle.ssa_oracle as O
+import oracle_pins as P
+
+_pool, _scores, _select_row, _rows, _loss = (O.pool_blocks, O.block_score_matrix,
+                                             O.select_row, O.dual_attention_rows, O.align_loss)
+
+
+def m_pool_sum(x, block):                      # sum instead of mean
+    return (_pool(x, block).astype(np.float64) * block).astype(np.float32)
+
+
+def m_pool_strided(x, block):                  # blocks taken with a stride
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-2]
+    xb = x.reshape(x.shape[:-2] + (block, n // block, x.shape[-1]))
+    return xb.mean(axis=-3).astype(np.float32)
+
+
+def m_scores_transposed(qbar, kbar):           # operands swapped
+    return _scores(kbar, qbar)
+
+
+def m_select_high_tie(scores, diag, budget, n_sink, n_local):   # ties to the higher index
+    forced = O.forced_blocks(diag, n_sink, n_local)
+    free = budget - len(forced)
+    c = [kb for kb in range(diag + 1) if kb not in forced]
+    picks = c if len(c) <= free else sorted(c, key=lambda kb: (-scores[kb], -kb))[:free]
+    return sorted(forced + list(picks))
+
+
+def m_select_no_forced(scores, diag, budget, n_sink, n_local):  # forced blocks ignored
+    c = list(range(diag + 1))
+    return sorted(sorted(c, key=lambda kb: (-scores[kb], kb))[:budget])
+
+
+def m_rows_strict_causal(q, pos, k, v, sel, *, block, scale):   # j < t instead of j <= t
+    pos = np.asarray(pos)
+    return _rows(q, np.maximum(pos - 1, 0), k, v, sel, block=block, scale=scale)
+
+
+def m_rows_no_renorm(q, pos, k, v, sel, *, block, scale):       # sparse not renormalised
+    hf, hs, dl = _rows(q, pos, k, v, sel, block=block, scale=scale)
+    return hf, hs * (1.0 - dl)[:, None], dl
+
+
+def m_rows_no_scale(q, pos, k, v, sel, *, block, scale):        # logit scale dropped
+    return _rows(q, pos, k, v, sel, block=block, scale=1.0)
+
+
+def m_rows_delta_kept(q, pos, k, v, sel, *, block, scale):      # delta = kept mass
+    hf, hs, dl = _rows(q, pos, k, v, sel, block=block, scale=scale)
+    return hf, hs, 1.0 - dl
+
+
+def m_loss_row_mean(hf, hs):                   # mean over rows, not elements
+    a, b, c, d = _loss(hf, hs)
+    D = np.asarray(hf).shape[-1]
+    return a * D, b * D, c * D, d * D
+
+
+def m_loss_grad_sign(hf, hs):                  # gradient seeds swapped
+    a, b, c, d = _loss(hf, hs)
+    return a, b, d, c
+
+
+MUTATIONS = [
+    ("pool_blocks", m_pool_sum), ("pool_blocks", m_pool_strided),
+    ("block_score_matrix", m_scores_transposed),
+    ("select_row", m_select_high_tie), ("select_row", m_select_no_forced),
+    ("dual_attention_rows", m_rows_strict_causal), ("dual_attention_rows", m_rows_no_renorm),
+    ("dual_attention_rows", m_rows_no_scale), ("dual_attention_rows", m_rows_delta_kept),
+    ("align_loss", m_loss_row_mean), ("align_loss", m_loss_grad_sign),
+]
+
+
+@pytest.mark.parametrize("name,fn", MUTATIONS, ids=[m[1].__name__ for m in MUTATIONS])
+def test_mutation_is_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(O, name, fn)
+    caught = []
+    for check in P.ALL_CHECKS:
+        try:
+            check()
+        except Exception as e:  # AssertionError, or a shape error
+            caught.append(check.__name__)
+    assert caught, f"no pin caught mutation {fn.__name__}"

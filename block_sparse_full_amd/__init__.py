@@ -1,0 +1,8 @@
+"""SSA dual-stream block-sparse attention forward for AMD MI355X (gfx950).
+
+The computation lives in libssa.so (HIP kernels behind the C ABI declared in
+include/ssa.h); `block_sparse_full_amd.ssa` is the thin ctypes binding.
+"""
+from .ssa import (SSA_BF16, SSA_F32, Problem, SsaError, align_loss, alloc_workspace,
+                  attn_fwd, dual_attention, load_library, pool_blocks, problem_for,
+                  select_blocks, workspace_bytes)

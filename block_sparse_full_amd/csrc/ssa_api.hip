@@ -1,0 +1,273 @@
+// C ABI of the SSA dual-stream attention library: host-side validation,
+// workspace layout and kernel launches. Every check runs before the first
+// launch; no call allocates memory or synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/ssa.h"
+#include "ssa_common.h"
+#include "ssa_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ssa_status fail(ssa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+ssa_status ok() {
+  g_err[0] = '\0';
+  return SSA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Problem {
+  ssa::Dims d;
+  ssa::HeadMap hm;
+  bool bf16;
+  bool decode;
+};
+
+struct Layout {
+  size_t qbar, kbar, vt, partials, loss, total;
+};
+
+Layout layout_of(const Problem& P) {
+  const ssa::Dims& d = P.d;
+  Layout L;
+  size_t off = 0;
+  L.qbar = off;
+  off += align256((size_t)d.B * d.Hq * d.nQB * d.D * sizeof(float));
+  L.kbar = off;
+  off += align256((size_t)d.B * d.Hkv * d.nKB * d.D * sizeof(float));
+  L.vt = off;
+  if (P.bf16 && !P.decode) off += align256((size_t)d.B * d.Hkv * d.D * d.Nk * sizeof(uint16_t));
+  L.partials = off;
+  if (P.bf16 && P.decode) {
+    int ns = ssa::decode_splits(d.nKB);
+    if (ns < ssa::kDecSparseParts) ns = ssa::kDecSparseParts;
+    off += align256((size_t)d.B * d.Hq * ns * ssa::decode_partial_floats(d.D) * sizeof(float));
+  }
+  L.loss = off;
+  off += align256((size_t)ssa::kLossPartials * sizeof(double));
+  L.total = off;
+  return L;
+}
+
+ssa_status build(const ssa_problem* p, Problem* P) {
+  if (p == nullptr) return fail(SSA_ERR_INVALID_ARG, "problem is NULL");
+  if (p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->Nq <= 0 || p->Nk <= 0 || p->D <= 0 ||
+      p->block_size <= 0 || p->budget <= 0)
+    return fail(SSA_ERR_INVALID_ARG, "sizes must be positive (B=%d Hq=%d Hkv=%d Nq=%d Nk=%d D=%d "
+                "block_size=%d budget=%d)", p->B, p->Hq, p->Hkv, p->Nq, p->Nk, p->D,
+                p->block_size, p->budget);
+  if (p->n_sink < 0 || p->n_local < 0)
+    return fail(SSA_ERR_INVALID_ARG, "n_sink and n_local must be >= 0");
+  if (p->Hq % p->Hkv != 0)
+    return fail(SSA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+  if (p->budget < p->n_sink + p->n_local)
+    return fail(SSA_ERR_INVALID_ARG, "budget (%d) is below the forced blocks n_sink + n_local (%d)",
+                p->budget, p->n_sink + p->n_local);
+  if (p->Nq != p->Nk && p->Nq != 1)
+    return fail(SSA_ERR_UNSUPPORTED, "Nq must equal Nk (prefill) or be 1 (decode); got Nq=%d Nk=%d",
+                p->Nq, p->Nk);
+  if (p->dtype != SSA_F32 && p->dtype != SSA_BF16)
+    return fail(SSA_ERR_UNSUPPORTED, "dtype %d is not SSA_F32 or SSA_BF16", p->dtype);
+  if (p->D != 64 && p->D != 128) return fail(SSA_ERR_UNSUPPORTED, "D must be 64 or 128; got %d", p->D);
+  if (p->block_size != ssa::kBlock)
+    return fail(SSA_ERR_UNSUPPORTED, "block_size must be 64; got %d", p->block_size);
+  if (p->Nk % ssa::kBlock != 0)
+    return fail(SSA_ERR_UNSUPPORTED, "Nk (%d) must be a multiple of 64", p->Nk);
+  if (p->Nk / ssa::kBlock > ssa::kMaxKeyBlocks)
+    return fail(SSA_ERR_UNSUPPORTED, "Nk (%d) exceeds %d key blocks", p->Nk, ssa::kMaxKeyBlocks);
+  if (p->Hq > ssa::kMaxHq) return fail(SSA_ERR_UNSUPPORTED, "Hq (%d) exceeds %d", p->Hq, ssa::kMaxHq);
+  const int G = p->Hq / p->Hkv;
+  if (G > ssa::kMaxGroup)
+    return fail(SSA_ERR_UNSUPPORTED, "Hq/Hkv (%d) exceeds %d", G, ssa::kMaxGroup);
+  const bool decode = p->Nq == 1 && p->Nk != 1;
+  if (decode && p->dtype == SSA_BF16 && G > ssa::kDecMaxGroup)
+    return fail(SSA_ERR_UNSUPPORTED, "bf16 decode supports Hq/Hkv <= %d; got %d", ssa::kDecMaxGroup, G);
+  if (!(p->scale >= 0.f) || isinf(p->scale))
+    return fail(SSA_ERR_INVALID_ARG, "scale must be finite and >= 0 (0 selects 1/sqrt(D))");
+  const double total = (double)p->B * p->Hq * p->Nq * p->D;
+  const double kv = (double)p->B * p->Hkv * p->Nk * p->D;
+  if (total > 1.0e12 || kv > 1.0e12) return fail(SSA_ERR_UNSUPPORTED, "problem too large");
+  if ((double)p->B * p->Hq * (p->Nq == 1 ? 1 : p->Nq / ssa::kBlock) > 2.0e9)
+    return fail(SSA_ERR_UNSUPPORTED, "too many query blocks");
+
+  ssa::HeadMap& hm = P->hm;
+  memset(&hm, 0, sizeof(hm));
+  int count[ssa::kMaxHq];
+  for (int g = 0; g < p->Hkv && g < ssa::kMaxHq; ++g) count[g] = 0;
+  for (int h = 0; h < p->Hq; ++h) {
+    const int g = p->head_map ? p->head_map[h] : h / G;
+    if (g < 0 || g >= p->Hkv)
+      return fail(SSA_ERR_INVALID_ARG, "head_map[%d] = %d is outside [0, %d)", h, g, p->Hkv);
+    if (count[g] >= G)
+      return fail(SSA_ERR_INVALID_ARG, "head_map gives kv head %d more than Hq/Hkv = %d q heads", g, G);
+    hm.kv_of_q[h] = (uint8_t)g;
+    hm.q_of_kv[g * G + count[g]] = (uint8_t)h;
+    count[g]++;
+  }
+
+  ssa::Dims& d = P->d;
+  d.B = p->B; d.Hq = p->Hq; d.Hkv = p->Hkv; d.Nq = p->Nq; d.Nk = p->Nk; d.D = p->D;
+  d.budget = p->budget; d.n_sink = p->n_sink; d.n_local = p->n_local;
+  d.nKB = p->Nk / ssa::kBlock;
+  if (p->Nq == p->Nk) {
+    if (p->Nq % ssa::kBlock != 0)
+      return fail(SSA_ERR_UNSUPPORTED, "Nq (%d) must be a multiple of 64", p->Nq);
+    d.nQB = p->Nq / ssa::kBlock;
+  } else {
+    d.nQB = 1;
+  }
+  d.G = G;
+  d.scale = p->scale > 0.f ? p->scale : (float)(1.0 / sqrt((double)p->D));
+  d.scale_log2 = d.scale * ssa::kLog2e;
+  P->bf16 = p->dtype == SSA_BF16;
+  P->decode = decode;
+  return SSA_OK;
+}
+
+ssa_status check_ws(const Problem& P, const void* ws, size_t ws_bytes, Layout* L) {
+  *L = layout_of(P);
+  if (ws == nullptr) return fail(SSA_ERR_WORKSPACE, "workspace is NULL");
+  if (((uintptr_t)ws & 255u) != 0) return fail(SSA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (ws_bytes < L->total)
+    return fail(SSA_ERR_WORKSPACE, "workspace has %zu bytes; %zu needed", ws_bytes, L->total);
+  return SSA_OK;
+}
+
+ssa_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssa_workspace_bytes(const ssa_problem* p) {
+  Problem P;
+  if (build(p, &P) != SSA_OK) return 0;
+  return layout_of(P).total;
+}
+
+ssa_status ssa_pool_blocks(const ssa_problem* p, const void* x, int32_t H, float* pooled,
+                           void* stream) {
+  Problem P;
+  ssa_status s = build(p, &P);
+  if (s != SSA_OK) return s;
+  if (x == nullptr || pooled == nullptr) return fail(SSA_ERR_INVALID_ARG, "x or pooled is NULL");
+  if (H <= 0) return fail(SSA_ERR_INVALID_ARG, "H must be positive; got %d", H);
+  const long nblk = (long)P.d.B * H * P.d.nKB;
+  return hip_status(ssa::launch_pool(x, P.bf16, pooled, nblk, ssa::kBlock, P.d.D,
+                                     (hipStream_t)stream), "pool");
+}
+
+ssa_status ssa_select_blocks(const ssa_problem* p, const void* q, const void* k,
+                             const float* k_pooled, int32_t* idx, int32_t* cnt, void* ws,
+                             size_t ws_bytes, void* stream) {
+  Problem P;
+  ssa_status s = build(p, &P);
+  if (s != SSA_OK) return s;
+  if (q == nullptr || idx == nullptr || cnt == nullptr)
+    return fail(SSA_ERR_INVALID_ARG, "q, idx or cnt is NULL");
+  if (k == nullptr && k_pooled == nullptr)
+    return fail(SSA_ERR_INVALID_ARG, "one of k and k_pooled must be given");
+  Layout L;
+  if ((s = check_ws(P, ws, ws_bytes, &L)) != SSA_OK) return s;
+  const ssa::Dims& d = P.d;
+  hipStream_t st = (hipStream_t)stream;
+  char* w = (char*)ws;
+  float* qbar = (float*)(w + L.qbar);
+  hipError_t e;
+  if (P.decode)  // the query is its own block representation
+    e = ssa::launch_pool(q, P.bf16, qbar, (long)d.B * d.Hq, 1, d.D, st);
+  else
+    e = ssa::launch_pool(q, P.bf16, qbar, (long)d.B * d.Hq * d.nQB, ssa::kBlock, d.D, st);
+  if (e != hipSuccess) return hip_status(e, "pool q");
+  const float* kbar = k_pooled;
+  if (kbar == nullptr) {
+    float* kb = (float*)(w + L.kbar);
+    e = ssa::launch_pool(k, P.bf16, kb, (long)d.B * d.Hkv * d.nKB, ssa::kBlock, d.D, st);
+    if (e != hipSuccess) return hip_status(e, "pool k");
+    kbar = kb;
+  }
+  return hip_status(ssa::launch_select(qbar, kbar, idx, cnt, d, P.hm, st), "select");
+}
+
+ssa_status ssa_attn_fwd(const ssa_problem* p, const void* q, const void* k, const void* v,
+                        const int32_t* idx, const int32_t* cnt, void* h_full, void* h_sparse,
+                        float* delta, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Problem P;
+  ssa_status s = build(p, &P);
+  if (s != SSA_OK) return s;
+  if (q == nullptr || k == nullptr || v == nullptr || idx == nullptr || cnt == nullptr)
+    return fail(SSA_ERR_INVALID_ARG, "q, k, v, idx or cnt is NULL");
+  if (h_sparse == nullptr) return fail(SSA_ERR_INVALID_ARG, "h_sparse is NULL");
+  if (h_full == nullptr && delta != nullptr)
+    return fail(SSA_ERR_INVALID_ARG, "delta needs h_full (sparse-only mode has no dropped mass)");
+  Layout L;
+  if ((s = check_ws(P, ws, ws_bytes, &L)) != SSA_OK) return s;
+  const ssa::Dims& d = P.d;
+  hipStream_t st = (hipStream_t)stream;
+  char* w = (char*)ws;
+  if (!P.bf16)
+    return hip_status(ssa::launch_attn_rows_f32((const float*)q, (const float*)k, (const float*)v,
+                                                idx, cnt, (float*)h_full, (float*)h_sparse, delta,
+                                                lse, d, P.hm, st), "attention (f32)");
+  if (P.decode)
+    return hip_status(ssa::launch_attn_decode_bf16((const uint16_t*)q, (const uint16_t*)k,
+                                                   (const uint16_t*)v, idx, cnt,
+                                                   (uint16_t*)h_full, (uint16_t*)h_sparse, delta,
+                                                   lse, (float*)(w + L.partials), d, P.hm, st),
+                      "attention (decode)");
+  uint16_t* vt = (uint16_t*)(w + L.vt);
+  hipError_t e = ssa::launch_transpose((const uint16_t*)v, vt, d.B * d.Hkv, d.Nk, d.D, st);
+  if (e != hipSuccess) return hip_status(e, "transpose v");
+  return hip_status(ssa::launch_attn_prefill_bf16((const uint16_t*)q, (const uint16_t*)k, vt, idx,
+                                                  cnt, (uint16_t*)h_full, (uint16_t*)h_sparse,
+                                                  delta, lse, d, P.hm, st),
+                    "attention (prefill)");
+}
+
+ssa_status ssa_align_loss(const ssa_problem* p, const void* h_full, const void* h_sparse,
+                          float* loss, void* grad_full, void* grad_sparse, void* ws,
+                          size_t ws_bytes, void* stream) {
+  Problem P;
+  ssa_status s = build(p, &P);
+  if (s != SSA_OK) return s;
+  if (h_full == nullptr || h_sparse == nullptr || loss == nullptr)
+    return fail(SSA_ERR_INVALID_ARG, "h_full, h_sparse or loss is NULL");
+  Layout L;
+  if ((s = check_ws(P, ws, ws_bytes, &L)) != SSA_OK) return s;
+  const long n = (long)P.d.B * P.d.Hq * P.d.Nq * P.d.D;
+  return hip_status(ssa::launch_align_loss(h_full, h_sparse, P.bf16, n, loss, grad_full,
+                                           grad_sparse, (double*)((char*)ws + L.loss),
+                                           (hipStream_t)stream),
+                    "align loss");
+}
+
+const char* ssa_status_string(ssa_status s) {
+  switch (s) {
+    case SSA_OK: return "SSA_OK";
+    case SSA_ERR_INVALID_ARG: return "SSA_ERR_INVALID_ARG";
+    case SSA_ERR_UNSUPPORTED: return "SSA_ERR_UNSUPPORTED";
+    case SSA_ERR_WORKSPACE: return "SSA_ERR_WORKSPACE";
+    case SSA_ERR_HIP: return "SSA_ERR_HIP";
+  }
+  return "SSA_ERR_UNKNOWN";
+}
+
+const char* ssa_last_error_message(void) { return g_err; }
+
+}  // extern "C"

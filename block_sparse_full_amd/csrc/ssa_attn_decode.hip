@@ -1,0 +1,380 @@
+// Single-query (decode) dual-stream attention, bf16, split over the KV
+// length, and the merge of the partial results.
+//
+// Method: the same two streams and dropped mass as the prefill kernel
+// ("SSA: Achieving Sparser Attention by Aligning Full and Sparse Attention
+// Outputs in Feature Space", sections "SSA's Dual-Stream Training Mechanism"
+// and "Practical Implementation of SSA"; "Technische Samenvatting: SSA",
+// "2. Methodologie") for one query per (sequence, q head) at the last
+// position, as in generation with either inference mode ("SSA: Sparse Sparse
+// Attention", "Inference with Sparse or Full Mode").
+//
+// Decode reads each K/V byte once, so it is bound by HBM bandwidth. A
+// workgroup owns one (b, kv head) and a range of key blocks; the q heads of
+// that kv head (the GQA group) all use every K/V load. Per head it keeps the
+// running max m, l_sel / l_drop and two accumulators: acc_full over every key
+// and acc_sel over the head's selected blocks only (a block's PV goes into
+// acc_sel in addition only when that head selected it, so the extra work is
+// proportional to the budget). Dual mode walks every block; sparse-only mode
+// walks only the union of the group's selected blocks and skips acc_full.
+#include "ssa_common.h"
+#include "ssa_kernels.h"
+
+namespace ssa {
+
+__device__ __forceinline__ float dexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Bit kb of head n in the selection bitmap.
+__device__ __forceinline__ bool sel_bit(const unsigned* bits, int words, int n, int kb) {
+  return (bits[n * words + (kb >> 5)] >> (kb & 31)) & 1u;
+}
+
+template <int D, int GP>
+struct DecLayout {
+  static constexpr int LPR = D / 8;        // lanes per K/V row in the PV layout
+  static constexpr int RPI = 64 / LPR;     // rows per load instruction
+  static constexpr int KPL = kBlock / RPI; // keys per lane per block
+  static constexpr int NKS = D / 32;       // k-steps of the 16x16x32 MFMA
+};
+
+// partial layout per (b, q head, split): m (log2 units), l_sel, l_drop, 0,
+// acc_full[D], acc_sel[D].
+template <int D, int GP>
+__global__ __launch_bounds__(256) void attn_decode_bf16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const int* __restrict__ idx, const int* __restrict__ cnt,
+    float* __restrict__ partials, Dims d, HeadMap hm, int sparse_only, int nsplit) {
+  using L = DecLayout<D, GP>;
+  constexpr int PF = 2 * D + 4;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int words = (d.nKB + 31) >> 5;
+  unsigned* bits = (unsigned*)smem;                          // [GP][words] selection bitmaps
+  int* ulist = (int*)(bits + GP * words);                    // [nKB] union list (sparse-only)
+  float* ps = (float*)(ulist + d.nKB);                       // [kDecWaves][kBlock][GP]
+  float* als = ps + kDecWaves * kBlock * GP;                 // [kDecWaves][GP]
+  float* red = als + kDecWaves * GP;                         // [kDecWaves][GP][PF]
+  __shared__ int s_nunion;
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = d.G;
+  const float sl2 = d.scale_log2;
+
+  // ---- selection bitmaps of the group's heads
+  for (int i = tid; i < GP * words; i += 256) bits[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < G * d.budget; i += 256) {
+    const int n = i / d.budget, e = i - n * d.budget;
+    const int h = hm.q_of_kv[g * G + n];
+    const int c = cnt[b * d.Hq + h];
+    const int kb = idx[(size_t)(b * d.Hq + h) * d.budget + e];
+    if (e < c && kb >= 0 && kb < d.nKB) atomicOr(&bits[n * words + (kb >> 5)], 1u << (kb & 31));
+  }
+  __syncthreads();
+
+  // ---- the blocks this workgroup walks
+  int blk_begin, blk_count, blk_stride;
+  if (sparse_only) {
+    if (tid == 0) {
+      int nu = 0;
+      for (int w = 0; w < words; ++w) {
+        unsigned u = 0u;
+        for (int n = 0; n < G; ++n) u |= bits[n * words + w];
+        while (u) {
+          const int bit = __ffs(u) - 1;
+          u &= u - 1u;
+          ulist[nu++] = w * 32 + bit;
+        }
+      }
+      s_nunion = nu;
+    }
+    __syncthreads();
+    const int nu = s_nunion;
+    const int per = (nu + nsplit - 1) / nsplit;
+    blk_begin = split * per;
+    blk_count = max(0, min(per, nu - blk_begin));
+    blk_stride = kDecWaves;  // wave w takes entries w, w+4, ...
+  } else {
+    blk_begin = split * kDecWaves * kDecWaveBlocks;
+    blk_count = max(0, min(kDecWaves * kDecWaveBlocks, d.nKB - blk_begin));
+    blk_stride = kDecWaves;
+  }
+
+  // ---- per-lane state
+  // QK^T layout (16x16x32): lane column n = lane & 15 is head n; rows
+  // 4*(lane>>4) + r of key tile kt are its keys.
+  const int n_col = lane & 15;
+  const int kgrp = lane >> 4;
+  bf16x8_t qf[L::NKS];
+  {
+    const bool valid = n_col < G;
+    const int h = valid ? hm.q_of_kv[g * G + n_col] : 0;
+    const uint16_t* qp = Q + (size_t)(b * d.Hq + h) * D + 8 * kgrp;
+#pragma unroll
+    for (int ks = 0; ks < L::NKS; ++ks) {
+      bf16x8_t v = *(const bf16x8_t*)(qp + 32 * ks);
+      if (!valid) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = static_cast<__bf16>(0.f);
+      }
+      qf[ks] = v;
+    }
+  }
+  float m_run = -INFINITY, l_sel = 0.f, l_drop = 0.f;  // of head n_col (lane partials)
+  // PV layout: lane owns d = 8*(lane % LPR) .. +7 and keys RPI*i + lane / LPR.
+  const int pv_d0 = 8 * (lane % L::LPR);
+  const int pv_k0 = lane / L::LPR;
+  float acc_full[GP][8], acc_sel[GP][8];
+#pragma unroll
+  for (int n = 0; n < GP; ++n)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { acc_full[n][e] = 0.f; acc_sel[n][e] = 0.f; }
+
+  float* wps = ps + wave * kBlock * GP;
+  float* wal = als + wave * GP;
+  const uint16_t* kbase = K + ((size_t)(b * d.Hkv + g) * d.Nk) * D;
+  const uint16_t* vbase = V + ((size_t)(b * d.Hkv + g) * d.Nk) * D;
+
+  for (int it = wave; it < blk_count; it += blk_stride) {
+    const int kb = sparse_only ? ulist[blk_begin + it] : blk_begin + it;
+    const uint16_t* kg = kbase + (size_t)kb * kBlock * D;
+    const uint16_t* vg = vbase + (size_t)kb * kBlock * D;
+    // V rows for the PV step (independent of QK^T: issued first).
+    uint4 vr[L::KPL];
+#pragma unroll
+    for (int i = 0; i < L::KPL; ++i)
+      vr[i] = *(const uint4*)(vg + (size_t)(L::RPI * i + pv_k0) * D + pv_d0);
+    // S^T = K q^T: 4 key tiles of 16.
+    f32x4_t s[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < L::NKS; ++ks) {
+        const bf16x8_t a =
+            *(const bf16x8_t*)(kg + (size_t)(16 * kt + n_col) * D + 32 * ks + 8 * kgrp);
+        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], s[kt], 0, 0, 0);
+      }
+    }
+    // Softmax statistics of head n_col over this block.
+    const bool mine = n_col < G && sel_bit(bits, words, n_col, kb);
+    const bool active = !sparse_only || mine;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = active ? s[kt][r] * sl2 : -INFINITY;
+        s[kt][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const bool live = m_new != -INFINITY;
+    const float alpha = live ? dexp2(m_run - m_new) : 1.f;
+    m_run = m_new;
+    float lsum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = live ? dexp2(s[kt][r] - m_new) : 0.f;
+        lsum += p;
+        if (n_col < GP) wps[(16 * kt + 4 * kgrp + r) * GP + n_col] = p;
+      }
+    l_sel *= alpha;
+    l_drop *= alpha;
+    if (mine) l_sel += lsum; else l_drop += lsum;
+    if (lane < GP) wal[lane] = alpha;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    // PV on the VALU: rescale, then accumulate this lane's keys.
+    float al[GP];
+#pragma unroll
+    for (int n = 0; n < GP; ++n) al[n] = wal[n];
+#pragma unroll
+    for (int n = 0; n < GP; ++n)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { acc_full[n][e] *= al[n]; acc_sel[n][e] *= al[n]; }
+    bool hsel[GP];
+#pragma unroll
+    for (int n = 0; n < GP; ++n) hsel[n] = n < G && sel_bit(bits, words, n, kb);
+#pragma unroll
+    for (int i = 0; i < L::KPL; ++i) {
+      const int key = L::RPI * i + pv_k0;
+      const unsigned w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+      float vv[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vv[2 * e] = __uint_as_float(w[e] << 16);
+        vv[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      }
+      float p[GP];
+#pragma unroll
+      for (int n = 0; n < GP; ++n) p[n] = wps[key * GP + n];
+      if (!sparse_only) {
+#pragma unroll
+        for (int n = 0; n < GP; ++n)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc_full[n][e] = fmaf(p[n], vv[e], acc_full[n][e]);
+      }
+#pragma unroll
+      for (int n = 0; n < GP; ++n) {
+        if (hsel[n]) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc_sel[n][e] = fmaf(p[n], vv[e], acc_sel[n][e]);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  }
+
+  // ---- reduce lane partials inside the wave
+  l_sel += __shfl_xor(l_sel, 16);
+  l_sel += __shfl_xor(l_sel, 32);
+  l_drop += __shfl_xor(l_drop, 16);
+  l_drop += __shfl_xor(l_drop, 32);
+#pragma unroll
+  for (int n = 0; n < GP; ++n)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float a = acc_full[n][e], c = acc_sel[n][e];
+#pragma unroll
+      for (int off = L::LPR; off < 64; off <<= 1) {
+        a += __shfl_xor(a, off);
+        c += __shfl_xor(c, off);
+      }
+      acc_full[n][e] = a;
+      acc_sel[n][e] = c;
+    }
+  float* wred = red + wave * GP * PF;
+  if (lane < GP) {
+    wred[lane * PF + 0] = m_run;
+    wred[lane * PF + 1] = l_sel;
+    wred[lane * PF + 2] = l_drop;
+  }
+  if (lane < L::LPR) {
+#pragma unroll
+    for (int n = 0; n < GP; ++n)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        wred[n * PF + 4 + pv_d0 + e] = acc_full[n][e];
+        wred[n * PF + 4 + D + pv_d0 + e] = acc_sel[n][e];
+      }
+  }
+  __syncthreads();
+
+  // ---- merge the waves, write this split's partial for every head
+  for (int i = tid; i < G * (D + 1); i += 256) {
+    const int n = i / (D + 1), j = i - n * (D + 1);
+    float M = -INFINITY;
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, red[(w * GP + n) * PF]);
+    const int h = hm.q_of_kv[g * G + n];
+    float* out = partials + ((size_t)(b * d.Hq + h) * nsplit + split) * PF;
+    if (j == D) {
+      float ls = 0.f, ld = 0.f;
+      if (M != -INFINITY)
+        for (int w = 0; w < kDecWaves; ++w) {
+          const float* r = red + (w * GP + n) * PF;
+          const float f = dexp2(r[0] - M);
+          ls += f * r[1];
+          ld += f * r[2];
+        }
+      out[0] = M;
+      out[1] = ls;
+      out[2] = ld;
+      out[3] = 0.f;
+    } else {
+      float af = 0.f, as = 0.f;
+      if (M != -INFINITY)
+        for (int w = 0; w < kDecWaves; ++w) {
+          const float* r = red + (w * GP + n) * PF;
+          const float f = dexp2(r[0] - M);
+          af += f * r[4 + j];
+          as += f * r[4 + D + j];
+        }
+      out[4 + j] = af;
+      out[4 + D + j] = as;
+    }
+  }
+}
+
+// One workgroup of D threads per (b, q head): combine the splits.
+__global__ __launch_bounds__(128) void decode_merge_kernel(
+    const float* __restrict__ partials, uint16_t* __restrict__ Hf, uint16_t* __restrict__ Hs,
+    float* __restrict__ delta, float* __restrict__ lse, int D, int nsplit, int sparse_only,
+    size_t plane) {
+  const int bh = blockIdx.x;
+  const int j = threadIdx.x;
+  const int PF = 2 * D + 4;
+  const float* pp = partials + (size_t)bh * nsplit * PF;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pp[s * PF]);
+  float ls = 0.f, ld = 0.f, af = 0.f, as = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float* r = pp + s * PF;
+    if (r[0] == -INFINITY) continue;
+    const float f = dexp2(r[0] - M);
+    ls += f * r[1];
+    ld += f * r[2];
+    if (j < D) {
+      af += f * r[4 + j];
+      as += f * r[4 + D + j];
+    }
+  }
+  if (j < D) {
+    Hs[(size_t)bh * D + j] = f32_to_bf16(as / ls);
+    if (!sparse_only) Hf[(size_t)bh * D + j] = f32_to_bf16(af / (ls + ld));
+  }
+  if (j == 0) {
+    if (!sparse_only && delta != nullptr) delta[bh] = ld / (ls + ld);
+    if (lse != nullptr) {
+      lse[plane + bh] = (M + __log2f(ls)) * kLn2;
+      if (!sparse_only) lse[bh] = (M + __log2f(ls + ld)) * kLn2;
+    }
+  }
+}
+
+template <int D, int GP>
+static hipError_t launch_dec(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const int* idx, const int* cnt, float* partials, const Dims& d,
+                             const HeadMap& hm, int sparse_only, int nsplit, hipStream_t stream) {
+  const int words = (d.nKB + 31) >> 5;
+  const size_t smem = (size_t)GP * words * 4 + (size_t)d.nKB * 4 +
+                      (size_t)kDecWaves * kBlock * GP * 4 + (size_t)kDecWaves * GP * 4 +
+                      (size_t)kDecWaves * GP * (2 * D + 4) * 4;
+  hipLaunchKernelGGL((attn_decode_bf16_kernel<D, GP>), dim3(nsplit, d.Hkv, d.B), dim3(256), smem,
+                     stream, q, k, v, idx, cnt, partials, d, hm, sparse_only, nsplit);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_dec_g(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const int* idx, const int* cnt, float* partials, const Dims& d,
+                               const HeadMap& hm, int sparse_only, int nsplit,
+                               hipStream_t stream) {
+  if (d.G <= 1) return launch_dec<D, 1>(q, k, v, idx, cnt, partials, d, hm, sparse_only, nsplit, stream);
+  if (d.G <= 2) return launch_dec<D, 2>(q, k, v, idx, cnt, partials, d, hm, sparse_only, nsplit, stream);
+  if (d.G <= 4) return launch_dec<D, 4>(q, k, v, idx, cnt, partials, d, hm, sparse_only, nsplit, stream);
+  return launch_dec<D, 8>(q, k, v, idx, cnt, partials, d, hm, sparse_only, nsplit, stream);
+}
+
+hipError_t launch_attn_decode_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const int* idx, const int* cnt, uint16_t* hf, uint16_t* hs,
+                                   float* delta, float* lse, float* partials, const Dims& d,
+                                   const HeadMap& hm, hipStream_t stream) {
+  const int sparse_only = hf == nullptr ? 1 : 0;
+  const int nsplit = sparse_only ? kDecSparseParts : decode_splits(d.nKB);
+  hipError_t e = d.D == 128
+                     ? launch_dec_g<128>(q, k, v, idx, cnt, partials, d, hm, sparse_only, nsplit, stream)
+                     : launch_dec_g<64>(q, k, v, idx, cnt, partials, d, hm, sparse_only, nsplit, stream);
+  if (e != hipSuccess) return e;
+  const size_t plane = (size_t)d.B * d.Hq;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(d.B * d.Hq), dim3(d.D), 0, stream, partials, hf,
+                     hs, delta, lse, d.D, nsplit, sparse_only, plane);
+  return hipGetLastError();
+}
+
+}  // namespace ssa

@@ -1,0 +1,50 @@
+// Host-side launchers of the SSA kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ssa_common.h"
+
+namespace ssa {
+
+constexpr int kMaxKeyBlocks = 4096;        // Nk <= 262144 tokens
+constexpr size_t kSelKeyBytes = 32 * 1024; // LDS for the selection keys
+
+// Decode split-KV geometry: each wave walks kDecWaveBlocks key blocks, a
+// workgroup has kDecWaves waves.
+constexpr int kDecWaves = 4;
+constexpr int kDecWaveBlocks = 8;
+constexpr int kDecSparseParts = 4;         // workgroups per (b, kv head), sparse-only
+constexpr int kDecMaxGroup = 8;            // q heads per kv head in bf16 decode
+
+inline int decode_splits(int nKB) {        // partial results per (b, q head), dual mode
+  const int per_wg = kDecWaves * kDecWaveBlocks;
+  return (nKB + per_wg - 1) / per_wg;
+}
+inline int decode_partial_floats(int D) { return 2 * D + 4; }
+
+hipError_t launch_pool(const void* x, bool bf16, float* out, long nblk_total, int bs, int D,
+                       hipStream_t stream);
+hipError_t launch_select(const float* qbar, const float* kbar, int* idx, int* cnt,
+                         const Dims& d, const HeadMap& hm, hipStream_t stream);
+hipError_t launch_transpose(const uint16_t* v, uint16_t* vt, int BH, int N, int D,
+                            hipStream_t stream);
+
+hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* vt,
+                                    const int* idx, const int* cnt, uint16_t* hf, uint16_t* hs,
+                                    float* delta, float* lse, const Dims& d, const HeadMap& hm,
+                                    hipStream_t stream);
+hipError_t launch_attn_rows_f32(const float* q, const float* k, const float* v, const int* idx,
+                                const int* cnt, float* hf, float* hs, float* delta, float* lse,
+                                const Dims& d, const HeadMap& hm, hipStream_t stream);
+hipError_t launch_attn_decode_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const int* idx, const int* cnt, uint16_t* hf, uint16_t* hs,
+                                   float* delta, float* lse, float* partials, const Dims& d,
+                                   const HeadMap& hm, hipStream_t stream);
+hipError_t launch_align_loss(const void* hf, const void* hs, bool bf16, long n, float* loss,
+                             void* gf, void* gs, double* partials, hipStream_t stream);
+constexpr int kLossPartials = 1024;
+
+}  // namespace ssa

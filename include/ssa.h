@@ -1,0 +1,166 @@
+/*
+ * ssa.h - C ABI of the SSA dual-stream block-sparse attention forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (the method is described on the pages on SSA,
+ * "Sparse Sparse Attention"):
+ *   - "SSA: Achieving Sparser Attention by Aligning Full and Sparse Attention
+ *     Outputs in Feature Space" (xugj520.cn), section "Practical
+ *     Implementation of SSA": the sequence is cut into blocks, each block is
+ *     mean-pooled, the query is scored against the earlier block
+ *     representations, the top-k blocks are kept and attention runs over
+ *     their tokens only;
+ *   - same page, "SSA's Dual-Stream Training Mechanism" and "Bidirectional
+ *     Attention Alignment": a full and a sparse attention stream per layer,
+ *     compared by the sparsity loss ||a_full - sg[a_sparse]|| and the
+ *     commitment loss ||a_sparse - sg[a_full]||;
+ *   - "Technische Samenvatting: SSA (Sparse Sparse Attention)"
+ *     (gist.science), "2. Methodologie": the counterpart output per layer and
+ *     the dropped attention mass delta(t).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major, on the device: Q [B,Hq,Nq,D],
+ *     K and V [B,Hkv,Nk,D], outputs [B,Hq,Nq,D]. Query i sits at key
+ *     position Nk - Nq + i. Prefill has Nq == Nk; decode has Nq == 1.
+ *   - Element type: SSA_BF16 (bfloat16) or SSA_F32 for Q, K, V and the two
+ *     attention outputs. delta, lse, pooled vectors and losses are float32.
+ *   - Supported (else SSA_ERR_UNSUPPORTED): D in {64, 128}; block_size 64;
+ *     Nk a multiple of 64; Nq in {Nk, 1}; Hq <= 256; Hq/Hkv <= 16.
+ *   - Ownership: the caller owns every buffer; the library never allocates
+ *     device or host memory. Scratch memory is the caller's workspace of
+ *     ssa_workspace_bytes() bytes (device memory, 256-byte aligned).
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ *     stream). Every call only enqueues kernels on it and returns without
+ *     synchronising. Calls are reentrant; calls that share a workspace must
+ *     be ordered on one stream.
+ *   - Errors: all validation happens on the host before any launch; a
+ *     failing call enqueues nothing (except SSA_ERR_HIP, reported from the
+ *     launch itself). No call aborts or throws. ssa_last_error_message()
+ *     gives the thread's last error text. Non-finite inputs give unspecified
+ *     outputs (they are not checked).
+ */
+#ifndef SSA_H
+#define SSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSA_OK = 0,
+  SSA_ERR_INVALID_ARG = 1,  /* null pointer, inconsistent shape or head map,
+                               budget below the forced blocks, sizes <= 0 */
+  SSA_ERR_UNSUPPORTED = 2,  /* a valid problem outside the supported set */
+  SSA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than needed */
+  SSA_ERR_HIP = 4           /* a HIP runtime error while launching */
+} ssa_status;
+
+typedef enum { SSA_F32 = 0, SSA_BF16 = 1 } ssa_dtype;
+
+/* One attention problem (one layer's attention of one batch).
+ *   B, Hq, Hkv : batch, query heads, key/value heads (Hq % Hkv == 0)
+ *   Nq, Nk     : query rows and key positions per head
+ *   D          : head dimension
+ *   block_size : tokens per key block and query rows per query block
+ *   budget     : selected key blocks per row, forced blocks included
+ *   n_sink     : leading blocks always kept ("sink")
+ *   n_local    : blocks ending at the query's own block always kept ("local")
+ *   scale      : attention logit scale; 0 means 1/sqrt(D)
+ *   dtype      : ssa_dtype of Q, K, V and the attention outputs
+ *   head_map   : host array [Hq] giving the kv head of each q head, or NULL
+ *                for h / (Hq/Hkv); every kv head must receive exactly Hq/Hkv
+ *                q heads. Read during the call only. */
+typedef struct {
+  int32_t B, Hq, Hkv, Nq, Nk, D, block_size, budget, n_sink, n_local;
+  float scale;
+  int32_t dtype;
+  const int32_t* head_map;
+} ssa_problem;
+
+/* Device workspace bytes needed by every call below for problem p (the
+ * largest of their needs, so one workspace serves them all). Returns 0 when
+ * p is invalid or unsupported. */
+size_t ssa_workspace_bytes(const ssa_problem* p);
+
+/* Block mean-pool ("Practical Implementation of SSA": mean pooling of each
+ * block). x is [B, H, N, D] of p->dtype on the device (N = p->Nk);
+ * pooled is [B, H, N/block_size, D] float32: per block and d, the float64
+ * sum of the block's tokens in ascending order, divided by block_size,
+ * rounded once to float32. Used by decode callers to keep the pooled-key
+ * table of a KV cache; H is the head count of x. */
+ssa_status ssa_pool_blocks(const ssa_problem* p, const void* x, int32_t H,
+                           float* pooled, void* stream);
+
+/* Block selection ("Practical Implementation of SSA": similarity with every
+ * earlier block representation, top-k most relevant blocks).
+ *   q        : [B,Hq,Nq,D] device, p->dtype
+ *   k        : [B,Hkv,Nk,D] device, p->dtype; may be NULL when k_pooled is
+ *              given
+ *   k_pooled : [B,Hkv,Nk/block_size,D] float32 device from ssa_pool_blocks,
+ *              or NULL to pool k here
+ *   idx      : out [B,Hq,nQB,budget] int32, nQB = Nq/block_size (prefill) or
+ *              1 (decode); the selected key blocks of each (b, h, query
+ *              block) in ascending order, padded with -1
+ *   cnt      : out [B,Hq,nQB] int32, the number of valid idx entries
+ * The query block's representation is its mean-pooled Q (decode: the query
+ * itself). Scores are float64 dot products of the float32 pooled vectors,
+ * summed over d in ascending order, unscaled. Forced blocks (the first
+ * n_sink blocks and the n_local blocks ending at the query's own block) are
+ * always kept; the remaining budget goes to the best-scoring causal blocks,
+ * exact ties to the lower block index; when no more candidates than free
+ * slots remain every causal block is kept. */
+ssa_status ssa_select_blocks(const ssa_problem* p, const void* q, const void* k,
+                             const float* k_pooled, int32_t* idx, int32_t* cnt,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Dual-stream attention forward ("SSA's Dual-Stream Training Mechanism":
+ * full stream over every causal key; "Practical Implementation of SSA":
+ * sparse stream over the tokens of the selected blocks; "2. Methodologie":
+ * the counterpart output and the dropped mass).
+ *   q, k, v  : device inputs as above; idx, cnt from ssa_select_blocks
+ *   h_full   : out [B,Hq,Nq,D] p->dtype: softmax(scale q k^T) v over keys
+ *              j <= position of the query; NULL selects sparse-only mode
+ *              (only the selected blocks are read)
+ *   h_sparse : out [B,Hq,Nq,D] p->dtype: the same with the softmax taken
+ *              over the causal keys of the selected blocks only (required)
+ *   delta    : out [B,Hq,Nq] float32 or NULL: full-softmax mass on causal
+ *              keys outside the selected blocks (must be NULL when h_full is)
+ *   lse      : out [2,B,Hq,Nq] float32 or NULL: natural-log log-sum-exp of
+ *              the scaled logits of the full (plane 0) and sparse (plane 1)
+ *              streams; plane 0 is left untouched in sparse-only mode
+ * The float32 accumulators are rounded once to the output type. */
+ssa_status ssa_attn_fwd(const ssa_problem* p, const void* q, const void* k,
+                        const void* v, const int32_t* idx, const int32_t* cnt,
+                        void* h_full, void* h_sparse, float* delta, float* lse,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Alignment losses ("Bidirectional Attention Alignment"), read as mean
+ * squared errors over all B*Hq*Nq*D elements.
+ *   h_full, h_sparse : device inputs [B,Hq,Nq,D] p->dtype
+ *   loss             : out device float32[2] = {L_sparsity, L_commitment};
+ *                      both forward values are mean((h_full - h_sparse)^2),
+ *                      reduced deterministically from float64 partials
+ *   grad_full        : out [B,Hq,Nq,D] p->dtype or NULL:
+ *                      dL_sparsity/dh_full = 2 (h_full - h_sparse) / n
+ *   grad_sparse      : out [B,Hq,Nq,D] p->dtype or NULL:
+ *                      dL_commitment/dh_sparse = 2 (h_sparse - h_full) / n
+ * (the stop-gradient side of each loss receives no gradient). */
+ssa_status ssa_align_loss(const ssa_problem* p, const void* h_full,
+                          const void* h_sparse, float* loss, void* grad_full,
+                          void* grad_sparse, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* Static text of a status code. */
+const char* ssa_status_string(ssa_status s);
+
+/* Text of the calling thread's last error (empty if none). */
+const char* ssa_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSA_H */

@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/ssa.h declares, and rejects invalid problems with the
+documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from block_sparse_full_amd import ssa
+    if not os.path.exists(ssa.lib_path()):
+        from block_sparse_full_amd.build import build_library
+        build_library()
+    return ssa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("ssa_select_blocks", "ssa_attn_fwd", "ssa_align_loss", "ssa_pool_blocks",
+              "ssa_workspace_bytes", "ssa_status_string", "ssa_last_error_message"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in ssa.h but not exported"
+
+
+def _p(**kw):
+    from block_sparse_full_amd.ssa import Problem
+    base = dict(B=1, Hq=8, Hkv=2, Nq=4096, Nk=4096, D=128, budget=16)
+    base.update(kw)
+    return Problem(**base)
+
+
+def _status_of(lib, prob, fn="ssa_select_blocks"):
+    c, keep = prob.to_c()
+    if fn == "ssa_select_blocks":
+        return lib.ssa_select_blocks(ctypes.byref(c), 16, 16, None, 16, 16, None, 0, None)
+    if fn == "ssa_attn_fwd":
+        return lib.ssa_attn_fwd(ctypes.byref(c), 16, 16, 16, 16, 16, 16, 16, None, None, None, 0, None)
+    raise ValueError(fn)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 1), (dict(Hq=0), 1), (dict(budget=0), 1), (dict(n_sink=-1), 1),
+    (dict(Hq=8, Hkv=3), 1), (dict(budget=1, n_sink=1, n_local=1), 1),
+    (dict(head_map=[0, 0, 0, 0, 0, 1, 1, 1]), 1), (dict(head_map=[0, 1, 2, 0, 1, 0, 1, 0]), 1),
+    (dict(D=96), 2), (dict(block_size=32), 2), (dict(Nk=4000, Nq=4000), 2),
+    (dict(Nq=7), 2), (dict(dtype=5), 2), (dict(Hq=64, Hkv=2), 2), (dict(scale=-1.0), 1),
+    (dict(Nq=1, Nk=4096, Hq=32, Hkv=2), 2),        # bf16 decode with 16 q heads per kv head
+    (dict(), 3),                                    # valid problem, no workspace
+])
+def test_invalid_problems_are_rejected(lib, kw, status):
+    st = _status_of(lib, _p(**kw))
+    assert st == status, (kw, st, lib.ssa_last_error_message())
+    assert lib.ssa_last_error_message()  # a reason is given
+
+
+def test_null_pointers(lib):
+    c, keep = _p().to_c()
+    assert lib.ssa_select_blocks(ctypes.byref(c), None, 16, None, 16, 16, None, 0, None) == 1
+    assert lib.ssa_select_blocks(ctypes.byref(c), 16, None, None, 16, 16, None, 0, None) == 1
+    assert lib.ssa_attn_fwd(ctypes.byref(c), 16, 16, 16, 16, 16, 16, None, None, None, None, 0, None) == 1
+    # delta without h_full (sparse-only mode has no dropped mass)
+    assert lib.ssa_attn_fwd(ctypes.byref(c), 16, 16, 16, 16, 16, None, 16, 16, None, None, 0, None) == 1
+    assert lib.ssa_align_loss(ctypes.byref(c), None, 16, 16, None, None, None, 0, None) == 1
+    assert lib.ssa_pool_blocks(ctypes.byref(c), None, 2, 16, None) == 1
+    assert lib.ssa_pool_blocks(ctypes.byref(c), 16, 0, 16, None) == 1
+    assert lib.ssa_select_blocks(None, 16, 16, None, 16, 16, None, 0, None) == 1
+
+
+def test_workspace_checks(lib):
+    from block_sparse_full_amd.ssa import workspace_bytes
+    p = _p()
+    need = workspace_bytes(p)
+    # pooled Q + pooled K + transposed V + loss partials, each 256-byte aligned
+    expect = 8 * 64 * 128 * 4 + 2 * 64 * 128 * 4 + 2 * 128 * 4096 * 2 + 1024 * 8
+    assert need == expect
+    c, keep = p.to_c()
+    st = lib.ssa_align_loss(ctypes.byref(c), 16, 16, 16, None, None, 4096, need - 256, None)
+    assert st == 3
+    st = lib.ssa_align_loss(ctypes.byref(c), 16, 16, 16, None, None, 4096 + 8, need, None)
+    assert st == 3  # not 256-byte aligned
+    bad = _p(D=96)
+    c2, keep2 = bad.to_c()
+    assert lib.ssa_workspace_bytes(ctypes.byref(c2)) == 0
+
+
+def test_status_strings(lib):
+    assert lib.ssa_status_string(0) == b"SSA_OK"
+    assert lib.ssa_status_string(3) == b"SSA_ERR_WORKSPACE"
+    assert lib.ssa_status_string(99) == b"SSA_ERR_UNKNOWN"

@@ -1,0 +1,330 @@
+"""Benchmark of the SSA dual-stream attention forward on one MI355X.
+
+A step is one pass of the prefill hot path over the 32K-context GQA workload
+(batch 1, 32 q heads / 8 kv heads, N = 32768, D = 128, block 64, budget 16
+blocks including the sink and local blocks, planted peaked key blocks):
+block pooling + top-k selection, the fused dual-stream attention (h_full,
+h_sparse, delta) and the alignment losses. `value` is the algorithmic MFMA
+work of the full causal stream, 4*D*64*64 FLOP per (query block, causal key
+block) pair (the sparse stream adds none), divided by the step time.
+
+The same run also times the single-query decode path (64 sequences x 32/8
+heads, KV length 65536, budget 32) in dual and sparse-only mode, reported in
+GB/s of algorithmic HBM bytes, and the fp64 CPU oracle on a bounded sample of
+the prefill workload (the `cpu_baseline` object).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_flops(cfg) -> float:
+    nkb = cfg.N // cfg.block
+    pairs = nkb * (nkb + 1) // 2
+    return 4.0 * cfg.D * cfg.block * cfg.block * pairs * cfg.B * cfg.Hq
+
+
+class EventTimer:
+    """Sums the device time of bracketed regions on torch's current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append([e, None])
+
+    def stop(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs[-1][1] = e
+
+    def total_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs)
+
+    def mean_ms(self):
+        return self.total_ms() / max(1, len(self.pairs))
+
+
+def run_prefill(ssa, torch, cfg, steps, warmup, budgets):
+    from ssa_inputs import make_inputs
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    x = make_inputs(cfg, workers=16)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    del x
+    log(f"[bench] prefill inputs ready in {time.time() - t0:.1f}s")
+    p = ssa.problem_for(q, k, budget=cfg.budget, n_sink=cfg.n_sink, n_local=cfg.n_local)
+    ws = ssa.alloc_workspace(p, dev)
+    idx, cnt = ssa.select_blocks(p, q, k, ws=ws)
+    out = ssa.attn_fwd(p, q, k, v, idx, cnt, ws=ws)
+    loss = torch.empty(2, dtype=torch.float32, device=dev)
+
+    def step(attn_timer=None):
+        ssa.select_blocks(p, q, k, ws=ws, idx=idx, cnt=cnt)
+        if attn_timer is not None:
+            attn_timer.start()
+        ssa.attn_fwd(p, q, k, v, idx, cnt, ws=ws, out=out)
+        if attn_timer is not None:
+            attn_timer.stop()
+        ssa.align_loss(p, out["h_full"], out["h_sparse"], ws=ws, loss=loss)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    attn_t = EventTimer(torch)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(attn_t)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    res = {"ms_per_step": wall * 1e3 / steps, "attn_ms": attn_t.mean_ms(),
+           "loss": float(loss[0]), "delta_mean": float(out["delta"].mean())}
+    # budget sweep: attention time per budget (selection re-run per budget)
+    sweep = {}
+    for bgt in budgets:
+        pb = ssa.problem_for(q, k, budget=bgt, n_sink=cfg.n_sink, n_local=cfg.n_local)
+        ib, cb = ssa.select_blocks(pb, q, k, ws=ws)
+        ssa.attn_fwd(pb, q, k, v, ib, cb, ws=ws, out=out)
+        tm = EventTimer(torch)
+        for _ in range(max(3, steps // 4)):
+            tm.start()
+            ssa.attn_fwd(pb, q, k, v, ib, cb, ws=ws, out=out)
+            tm.stop()
+        sp = EventTimer(torch)
+        for _ in range(max(3, steps // 4)):
+            sp.start()
+            ssa.attn_fwd(pb, q, k, v, ib, cb, ws=ws, out={"h_sparse": out["h_sparse"]},
+                         sparse_only=True)
+            sp.stop()
+        torch.cuda.synchronize()
+        sweep[str(bgt)] = {"dual_attn_ms": round(tm.mean_ms(), 4),
+                           "sparse_only_attn_ms": round(sp.mean_ms(), 4),
+                           "delta_mean": round(float(out["delta"].mean()), 4)}
+    res["sweep"] = sweep
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_decode(ssa, torch, cfg, steps, warmup):
+    from ssa_inputs import make_inputs
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    x = make_inputs(cfg, workers=16)
+    q = x["q"].to(dev)
+    k = x["k"].to(dev)
+    v = x["v"].to(dev)
+    del x
+    log(f"[bench] decode inputs ready in {time.time() - t0:.1f}s")
+    p = ssa.problem_for(q, k, budget=cfg.budget, n_sink=cfg.n_sink, n_local=cfg.n_local)
+    ws = ssa.alloc_workspace(p, dev)
+    kp = ssa.pool_blocks(p, k)   # the pooled-key table kept beside the cache
+    idx, cnt = ssa.select_blocks(p, q, None, kp, ws=ws)
+    out = ssa.attn_fwd(p, q, k, v, idx, cnt, ws=ws)
+    loss = torch.empty(2, dtype=torch.float32, device=dev)
+
+    def step(t_sel=None, t_attn=None):
+        if t_sel is not None:
+            t_sel.start()
+        ssa.select_blocks(p, q, None, kp, ws=ws, idx=idx, cnt=cnt)
+        if t_sel is not None:
+            t_sel.stop()
+            t_attn.start()
+        ssa.attn_fwd(p, q, k, v, idx, cnt, ws=ws, out=out)
+        if t_attn is not None:
+            t_attn.stop()
+        ssa.align_loss(p, out["h_full"], out["h_sparse"], ws=ws, loss=loss)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ts, ta = EventTimer(torch), EventTimer(torch)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(ts, ta)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # sparse-only mode
+    sp_out = {"h_sparse": torch.empty_like(out["h_sparse"])}
+    for _ in range(warmup):
+        ssa.attn_fwd(p, q, k, v, idx, cnt, ws=ws, out=sp_out, sparse_only=True)
+    tsp = EventTimer(torch)
+    for _ in range(steps):
+        tsp.start()
+        ssa.attn_fwd(p, q, k, v, idx, cnt, ws=ws, out=sp_out, sparse_only=True)
+        tsp.stop()
+    torch.cuda.synchronize()
+
+    esz = 2
+    kv_bytes = 2 * cfg.B * cfg.Hkv * cfg.N * cfg.D * esz
+    table_bytes = cfg.B * cfg.Hkv * (cfg.N // cfg.block) * cfg.D * 4
+    q_bytes = cfg.B * cfg.Hq * cfg.D * esz
+    out_bytes = 2 * cfg.B * cfg.Hq * cfg.D * esz + cfg.B * cfg.Hq * 4
+    idx_bytes = cfg.B * cfg.Hq * (cfg.budget + 1) * 4
+    attn_bytes = kv_bytes + q_bytes + out_bytes + idx_bytes
+    # sparse-only: the union of the group's selected blocks per (seq, kv head)
+    G = cfg.Hq // cfg.Hkv
+    ic = idx.view(cfg.B, cfg.Hkv, G, cfg.budget).cpu()
+    union = 0
+    for b in range(cfg.B):
+        for g in range(cfg.Hkv):
+            s = set(ic[b, g].flatten().tolist())
+            s.discard(-1)
+            union += len(s)
+    sp_bytes = union * 2 * cfg.block * cfg.D * esz + q_bytes + cfg.B * cfg.Hq * cfg.D * esz + idx_bytes
+    attn_ms, sel_ms, sp_ms = ta.mean_ms(), ts.mean_ms(), tsp.mean_ms()
+    res = {
+        "workload": f"gqa decode: {cfg.B} seqs x {cfg.Hq}/{cfg.Hkv} heads, KV {cfg.N}, D {cfg.D}, "
+                    f"block {cfg.block}, budget {cfg.budget}",
+        "ms_per_step": wall * 1e3 / steps,
+        "tokens_per_s": cfg.B / (wall / steps),
+        "select_ms": sel_ms,
+        "attn_ms": attn_ms,
+        "attn_bytes": attn_bytes,
+        "attn_GBps": attn_bytes / attn_ms / 1e6,
+        "attn_hbm_frac": attn_bytes / attn_ms / 1e6 / HBM_PEAK_GBS,
+        "step_GBps": (attn_bytes + table_bytes) / (sel_ms + attn_ms) / 1e6,
+        "sparse_only_attn_ms": sp_ms,
+        "sparse_only_bytes": sp_bytes + table_bytes,
+        "sparse_only_GBps": (sp_bytes + table_bytes) / (sp_ms + sel_ms) / 1e6,
+        "sparse_only_union_blocks_per_group": union / (cfg.B * cfg.Hkv),
+    }
+    del q, k, v, kp, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(cfg, seconds_target=15.0):
+    """The fp64 oracle on a bounded sample of the prefill workload: one q head,
+    its selection, and query rows sampled evenly over the sequence."""
+    import numpy as np
+    from oracle import ssa_oracle as O
+    from ssa_inputs import default_head_map, make_head, scale_for
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    h = 5
+    x = make_head(cfg, 0, h)
+    q = x["q"].float().numpy()[None, None]
+    k = x["k"].float().numpy()[None, None]
+    v = x["v"].float().numpy()[None, None]
+    t0 = time.perf_counter()
+    idx, cnt = O.select_blocks(q, k, block=cfg.block, budget=cfg.budget, n_sink=cfg.n_sink,
+                               n_local=cfg.n_local, head_map=[0])
+    t_sel = time.perf_counter() - t0
+    rows_done, flops, t_att = 0, 0.0, 0.0
+    # random rows, 256 at a time, until the time target is met
+    order = np.random.default_rng(0).permutation(cfg.N)
+    pos = 0
+    while t_att < seconds_target and pos < cfg.N:
+        r = np.sort(order[pos:pos + 256])
+        pos += 256
+        t1 = time.perf_counter()
+        O.dual_attention(q, k, v, idx, block=cfg.block, scale=scale_for(cfg), head_map=[0],
+                         rows={(0, 0): r})
+        t_att += time.perf_counter() - t1
+        flops += float(sum(4.0 * cfg.D * cfg.block * (rr // cfg.block + 1) for rr in r))
+        rows_done += len(r)
+    # scale: selection share of one head out of Hq heads plus the sampled rows
+    sel_share = t_sel * rows_done / cfg.N
+    total_s = t_att + sel_share
+    return {"value": flops / total_s / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle, q head {h} of {cfg.name} (N={cfg.N}, budget "
+                      f"{cfg.budget}): selection for all {cfg.N // cfg.block} query blocks "
+                      f"({t_sel:.2f}s, charged pro rata) + both streams and delta for "
+                      f"{rows_done} random query rows ({t_att:.1f}s); value = algorithmic "
+                      f"full-stream FLOPs of those rows / time",
+            "rows": rows_done, "seconds": round(total_s, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--budget", type=int, default=16)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_full_amd as ssa
+    from ssa_inputs import CONFIGS
+    ssa.load_library()
+
+    cfg = CONFIGS["gqa_32k_sweep"].with_budget(args.budget)
+    pre = run_prefill(ssa, torch, cfg, args.steps, args.warmup,
+                      [] if args.no_sweep else list(cfg.budgets))
+    flops = prefill_flops(cfg)
+    step_s = pre["ms_per_step"] / 1e3
+    value = flops / step_s / 1e12
+    attn_tflops = flops / (pre["attn_ms"] / 1e3) / 1e12
+    result = {
+        "metric": "dual-stream attn fwd TFLOP/s + tokens/s at 32K (% MFMA peak); decode GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V with planted peaked key blocks)",
+        "config": {"workload": f"gqa prefill 32K: B {cfg.B}, {cfg.Hq} q heads / {cfg.Hkv} kv "
+                               f"heads, N {cfg.N}, D {cfg.D}, block {cfg.block}, budget "
+                               f"{cfg.budget} (sink + local included)",
+                   "global_batch": cfg.B, "seq_len": cfg.N, "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round(cfg.B * cfg.N / step_s, 1),
+        "mfma_frac_step": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+        "attn_ms": round(pre["attn_ms"], 4),
+        "roofline": {"bound": "mfma", "kernel": "ssa_attn_fwd (prefill)",
+                     "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "loss_sparsity": pre["loss"],
+        "delta_mean": round(pre["delta_mean"], 4),
+        "budget_sweep": pre.get("sweep"),
+    }
+    if not args.no_decode:
+        dec = run_decode(ssa, torch, CONFIGS["gqa_decode_64k"], max(5, args.steps // 2),
+                         args.warmup)
+        result["decode"] = {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                            for kk, vv in dec.items()}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -148,7 +148,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
     __syncthreads();
     const bool take_all = n_cand <= free_slots;
-    if (!take_all) {
+    const bool forced_only = !take_all && free_slots <= 0;
+    if (!take_all && !forced_only) {
       // Scores of every candidate for the nh heads.
       for (int kb = tid; kb < ncausal; kb += kSelThreads) {
         if (is_forced(kb, diag, d.n_sink, d.n_local)) continue;
@@ -181,6 +182,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       __syncthreads();
       if (take_all) {
         for (int kb = tid; kb < ncausal; kb += kSelThreads) atomicOr(&sel_bits[kb >> 5], 1u << (kb & 31));
+      } else if (forced_only) {
+        for (int kb = tid; kb < ncausal; kb += kSelThreads)
+          if (is_forced(kb, diag, d.n_sink, d.n_local)) atomicOr(&sel_bits[kb >> 5], 1u << (kb & 31));
       } else {
         if (tid == 0) { s_prefix = 0ull; s_mask = 0ull; s_k = free_slots; }
         __syncthreads();
@@ -264,10 +268,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       for (int kb = tid; kb < ncausal; kb += kSelThreads) {
         const unsigned bit = 1u << (kb & 31);
         const unsigned w = sel_bits[kb >> 5];
-        if (w & bit) out[word_prefix[kb >> 5] + __popc(w & (bit - 1u))] = kb;
+        if (w & bit) {
+          const int pos = word_prefix[kb >> 5] + __popc(w & (bit - 1u));
+          if (pos < d.budget) out[pos] = kb;  // always true; bounds the write to the row
+        }
       }
       for (int i = total + tid; i < d.budget; i += kSelThreads) out[i] = -1;
-      if (tid == 0) cnt[row] = total;
+      if (tid == 0) cnt[row] = min(total, d.budget);
       __syncthreads();
     }
   }

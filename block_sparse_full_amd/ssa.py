@@ -187,12 +187,17 @@ def pool_blocks(p: Problem, x: torch.Tensor, out: Optional[torch.Tensor] = None)
 
 
 def select_blocks(p: Problem, q: torch.Tensor, k: Optional[torch.Tensor] = None,
-                  k_pooled: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+                  k_pooled: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                  idx: Optional[torch.Tensor] = None, cnt: Optional[torch.Tensor] = None):
     """Selected key blocks (idx [B,Hq,nQB,budget] int32, cnt [B,Hq,nQB] int32)."""
     dev = q.device
     nqb = p.n_qblocks
-    idx = torch.empty(p.B, p.Hq, nqb, p.budget, dtype=torch.int32, device=dev)
-    cnt = torch.empty(p.B, p.Hq, nqb, dtype=torch.int32, device=dev)
+    if idx is None:
+        idx = torch.empty(p.B, p.Hq, nqb, p.budget, dtype=torch.int32, device=dev)
+    if cnt is None:
+        cnt = torch.empty(p.B, p.Hq, nqb, dtype=torch.int32, device=dev)
+    _dev(idx, "idx", torch.int32, (p.B, p.Hq, nqb, p.budget))
+    _dev(cnt, "cnt", torch.int32, (p.B, p.Hq, nqb))
     ws = ws if ws is not None else alloc_workspace(p, dev)
     wp, wn = _ws_ptr(ws)
     c, keep = p.to_c()
@@ -238,11 +243,13 @@ def attn_fwd(p: Problem, q, k, v, idx, cnt, *, sparse_only: bool = False, want_d
 
 
 def align_loss(p: Problem, h_full, h_sparse, *, want_grads: bool = False,
-               ws: Optional[torch.Tensor] = None):
+               ws: Optional[torch.Tensor] = None, loss: Optional[torch.Tensor] = None):
     """(loss float32[2] on the device, grad_full, grad_sparse or None)."""
     dev = h_full.device
     shp = (p.B, p.Hq, p.Nq, p.D)
-    loss = torch.empty(2, dtype=torch.float32, device=dev)
+    if loss is None:
+        loss = torch.empty(2, dtype=torch.float32, device=dev)
+    _dev(loss, "loss", torch.float32, (2,))
     gf = torch.empty(shp, dtype=p.torch_dtype, device=dev) if want_grads else None
     gs = torch.empty(shp, dtype=p.torch_dtype, device=dev) if want_grads else None
     ws = ws if ws is not None else alloc_workspace(p, dev)

@@ -33,25 +33,89 @@ __device__ __forceinline__ int kperm(int c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bfloat16 (round to nearest even) in one instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_t r = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// LDS tiles are stored without padding; 16-byte chunks are XOR-swizzled per
+// row so that the ds_read_b128 of 16 lanes (16 different rows, same logical
+// chunk) hit 16 distinct 4-bank groups. Rows of 256 bytes (16 chunks) use
+// chunk ^ (row & 15); rows of 128 bytes (8 chunks) use chunk ^ ((row>>1) & 7).
+template <int SPR>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  if constexpr (SPR == 16) return chunk ^ (row & 15);
+  else return chunk ^ ((row >> 1) & 7);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) const void* gbl_ptr_t;
+
+// Asynchronous global -> LDS copy of one tile of `rows` x (SPR*16 bytes):
+// lane i of wave instruction j fills LDS chunk slot (base_slot + 64 j + i)
+// and fetches the global chunk that the swizzle maps to that slot.
+template <int SPR, int ROWS>
+__device__ __forceinline__ void tile_to_lds(const uint16_t* g, size_t g_row_stride,
+                                            uint16_t* lds, int wave, int lane) {
+  constexpr int SLOTS = ROWS * SPR;
+  constexpr int PER_WAVE = SLOTS / 2;          // two waves share the copy
+#pragma unroll
+  for (int j = 0; j < PER_WAVE / 64; ++j) {
+    const int slot0 = wave * PER_WAVE + j * 64;
+    const int p = slot0 + lane;
+    const int r = p / SPR, sl = p % SPR;
+    const int c = swz<SPR>(r, sl);              // the map is an involution
+    const uint16_t* src = g + (size_t)r * g_row_stride + c * 8;
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(lds + slot0 * 8), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Largest of x and the same lane's value in the other half of the wave.
+__device__ __forceinline__ float pair_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // One workgroup = one (b, q head, 64-row query block); two waves of 32 query
 // rows each. MFMA 32x32x16 bf16 computes S^T = K Q^T (keys x queries, so a
-// lane owns one query column and row statistics stay in-lane up to one
-// exchange with lane ^ 32) and O^T = V^T P^T. K and V^T tiles are staged in
-// padded LDS (conflict-free ds_read_b128).
+// lane owns one query column and row statistics stay in-lane up to one swap
+// with lane ^ 32) and O^T = V^T P^T.
+//
+// Pipeline per key block i (K and V^T tiles each have one LDS buffer):
+//   QK^T(i) from K; softmax(i); [V(i) landed, barrier] start K(i+1) load;
+//   PV(i) from V^T;            [K(i+1) landed, barrier] start V(i+1) load.
+// Each asynchronous copy overlaps one compute phase, and with 32 KB of LDS
+// and <= 256 registers per wave four workgroups (two waves per SIMD) share a
+// CU, so one workgroup's waits overlap another's MFMA work.
+//
+// The running max is updated lazily: the accumulator keeps its reference
+// max until some row's block max exceeds it by more than 2^8, so most blocks
+// skip the rescale (P stays <= 256, exact enough in bf16 and float32).
 template <int D>
-__global__ __launch_bounds__(128) void attn_prefill_bf16_kernel(
+__global__ __launch_bounds__(128, 2) void attn_prefill_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vt, const int* __restrict__ idx, const int* __restrict__ cnt,
     uint16_t* __restrict__ Hf, uint16_t* __restrict__ Hs, float* __restrict__ delta,
     float* __restrict__ lse, Dims d, HeadMap hm) {
-  constexpr int KSTR = D + 8;       // K tile row stride (elements)
-  constexpr int VSTR = kBlock + 8;  // V^T tile row stride (elements)
+  constexpr int KSPR = D / 8;       // 16-byte chunks per K row
+  constexpr int VSPR = kBlock / 8;  // 16-byte chunks per V^T row
   constexpr int NKS = D / 16;       // k-steps of QK^T
   constexpr int NDT = D / 32;       // d tiles of O^T
-  constexpr int KCH = kBlock * D / 8 / 128;  // 16-byte chunks per thread, K tile
-  constexpr int VCH = D * kBlock / 8 / 128;  // same, V^T tile
-  __shared__ __align__(16) uint16_t Ks[kBlock * KSTR];
-  __shared__ __align__(16) uint16_t Vs[D * VSTR];
+  constexpr float kTau = 8.0f;      // lazy-rescale threshold (log2 units)
+  __shared__ __align__(16) uint16_t Ks[kBlock * D];
+  __shared__ __align__(16) uint16_t Vs[D * kBlock];
 
   const int total = d.B * d.Hq * d.nQB;
   const int lin = xcd_remap(blockIdx.x, total);
@@ -75,6 +139,32 @@ __global__ __launch_bounds__(128) void attn_prefill_bf16_kernel(
   const int diag = qb;
   const float sl2 = d.scale_log2;
 
+  const uint16_t* kbase = K + ((size_t)(b * d.Hkv + g) * d.Nk) * D;
+  const uint16_t* vbase = Vt + ((size_t)(b * d.Hkv + g) * D) * d.Nk;
+  const int* my_idx = idx + ((size_t)bh * d.nQB + qb) * d.budget;
+  const int n_sel = min(max(cnt[(size_t)bh * d.nQB + qb], 0), d.budget);
+
+  // Walk order: the selected blocks (ascending), then the other causal
+  // blocks (ascending). next_block() returns -1 when the walk is over.
+  // State is wave-uniform (scalar registers).
+  int it_sel = 0, it_rest = 0, j_sel = 0;
+  const bool sparse_only = (Hf == nullptr);
+  auto next_block = [&](bool& selected) -> int {
+    while (it_sel < n_sel) {
+      const int kb = my_idx[it_sel++];
+      if (kb >= 0 && kb <= diag) { selected = true; return kb; }
+    }
+    if (sparse_only) return -1;
+    while (it_rest <= diag) {
+      const int kb = it_rest++;
+      while (j_sel < n_sel && my_idx[j_sel] < kb) ++j_sel;
+      if (j_sel < n_sel && my_idx[j_sel] == kb) continue;
+      selected = false;
+      return kb;
+    }
+    return -1;
+  };
+
   // Q^T operand of QK^T: lane holds Q[qrow][16ks + 8gl .. +7].
   bf16x8_t qf[NKS];
   {
@@ -88,105 +178,8 @@ __global__ __launch_bounds__(128) void attn_prefill_bf16_kernel(
   for (int i = 0; i < NDT; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
-  float m_run = -INFINITY, l_sel = 0.f, l_drop = 0.f;
-
-  const uint16_t* kbase = K + ((size_t)(b * d.Hkv + g) * d.Nk) * D;
-  const uint16_t* vbase = Vt + ((size_t)(b * d.Hkv + g) * D) * d.Nk;
+  float m_ref = -INFINITY, l_sel = 0.f, l_drop = 0.f;
   const int pr = kperm(c);
-
-  auto process = [&](int kb, bool selected) {
-    // ---- stage K and V^T tiles
-    {
-      const uint16_t* kg = kbase + (size_t)kb * kBlock * D;
-      const uint16_t* vg = vbase + (size_t)kb * kBlock;
-      uint4 kr[KCH], vr[VCH];
-#pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        const int ch = tid + 128 * i;
-        const int r = ch / (D / 8), cc = (ch % (D / 8)) * 8;
-        kr[i] = *(const uint4*)(kg + r * D + cc);
-      }
-#pragma unroll
-      for (int i = 0; i < VCH; ++i) {
-        const int ch = tid + 128 * i;
-        const int r = ch >> 3, cc = (ch & 7) * 8;
-        vr[i] = *(const uint4*)(vg + (size_t)r * d.Nk + cc);
-      }
-#pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        const int ch = tid + 128 * i;
-        const int r = ch / (D / 8), cc = (ch % (D / 8)) * 8;
-        *(uint4*)(Ks + r * KSTR + cc) = kr[i];
-      }
-#pragma unroll
-      for (int i = 0; i < VCH; ++i) {
-        const int ch = tid + 128 * i;
-        const int r = ch >> 3, cc = (ch & 7) * 8;
-        *(uint4*)(Vs + r * VSTR + cc) = vr[i];
-      }
-    }
-    __syncthreads();
-
-    // ---- S^T = K Q^T for 64 keys x 32 queries
-    f32x16_t s0, s1;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) { s0[v] = 0.f; s1[v] = 0.f; }
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8_t a0 = *(const bf16x8_t*)(Ks + pr * KSTR + 16 * ks + 8 * gl);
-      const bf16x8_t a1 = *(const bf16x8_t*)(Ks + (32 + pr) * KSTR + 16 * ks + 8 * gl);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
-    }
-
-    // ---- online softmax (log2 domain), causal mask on the diagonal block
-    const bool on_diag = (kb == diag);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float x0 = s0[v] * sl2, x1 = s1[v] * sl2;
-      if (on_diag) {
-        const int key0 = 16 * (v >> 3) + 8 * gl + (v & 7);
-        if (key0 > qq) x0 = -INFINITY;
-        if (key0 + 32 > qq) x1 = -INFINITY;
-      }
-      s0[v] = x0;
-      s1[v] = x1;
-      mx = fmaxf(mx, fmaxf(x0, x1));
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    float ls = 0.f;
-    bf16x8_t pb[4];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float p0 = fast_exp2(s0[v] - m_new);
-      const float p1 = fast_exp2(s1[v] - m_new);
-      ls += p0 + p1;
-      pb[v >> 3][v & 7] = static_cast<__bf16>(p0);
-      pb[2 + (v >> 3)][v & 7] = static_cast<__bf16>(p1);
-    }
-#pragma unroll
-    for (int i = 0; i < NDT; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
-    l_sel *= alpha;
-    l_drop *= alpha;
-    if (selected) l_sel += ls; else l_drop += ls;
-
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8_t a = *(const bf16x8_t*)(Vs + (32 * dt + c) * VSTR + 16 * s + 8 * gl);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s], o[dt], 0, 0, 0);
-      }
-    }
-    __syncthreads();
-  };
 
   auto store = [&](uint16_t* H, float inv) {
     uint16_t* hp = H + ((size_t)bh * d.Nq + qrow) * D;
@@ -195,44 +188,133 @@ __global__ __launch_bounds__(128) void attn_prefill_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d0 = 32 * dt + 8 * i + 4 * gl;
-        const uint32_t lo = (uint32_t)f32_to_bf16(o[dt][4 * i] * inv) |
-                            ((uint32_t)f32_to_bf16(o[dt][4 * i + 1] * inv) << 16);
-        const uint32_t hi2 = (uint32_t)f32_to_bf16(o[dt][4 * i + 2] * inv) |
-                             ((uint32_t)f32_to_bf16(o[dt][4 * i + 3] * inv) << 16);
+        const uint32_t lo = pack_bf16x2(o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv);
+        const uint32_t hi2 = pack_bf16x2(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv);
         *(uint2*)(hp + d0) = make_uint2(lo, hi2);
       }
     }
   };
 
-  const int* my_idx = idx + ((size_t)bh * d.nQB + qb) * d.budget;
-  const int n_sel = min(max(cnt[(size_t)bh * d.nQB + qb], 0), d.budget);
-  for (int it = 0; it < n_sel; ++it) {
-    const int kb = my_idx[it];
-    if (kb >= 0 && kb <= diag) process(kb, true);
-  }
+  // One key block: QK^T, softmax statistics, PV, with the next block's
+  // tiles streaming into LDS behind the two compute phases.
+  auto body = [&](int kb, bool selected, int kb_next) {
+    // ---- S^T = K Q^T for 64 keys x 32 queries
+    f32x16_t s0, s1;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { s0[v] = 0.f; s1[v] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int ch = 2 * ks + gl;
+      const bf16x8_t a0 = *(const bf16x8_t*)(Ks + (pr * KSPR + swz<KSPR>(pr, ch)) * 8);
+      const bf16x8_t a1 =
+          *(const bf16x8_t*)(Ks + ((32 + pr) * KSPR + swz<KSPR>(32 + pr, ch)) * 8);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
+    }
+
+    // ---- softmax statistics (scale folded into the exponent)
+    if (kb == diag) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key0 = 16 * (v >> 3) + 8 * gl + (v & 7);
+        if (key0 > qq) s0[v] = -INFINITY;
+        if (key0 + 32 > qq) s1[v] = -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
+    const float m_blk = pair_max(mx) * sl2;
+    if (__builtin_amdgcn_ballot_w64(m_blk > m_ref + kTau) != 0) {
+      const float m_new = fmaxf(m_ref, m_blk);
+      const float alpha = fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+      l_sel *= alpha;
+      l_drop *= alpha;
+    }
+    float ls = 0.f;
+    uint32_t pw[16];
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      const float a0 = fast_exp2(fmaf(s0[v], sl2, -m_ref));
+      const float a1 = fast_exp2(fmaf(s0[v + 1], sl2, -m_ref));
+      const float b0 = fast_exp2(fmaf(s1[v], sl2, -m_ref));
+      const float b1 = fast_exp2(fmaf(s1[v + 1], sl2, -m_ref));
+      ls += (a0 + a1) + (b0 + b1);
+      pw[v >> 1] = pack_bf16x2(a0, a1);
+      pw[8 + (v >> 1)] = pack_bf16x2(b0, b1);
+    }
+    if (selected) l_sel += ls; else l_drop += ls;
+
+    // ---- V(i) has landed and every wave is done with K(i): prefetch K(i+1)
+    wait_vm();
+    __syncthreads();
+    if (kb_next >= 0)
+      tile_to_lds<KSPR, kBlock>(kbase + (size_t)kb_next * kBlock * D, D, Ks, wave, lane);
+
+    // ---- O^T += V^T P^T (B operand of k-step s: keys 16s + 8gl .. +7)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 w = make_uint4(pw[4 * s], pw[4 * s + 1], pw[4 * s + 2], pw[4 * s + 3]);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, w);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int r = 32 * dt + c;
+        const bf16x8_t a = *(const bf16x8_t*)(Vs + (r * VSPR + swz<VSPR>(r, 2 * s + gl)) * 8);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[dt], 0, 0, 0);
+      }
+    }
+
+    // ---- K(i+1) has landed and every wave is done with V(i): prefetch V(i+1)
+    wait_vm();
+    __syncthreads();
+    if (kb_next >= 0)
+      tile_to_lds<VSPR, D>(vbase + (size_t)kb_next * kBlock, d.Nk, Vs, wave, lane);
+  };
+
   const size_t plane = (size_t)d.B * d.Hq * d.Nq;
+  bool sel_cur = false;
+  int kb = next_block(sel_cur);
+  if (kb >= 0) {
+    tile_to_lds<KSPR, kBlock>(kbase + (size_t)kb * kBlock * D, D, Ks, wave, lane);
+    tile_to_lds<VSPR, D>(vbase + (size_t)kb * kBlock, d.Nk, Vs, wave, lane);
+    wait_vm();
+    __syncthreads();
+  }
+  // Phase 1: the selected blocks.
+  while (kb >= 0 && sel_cur) {
+    bool sel_next = false;
+    const int kb_next = next_block(sel_next);
+    body(kb, true, kb_next);
+    kb = kb_next;
+    sel_cur = sel_next;
+  }
+  // Snapshot of the sparse stream.
   {
-    const float lt = l_sel + __shfl_xor(l_sel, 32);
+    const float lt = pair_sum(l_sel);
     store(Hs, 1.f / lt);
     if (lse != nullptr && gl == 0)
-      lse[plane + (size_t)bh * d.Nq + qrow] = (m_run + __log2f(lt)) * kLn2;
+      lse[plane + (size_t)bh * d.Nq + qrow] = (m_ref + __log2f(lt)) * kLn2;
   }
-  if (Hf == nullptr) return;  // sparse-only mode
-  {
-    int j = 0;
-    for (int kb = 0; kb <= diag; ++kb) {
-      while (j < n_sel && my_idx[j] < kb) ++j;
-      if (j < n_sel && my_idx[j] == kb) continue;
-      process(kb, false);
-    }
+  if (sparse_only) return;
+  // Phase 2: the remaining causal blocks.
+  while (kb >= 0) {
+    bool sel_next = false;
+    const int kb_next = next_block(sel_next);
+    body(kb, false, kb_next);
+    kb = kb_next;
   }
-  const float ls_t = l_sel + __shfl_xor(l_sel, 32);
-  const float ld_t = l_drop + __shfl_xor(l_drop, 32);
+  const float ls_t = pair_sum(l_sel);
+  const float ld_t = pair_sum(l_drop);
   const float lt = ls_t + ld_t;
   store(Hf, 1.f / lt);
   if (gl == 0) {
     if (delta != nullptr) delta[(size_t)bh * d.Nq + qrow] = ld_t / lt;
-    if (lse != nullptr) lse[(size_t)bh * d.Nq + qrow] = (m_run + __log2f(lt)) * kLn2;
+    if (lse != nullptr) lse[(size_t)bh * d.Nq + qrow] = (m_ref + __log2f(lt)) * kLn2;
   }
 }
 

@@ -270,6 +270,10 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (x3), the reference for "
+                         "scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -277,11 +281,24 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.int16, device="cuda:0")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 2, "copy_bytes_written":
+                          dst.numel() * 2, "copies": 3}), flush=True)
+        return
     import block_sparse_full_amd as ssa
     from ssa_inputs import CONFIGS
     ssa.load_library()
 
     cfg = CONFIGS["gqa_32k_sweep"].with_budget(args.budget)
+    if args.no_prefill:
+        dec = run_decode(ssa, torch, CONFIGS["gqa_decode_64k"], args.steps, args.warmup)
+        print(json.dumps({"decode": dec}), flush=True)
+        return
     pre = run_prefill(ssa, torch, cfg, args.steps, args.warmup,
                       [] if args.no_sweep else list(cfg.budgets))
     flops = prefill_flops(cfg)

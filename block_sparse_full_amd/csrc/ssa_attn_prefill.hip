@@ -53,24 +53,37 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) const void* gbl_ptr_t;
 
-// Asynchronous global -> LDS copy of one tile of `rows` x (SPR*16 bytes):
-// lane i of wave instruction j fills LDS chunk slot (base_slot + 64 j + i)
-// and fetches the global chunk that the swizzle maps to that slot.
+// Buffer resource over [base, base + bytes): loads past the end read 0. The
+// base is made wave-uniform explicitly so the descriptor lives in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* u = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, 0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// Asynchronous global -> LDS copy of one tile of ROWS rows x SPR 16-byte
+// chunks, starting `tile_off` bytes into the buffer, rows `row_bytes` apart.
+// Lane i of wave instruction j fills LDS chunk slot (slot0 + i) and fetches
+// the global chunk that the swizzle maps to that slot; the per-lane offset
+// only depends on the lane and the swizzle phase, the rest is scalar.
 template <int SPR, int ROWS>
-__device__ __forceinline__ void tile_to_lds(const uint16_t* g, size_t g_row_stride,
-                                            uint16_t* lds, int wave, int lane) {
+__device__ __forceinline__ void tile_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t tile_off,
+                                            uint32_t row_bytes, uint16_t* lds, int wave,
+                                            int lane) {
   constexpr int SLOTS = ROWS * SPR;
   constexpr int PER_WAVE = SLOTS / 2;          // two waves share the copy
 #pragma unroll
   for (int j = 0; j < PER_WAVE / 64; ++j) {
     const int slot0 = wave * PER_WAVE + j * 64;
-    const int p = slot0 + lane;
-    const int r = p / SPR, sl = p % SPR;
-    const int c = swz<SPR>(r, sl);              // the map is an involution
-    const uint16_t* src = g + (size_t)r * g_row_stride + c * 8;
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(lds + slot0 * 8), 16, 0, 0);
+    const int r0 = slot0 / SPR;                 // first row of this instruction
+    const int rl = lane / SPR, sl = lane % SPR;
+    const int c = swz<SPR>(r0 + rl, sl);        // the swizzle is an involution
+    const uint32_t voff = (uint32_t)rl * row_bytes + (uint32_t)c * 16u;
+    const uint32_t soff = tile_off + (uint32_t)r0 * row_bytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + slot0 * 8), 16, voff, soff, 0, 0);
   }
 }
 
@@ -132,7 +145,8 @@ __global__ __launch_bounds__(128, 2) void attn_prefill_bf16_kernel(
   const int bh = b * d.Hq + h;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int c = lane & 31, gl = lane >> 5;
   const int qq = wave * 32 + c;                 // query row within the block
   const int qrow = qb * kBlock + qq;            // query row (== key position)
@@ -141,8 +155,12 @@ __global__ __launch_bounds__(128, 2) void attn_prefill_bf16_kernel(
 
   const uint16_t* kbase = K + ((size_t)(b * d.Hkv + g) * d.Nk) * D;
   const uint16_t* vbase = Vt + ((size_t)(b * d.Hkv + g) * D) * d.Nk;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)((size_t)d.Nk * D * 2));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)((size_t)d.Nk * D * 2));
+  const uint32_t k_row_bytes = D * 2, v_row_bytes = (uint32_t)d.Nk * 2;
   const int* my_idx = idx + ((size_t)bh * d.nQB + qb) * d.budget;
-  const int n_sel = min(max(cnt[(size_t)bh * d.nQB + qb], 0), d.budget);
+  const int n_sel =
+      __builtin_amdgcn_readfirstlane(min(max(cnt[(size_t)bh * d.nQB + qb], 0), d.budget));
 
   // Walk order: the selected blocks (ascending), then the other causal
   // blocks (ascending). next_block() returns -1 when the walk is over.
@@ -151,14 +169,14 @@ __global__ __launch_bounds__(128, 2) void attn_prefill_bf16_kernel(
   const bool sparse_only = (Hf == nullptr);
   auto next_block = [&](bool& selected) -> int {
     while (it_sel < n_sel) {
-      const int kb = my_idx[it_sel++];
+      const int kb = __builtin_amdgcn_readfirstlane(my_idx[it_sel++]);
       if (kb >= 0 && kb <= diag) { selected = true; return kb; }
     }
     if (sparse_only) return -1;
     while (it_rest <= diag) {
       const int kb = it_rest++;
-      while (j_sel < n_sel && my_idx[j_sel] < kb) ++j_sel;
-      if (j_sel < n_sel && my_idx[j_sel] == kb) continue;
+      while (j_sel < n_sel && __builtin_amdgcn_readfirstlane(my_idx[j_sel]) < kb) ++j_sel;
+      if (j_sel < n_sel && __builtin_amdgcn_readfirstlane(my_idx[j_sel]) == kb) continue;
       selected = false;
       return kb;
     }
@@ -254,7 +272,7 @@ __global__ __launch_bounds__(128, 2) void attn_prefill_bf16_kernel(
     wait_vm();
     __syncthreads();
     if (kb_next >= 0)
-      tile_to_lds<KSPR, kBlock>(kbase + (size_t)kb_next * kBlock * D, D, Ks, wave, lane);
+      tile_to_lds<KSPR, kBlock>(krs, (uint32_t)kb_next * kBlock * k_row_bytes, k_row_bytes, Ks, wave, lane);
 
     // ---- O^T += V^T P^T (B operand of k-step s: keys 16s + 8gl .. +7)
 #pragma unroll
@@ -273,15 +291,15 @@ __global__ __launch_bounds__(128, 2) void attn_prefill_bf16_kernel(
     wait_vm();
     __syncthreads();
     if (kb_next >= 0)
-      tile_to_lds<VSPR, D>(vbase + (size_t)kb_next * kBlock, d.Nk, Vs, wave, lane);
+      tile_to_lds<VSPR, D>(vrs, (uint32_t)kb_next * kBlock * 2, v_row_bytes, Vs, wave, lane);
   };
 
   const size_t plane = (size_t)d.B * d.Hq * d.Nq;
   bool sel_cur = false;
   int kb = next_block(sel_cur);
   if (kb >= 0) {
-    tile_to_lds<KSPR, kBlock>(kbase + (size_t)kb * kBlock * D, D, Ks, wave, lane);
-    tile_to_lds<VSPR, D>(vbase + (size_t)kb * kBlock, d.Nk, Vs, wave, lane);
+    tile_to_lds<KSPR, kBlock>(krs, (uint32_t)kb * kBlock * k_row_bytes, k_row_bytes, Ks, wave, lane);
+    tile_to_lds<VSPR, D>(vrs, (uint32_t)kb * kBlock * 2, v_row_bytes, Vs, wave, lane);
     wait_vm();
     __syncthreads();
   }

@@ -162,25 +162,47 @@ __global__ __launch_bounds__(128, 2) void attn_prefill_bf16_kernel(
   const int n_sel =
       __builtin_amdgcn_readfirstlane(min(max(cnt[(size_t)bh * d.nQB + qb], 0), d.budget));
 
+  // Selected-block bitmap of this query block, built once in LDS from the
+  // index list; the walk below reads it one 32-block word at a time into
+  // scalar registers, so choosing the next block costs no memory access.
+  __shared__ uint32_t sel_mask[kMaxKeyBlocks / 32];
+  const int nwords = (diag >> 5) + 1;
+  for (int w = tid; w < nwords; w += 128) sel_mask[w] = 0u;
+  __syncthreads();
+  for (int e = tid; e < n_sel; e += 128) {
+    const int kb = my_idx[e];
+    if (kb >= 0 && kb <= diag) atomicOr(&sel_mask[kb >> 5], 1u << (kb & 31));
+  }
+  __syncthreads();
+
   // Walk order: the selected blocks (ascending), then the other causal
-  // blocks (ascending). next_block() returns -1 when the walk is over.
-  // State is wave-uniform (scalar registers).
-  int it_sel = 0, it_rest = 0, j_sel = 0;
+  // blocks (ascending). The state is wave-uniform (scalar registers):
+  // `phase` 0 scans set bits, 1 scans clear bits up to diag.
   const bool sparse_only = (Hf == nullptr);
+  int phase = 0, wcur = 0;
+  uint32_t bits = __builtin_amdgcn_readfirstlane(sel_mask[0]);
   auto next_block = [&](bool& selected) -> int {
-    while (it_sel < n_sel) {
-      const int kb = __builtin_amdgcn_readfirstlane(my_idx[it_sel++]);
-      if (kb >= 0 && kb <= diag) { selected = true; return kb; }
+    while (true) {
+      if (bits != 0u) {
+        const int kb = (wcur << 5) + __builtin_ctz(bits);
+        bits &= bits - 1u;
+        if (kb > diag) { bits = 0u; continue; }
+        selected = (phase == 0);
+        return kb;
+      }
+      if (++wcur < nwords) {
+        const uint32_t w = __builtin_amdgcn_readfirstlane(sel_mask[wcur]);
+        bits = phase == 0 ? w : ~w;
+        continue;
+      }
+      if (phase == 0 && !sparse_only) {
+        phase = 1;
+        wcur = 0;
+        bits = ~__builtin_amdgcn_readfirstlane(sel_mask[0]);
+        continue;
+      }
+      return -1;
     }
-    if (sparse_only) return -1;
-    while (it_rest <= diag) {
-      const int kb = it_rest++;
-      while (j_sel < n_sel && __builtin_amdgcn_readfirstlane(my_idx[j_sel]) < kb) ++j_sel;
-      if (j_sel < n_sel && __builtin_amdgcn_readfirstlane(my_idx[j_sel]) == kb) continue;
-      selected = false;
-      return kb;
-    }
-    return -1;
   };
 
   // Q^T operand of QK^T: lane holds Q[qrow][16ks + 8gl .. +7].

@@ -22,15 +22,6 @@
 
 namespace ssa {
 
-// Row of the K tile that MFMA row c reads. With this permutation the S^T
-// output register v of lane group gl holds key 16*(v/8) + 8*gl + (v%8) of its
-// 32-key tile, which is exactly the 8 consecutive keys the PV MFMA needs in
-// its B operand, so P never leaves registers.
-__device__ __forceinline__ int kperm(int c) {
-  const int i = c >> 3, gp = (c >> 2) & 1, j = c & 3;
-  return 16 * (i >> 1) + 8 * gp + 4 * (i & 1) + j;
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -44,13 +35,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 // LDS tiles are stored without padding; 16-byte chunks are XOR-swizzled per
 // row so that the ds_read_b128 of 16 lanes (16 different rows, same logical
-// chunk) hit 16 distinct 4-bank groups. Rows of 256 bytes (16 chunks) use
-// chunk ^ (row & 15); rows of 128 bytes (8 chunks) use chunk ^ ((row>>1) & 7).
-template <int SPR>
-__device__ __forceinline__ int swz(int row, int chunk) {
-  if constexpr (SPR == 16) return chunk ^ (row & 15);
-  else return chunk ^ ((row >> 1) & 7);
-}
+// chunk) hit 16 distinct 16-byte bank groups. V^T rows are 128 bytes (two
+// rows per 256-byte bank sweep) and the 16 rows of one read are consecutive:
+// chunk ^ ((row >> 1) & 7) separates them.
+__device__ __forceinline__ int vswz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -64,76 +52,101 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(u, 0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Largest of x over the four lanes n, n+16, n+32, n+48 (one query column of
+// a 16x16 MFMA tile), and the same for sums.
+__device__ __forceinline__ float quad_max(float x) {
+  unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  u = __float_as_uint(y);
+  const auto t = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  u = __float_as_uint(y);
+  const auto t = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
+// K-tile row read by MFMA row m of key tile kt (16 keys): chosen so that the
+// S^T output rows 4*g4 + r of tiles 2j and 2j+1 held by lane group g4 are the
+// keys 32j + 8*g4 .. +7 that the PV B operand of k-step j needs.
+__device__ __forceinline__ int kperm16(int kt, int m) {
+  return 32 * (kt >> 1) + 8 * (m >> 2) + 4 * (kt & 1) + (m & 3);
+}
+// K-tile swizzles under that permutation: the 16 rows one ds_read_b128 phase
+// touches land on 16 distinct 16-byte bank groups. 256-byte rows (D = 128,
+// 16 chunks) use chunk ^ f(row) with f taking row bits 0,1,3,4; 128-byte rows
+// (D = 64, 8 chunks, two rows per 256 bytes) use row bits 1,3,4.
+template <int SPR>
+__device__ __forceinline__ int kswz(int row, int chunk) {
+  if constexpr (SPR == 16) return chunk ^ ((row & 3) | ((row >> 1) & 12));
+  else return chunk ^ (((row >> 1) & 1) | ((row >> 2) & 6));
+}
+
 // Asynchronous global -> LDS copy of one tile of ROWS rows x SPR 16-byte
-// chunks, starting `tile_off` bytes into the buffer, rows `row_bytes` apart.
-// Lane i of wave instruction j fills LDS chunk slot (slot0 + i) and fetches
-// the global chunk that the swizzle maps to that slot; the per-lane offset
-// only depends on the lane and the swizzle phase, the rest is scalar.
-template <int SPR, int ROWS>
+// chunks, starting `tile_off` bytes into the buffer, rows `row_bytes` apart,
+// shared by NWAVES waves. Lane i of wave instruction j fills LDS chunk slot
+// (slot0 + i) and fetches the global chunk that the swizzle (an involution)
+// maps to that slot; the per-lane offset depends only on the lane and the
+// swizzle phase, the rest is scalar.
+template <int SPR, int ROWS, int NWAVES, bool KMAP>
 __device__ __forceinline__ void tile_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t tile_off,
-                                            uint32_t row_bytes, uint16_t* lds, int wave,
-                                            int lane) {
+                                              uint32_t row_bytes, uint16_t* lds, int wave,
+                                              int lane) {
   constexpr int SLOTS = ROWS * SPR;
-  constexpr int PER_WAVE = SLOTS / 2;          // two waves share the copy
+  constexpr int PER_WAVE = SLOTS / NWAVES;
 #pragma unroll
   for (int j = 0; j < PER_WAVE / 64; ++j) {
     const int slot0 = wave * PER_WAVE + j * 64;
-    const int r0 = slot0 / SPR;                 // first row of this instruction
+    const int r0 = slot0 / SPR;
     const int rl = lane / SPR, sl = lane % SPR;
-    const int c = swz<SPR>(r0 + rl, sl);        // the swizzle is an involution
+    const int c = KMAP ? kswz<SPR>(r0 + rl, sl) : vswz(r0 + rl, sl);
     const uint32_t voff = (uint32_t)rl * row_bytes + (uint32_t)c * 16u;
     const uint32_t soff = tile_off + (uint32_t)r0 * row_bytes;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + slot0 * 8), 16, voff, soff, 0, 0);
   }
 }
 
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Largest of x and the same lane's value in the other half of the wave.
-__device__ __forceinline__ float pair_max(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// One workgroup = one (b, q head, 64-row query block); two waves of 32 query
-// rows each. MFMA 32x32x16 bf16 computes S^T = K Q^T (keys x queries, so a
-// lane owns one query column and row statistics stay in-lane up to one swap
-// with lane ^ 32) and O^T = V^T P^T.
+// One workgroup = one (b, q head, 64-row query block); four waves of 16
+// query rows each. MFMA 16x16x32 bf16 computes S^T = K Q^T (keys x queries:
+// a lane owns one query column, so row statistics stay in-lane up to a
+// reduction over the four lanes of that column) and O^T = V^T P^T, with P
+// handed from the S^T output registers to the PV B operand directly thanks
+// to the K row permutation kperm16. The small per-wave state (about 110
+// VGPRs) lets four waves share each SIMD, so one wave's softmax VALU work
+// overlaps another's MFMA work.
 //
-// Pipeline per key block i (K and V^T tiles each have one LDS buffer):
-//   QK^T(i) from K; softmax(i); [V(i) landed, barrier] start K(i+1) load;
-//   PV(i) from V^T;            [K(i+1) landed, barrier] start V(i+1) load.
-// Each asynchronous copy overlaps one compute phase, and with 32 KB of LDS
-// and <= 256 registers per wave four workgroups (two waves per SIMD) share a
-// CU, so one workgroup's waits overlap another's MFMA work.
+// Per key block: QK^T from the K tile, softmax statistics, [V landed,
+// barrier] start the next K copy, PV from the V^T tile, [K landed, barrier]
+// start the next V copy. K and V^T tiles (16 KB each) have one LDS buffer
+// each; every asynchronous copy overlaps one compute phase.
 //
 // The running max is updated lazily: the accumulator keeps its reference
 // max until some row's block max exceeds it by more than 2^8, so most blocks
 // skip the rescale (P stays <= 256, exact enough in bf16 and float32).
 template <int D>
-__global__ __launch_bounds__(128, 2) void attn_prefill_bf16_kernel(
+__global__ __launch_bounds__(256, 4) void attn_prefill_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vt, const int* __restrict__ idx, const int* __restrict__ cnt,
     uint16_t* __restrict__ Hf, uint16_t* __restrict__ Hs, float* __restrict__ delta,
     float* __restrict__ lse, Dims d, HeadMap hm) {
   constexpr int KSPR = D / 8;       // 16-byte chunks per K row
   constexpr int VSPR = kBlock / 8;  // 16-byte chunks per V^T row
-  constexpr int NKS = D / 16;       // k-steps of QK^T
-  constexpr int NDT = D / 32;       // d tiles of O^T
-  constexpr float kTau = 8.0f;      // lazy-rescale threshold (log2 units)
+  constexpr int NKS = D / 32;       // k-steps of QK^T
+  constexpr int NDT = D / 16;       // d tiles of O^T
+  constexpr float kTau = 8.0f;
   __shared__ __align__(16) uint16_t Ks[kBlock * D];
   __shared__ __align__(16) uint16_t Vs[D * kBlock];
+  __shared__ uint32_t sel_mask[kMaxKeyBlocks / 32];
 
   const int total = d.B * d.Hq * d.nQB;
   const int lin = xcd_remap(blockIdx.x, total);
-  // Logical order: (b, kv head) groups, then query blocks longest first,
-  // then the group's q heads.
   const int per_group = d.G * d.nQB;
   const int grp = lin / per_group;
   const int rem = lin - grp * per_group;
@@ -146,10 +159,10 @@ __global__ __launch_bounds__(128, 2) void attn_prefill_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
-  const int c = lane & 31, gl = lane >> 5;
-  const int qq = wave * 32 + c;                 // query row within the block
-  const int qrow = qb * kBlock + qq;            // query row (== key position)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g4 = lane >> 4;
+  const int qq = wave * 16 + n;
+  const int qrow = qb * kBlock + qq;
   const int diag = qb;
   const float sl2 = d.scale_log2;
 
@@ -158,26 +171,27 @@ __global__ __launch_bounds__(128, 2) void attn_prefill_bf16_kernel(
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)((size_t)d.Nk * D * 2));
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)((size_t)d.Nk * D * 2));
   const uint32_t k_row_bytes = D * 2, v_row_bytes = (uint32_t)d.Nk * 2;
+  auto load_k = [&](int kb) {
+    tile_to_lds<KSPR, kBlock, 4, true>(krs, (uint32_t)kb * kBlock * k_row_bytes, k_row_bytes,
+                                         Ks, wave, lane);
+  };
+  auto load_v = [&](int kb) {
+    tile_to_lds<VSPR, D, 4, false>(vrs, (uint32_t)kb * kBlock * 2, v_row_bytes, Vs, wave, lane);
+  };
+  auto kchunk = [&](int row, int ch) { return kswz<KSPR>(row, ch); };
+
   const int* my_idx = idx + ((size_t)bh * d.nQB + qb) * d.budget;
   const int n_sel =
       __builtin_amdgcn_readfirstlane(min(max(cnt[(size_t)bh * d.nQB + qb], 0), d.budget));
-
-  // Selected-block bitmap of this query block, built once in LDS from the
-  // index list; the walk below reads it one 32-block word at a time into
-  // scalar registers, so choosing the next block costs no memory access.
-  __shared__ uint32_t sel_mask[kMaxKeyBlocks / 32];
   const int nwords = (diag >> 5) + 1;
-  for (int w = tid; w < nwords; w += 128) sel_mask[w] = 0u;
+  for (int w = tid; w < nwords; w += 256) sel_mask[w] = 0u;
   __syncthreads();
-  for (int e = tid; e < n_sel; e += 128) {
+  for (int e = tid; e < n_sel; e += 256) {
     const int kb = my_idx[e];
     if (kb >= 0 && kb <= diag) atomicOr(&sel_mask[kb >> 5], 1u << (kb & 31));
   }
   __syncthreads();
 
-  // Walk order: the selected blocks (ascending), then the other causal
-  // blocks (ascending). The state is wave-uniform (scalar registers):
-  // `phase` 0 scans set bits, 1 scans clear bits up to diag.
   const bool sparse_only = (Hf == nullptr);
   int phase = 0, wcur = 0;
   uint32_t bits = __builtin_amdgcn_readfirstlane(sel_mask[0]);
@@ -205,66 +219,54 @@ __global__ __launch_bounds__(128, 2) void attn_prefill_bf16_kernel(
     }
   };
 
-  // Q^T operand of QK^T: lane holds Q[qrow][16ks + 8gl .. +7].
+  // Q^T operand: lane holds Q[qrow][32ks + 8g4 .. +7].
   bf16x8_t qf[NKS];
   {
-    const uint16_t* qp = Q + ((size_t)bh * d.Nq + qrow) * D + 8 * gl;
+    const uint16_t* qp = Q + ((size_t)bh * d.Nq + qrow) * D + 8 * g4;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8_t*)(qp + 16 * ks);
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8_t*)(qp + 32 * ks);
   }
-
-  f32x16_t o[NDT];
+  f32x4_t o[NDT];
 #pragma unroll
-  for (int i = 0; i < NDT; ++i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
+  for (int i = 0; i < NDT; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_sel = 0.f, l_drop = 0.f;
-  const int pr = kperm(c);
 
   auto store = [&](uint16_t* H, float inv) {
     uint16_t* hp = H + ((size_t)bh * d.Nq + qrow) * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d0 = 32 * dt + 8 * i + 4 * gl;
-        const uint32_t lo = pack_bf16x2(o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv);
-        const uint32_t hi2 = pack_bf16x2(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv);
-        *(uint2*)(hp + d0) = make_uint2(lo, hi2);
-      }
+      const int d0 = 16 * dt + 4 * g4;
+      const uint32_t lo = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+      const uint32_t hi2 = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
+      *(uint2*)(hp + d0) = make_uint2(lo, hi2);
     }
   };
 
-  // One key block: QK^T, softmax statistics, PV, with the next block's
-  // tiles streaming into LDS behind the two compute phases.
   auto body = [&](int kb, bool selected, int kb_next) {
-    // ---- S^T = K Q^T for 64 keys x 32 queries
-    f32x16_t s0, s1;
+    f32x4_t s[4];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) { s0[v] = 0.f; s1[v] = 0.f; }
+    for (int kt = 0; kt < 4; ++kt) {
+      s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int row = kperm16(kt, n);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int ch = 2 * ks + gl;
-      const bf16x8_t a0 = *(const bf16x8_t*)(Ks + (pr * KSPR + swz<KSPR>(pr, ch)) * 8);
-      const bf16x8_t a1 =
-          *(const bf16x8_t*)(Ks + ((32 + pr) * KSPR + swz<KSPR>(32 + pr, ch)) * 8);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8_t a = *(const bf16x8_t*)(Ks + (row * KSPR + kchunk(row, 4 * ks + g4)) * 8);
+        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], s[kt], 0, 0, 0);
+      }
     }
-
-    // ---- softmax statistics (scale folded into the exponent)
     if (kb == diag) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key0 = 16 * (v >> 3) + 8 * gl + (v & 7);
-        if (key0 > qq) s0[v] = -INFINITY;
-        if (key0 + 32 > qq) s1[v] = -INFINITY;
-      }
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kperm16(kt, 4 * g4 + r) > qq) s[kt][r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
-    const float m_blk = pair_max(mx) * sl2;
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kt][r]);
+    const float m_blk = quad_max(mx) * sl2;
     if (__builtin_amdgcn_ballot_w64(m_blk > m_ref + kTau) != 0) {
       const float m_new = fmaxf(m_ref, m_blk);
       const float alpha = fast_exp2(m_ref - m_new);
@@ -272,60 +274,55 @@ __global__ __launch_bounds__(128, 2) void attn_prefill_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < NDT; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+        for (int v = 0; v < 4; ++v) o[i][v] *= alpha;
       l_sel *= alpha;
       l_drop *= alpha;
     }
     float ls = 0.f;
-    uint32_t pw[16];
+    uint32_t pw[8];
 #pragma unroll
-    for (int v = 0; v < 16; v += 2) {
-      const float a0 = fast_exp2(fmaf(s0[v], sl2, -m_ref));
-      const float a1 = fast_exp2(fmaf(s0[v + 1], sl2, -m_ref));
-      const float b0 = fast_exp2(fmaf(s1[v], sl2, -m_ref));
-      const float b1 = fast_exp2(fmaf(s1[v + 1], sl2, -m_ref));
-      ls += (a0 + a1) + (b0 + b1);
-      pw[v >> 1] = pack_bf16x2(a0, a1);
-      pw[8 + (v >> 1)] = pack_bf16x2(b0, b1);
+    for (int kt = 0; kt < 4; ++kt) {
+      const float p0 = fast_exp2(fmaf(s[kt][0], sl2, -m_ref));
+      const float p1 = fast_exp2(fmaf(s[kt][1], sl2, -m_ref));
+      const float p2 = fast_exp2(fmaf(s[kt][2], sl2, -m_ref));
+      const float p3 = fast_exp2(fmaf(s[kt][3], sl2, -m_ref));
+      ls += (p0 + p1) + (p2 + p3);
+      pw[2 * kt] = pack_bf16x2(p0, p1);
+      pw[2 * kt + 1] = pack_bf16x2(p2, p3);
     }
     if (selected) l_sel += ls; else l_drop += ls;
 
-    // ---- V(i) has landed and every wave is done with K(i): prefetch K(i+1)
     wait_vm();
     __syncthreads();
-    if (kb_next >= 0)
-      tile_to_lds<KSPR, kBlock>(krs, (uint32_t)kb_next * kBlock * k_row_bytes, k_row_bytes, Ks, wave, lane);
+    if (kb_next >= 0) load_k(kb_next);
 
-    // ---- O^T += V^T P^T (B operand of k-step s: keys 16s + 8gl .. +7)
+    // O^T += V^T P^T; k-step j (32 keys) takes tiles 2j, 2j+1.
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint4 w = make_uint4(pw[4 * s], pw[4 * s + 1], pw[4 * s + 2], pw[4 * s + 3]);
+    for (int j = 0; j < 2; ++j) {
+      const uint4 w = make_uint4(pw[4 * j], pw[4 * j + 1], pw[4 * j + 2], pw[4 * j + 3]);
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, w);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const int r = 32 * dt + c;
-        const bf16x8_t a = *(const bf16x8_t*)(Vs + (r * VSPR + swz<VSPR>(r, 2 * s + gl)) * 8);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[dt], 0, 0, 0);
+        const int r = 16 * dt + n;
+        const bf16x8_t a = *(const bf16x8_t*)(Vs + (r * VSPR + vswz(r, 4 * j + g4)) * 8);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[dt], 0, 0, 0);
       }
     }
 
-    // ---- K(i+1) has landed and every wave is done with V(i): prefetch V(i+1)
     wait_vm();
     __syncthreads();
-    if (kb_next >= 0)
-      tile_to_lds<VSPR, D>(vrs, (uint32_t)kb_next * kBlock * 2, v_row_bytes, Vs, wave, lane);
+    if (kb_next >= 0) load_v(kb_next);
   };
 
   const size_t plane = (size_t)d.B * d.Hq * d.Nq;
   bool sel_cur = false;
   int kb = next_block(sel_cur);
   if (kb >= 0) {
-    tile_to_lds<KSPR, kBlock>(krs, (uint32_t)kb * kBlock * k_row_bytes, k_row_bytes, Ks, wave, lane);
-    tile_to_lds<VSPR, D>(vrs, (uint32_t)kb * kBlock * 2, v_row_bytes, Vs, wave, lane);
+    load_k(kb);
+    load_v(kb);
     wait_vm();
     __syncthreads();
   }
-  // Phase 1: the selected blocks.
   while (kb >= 0 && sel_cur) {
     bool sel_next = false;
     const int kb_next = next_block(sel_next);
@@ -333,26 +330,24 @@ __global__ __launch_bounds__(128, 2) void attn_prefill_bf16_kernel(
     kb = kb_next;
     sel_cur = sel_next;
   }
-  // Snapshot of the sparse stream.
   {
-    const float lt = pair_sum(l_sel);
+    const float lt = quad_sum(l_sel);
     store(Hs, 1.f / lt);
-    if (lse != nullptr && gl == 0)
+    if (lse != nullptr && g4 == 0)
       lse[plane + (size_t)bh * d.Nq + qrow] = (m_ref + __log2f(lt)) * kLn2;
   }
   if (sparse_only) return;
-  // Phase 2: the remaining causal blocks.
   while (kb >= 0) {
     bool sel_next = false;
     const int kb_next = next_block(sel_next);
     body(kb, false, kb_next);
     kb = kb_next;
   }
-  const float ls_t = pair_sum(l_sel);
-  const float ld_t = pair_sum(l_drop);
+  const float ls_t = quad_sum(l_sel);
+  const float ld_t = quad_sum(l_drop);
   const float lt = ls_t + ld_t;
   store(Hf, 1.f / lt);
-  if (gl == 0) {
+  if (g4 == 0) {
     if (delta != nullptr) delta[(size_t)bh * d.Nq + qrow] = ld_t / lt;
     if (lse != nullptr) lse[(size_t)bh * d.Nq + qrow] = (m_ref + __log2f(lt)) * kLn2;
   }
@@ -364,10 +359,10 @@ hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const 
                                     hipStream_t stream) {
   const int total = d.B * d.Hq * d.nQB;
   if (d.D == 128)
-    hipLaunchKernelGGL(attn_prefill_bf16_kernel<128>, dim3(total), dim3(128), 0, stream, q, k,
+    hipLaunchKernelGGL(attn_prefill_bf16_kernel<128>, dim3(total), dim3(256), 0, stream, q, k,
                        vt, idx, cnt, hf, hs, delta, lse, d, hm);
   else
-    hipLaunchKernelGGL(attn_prefill_bf16_kernel<64>, dim3(total), dim3(128), 0, stream, q, k,
+    hipLaunchKernelGGL(attn_prefill_bf16_kernel<64>, dim3(total), dim3(256), 0, stream, q, k,
                        vt, idx, cnt, hf, hs, delta, lse, d, hm);
   return hipGetLastError();
 }

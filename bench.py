@@ -30,6 +30,23 @@ if ROOT not in sys.path:
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 
+# HBM bytes per launch of the prefill attention kernel, from two rocprofv3
+# --pmc runs (FETCH_SIZE, WRITE_SIZE) scaled by a plain 1 GiB copy (see the
+# HBM-counter summary under profiles/), keyed by the SHA-256 of the kernel
+# source they were taken on; any other source reports traffic as null.
+PREFILL_TRAFFIC = {}
+PREFILL_SRC = os.path.join(ROOT, "block_sparse_full_amd", "csrc", "ssa_attn_prefill.hip")
+
+
+def prefill_traffic():
+    import hashlib
+    try:
+        with open(PREFILL_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    return PREFILL_TRAFFIC.get(sha)
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -328,7 +345,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "ssa_attn_fwd (prefill)",
                      "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": prefill_traffic()},
         "loss_sparsity": pre["loss"],
         "delta_mean": round(pre["delta_mean"], 4),
         "budget_sweep": pre.get("sweep"),

@@ -78,14 +78,18 @@ hipError_t launch_pool(const void* x, bool bf16, float* out, long nblk_total, in
 }
 
 // ---------------------------------------------------------------- selection
-// One workgroup per (b, kv head, query row block). It scores the causal
-// candidate blocks of up to `hc` q heads of the group at once (each pooled
-// key row is read once for all of them), then runs an exact radix select per
-// head: the free-th largest 64-bit orderable key is found 8 bits at a time
-// from the most significant byte; keys above it are taken, and among keys
-// equal to it the lowest block indices fill the remaining slots.
+// One workgroup (four waves) per (b, kv head, query row block). All threads
+// first score the causal candidate blocks of up to `hc` q heads of the group
+// at once (each pooled key row is read once for all of them) into LDS as
+// 64-bit orderable keys. Then each wave selects for one head on its own,
+// with no workgroup barrier: an exact radix select finds the free-th largest
+// key 8 bits at a time from the most significant byte (per-wave LDS
+// histogram, wave prefix scans); keys above it are taken and, among keys
+// equal to it, the lowest block indices fill the remaining slots. The
+// ascending index list is written by a ballot/popcount compaction over the
+// causal blocks in order.
 constexpr int kSelThreads = 256;
-constexpr int kSelMaxWords = kMaxKeyBlocks / 32;
+constexpr int kSelWaves = kSelThreads / 64;
 
 __device__ __forceinline__ uint64_t orderable_key(double s) {
   if (s == 0.0) s = 0.0;  // -0.0 and +0.0 rank equal
@@ -108,6 +112,11 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar,
     int* __restrict__ idx, int* __restrict__ cnt, Dims d, HeadMap hm, int hc) {
@@ -115,21 +124,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // layout: keys[hc][nKB] u64 | qv[hc][D] f32
   uint64_t* keys = (uint64_t*)smem;
   float* qv = (float*)(smem + (size_t)hc * d.nKB * sizeof(uint64_t));
-  __shared__ unsigned hist[256];
-  __shared__ unsigned sel_bits[kSelMaxWords];
-  __shared__ unsigned eq_bits[kSelMaxWords];
-  __shared__ int word_prefix[kSelMaxWords];
-  __shared__ unsigned long long s_prefix, s_mask;
-  __shared__ int s_k;
+  __shared__ unsigned hist[kSelWaves][256];
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qb = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int diag = row_block_diag(d, qb);
   const int ncausal = diag + 1;
-  const int nwords = (ncausal + 31) >> 5;
   const float* krow0 = kbar + ((size_t)(b * d.Hkv + g) * d.nKB) * d.D;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes below
 
   // Forced set and slot count (identical for every head of the group).
   const int a_end = min(d.n_sink, ncausal);
@@ -137,6 +143,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int n_forced = a_end + (ncausal - l_begin) - max(0, a_end - l_begin);
   const int n_cand = ncausal - n_forced;
   const int free_slots = d.budget - n_forced;
+  const bool take_all = n_cand <= free_slots;
+  const bool forced_only = !take_all && free_slots <= 0;
 
   for (int h0 = 0; h0 < d.G; h0 += hc) {
     const int nh = min(hc, d.G - h0);
@@ -147,15 +155,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       qv[i] = qbar[((size_t)(b * d.Hq + h) * d.nQB + qb) * d.D + dd];
     }
     __syncthreads();
-    const bool take_all = n_cand <= free_slots;
-    const bool forced_only = !take_all && free_slots <= 0;
     if (!take_all && !forced_only) {
       // Scores of every candidate for the nh heads.
       for (int kb = tid; kb < ncausal; kb += kSelThreads) {
         if (is_forced(kb, diag, d.n_sink, d.n_local)) continue;
         const float* kr = krow0 + (size_t)kb * d.D;
         for (int hb = 0; hb < nh; hb += 4) {
-          double s[4] = {0.0, 0.0, 0.0, 0.0};
+          double sc[4] = {0.0, 0.0, 0.0, 0.0};
           for (int dd = 0; dd < d.D; dd += 4) {
             const float4 k4 = *(const float4*)(kr + dd);
             const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
@@ -164,118 +170,90 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
               const double kv = (double)kk[e];
 #pragma unroll
               for (int j = 0; j < 4; ++j)
-                if (hb + j < nh) s[j] = __fma_rn((double)qv[(hb + j) * d.D + dd + e], kv, s[j]);
+                if (hb + j < nh) sc[j] = __fma_rn((double)qv[(hb + j) * d.D + dd + e], kv, sc[j]);
             }
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (hb + j < nh) keys[(size_t)(hb + j) * d.nKB + kb] = orderable_key(s[j]);
+            if (hb + j < nh) keys[(size_t)(hb + j) * d.nKB + kb] = orderable_key(sc[j]);
         }
       }
     }
     __syncthreads();
 
-    for (int hh = 0; hh < nh; ++hh) {
+    // ---- per-wave selection, one head at a time
+    for (int hh = wave; hh < nh; hh += kSelWaves) {
       const int h = hm.q_of_kv[g * d.G + h0 + hh];
       const uint64_t* hk = keys + (size_t)hh * d.nKB;
-      for (int w = tid; w < nwords; w += kSelThreads) { sel_bits[w] = 0u; eq_bits[w] = 0u; }
-      __syncthreads();
-      if (take_all) {
-        for (int kb = tid; kb < ncausal; kb += kSelThreads) atomicOr(&sel_bits[kb >> 5], 1u << (kb & 31));
-      } else if (forced_only) {
-        for (int kb = tid; kb < ncausal; kb += kSelThreads)
-          if (is_forced(kb, diag, d.n_sink, d.n_local)) atomicOr(&sel_bits[kb >> 5], 1u << (kb & 31));
-      } else {
-        if (tid == 0) { s_prefix = 0ull; s_mask = 0ull; s_k = free_slots; }
-        __syncthreads();
+      uint64_t thr = 0ull;   // keys above thr are taken
+      int k_eq = 0;          // and this many of the keys equal to thr
+      if (!take_all && !forced_only) {
+        unsigned* hw = hist[wave];
+        uint64_t prefix = 0ull, pmask = 0ull;
+        int k = free_slots;
         for (int pass = 0; pass < 8; ++pass) {
           const int shift = 56 - 8 * pass;
-          hist[tid] = 0u;
-          __syncthreads();
-          const uint64_t pre = s_prefix, msk = s_mask;
-          for (int kb = tid; kb < ncausal; kb += kSelThreads) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) hw[lane * 4 + j] = 0u;
+          wave_lds_fence();
+          for (int kb = lane; kb < ncausal; kb += 64) {
             if (is_forced(kb, diag, d.n_sink, d.n_local)) continue;
             const uint64_t key = hk[kb];
-            if ((key & msk) == pre) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            if ((key & pmask) == prefix) atomicAdd(&hw[(key >> shift) & 255u], 1u);
           }
-          __syncthreads();
-          if (tid < 64) {
-            // lane l owns bins 255-4l .. 252-4l (descending order)
-            const int top = 255 - 4 * tid;
-            const unsigned c0 = hist[top], c1 = hist[top - 1], c2 = hist[top - 2], c3 = hist[top - 3];
-            const int c = (int)(c0 + c1 + c2 + c3);
-            const int incl = wave_incl_scan(c);
-            const int excl = incl - c;
-            const int k = s_k;
-            const bool mine = excl < k && k <= incl;
-            if (mine) {
-              int cum = excl, bin = top;
-              const unsigned cs[4] = {c0, c1, c2, c3};
-              for (int j = 0; j < 4; ++j) {
-                if (cum + (int)cs[j] >= k) { bin = top - j; break; }
-                cum += (int)cs[j];
-              }
-              s_k = k - cum;
-              s_prefix = pre | ((uint64_t)bin << shift);
-              s_mask = msk | (0xFFull << shift);
-            }
-          }
-          __syncthreads();
+          wave_lds_fence();
+          // lane l owns bins 255-4l .. 252-4l (descending order)
+          const int top = 255 - 4 * lane;
+          const int c0 = (int)hw[top], c1 = (int)hw[top - 1], c2 = (int)hw[top - 2],
+                    c3 = (int)hw[top - 3];
+          const int csum = c0 + c1 + c2 + c3;
+          const int incl = wave_incl_scan(csum);
+          const int excl = incl - csum;
+          const bool mine = excl < k && k <= incl;
+          int bin = top, rest = k - excl;
+          if (rest > c0) { rest -= c0; bin = top - 1;
+            if (rest > c1) { rest -= c1; bin = top - 2;
+              if (rest > c2) { rest -= c2; bin = top - 3; } } }
+          const uint64_t ball = __builtin_amdgcn_ballot_w64(mine);
+          const int src = ball ? __builtin_ctzll(ball) : 0;   // ball != 0 always
+          const int sbin = __builtin_amdgcn_readlane(bin, src);
+          k = __builtin_amdgcn_readlane(rest, src);
+          prefix |= (uint64_t)sbin << shift;
+          pmask |= 0xFFull << shift;
+          wave_lds_fence();
         }
-        const uint64_t thr = s_prefix;
-        const int k_eq = s_k;
-        for (int kb = tid; kb < ncausal; kb += kSelThreads) {
-          if (is_forced(kb, diag, d.n_sink, d.n_local)) {
-            atomicOr(&sel_bits[kb >> 5], 1u << (kb & 31));
-            continue;
-          }
-          const uint64_t key = hk[kb];
-          if (key > thr) atomicOr(&sel_bits[kb >> 5], 1u << (kb & 31));
-          else if (key == thr) atomicOr(&eq_bits[kb >> 5], 1u << (kb & 31));
-        }
-        __syncthreads();
-        // Equal keys: the k_eq lowest block indices.
-        for (int kb = tid; kb < ncausal; kb += kSelThreads) {
-          const unsigned bit = 1u << (kb & 31);
-          if (!(eq_bits[kb >> 5] & bit)) continue;
-          int rank = __popc(eq_bits[kb >> 5] & (bit - 1u));
-          for (int w = 0; w < (kb >> 5); ++w) rank += __popc(eq_bits[w]);
-          if (rank < k_eq) atomicOr(&sel_bits[kb >> 5], bit);
-        }
+        thr = prefix;
+        k_eq = k;
       }
-      __syncthreads();
-      // Exclusive prefix of popcounts over the words (wave 0, 4 words/lane).
-      if (tid < 64) {
-        int c[4], tot = 0;
-        for (int j = 0; j < 4; ++j) {
-          const int w = tid * 4 + j;
-          c[j] = (w < nwords) ? __popc(sel_bits[w]) : 0;
-          tot += c[j];
-        }
-        const int incl = wave_incl_scan(tot);
-        int run = incl - tot;
-        for (int j = 0; j < 4; ++j) {
-          const int w = tid * 4 + j;
-          if (w < kSelMaxWords) word_prefix[w] = run;
-          run += c[j];
-        }
-        if (tid == 63) s_k = incl;  // total selected
-      }
-      __syncthreads();
-      const int total = s_k;
+      // ---- ascending compaction over the causal blocks, 64 at a time
       const size_t row = (size_t)(b * d.Hq + h) * d.nQB + qb;
       int* out = idx + row * d.budget;
-      for (int kb = tid; kb < ncausal; kb += kSelThreads) {
-        const unsigned bit = 1u << (kb & 31);
-        const unsigned w = sel_bits[kb >> 5];
-        if (w & bit) {
-          const int pos = word_prefix[kb >> 5] + __popc(w & (bit - 1u));
-          if (pos < d.budget) out[pos] = kb;  // always true; bounds the write to the row
+      int n_out = 0, eq_seen = 0;
+      for (int base = 0; base < ncausal; base += 64) {
+        const int kb = base + lane;
+        const bool causal = kb < ncausal;
+        const bool forced = causal && is_forced(kb, diag, d.n_sink, d.n_local);
+        bool take = false, eq = false;
+        if (causal && !forced) {
+          if (take_all) {
+            take = true;
+          } else if (!forced_only) {
+            const uint64_t key = hk[kb];
+            take = key > thr;
+            eq = key == thr;
+          }
         }
+        const uint64_t eq_ball = __builtin_amdgcn_ballot_w64(eq);
+        if (eq) take = (eq_seen + __popcll(eq_ball & lt_mask)) < k_eq;
+        eq_seen += __popcll(eq_ball);
+        const bool sel = forced || take;
+        const uint64_t sel_ball = __builtin_amdgcn_ballot_w64(sel);
+        const int pos = n_out + __popcll(sel_ball & lt_mask);
+        if (sel && pos < d.budget) out[pos] = kb;   // pos < budget always holds
+        n_out += __popcll(sel_ball);
       }
-      for (int i = total + tid; i < d.budget; i += kSelThreads) out[i] = -1;
-      if (tid == 0) cnt[row] = min(total, d.budget);
-      __syncthreads();
+      for (int i = n_out + lane; i < d.budget; i += 64) out[i] = -1;
+      if (lane == 0) cnt[row] = min(n_out, d.budget);
     }
   }
 }

@@ -103,3 +103,23 @@ def test_status_strings(lib):
     assert lib.ssa_status_string(0) == b"SSA_OK"
     assert lib.ssa_status_string(3) == b"SSA_ERR_WORKSPACE"
     assert lib.ssa_status_string(99) == b"SSA_ERR_UNKNOWN"
+
+
+def test_binding_refuses_host_tensors(lib):
+    """The binding never computes on the CPU: host tensors are rejected."""
+    import torch
+    from block_sparse_full_amd import ssa
+    q = torch.zeros(1, 2, 128, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16)
+    p = ssa.problem_for(q, k, budget=2)
+    ws = torch.zeros(ssa.workspace_bytes(p) + 256, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="device tensor"):
+        ssa.select_blocks(p, q, k, ws=ws)
+    with pytest.raises(TypeError):
+        ssa.problem_for(q.to(torch.float16), k, budget=2)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    from block_sparse_full_amd import ssa
+    with pytest.raises(RuntimeError, match="no fallback"):
+        ssa.load_library(str(tmp_path / "libssa.so"))

@@ -35,8 +35,8 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 # HBM-counter summary under profiles/), keyed by the SHA-256 of the kernel
 # source they were taken on; any other source reports traffic as null.
 PREFILL_TRAFFIC = {
-    # 2225228 KiB x 2.000 read + 528471 KiB x 1.000 written per dispatch
-    "cd9539603555a832d1162cf704b7bf1f5eceaec546f77d586ab2f2237d553cbd": int(2225228 * 2.0 * 1024 + 528471 * 1.0 * 1024),
+    # 786997 KiB x 2.000 read + 528385 KiB x 1.000 written per dispatch
+    "2f5cf956d52973ad6f32d54dc9fb3113d158987f6bb0f312e147f16e7ebaa820": int(786997 * 2.0 * 1024 + 528385 * 1.0 * 1024),
 }
 PREFILL_SRC = os.path.join(ROOT, "block_sparse_full_amd", "csrc", "ssa_attn_prefill.hip")
 

@@ -1,4 +1,6 @@
-// Fused dual-stream causal attention forward (prefill), bf16 on MFMA, and a
+// Fused dual-stream causal attention forward (prefill): two bf16 MFMA kernels
+// (one workgroup per q head and query block; one workgroup per kv head and
+// query block serving four q heads, for D = 128 and GQA groups of 4k) and a
 // float32 VALU kernel for float32 problems.
 //
 // Method: "SSA: Achieving Sparser Attention by Aligning Full and Sparse
@@ -20,6 +22,8 @@
 #include "ssa_common.h"
 #include "ssa_kernels.h"
 
+#include <type_traits>
+
 namespace ssa {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -31,6 +35,13 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const bf16x2_t r = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
   return __builtin_bit_cast(uint32_t, r);
+}
+// c + a.x + a.y for two packed bfloat16 values, in one instruction. The row
+// sums of both bf16 kernels add the bfloat16 weights that the PV MFMAs
+// apply to V, so each output row is normalised by exactly its own weights.
+__device__ __forceinline__ float add_bf16x2(uint32_t a, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, 0x3f803f80u), c, false);
 }
 
 // LDS tiles are stored without padding; 16-byte chunks are XOR-swizzled per
@@ -113,12 +124,28 @@ __device__ __forceinline__ void tile_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_
   }
 }
 
+// Scheduling pattern for a block of N LDS fragment reads feeding N MFMAs in
+// order: PF reads first, then alternating (MFMA, read) pairs, then the last
+// PF MFMAs; the reads run PF MFMAs ahead of their use instead of each MFMA
+// waiting for its own read.
+template <int N, int PF>
+__device__ __forceinline__ void pipeline_reads() {
+  static_assert(PF <= N, "prefetch depth");
+  __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);   // DS reads
+#pragma unroll
+  for (int k = 0; k < N - PF; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+}
+
 // One workgroup = one (b, q head, 64-row query block); four waves of 16
 // query rows each. MFMA 16x16x32 bf16 computes S^T = K Q^T (keys x queries:
 // a lane owns one query column, so row statistics stay in-lane up to a
 // reduction over the four lanes of that column) and O^T = V^T P^T, with P
 // handed from the S^T output registers to the PV B operand directly thanks
-// to the K row permutation kperm16. The small per-wave state (about 110
+// to the K row permutation kperm16. The small per-wave state (about 116
 // VGPRs) lets four waves share each SIMD, so one wave's softmax VALU work
 // overlaps another's MFMA work.
 //
@@ -141,6 +168,7 @@ __global__ __launch_bounds__(256, 4) void attn_prefill_bf16_kernel(
   constexpr int NKS = D / 32;       // k-steps of QK^T
   constexpr int NDT = D / 16;       // d tiles of O^T
   constexpr float kTau = 8.0f;
+  constexpr int kPrefetch = 4;      // LDS fragment reads in flight ahead of the MFMAs
   __shared__ __align__(16) uint16_t Ks[kBlock * D];
   __shared__ __align__(16) uint16_t Vs[D * kBlock];
   __shared__ uint32_t sel_mask[kMaxKeyBlocks / 32];
@@ -244,15 +272,27 @@ __global__ __launch_bounds__(256, 4) void attn_prefill_bf16_kernel(
 
   auto body = [&](int kb, bool selected, int kb_next) {
     f32x4_t s[4];
+    {
+      // MFMA work runs at raised wave priority, so that a wave with its
+      // operands ready takes the matrix unit ahead of waves in their softmax
+      __builtin_amdgcn_s_setprio(1);
+      bf16x8_t fr[4 * NKS];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int row = kperm16(kt, n);
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8_t a = *(const bf16x8_t*)(Ks + (row * KSPR + kchunk(row, 4 * ks + g4)) * 8);
-        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], s[kt], 0, 0, 0);
-      }
+        for (int kt = 0; kt < 4; ++kt) {
+          const int row = kperm16(kt, n);
+          fr[ks * 4 + kt] = *(const bf16x8_t*)(Ks + (row * KSPR + kchunk(row, 4 * ks + g4)) * 8);
+        }
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[ks * 4 + kt], qf[ks], s[kt], 0, 0, 0);
+      pipeline_reads<4 * NKS, kPrefetch>();
+      __builtin_amdgcn_s_setprio(0);
     }
     if (kb == diag) {
 #pragma unroll
@@ -286,9 +326,10 @@ __global__ __launch_bounds__(256, 4) void attn_prefill_bf16_kernel(
       const float p1 = fast_exp2(fmaf(s[kt][1], sl2, -m_ref));
       const float p2 = fast_exp2(fmaf(s[kt][2], sl2, -m_ref));
       const float p3 = fast_exp2(fmaf(s[kt][3], sl2, -m_ref));
-      ls += (p0 + p1) + (p2 + p3);
       pw[2 * kt] = pack_bf16x2(p0, p1);
       pw[2 * kt + 1] = pack_bf16x2(p2, p3);
+      ls = add_bf16x2(pw[2 * kt], ls);
+      ls = add_bf16x2(pw[2 * kt + 1], ls);
     }
     if (selected) l_sel += ls; else l_drop += ls;
 
@@ -297,16 +338,26 @@ __global__ __launch_bounds__(256, 4) void attn_prefill_bf16_kernel(
     if (kb_next >= 0) load_k(kb_next);
 
     // O^T += V^T P^T; k-step j (32 keys) takes tiles 2j, 2j+1.
+    {
+      __builtin_amdgcn_s_setprio(1);
+      bf16x8_t fr[2 * NDT];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint4 w = make_uint4(pw[4 * j], pw[4 * j + 1], pw[4 * j + 2], pw[4 * j + 3]);
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, w);
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int r = 16 * dt + n;
-        const bf16x8_t a = *(const bf16x8_t*)(Vs + (r * VSPR + vswz(r, 4 * j + g4)) * 8);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[dt], 0, 0, 0);
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int r = 16 * dt + n;
+          fr[j * NDT + dt] = *(const bf16x8_t*)(Vs + (r * VSPR + vswz(r, 4 * j + g4)) * 8);
+        }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint4 w = make_uint4(pw[4 * j], pw[4 * j + 1], pw[4 * j + 2], pw[4 * j + 3]);
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, w);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[j * NDT + dt], pb, o[dt], 0, 0, 0);
       }
+      pipeline_reads<2 * NDT, kPrefetch>();
+      __builtin_amdgcn_s_setprio(0);
     }
 
     wait_vm();
@@ -353,10 +404,477 @@ __global__ __launch_bounds__(256, 4) void attn_prefill_bf16_kernel(
   }
 }
 
+// Row of the K tile that 32x32 MFMA row c reads: the S^T output register v
+// of lane half gl then holds key 16*(v/8) + 8*gl + (v%8) of its 32-key tile,
+// exactly the 8 consecutive keys of the PV B operand.
+__device__ __forceinline__ int kperm32(int c) {
+  const int i = c >> 3, gp = (c >> 2) & 1, j = c & 3;
+  return 16 * (i >> 1) + 8 * gp + 4 * (i & 1) + j;
+}
+// 256-byte K rows: the 16 rows one ds_read_b128 phase touches have distinct
+// low four bits, so chunk ^ (row & 15) spreads them over all bank groups.
+__device__ __forceinline__ int kswz32(int row, int chunk) { return chunk ^ (row & 15); }
+__device__ __forceinline__ float pair_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+// Buffer descriptor words for [base, base + bytes) (stride 0, raw buffer).
+__device__ __forceinline__ i32x4_t make_rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  return i32x4_t{(int)__builtin_amdgcn_readfirstlane((uint32_t)p),
+                 (int)(__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) & 0xffffu),
+                 (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
+// One 16-byte-per-lane global -> LDS copy (buffer_load_dwordx4 ... lds),
+// issued from inline assembly so that the compiler inserts no wait of its
+// own before later LDS reads: the caller orders every copy against the
+// reads of its stage with explicit vmcnt waits and barriers. m0 (the LDS
+// destination of lane 0) is saved and restored around the copy.
+__device__ __forceinline__ void copy16_to_lds(i32x4_t rsrc, uint32_t soff, uint32_t voff,
+                                              uint32_t lds_addr) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+template <int SPR, int ROWS, int NWAVES, bool KMAP>
+__device__ __forceinline__ void tile_to_lds_asm(i32x4_t rsrc, uint32_t tile_off,
+                                                uint32_t row_bytes, uint16_t* lds, int wave,
+                                                int lane) {
+  constexpr int SLOTS = ROWS * SPR;
+  constexpr int PER_WAVE = SLOTS / NWAVES;
+#pragma unroll
+  for (int j = 0; j < PER_WAVE / 64; ++j) {
+    const int slot0 = wave * PER_WAVE + j * 64;
+    const int r0 = slot0 / SPR;
+    const int rl = lane / SPR, sl = lane % SPR;
+    const int c = KMAP ? kswz32(r0 + rl, sl) : vswz(r0 + rl, sl);
+    const uint32_t voff = (uint32_t)rl * row_bytes + (uint32_t)c * 16u;
+    const uint32_t soff = __builtin_amdgcn_readfirstlane(tile_off + (uint32_t)r0 * row_bytes);
+    const uint32_t la = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds_ptr_t)(lds + slot0 * 8));
+    copy16_to_lds(rsrc, soff, voff, la);
+  }
+}
+
+
+// D = 128, G % 4 == 0: one workgroup = one (b, kv head, 64-row query block)
+// serving four q heads of that kv head, so each K/V tile crosses L2 -> LDS
+// once for 256 query rows. Eight waves of 32 rows on MFMA 32x32x16 bf16:
+// wave w takes rows 32*(w/4) .. +31 of head w%4, so each SIMD holds one wave
+// of group A (waves 0-3) and one of group B (waves 4-7).
+//
+// Walk: list entries [0, nA) are the union of the four heads' selected
+// blocks, [nA, n) the causal blocks not selected by all four, both
+// ascending; a head computes an entry of the first part when it selected it
+// and of the second part when it did not. Each head thus sees exactly its
+// selected blocks, a snapshot (h_sparse), then its other causal blocks.
+//
+// Ping-pong: time is cut into slots separated by workgroup barriers; in
+// slot 2e group A runs GEMM(e) = QK^T(e) + PV(e-1) while group B runs
+// softmax(e-1), in slot 2e+1 the roles swap. So on every SIMD one wave's MFMA
+// work overlaps the other wave's VALU work. K/V tiles live in NST LDS
+// stages; after its GEMM(e) each wave requests its share of K(e+NST-1) and
+// V(e+NST-2).
+template <int D, int NST>
+__global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ Vt, const int* __restrict__ idx, const int* __restrict__ cnt,
+    uint16_t* __restrict__ Hf, uint16_t* __restrict__ Hs, float* __restrict__ delta,
+    float* __restrict__ lse, Dims d, HeadMap hm) {
+  constexpr int HPW = 4;
+  constexpr int NW = 8;
+  constexpr int KSPR = D / 8;
+  constexpr int VSPR = kBlock / 8;
+  constexpr int NKS = D / 16;
+  constexpr int NDT = D / 32;
+  constexpr int TILE = kBlock * D;
+  constexpr int LPH = (TILE / 8) / (64 * NW);   // buffer loads per half tile (K or V) per wave
+  constexpr float kTau = 8.0f;
+  constexpr int kMaxWords = kMaxKeyBlocks / 32;
+  // one LDS object per stage, always addressed with a compile-time stage,
+  // so copies into one stage and reads of another are known not to alias
+  __shared__ __align__(16) uint16_t K0[TILE], K1[TILE], K2[TILE], K3[NST > 3 ? TILE : 8];
+  __shared__ __align__(16) uint16_t V0[TILE], V1[TILE], V2[TILE], V3[NST > 3 ? TILE : 8];
+  __shared__ uint32_t sel_mask[HPW][kMaxWords];
+  __shared__ uint16_t list[2 * kMaxKeyBlocks];
+  __shared__ int scan_u[kMaxWords], scan_c[kMaxWords];
+  __shared__ int counts[2];
+
+  const int ngrp = d.G / HPW;
+  const int total = d.B * d.Hkv * ngrp * d.nQB;
+  const int lin = xcd_remap(blockIdx.x, total);
+  const int per_group = ngrp * d.nQB;
+  const int grp = lin / per_group;
+  const int rem = lin - grp * per_group;
+  const int qb = d.nQB - 1 - rem / ngrp;
+  const int hg = rem - (rem / ngrp) * ngrp;
+  const int b = grp / d.Hkv;
+  const int g = grp - b * d.Hkv;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hs = wave & 3;
+  const bool group_a = wave < 4;
+  const int h = hm.q_of_kv[g * d.G + hg * HPW + hs];
+  const int bh = b * d.Hq + h;
+  const int c = lane & 31, gl = lane >> 5;
+  const int qq = (wave >> 2) * 32 + c;
+  const int qrow = qb * kBlock + qq;
+  const int diag = qb;
+  const float sl2 = d.scale_log2;
+  const bool sparse_only = (Hf == nullptr);
+
+  // ---- walk list
+  const int nwords = (diag >> 5) + 1;
+  for (int w = tid; w < HPW * kMaxWords; w += 64 * NW) (&sel_mask[0][0])[w] = 0u;
+  {
+    // GEMM(0) multiplies the V stage of the (absent) entry -1 by P = 0
+    uint16_t* vz = (NST - 1) == 1 ? V1 : (NST - 1) == 2 ? V2 : V3;
+    for (int w = tid; w < TILE / 8; w += 64 * NW) ((uint4*)vz)[w] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
+  for (int u = 0; u < HPW; ++u) {
+    const int hu = hm.q_of_kv[g * d.G + hg * HPW + u];
+    const size_t row = (size_t)(b * d.Hq + hu) * d.nQB + qb;
+    const int ns = min(max(cnt[row], 0), d.budget);
+    for (int e = tid; e < ns; e += 64 * NW) {
+      const int kb = idx[row * d.budget + e];
+      if (kb >= 0 && kb <= diag) atomicOr(&sel_mask[u][kb >> 5], 1u << (kb & 31));
+    }
+  }
+  __syncthreads();
+  uint32_t wu = 0u, wc = 0u;
+  if (tid < nwords) {
+    const uint32_t lim = (tid == nwords - 1) ? (0xffffffffu >> (31 - (diag & 31))) : 0xffffffffu;
+    uint32_t any = 0u, all = 0xffffffffu;
+#pragma unroll
+    for (int u = 0; u < HPW; ++u) { any |= sel_mask[u][tid]; all &= sel_mask[u][tid]; }
+    wu = any & lim;
+    wc = sparse_only ? 0u : (~all & lim);
+    scan_u[tid] = __popc(wu);
+    scan_c[tid] = __popc(wc);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int su = 0, sc = 0;
+    for (int w = 0; w < nwords; ++w) {
+      const int pu = scan_u[w], pc = scan_c[w];
+      scan_u[w] = su; scan_c[w] = sc;
+      su += pu; sc += pc;
+    }
+    counts[0] = su;
+    counts[1] = sc;
+  }
+  __syncthreads();
+  const int nA = __builtin_amdgcn_readfirstlane(counts[0]);
+  const int nB = __builtin_amdgcn_readfirstlane(counts[1]);
+  const int n = nA + nB;
+  __syncthreads();
+  if (tid < nwords) {
+    uint32_t m[HPW];
+#pragma unroll
+    for (int u = 0; u < HPW; ++u) m[u] = sel_mask[u][tid];
+    int pos = scan_u[tid];
+    for (uint32_t bb = wu; bb != 0u; bb &= bb - 1u) {
+      const int bit = __builtin_ctz(bb);
+      uint32_t act = 0u;
+#pragma unroll
+      for (int u = 0; u < HPW; ++u) act |= ((m[u] >> bit) & 1u) << u;
+      list[pos++] = (uint16_t)(((tid << 5) + bit) | (act << 12));
+    }
+    pos = nA + scan_c[tid];
+    for (uint32_t bb = wc; bb != 0u; bb &= bb - 1u) {
+      const int bit = __builtin_ctz(bb);
+      uint32_t act = 0u;
+#pragma unroll
+      for (int u = 0; u < HPW; ++u) act |= (((m[u] >> bit) & 1u) ^ 1u) << u;
+      list[pos++] = (uint16_t)(((tid << 5) + bit) | (act << 12));
+    }
+  }
+  __syncthreads();
+
+  // ---- tiles
+  const uint16_t* kbase = K + ((size_t)(b * d.Hkv + g) * d.Nk) * D;
+  const uint16_t* vbase = Vt + ((size_t)(b * d.Hkv + g) * D) * d.Nk;
+  const i32x4_t krs = make_rsrc_words(kbase, (uint32_t)((size_t)d.Nk * D * 2));
+  const i32x4_t vrs = make_rsrc_words(vbase, (uint32_t)((size_t)d.Nk * D * 2));
+  const uint32_t k_row_bytes = D * 2, v_row_bytes = (uint32_t)d.Nk * 2;
+  auto entry_kb = [&](int e) __attribute__((always_inline)) {
+    return __builtin_amdgcn_readfirstlane((int)list[e]) & 0xfff;
+  };
+  auto entry_act = [&](int e) __attribute__((always_inline)) {
+    return ((__builtin_amdgcn_readfirstlane((int)list[e]) >> (12 + hs)) & 1) != 0;
+  };
+  // copies past the end of the list repeat its last block (or block 0):
+  // every slot issues the same number of copies, so the waits are static
+  auto entry_kb_c = [&](int e) __attribute__((always_inline)) {
+    const int ec = min(e, n - 1);
+    return ec >= 0 ? entry_kb(ec) : 0;
+  };
+  auto load_k_kb = [&](auto stc, int kb) __attribute__((always_inline)) {
+    constexpr int st = decltype(stc)::value;
+    uint16_t* kt = st == 0 ? K0 : st == 1 ? K1 : st == 2 ? K2 : K3;
+    tile_to_lds_asm<KSPR, kBlock, NW, true>(krs, (uint32_t)kb * kBlock * k_row_bytes,
+                                           k_row_bytes, kt, wave, lane);
+  };
+  auto load_v_kb = [&](auto stc, int kb) __attribute__((always_inline)) {
+    constexpr int st = decltype(stc)::value;
+    uint16_t* vt = st == 0 ? V0 : st == 1 ? V1 : st == 2 ? V2 : V3;
+    tile_to_lds_asm<VSPR, D, NW, false>(vrs, (uint32_t)kb * kBlock * 2, v_row_bytes, vt,
+                                       wave, lane);
+  };
+  auto load_k = [&](auto stc, int e) __attribute__((always_inline)) {
+    load_k_kb(stc, entry_kb_c(e));
+  };
+  auto load_v = [&](auto stc, int e) __attribute__((always_inline)) {
+    load_v_kb(stc, entry_kb_c(e));
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  bf16x8_t qf[NKS];
+  {
+    const uint16_t* qp = Q + ((size_t)bh * d.Nq + qrow) * D + 8 * gl;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8_t*)(qp + 16 * ks);
+  }
+  // the Q fragments land before any LDS copy is issued: the compiler does
+  // not count the copies, so it must see no load of its own outstanding
+  __builtin_amdgcn_s_waitcnt(0xF70);
+  // prologue = the copies of the virtual slots before slot 0: K(0..NST-2)
+  // and V(0..NST-3), with V(0) standing in for the missing V(-1)
+  load_k(I0{}, 0);
+  load_v(I0{}, 0);
+  load_k(I1{}, 1);
+  load_v(I0{}, 0);
+  if constexpr (NST > 3) {
+    load_k(I2{}, 2);
+    load_v(I1{}, 1);
+  }
+
+  f32x16_t o[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
+  f32x16_t s0, s1;
+  uint32_t pw[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) pw[k] = 0u;
+  float m_ref = -INFINITY, l_sel = 0.f, l_drop = 0.f;
+  const int pr = kperm32(c);
+  const size_t plane = (size_t)d.B * d.Hq * d.Nq;
+
+  auto store = [&](uint16_t* H, float inv) __attribute__((always_inline)) {
+    uint16_t* hp = H + ((size_t)bh * d.Nq + qrow) * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * dt + 8 * i + 4 * gl;
+        const uint32_t lo = pack_bf16x2(o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv);
+        const uint32_t hi2 = pack_bf16x2(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv);
+        *(uint2*)(hp + d0) = make_uint2(lo, hi2);
+      }
+    }
+  };
+  auto snapshot = [&]() __attribute__((always_inline)) {
+    const float lt = pair_sum(l_sel);
+    store(Hs, 1.f / lt);
+    if (lse != nullptr && gl == 0)
+      lse[plane + (size_t)bh * d.Nq + qrow] = (m_ref + __log2f(lt)) * kLn2;
+  };
+
+  // GEMM(e) = 16 MFMAs S(e) = K(e) Q^T plus 16 MFMAs O += V(e-1) P(e-1),
+  // branch-free: an entry a head skips has S ignored and P = 0. The 32 LDS
+  // fragment reads are pipelined PF ahead of the MFMAs that use them.
+  auto gemm = [&](auto stc) __attribute__((always_inline)) {
+    constexpr int sk = decltype(stc)::value;
+    constexpr int sv = (sk + NST - 1) % NST;
+    constexpr int PF = 4;
+    const uint16_t* Kt = sk == 0 ? K0 : sk == 1 ? K1 : sk == 2 ? K2 : K3;
+    const uint16_t* Vtl = sv == 0 ? V0 : sv == 1 ? V1 : sv == 2 ? V2 : V3;
+    bf16x8_t fr[2 * NKS + 4 * NDT];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int ch = 2 * ks + gl;
+      fr[2 * ks] = *(const bf16x8_t*)(Kt + (pr * KSPR + kswz32(pr, ch)) * 8);
+      fr[2 * ks + 1] = *(const bf16x8_t*)(Kt + ((32 + pr) * KSPR + kswz32(32 + pr, ch)) * 8);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int r = 32 * dt + c;
+        fr[2 * NKS + s * NDT + dt] = *(const bf16x8_t*)(Vtl + (r * VSPR + vswz(r, 2 * s + gl)) * 8);
+      }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { s0[v] = 0.f; s1[v] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[2 * ks], qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[2 * ks + 1], qf[ks], s1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 w = make_uint4(pw[4 * s], pw[4 * s + 1], pw[4 * s + 2], pw[4 * s + 3]);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, w);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[2 * NKS + s * NDT + dt], pb, o[dt], 0, 0, 0);
+    }
+    // schedule: PF reads, then (1 MFMA, 1 read) pairs, then the last PF MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+    for (int k = 0; k < 2 * NKS + 4 * NDT - PF; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+  };
+  // softmax(e): P(e) from S(e); the sparse snapshot is taken before the
+  // first entry of the second part can rescale the accumulator.
+  auto softmax = [&](int e) __attribute__((always_inline)) {
+    if (e == nA) snapshot();
+    if (e >= n || !entry_act(e)) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) pw[k] = 0u;
+      return;
+    }
+    const int kb = entry_kb(e);
+    if (kb == diag) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key0 = 16 * (v >> 3) + 8 * gl + (v & 7);
+        if (key0 > qq) s0[v] = -INFINITY;
+        if (key0 + 32 > qq) s1[v] = -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
+    const float m_blk = pair_max(mx) * sl2;
+    if (__builtin_amdgcn_ballot_w64(m_blk > m_ref + kTau) != 0) {
+      const float m_new = fmaxf(m_ref, m_blk);
+      const float alpha = fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+      l_sel *= alpha;
+      l_drop *= alpha;
+    }
+    float ls = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      const float a0 = fast_exp2(fmaf(s0[v], sl2, -m_ref));
+      const float a1 = fast_exp2(fmaf(s0[v + 1], sl2, -m_ref));
+      const float e0 = fast_exp2(fmaf(s1[v], sl2, -m_ref));
+      const float e1 = fast_exp2(fmaf(s1[v + 1], sl2, -m_ref));
+      pw[v >> 1] = pack_bf16x2(a0, a1);
+      pw[8 + (v >> 1)] = pack_bf16x2(e0, e1);
+      ls = add_bf16x2(pw[v >> 1], ls);
+      ls = add_bf16x2(pw[8 + (v >> 1)], ls);
+    }
+    if (e < nA) l_sel += ls; else l_drop += ls;
+  };
+  // Slots are opened by workgroup barriers. Group A runs GEMM(t) in slot 2t
+  // and softmax(t) in slot 2t+1, group B one slot later; each wave requests
+  // its share of K(t+NST-1) and V(t+NST-2) after its GEMM(t). Before a
+  // wave's GEMM barrier, its copies needed by the next GEMM slot of either
+  // group have landed: group A keeps the copies of its last NST-2 GEMM slots
+  // in flight, group B those of its last NST-3.
+  auto issue_tiles = [&](auto stc, int kbk, int kbv) __attribute__((always_inline)) {
+    constexpr int st = decltype(stc)::value;
+    load_k_kb(std::integral_constant<int, (st + NST - 1) % NST>{}, kbk);
+    load_v_kb(std::integral_constant<int, (st + NST - 2) % NST>{}, kbv);
+  };
+  // Workgroup barrier that the compiler may not move memory accesses across;
+  // this wave's LDS reads have completed before it (the stage it read may be
+  // overwritten once the barrier opens).
+  auto slot_barrier = [&]() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  // s_waitcnt immediates: vmcnt(k), expcnt and lgkmcnt left open
+  constexpr int kWaitA = 0xF70 | (2 * LPH * (NST - 2));
+  constexpr int kWaitB = 0xF70 | (2 * LPH * (NST - 3));
+  // group B's extra barrier opens slot 0, in which group A reads K(0)
+  if (!group_a) {
+    __builtin_amdgcn_s_waitcnt(kWaitA);
+    slot_barrier();
+  }
+  // blocks of the copies issued after GEMM(t), looked up one slot pair
+  // earlier (the lookups then wait only behind softmax work)
+  int kbk = entry_kb_c(NST - 1), kbv = entry_kb_c(NST - 2);
+  auto slots = [&](auto stc, int t) __attribute__((always_inline)) {
+    if (group_a) __builtin_amdgcn_s_waitcnt(kWaitA);
+    else __builtin_amdgcn_s_waitcnt(kWaitB);
+    slot_barrier();
+    __builtin_amdgcn_s_setprio(1);
+    gemm(stc);
+    __builtin_amdgcn_s_setprio(0);
+    issue_tiles(stc, kbk, kbv);
+    slot_barrier();
+    kbk = entry_kb_c(t + NST);
+    kbv = entry_kb_c(t + NST - 1);
+    softmax(t);
+  };
+  for (int t = 0; t <= n; t += NST) {
+    slots(I0{}, t);
+    if (t + 1 > n) break;
+    slots(I1{}, t + 1);
+    if (t + 2 > n) break;
+    slots(I2{}, t + 2);
+    if constexpr (NST > 3) {
+      if (t + 3 > n) break;
+      slots(I3{}, t + 3);
+    }
+  }
+  if (group_a) slot_barrier();
+  __builtin_amdgcn_s_waitcnt(0xF70);
+  if (sparse_only) return;
+  const float ls_t = pair_sum(l_sel);
+  const float ld_t = pair_sum(l_drop);
+  const float lt = ls_t + ld_t;
+  store(Hf, 1.f / lt);
+  if (gl == 0) {
+    if (delta != nullptr) delta[(size_t)bh * d.Nq + qrow] = ld_t / lt;
+    if (lse != nullptr) lse[(size_t)bh * d.Nq + qrow] = (m_ref + __log2f(lt)) * kLn2;
+  }
+}
+
 hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* vt,
                                     const int* idx, const int* cnt, uint16_t* hf, uint16_t* hs,
                                     float* delta, float* lse, const Dims& d, const HeadMap& hm,
                                     hipStream_t stream) {
+  // both modes of a shape go through the same kernel, so a sparse-only call
+  // reproduces the h_sparse of the dual call bit for bit
+  if (d.D == 128 && d.G % 4 == 0) {
+    const int groups = d.B * d.Hkv * (d.G / 4) * d.nQB;
+    hipLaunchKernelGGL((attn_prefill_bf16_pp_kernel<128, 3>), dim3(groups), dim3(512), 0, stream,
+                       q, k, vt, idx, cnt, hf, hs, delta, lse, d, hm);
+    return hipGetLastError();
+  }
   const int total = d.B * d.Hq * d.nQB;
   if (d.D == 128)
     hipLaunchKernelGGL(attn_prefill_bf16_kernel<128>, dim3(total), dim3(256), 0, stream, q, k,

@@ -12,6 +12,8 @@ import oracle.ssa_oracle as O
 BF16_ABS = 2e-2      # max-abs bar for bf16 inputs, float32 accumulation
 F32_ABS = 1e-5       # max-abs bar for float32 problems
 BF16_REL_L2 = 1e-2   # relative L2 bar (informative, asserted)
+# delta = l_drop / (l_sel + l_drop) from sums of bf16-rounded weights (each
+# relative error <= 2^-9): |d delta| <= delta (1 - delta) * 2 * 2^-9 <= 2^-10
 BF16_DELTA_ABS = 1e-3
 
 

@@ -75,8 +75,11 @@ def full_compare(cfg, x, got, *, budget, n_sink=1, n_local=1, head_map=None, lse
         rb = (torch.arange(nq) // cfg.block) if nq > 1 else torch.zeros(nq, dtype=torch.long)
         tokmask = sel[:, :, rb][..., torch.arange(nk) // cfg.block] & causal
         sparse = torch.logsumexp(z.masked_fill(~tokmask, -math.inf), -1)
-        assert_close("lse_full", got["lse"][0].double().numpy(), full.numpy(), 1e-3)
-        assert_close("lse_sparse", got["lse"][1].double().numpy(), sparse.numpy(), 1e-3)
+        # bf16: the row sums add the bfloat16-rounded weights (relative error
+        # <= 2^-9 each), so |d lse| <= ln(1 + 2^-9) ~ 1.95e-3; fp32 exact sums
+        lse_tol = 1e-3 if f32 else 2.5e-3
+        assert_close("lse_full", got["lse"][0].double().numpy(), full.numpy(), lse_tol)
+        assert_close("lse_sparse", got["lse"][1].double().numpy(), sparse.numpy(), lse_tol)
     return ref
 
 
@@ -92,6 +95,12 @@ SMALL = [
     ("mha_4k", dict(Hq=2, Hkv=2, N=640), 3, 0, 0),
     ("gqa_8k_peaked", dict(B=2, Hq=8, Hkv=2, N=1024), 4, 1, 1),
     ("gqa_8k_peaked", dict(B=1, Hq=4, Hkv=1, N=2048), 6, 2, 2),
+    # four q heads per workgroup: G = 8 (two groups per kv head), no forced
+    # blocks (the diagonal block may be dropped), several bitmap words, iid
+    # inputs (the heads' selections differ widely)
+    ("gqa_8k_peaked", dict(B=2, Hq=16, Hkv=2, N=1536), 5, 0, 0),
+    ("gqa_8k_peaked", dict(B=1, Hq=4, Hkv=1, N=4096), 7, 1, 2),
+    ("gqa_8k_peaked", dict(B=1, Hq=8, Hkv=2, N=2048, planted=False), 6, 1, 1),
     ("gqa_decode_64k", dict(B=3, Hq=8, Hkv=2, N=2048), 4, 1, 1),
     ("gqa_decode_64k", dict(B=2, Hq=8, Hkv=1, N=4096, D=64), 5, 1, 1),
     ("gqa_decode_64k", dict(B=2, Hq=2, Hkv=2, N=640), 3, 0, 1),
@@ -142,6 +151,16 @@ def test_full_budget_gives_identical_streams(ssa):
     assert float(got["loss"][0]) == 0.0
     nkb = 16
     assert torch.equal(got["idx"][0, 0, -1], torch.arange(nkb, dtype=torch.int32))
+
+
+def test_full_budget_gives_identical_streams_grouped(ssa):
+    """Four q heads per kv head (one workgroup serves all four): with every
+    block selected the walk has no second part and both streams coincide."""
+    cfg = CONFIGS["gqa_8k_peaked"].with_sizes(B=1, Hq=8, Hkv=2, N=1024)
+    x = make_inputs(cfg)
+    got = gpu_run(ssa, x, budget=20)
+    assert torch.equal(got["h_sparse"], got["h_full"])
+    assert torch.count_nonzero(got["delta"]) == 0
 
 
 def test_run_to_run_determinism(ssa):

@@ -867,9 +867,9 @@ hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const 
                                     const int* idx, const int* cnt, uint16_t* hf, uint16_t* hs,
                                     float* delta, float* lse, const Dims& d, const HeadMap& hm,
                                     hipStream_t stream) {
-  // both modes of a shape go through the same kernel, so a sparse-only call
-  // reproduces the h_sparse of the dual call bit for bit
-  if (d.D == 128 && d.G % 4 == 0) {
+  // dual mode with four q heads per workgroup; sparse-only calls go to the
+  // per-head kernel, which walks only each head's own selected blocks
+  if (d.D == 128 && d.G % 4 == 0 && hf != nullptr) {
     const int groups = d.B * d.Hkv * (d.G / 4) * d.nQB;
     hipLaunchKernelGGL((attn_prefill_bf16_pp_kernel<128, 3>), dim3(groups), dim3(512), 0, stream,
                        q, k, vt, idx, cnt, hf, hs, delta, lse, d, hm);

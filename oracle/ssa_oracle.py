@@ -36,6 +36,8 @@ reason in the design notes):
   `budget` counts all selected blocks, forced included; when no more
   candidates remain than free slots, all causal blocks are selected; exact
   score ties go to the lower block index;
+* optionally (group-shared selection) one list per GQA group, ranked by the
+  sum of the group's per-head scores, added in ascending head order;
 * token-level causal masking j <= t inside the query's own block, in both
   streams; logit scale 1/sqrt(D) unless given;
 * losses are mean squared errors over all B*Hq*Nq*D elements; their forward
@@ -95,6 +97,16 @@ def block_score_matrix(qbar: np.ndarray, kbar: np.ndarray) -> np.ndarray:
     return s
 
 
+def group_score_matrix(per_head: Sequence[np.ndarray]) -> np.ndarray:
+    """Score of a GQA group for group-shared selection: the sum of its q
+    heads' score matrices, added in the order given (ascending q head index)
+    in float64, starting from zero."""
+    s = np.zeros_like(np.asarray(per_head[0], dtype=np.float64))
+    for x in per_head:
+        s = s + np.asarray(x, dtype=np.float64)
+    return s
+
+
 def forced_blocks(diag: int, n_sink: int, n_local: int) -> List[int]:
     """Blocks every row keeps: the first n_sink blocks and the n_local blocks
     ending at the row's own block `diag`, restricted to [0, diag]."""
@@ -141,12 +153,19 @@ def row_block_diag(nq: int, nk: int, block: int, qb: int) -> int:
 
 def select_blocks(q: np.ndarray, k: np.ndarray, *, block: int, budget: int,
                   n_sink: int, n_local: int, head_map: Sequence[int],
-                  k_pooled: Optional[np.ndarray] = None):
+                  k_pooled: Optional[np.ndarray] = None, group_shared: bool = False):
     """Selection for every (b, q head, row block).
 
     q [B, Hq, Nq, D], k [B, Hkv, Nk, D]. Returns idx [B, Hq, nQB, budget]
     int32 (ascending, padded with -1) and cnt [B, Hq, nQB] int32.
     In decode (Nq == 1) the query row is its own representation.
+
+    group_shared: one list per (b, kv head, row block), given to every q head
+    of the group. The group's score of a key block is the sum of its q heads'
+    scores (float64, heads in ascending index order, starting from 0), i.e.
+    the pooled key against the sum of the heads' pooled queries. This is the
+    GQA-group-shared reading of "the query" in "Practical Implementation of
+    SSA" (the pages select per query; a GQA group reads one kv head).
     """
     B, Hq, nq, D = q.shape
     nk = k.shape[2]
@@ -159,6 +178,18 @@ def select_blocks(q: np.ndarray, k: np.ndarray, *, block: int, budget: int,
     idx = np.full((B, Hq, nqb, budget), -1, dtype=np.int32)
     cnt = np.zeros((B, Hq, nqb), dtype=np.int32)
     for b in range(B):
+        if group_shared:
+            for g in range(k.shape[1]):
+                heads = [h for h in range(Hq) if head_map[h] == g]
+                s = group_score_matrix([block_score_matrix(qbar[b, h], kbar[b, g])
+                                        for h in heads])
+                for qb in range(nqb):
+                    diag = row_block_diag(nq, nk, block, qb)
+                    sel = select_row(s[qb], diag, budget, n_sink, n_local)
+                    for h in heads:
+                        idx[b, h, qb, :len(sel)] = sel
+                        cnt[b, h, qb] = len(sel)
+            continue
         for h in range(Hq):
             s = block_score_matrix(qbar[b, h], kbar[b, head_map[h]])
             for qb in range(nqb):
@@ -286,7 +317,7 @@ def align_loss(h_full: np.ndarray, h_sparse: np.ndarray):
 
 def ssa_forward(q, k, v, *, block: int, budget: int, n_sink: int, n_local: int,
                 scale: Optional[float] = None, head_map: Optional[Sequence[int]] = None,
-                k_pooled: Optional[np.ndarray] = None):
+                k_pooled: Optional[np.ndarray] = None, group_shared: bool = False):
     """Selection, both streams, dropped mass and losses for a whole problem.
 
     q [B, Hq, Nq, D], k and v [B, Hkv, Nk, D] (any float dtype; used at their
@@ -303,7 +334,8 @@ def ssa_forward(q, k, v, *, block: int, budget: int, n_sink: int, n_local: int,
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     idx, cnt = select_blocks(q, k, block=block, budget=budget, n_sink=n_sink,
-                             n_local=n_local, head_map=head_map, k_pooled=k_pooled)
+                             n_local=n_local, head_map=head_map, k_pooled=k_pooled,
+                             group_shared=group_shared)
     res = dual_attention(q, k, v, idx, block=block, scale=scale, head_map=head_map)
     h_full = np.zeros((B, Hq, nq, D))
     h_sparse = np.zeros((B, Hq, nq, D))

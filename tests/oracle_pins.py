@@ -295,6 +295,67 @@ def check_gqa_equals_replicated(seed=9):
         assert np.allclose(a[key], b[key], atol=1e-14)
 
 
+def _brute_group_selection(q, k, bs, budget, n_sink, n_local, head_map):
+    """Group-shared lists from exact rational arithmetic on the raw inputs:
+    pooled means and dot products as Fractions, summed over the group's
+    heads, ranked by (-score, index); forced blocks added."""
+    B, Hq, nq, D = q.shape
+    Hkv, nk = k.shape[1], k.shape[2]
+    nqb, nkb = (1 if nq == 1 else nq // bs), nk // bs
+    out = {}
+    for b in range(B):
+        for g in range(Hkv):
+            heads = [h for h in range(Hq) if head_map[h] == g]
+            kbar = [[sum(Fraction(float(k[b, g, j * bs + t, d])) for t in range(bs)) / bs
+                     for d in range(D)] for j in range(nkb)]
+            for qb in range(nqb):
+                diag = O.row_block_diag(nq, nk, bs, qb)
+                score = [Fraction(0)] * nkb
+                for h in heads:
+                    if nq == 1:
+                        qv = [Fraction(float(q[b, h, 0, d])) for d in range(D)]
+                    else:
+                        qv = [sum(Fraction(float(q[b, h, qb * bs + t, d])) for t in range(bs)) / bs
+                              for d in range(D)]
+                    for j in range(nkb):
+                        score[j] += sum(qv[d] * kbar[j][d] for d in range(D))
+                forced = O.forced_blocks(diag, n_sink, n_local)
+                cands = [j for j in range(diag + 1) if j not in forced]
+                free = budget - len(forced)
+                picks = cands if len(cands) <= free else \
+                    sorted(cands, key=lambda j: (-score[j], j))[:free]
+                out[(b, g, qb)] = sorted(forced + picks)
+    return out
+
+
+def check_group_shared_selection(seed=12):
+    """Group-shared selection against exact rational brute force (small
+    integer inputs keep every float step exact), in prefill and decode; every
+    head of a group gets the group's list; with one q head per kv head the
+    group mode is the per-head mode."""
+    r = _rng(seed)
+    for nq_mode in ("prefill", "decode"):
+        B, Hq, Hkv, bs, nb, D = 2, 6, 2, 2, 7, 3
+        n = bs * nb
+        nq = n if nq_mode == "prefill" else 1
+        q = r.integers(-4, 5, size=(B, Hq, nq, D)).astype(np.float64)
+        k = r.integers(-4, 5, size=(B, Hkv, n, D)).astype(np.float64)
+        hm = [0, 1, 1, 0, 0, 1]
+        for budget, n_sink, n_local in ((3, 1, 1), (4, 0, 1), (5, 1, 0)):
+            idx, cnt = O.select_blocks(q, k, block=bs, budget=budget, n_sink=n_sink,
+                                       n_local=n_local, head_map=hm, group_shared=True)
+            want = _brute_group_selection(q, k, bs, budget, n_sink, n_local, hm)
+            for (b, g, qb), sel in want.items():
+                for h in [h for h in range(Hq) if hm[h] == g]:
+                    assert int(cnt[b, h, qb]) == len(sel), (nq_mode, b, g, qb)
+                    assert idx[b, h, qb, :len(sel)].tolist() == sel, (nq_mode, b, h, qb, sel)
+    q = r.standard_normal((1, 2, 16, 4)); k = r.standard_normal((1, 2, 16, 4))
+    a = O.select_blocks(q, k, block=4, budget=2, n_sink=1, n_local=0, head_map=[0, 1])
+    b2 = O.select_blocks(q, k, block=4, budget=2, n_sink=1, n_local=0, head_map=[0, 1],
+                         group_shared=True)
+    assert np.array_equal(a[0], b2[0]) and np.array_equal(a[1], b2[1])
+
+
 def check_decode_vs_sdpa(seed=10):
     """Decode: one query at the last position, its own block representation,
     diag = last block; streams equal SDPA on that single row."""
@@ -367,5 +428,5 @@ ALL_CHECKS = [
     check_attention_constant_keys, check_attention_graded_logits,
     check_full_budget_equals_full, check_decomposition_and_bound, check_nested_budgets,
     check_gqa_equals_replicated, check_decode_vs_sdpa, check_loss_vs_torch,
-    check_worked_example,
+    check_worked_example, check_group_shared_selection,
 ]

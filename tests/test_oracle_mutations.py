@@ -8,6 +8,7 @@ import oracle_pins as P
 
 _pool, _scores, _select_row, _rows, _loss = (O.pool_blocks, O.block_score_matrix,
                                              O.select_row, O.dual_attention_rows, O.align_loss)
+_group = O.group_score_matrix
 
 
 def m_pool_sum(x, block):                      # sum instead of mean
@@ -68,6 +69,14 @@ def m_loss_grad_sign(hf, hs):                  # gradient seeds swapped
     return a, b, d, c
 
 
+def m_group_first_head(per_head):             # group score = first head only
+    return _group(per_head[:1])
+
+
+def m_group_max(per_head):                     # max over heads instead of the sum
+    return np.maximum.reduce([np.asarray(x, dtype=np.float64) for x in per_head])
+
+
 MUTATIONS = [
     ("pool_blocks", m_pool_sum), ("pool_blocks", m_pool_strided),
     ("block_score_matrix", m_scores_transposed),
@@ -75,6 +84,7 @@ MUTATIONS = [
     ("dual_attention_rows", m_rows_strict_causal), ("dual_attention_rows", m_rows_no_renorm),
     ("dual_attention_rows", m_rows_no_scale), ("dual_attention_rows", m_rows_delta_kept),
     ("align_loss", m_loss_row_mean), ("align_loss", m_loss_grad_sign),
+    ("group_score_matrix", m_group_first_head), ("group_score_matrix", m_group_max),
 ]
 
 

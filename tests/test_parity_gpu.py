@@ -135,11 +135,28 @@ def test_decode_sparse_only_and_pooled_table(ssa):
 
 
 def test_prefill_sparse_only_matches_dual_bitwise(ssa):
-    cfg = CONFIGS["gqa_8k_peaked"].with_sizes(B=1, Hq=4, Hkv=1, N=1024, budget=4)
+    """Two q heads per kv head: both modes run the per-head kernel, whose
+    sparse-only walk is the first part of the dual walk."""
+    cfg = CONFIGS["gqa_8k_peaked"].with_sizes(B=1, Hq=4, Hkv=2, N=1024, budget=4)
     x = make_inputs(cfg)
     dual = gpu_run(ssa, x, budget=4)
     sp = gpu_run(ssa, x, budget=4, sparse_only=True)
     assert torch.equal(sp["h_sparse"], dual["h_sparse"])
+
+
+def test_prefill_sparse_only_grouped_shape(ssa):
+    """Four q heads per kv head: dual mode runs the grouped kernel, sparse-only
+    the per-head kernel; both match the oracle and each other."""
+    cfg = CONFIGS["gqa_8k_peaked"].with_sizes(B=1, Hq=8, Hkv=2, N=2048, budget=5)
+    say(f"[parity] sparse-only prefill {cfg}")
+    x = make_inputs(cfg)
+    dual = gpu_run(ssa, x, budget=5)
+    sp = gpu_run(ssa, x, budget=5, sparse_only=True)
+    ref = full_compare(cfg, x, dual, budget=5)
+    assert "h_full" not in sp
+    assert torch.equal(sp["idx"], dual["idx"])
+    assert_close("h_sparse (sparse-only)", to_np64(sp["h_sparse"]), ref["h_sparse"], BF16_ABS, BF16_REL_L2)
+    assert_close("sparse-only vs dual", to_np64(sp["h_sparse"]), to_np64(dual["h_sparse"]), 1e-2)
 
 
 def test_full_budget_gives_identical_streams(ssa):

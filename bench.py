@@ -35,8 +35,8 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 # HBM-counter summary under profiles/), keyed by the SHA-256 of the kernel
 # source they were taken on; any other source reports traffic as null.
 PREFILL_TRAFFIC = {
-    # 786997 KiB x 2.000 read + 528385 KiB x 1.000 written per dispatch
-    "2f5cf956d52973ad6f32d54dc9fb3113d158987f6bb0f312e147f16e7ebaa820": int(786997 * 2.0 * 1024 + 528385 * 1.0 * 1024),
+    # 773338 KiB x 2.000 read + 528444 KiB x 1.000 written per dispatch
+    "8cf5dca899277ab1e449c7dca790d59285f7b5264226489d5fe99b7eada8633c": int(773338 * 2.0 * 1024 + 528444 * 1.0 * 1024),
 }
 PREFILL_SRC = os.path.join(ROOT, "block_sparse_full_amd", "csrc", "ssa_attn_prefill.hip")
 
@@ -141,6 +141,23 @@ def run_prefill(ssa, torch, cfg, steps, warmup, budgets):
                            "sparse_only_attn_ms": round(sp.mean_ms(), 4),
                            "delta_mean": round(float(out["delta"].mean()), 4)}
     res["sweep"] = sweep
+    # group-shared selection (one list per GQA group) at the headline budget
+    pg = ssa.problem_for(q, k, budget=cfg.budget, n_sink=cfg.n_sink, n_local=cfg.n_local,
+                         group_select=True)
+    ig, cg = ssa.select_blocks(pg, q, k, ws=ws)
+    ssa.attn_fwd(pg, q, k, v, ig, cg, ws=ws, out=out)
+    tsel, tg = EventTimer(torch), EventTimer(torch)
+    for _ in range(max(3, steps // 4)):
+        tsel.start()
+        ssa.select_blocks(pg, q, k, ws=ws, idx=ig, cnt=cg)
+        tsel.stop()
+        tg.start()
+        ssa.attn_fwd(pg, q, k, v, ig, cg, ws=ws, out=out)
+        tg.stop()
+    torch.cuda.synchronize()
+    res["group_select"] = {"budget": cfg.budget, "select_ms": round(tsel.mean_ms(), 4),
+                           "dual_attn_ms": round(tg.mean_ms(), 4),
+                           "delta_mean": round(float(out["delta"].mean()), 4)}
     del q, k, v, out, ws
     torch.cuda.empty_cache()
     return res
@@ -352,6 +369,7 @@ def main():
         "loss_sparsity": pre["loss"],
         "delta_mean": round(pre["delta_mean"], 4),
         "budget_sweep": pre.get("sweep"),
+        "group_select": pre.get("group_select"),
     }
     if not args.no_decode:
         dec = run_decode(ssa, torch, CONFIGS["gqa_decode_64k"], max(5, args.steps // 2),

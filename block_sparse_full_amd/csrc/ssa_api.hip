@@ -95,6 +95,9 @@ ssa_status build(const ssa_problem* p, Problem* P) {
   const bool decode = p->Nq == 1 && p->Nk != 1;
   if (decode && p->dtype == SSA_BF16 && G > ssa::kDecMaxGroup)
     return fail(SSA_ERR_UNSUPPORTED, "bf16 decode supports Hq/Hkv <= %d; got %d", ssa::kDecMaxGroup, G);
+  if (p->selection != SSA_SELECT_PER_HEAD && p->selection != SSA_SELECT_GROUP)
+    return fail(SSA_ERR_INVALID_ARG, "selection must be SSA_SELECT_PER_HEAD (0) or SSA_SELECT_GROUP (1); "
+                "got %d", p->selection);
   if (!(p->scale >= 0.f) || isinf(p->scale))
     return fail(SSA_ERR_INVALID_ARG, "scale must be finite and >= 0 (0 selects 1/sqrt(D))");
   const double total = (double)p->B * p->Hq * p->Nq * p->D;
@@ -130,6 +133,7 @@ ssa_status build(const ssa_problem* p, Problem* P) {
     d.nQB = 1;
   }
   d.G = G;
+  d.group_select = p->selection == SSA_SELECT_GROUP ? 1 : 0;
   d.scale = p->scale > 0.f ? p->scale : (float)(1.0 / sqrt((double)p->D));
   d.scale_log2 = d.scale * ssa::kLog2e;
   P->bf16 = p->dtype == SSA_BF16;

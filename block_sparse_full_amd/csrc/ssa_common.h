@@ -22,6 +22,7 @@ struct Dims {
   int B, Hq, Hkv, Nq, Nk, D;
   int budget, n_sink, n_local;
   int nQB, nKB, G;     // query row blocks, key blocks, q heads per kv head
+  int group_select;    // 1: one selection per GQA group (summed head scores)
   float scale;         // logit scale
   float scale_log2;    // scale * log2(e)
 };

@@ -88,6 +88,11 @@ hipError_t launch_pool(const void* x, bool bf16, float* out, long nblk_total, in
 // equal to it, the lowest block indices fill the remaining slots. The
 // ascending index list is written by a ballot/popcount compaction over the
 // causal blocks in order.
+//
+// Group-shared selection (d.group_select): all G heads are scored in one
+// pass and only their sum is kept, added in the order of q_of_kv (ascending
+// q head index) in float64 from zero; every wave then runs the same select
+// on that single key row and writes the list for its heads.
 constexpr int kSelThreads = 256;
 constexpr int kSelWaves = kSelThreads / 64;
 
@@ -121,9 +126,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar,
     int* __restrict__ idx, int* __restrict__ cnt, Dims d, HeadMap hm, int hc) {
   extern __shared__ __align__(16) unsigned char smem[];
-  // layout: keys[hc][nKB] u64 | qv[hc][D] f32
+  // layout: keys[hc or 1][nKB] u64 | qv[hc][D] f32
   uint64_t* keys = (uint64_t*)smem;
-  float* qv = (float*)(smem + (size_t)hc * d.nKB * sizeof(uint64_t));
+  float* qv = (float*)(smem + (size_t)(d.group_select ? 1 : hc) * d.nKB * sizeof(uint64_t));
   __shared__ unsigned hist[kSelWaves][256];
 
   const int tid = threadIdx.x;
@@ -160,6 +165,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       for (int kb = tid; kb < ncausal; kb += kSelThreads) {
         if (is_forced(kb, diag, d.n_sink, d.n_local)) continue;
         const float* kr = krow0 + (size_t)kb * d.D;
+        double gsum = 0.0;
         for (int hb = 0; hb < nh; hb += 4) {
           double sc[4] = {0.0, 0.0, 0.0, 0.0};
           for (int dd = 0; dd < d.D; dd += 4) {
@@ -173,10 +179,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                 if (hb + j < nh) sc[j] = __fma_rn((double)qv[(hb + j) * d.D + dd + e], kv, sc[j]);
             }
           }
+          if (d.group_select) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (hb + j < nh) keys[(size_t)(hb + j) * d.nKB + kb] = orderable_key(sc[j]);
+            for (int j = 0; j < 4; ++j)
+              if (hb + j < nh) gsum += sc[j];
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (hb + j < nh) keys[(size_t)(hb + j) * d.nKB + kb] = orderable_key(sc[j]);
+          }
         }
+        if (d.group_select) keys[kb] = orderable_key(gsum);
       }
     }
     __syncthreads();
@@ -184,7 +197,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     // ---- per-wave selection, one head at a time
     for (int hh = wave; hh < nh; hh += kSelWaves) {
       const int h = hm.q_of_kv[g * d.G + h0 + hh];
-      const uint64_t* hk = keys + (size_t)hh * d.nKB;
+      const uint64_t* hk = keys + (size_t)(d.group_select ? 0 : hh) * d.nKB;
       uint64_t thr = 0ull;   // keys above thr are taken
       int k_eq = 0;          // and this many of the keys equal to thr
       if (!take_all && !forced_only) {
@@ -259,6 +272,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 }
 
 int select_heads_per_pass(const Dims& d) {
+  if (d.group_select) return d.G;   // one pass: every head feeds the one sum
   int hc = (int)(kSelKeyBytes / ((size_t)d.nKB * sizeof(uint64_t)));
   if (hc > d.G) hc = d.G;
   if (hc < 1) hc = 1;
@@ -266,7 +280,8 @@ int select_heads_per_pass(const Dims& d) {
 }
 
 size_t select_smem_bytes(const Dims& d, int hc) {
-  return (size_t)hc * d.nKB * sizeof(uint64_t) + (size_t)hc * d.D * sizeof(float);
+  const int key_rows = d.group_select ? 1 : hc;
+  return (size_t)key_rows * d.nKB * sizeof(uint64_t) + (size_t)hc * d.D * sizeof(float);
 }
 
 hipError_t launch_select(const float* qbar, const float* kbar, int* idx, int* cnt,

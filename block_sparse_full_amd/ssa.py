@@ -24,6 +24,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssa.so"
 _lib = None
 
 SSA_F32, SSA_BF16 = 0, 1
+SSA_SELECT_PER_HEAD, SSA_SELECT_GROUP = 0, 1
 STATUS = {0: "SSA_OK", 1: "SSA_ERR_INVALID_ARG", 2: "SSA_ERR_UNSUPPORTED",
           3: "SSA_ERR_WORKSPACE", 4: "SSA_ERR_HIP"}
 EXPORTS = ("ssa_workspace_bytes", "ssa_pool_blocks", "ssa_select_blocks", "ssa_attn_fwd",
@@ -43,7 +44,7 @@ class SsaProblem(ctypes.Structure):
                 ("block_size", ctypes.c_int32), ("budget", ctypes.c_int32),
                 ("n_sink", ctypes.c_int32), ("n_local", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
-                ("head_map", ctypes.POINTER(ctypes.c_int32))]
+                ("head_map", ctypes.POINTER(ctypes.c_int32)), ("selection", ctypes.c_int32)]
 
 
 def lib_path() -> str:
@@ -97,6 +98,7 @@ class Problem:
     scale: float = 0.0
     dtype: int = SSA_BF16
     head_map: Optional[Sequence[int]] = None
+    selection: int = SSA_SELECT_PER_HEAD
 
     def to_c(self):
         hm = None
@@ -105,7 +107,8 @@ class Problem:
             keep = (ctypes.c_int32 * len(self.head_map))(*[int(x) for x in self.head_map])
             hm = ctypes.cast(keep, ctypes.POINTER(ctypes.c_int32))
         c = SsaProblem(self.B, self.Hq, self.Hkv, self.Nq, self.Nk, self.D, self.block_size,
-                       self.budget, self.n_sink, self.n_local, float(self.scale), self.dtype, hm)
+                       self.budget, self.n_sink, self.n_local, float(self.scale), self.dtype, hm,
+                       int(self.selection))
         return c, keep
 
     @property
@@ -119,7 +122,7 @@ class Problem:
 
 def problem_for(q: torch.Tensor, k: torch.Tensor, *, budget: int, n_sink: int = 1,
                 n_local: int = 1, block_size: int = 64, scale: float = 0.0,
-                head_map: Optional[Sequence[int]] = None) -> Problem:
+                head_map: Optional[Sequence[int]] = None, group_select: bool = False) -> Problem:
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be 4-D [B, H, N, D]")
     dt = {torch.bfloat16: SSA_BF16, torch.float32: SSA_F32}.get(q.dtype)
@@ -127,7 +130,8 @@ def problem_for(q: torch.Tensor, k: torch.Tensor, *, budget: int, n_sink: int = 
         raise TypeError(f"unsupported dtype {q.dtype}")
     return Problem(B=q.shape[0], Hq=q.shape[1], Hkv=k.shape[1], Nq=q.shape[2], Nk=k.shape[2],
                    D=q.shape[3], budget=budget, n_sink=n_sink, n_local=n_local,
-                   block_size=block_size, scale=scale, dtype=dt, head_map=head_map)
+                   block_size=block_size, scale=scale, dtype=dt, head_map=head_map,
+                   selection=SSA_SELECT_GROUP if group_select else SSA_SELECT_PER_HEAD)
 
 
 def _check(status: int):
@@ -264,10 +268,12 @@ def align_loss(p: Problem, h_full, h_sparse, *, want_grads: bool = False,
 
 def dual_attention(q, k, v, *, budget: int, n_sink: int = 1, n_local: int = 1,
                    scale: float = 0.0, head_map=None, k_pooled=None, sparse_only: bool = False,
-                   want_lse: bool = False, want_grads: bool = False, ws=None):
-    """Selection, both attention streams, dropped mass and alignment losses."""
+                   want_lse: bool = False, want_grads: bool = False, ws=None,
+                   group_select: bool = False):
+    """Selection, both attention streams, dropped mass and alignment losses.
+    group_select: one block list per GQA group (SSA_SELECT_GROUP)."""
     p = problem_for(q, k, budget=budget, n_sink=n_sink, n_local=n_local, scale=scale,
-                    head_map=head_map)
+                    head_map=head_map, group_select=group_select)
     ws = ws if ws is not None else alloc_workspace(p, q.device)
     idx, cnt = select_blocks(p, q, None if k_pooled is not None else k, k_pooled, ws=ws)
     out = attn_fwd(p, q, k, v, idx, cnt, sparse_only=sparse_only, want_lse=want_lse, ws=ws)

@@ -60,6 +60,16 @@ typedef enum {
 
 typedef enum { SSA_F32 = 0, SSA_BF16 = 1 } ssa_dtype;
 
+/* Block selection granularity (ssa_problem.selection).
+ *   SSA_SELECT_PER_HEAD : one list per (b, q head, query block)
+ *   SSA_SELECT_GROUP    : one list per (b, kv head, query block), given to
+ *                         every q head of that GQA group; a key block's group
+ *                         score is the sum of its q heads' scores (float64,
+ *                         q heads in ascending index order). The pages select
+ *                         per query ("Practical Implementation of SSA"); the
+ *                         group reading lets a GQA group share one list. */
+typedef enum { SSA_SELECT_PER_HEAD = 0, SSA_SELECT_GROUP = 1 } ssa_selection;
+
 /* One attention problem (one layer's attention of one batch).
  *   B, Hq, Hkv : batch, query heads, key/value heads (Hq % Hkv == 0)
  *   Nq, Nk     : query rows and key positions per head
@@ -72,12 +82,14 @@ typedef enum { SSA_F32 = 0, SSA_BF16 = 1 } ssa_dtype;
  *   dtype      : ssa_dtype of Q, K, V and the attention outputs
  *   head_map   : host array [Hq] giving the kv head of each q head, or NULL
  *                for h / (Hq/Hkv); every kv head must receive exactly Hq/Hkv
- *                q heads. Read during the call only. */
+ *                q heads. Read during the call only.
+ *   selection  : ssa_selection; SSA_SELECT_PER_HEAD (0) unless set */
 typedef struct {
   int32_t B, Hq, Hkv, Nq, Nk, D, block_size, budget, n_sink, n_local;
   float scale;
   int32_t dtype;
   const int32_t* head_map;
+  int32_t selection;
 } ssa_problem;
 
 /* Device workspace bytes needed by every call below for problem p (the
@@ -107,7 +119,9 @@ ssa_status ssa_pool_blocks(const ssa_problem* p, const void* x, int32_t H,
  *   cnt      : out [B,Hq,nQB] int32, the number of valid idx entries
  * The query block's representation is its mean-pooled Q (decode: the query
  * itself). Scores are float64 dot products of the float32 pooled vectors,
- * summed over d in ascending order, unscaled. Forced blocks (the first
+ * summed over d in ascending order, unscaled. With p->selection ==
+ * SSA_SELECT_GROUP every q head of a GQA group receives the group's list,
+ * ranked by the float64 sum of the heads' scores (ascending q head order). Forced blocks (the first
  * n_sink blocks and the n_local blocks ending at the query's own block) are
  * always kept; the remaining budget goes to the best-scoring causal blocks,
  * exact ties to the lower block index; when no more candidates than free

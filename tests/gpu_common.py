@@ -22,7 +22,7 @@ def to_np64(t: torch.Tensor) -> np.ndarray:
 
 
 def gpu_run(ssa, x, *, budget, n_sink=1, n_local=1, head_map=None, want_lse=False,
-            want_grads=False, sparse_only=False, k_pooled=False):
+            want_grads=False, sparse_only=False, k_pooled=False, group_select=False):
     dev = torch.device("cuda:0")
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
     kp = None
@@ -31,7 +31,7 @@ def gpu_run(ssa, x, *, budget, n_sink=1, n_local=1, head_map=None, want_lse=Fals
         kp = ssa.pool_blocks(p, k)
     out = ssa.dual_attention(q, k, v, budget=budget, n_sink=n_sink, n_local=n_local,
                              head_map=head_map, want_lse=want_lse, want_grads=want_grads,
-                             sparse_only=sparse_only, k_pooled=kp)
+                             sparse_only=sparse_only, k_pooled=kp, group_select=group_select)
     torch.cuda.synchronize()
     res = {}
     for key, val in out.items():

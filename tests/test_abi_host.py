@@ -61,6 +61,8 @@ def _status_of(lib, prob, fn="ssa_select_blocks"):
     (dict(D=96), 2), (dict(block_size=32), 2), (dict(Nk=4000, Nq=4000), 2),
     (dict(Nq=7), 2), (dict(dtype=5), 2), (dict(Hq=64, Hkv=2), 2), (dict(scale=-1.0), 1),
     (dict(Nq=1, Nk=4096, Hq=32, Hkv=2), 2),        # bf16 decode with 16 q heads per kv head
+    (dict(selection=2), 1), (dict(selection=-1), 1),
+    (dict(selection=1), 3),                         # group selection, no workspace
     (dict(), 3),                                    # valid problem, no workspace
 ])
 def test_invalid_problems_are_rejected(lib, kw, status):

@@ -38,10 +38,10 @@ def np_inputs(x):
 
 
 def full_compare(cfg, x, got, *, budget, n_sink=1, n_local=1, head_map=None, lse=False,
-                 sparse_only=False):
+                 sparse_only=False, group_select=False):
     xn = np_inputs(x)
     ref = O.ssa_forward(xn["q"], xn["k"], xn["v"], block=cfg.block, budget=budget, n_sink=n_sink,
-                        n_local=n_local, head_map=head_map)
+                        n_local=n_local, head_map=head_map, group_shared=group_select)
     assert np.array_equal(got["idx"].numpy(), ref["idx"]), "selected blocks differ"
     assert np.array_equal(got["cnt"].numpy(), ref["cnt"]), "block counts differ"
     f32 = cfg.dtype == "f32"
@@ -180,6 +180,36 @@ def test_full_budget_gives_identical_streams_grouped(ssa):
     assert torch.count_nonzero(got["delta"]) == 0
 
 
+GROUP_SELECT = [
+    # prefill through the grouped kernel (4 q heads per kv head), through the
+    # per-head kernel (2 per kv head, D 64), and decode; a custom head map
+    ("gqa_8k_peaked", dict(B=2, Hq=8, Hkv=2, N=2048), 6, 1, 1, None),
+    ("gqa_8k_peaked", dict(B=1, Hq=8, Hkv=2, N=2048, planted=False), 5, 1, 1, [1, 0, 0, 1, 1, 0, 1, 0]),
+    ("mha_4k", dict(Hq=4, Hkv=2, N=1024, D=64), 4, 1, 1, None),
+    ("gqa_decode_64k", dict(B=3, Hq=8, Hkv=2, N=4096), 6, 1, 1, None),
+    ("gqa_decode_64k", dict(dtype="f32", B=2, Hq=4, Hkv=2, N=1024), 4, 1, 1, None),
+]
+
+
+@pytest.mark.parametrize("name,kw,budget,n_sink,n_local,hm", GROUP_SELECT,
+                         ids=[f"{g[0]}-{i}" for i, g in enumerate(GROUP_SELECT)])
+def test_group_select_parity(ssa, name, kw, budget, n_sink, n_local, hm):
+    """Group-shared selection (one list per GQA group): indices bit-exact,
+    identical within each group, streams and lse within the bars."""
+    cfg = CONFIGS[name].with_sizes(budget=budget, n_sink=n_sink, n_local=n_local, **kw)
+    say(f"[parity] group select {cfg} head_map={hm}")
+    x = make_inputs(cfg, head_map=hm)
+    got = gpu_run(ssa, x, budget=budget, n_sink=n_sink, n_local=n_local, head_map=hm,
+                  want_lse=True, group_select=True)
+    full_compare(cfg, x, got, budget=budget, n_sink=n_sink, n_local=n_local, head_map=hm,
+                 lse=True, group_select=True)
+    hmap = hm or default_head_map(cfg.Hq, cfg.Hkv)
+    idx = got["idx"].numpy()
+    for h in range(cfg.Hq):
+        first = hmap.index(hmap[h])
+        assert np.array_equal(idx[:, h], idx[:, first]), h
+
+
 def test_run_to_run_determinism(ssa):
     cfg = CONFIGS["gqa_8k_peaked"].with_sizes(B=1, Hq=8, Hkv=2, N=2048, budget=6)
     x = make_inputs(cfg)
@@ -246,12 +276,13 @@ def test_pool_blocks_bit_exact(ssa):
 
 # ---------------------------------------------------------------- full-size workloads
 
-def sampled_compare(cfg, x, got, *, budget, heads, rows_per_head, seed):
+def sampled_compare(cfg, x, got, *, budget, heads, rows_per_head, seed, group_select=False):
     xn = np_inputs(x)
     hm = default_head_map(cfg.Hq, cfg.Hkv)
     say(f"[oracle] selection for {cfg.name} budget {budget}")
     ref_idx, ref_cnt = O.select_blocks(xn["q"], xn["k"], block=cfg.block, budget=budget,
-                                       n_sink=cfg.n_sink, n_local=cfg.n_local, head_map=hm)
+                                       n_sink=cfg.n_sink, n_local=cfg.n_local, head_map=hm,
+                                       group_shared=group_select)
     assert np.array_equal(got["idx"].numpy(), ref_idx), "selected blocks differ"
     assert np.array_equal(got["cnt"].numpy(), ref_cnt), "block counts differ"
     rows = {bh: sample_rows(cfg.Nq, rows_per_head, seed + i) for i, bh in enumerate(heads)}
@@ -297,6 +328,17 @@ def test_full_size_gqa_32k(ssa, budget):
     got = gpu_run(ssa, x, budget=budget)
     sampled_compare(cfg, x, got, budget=budget, heads=[(0, 3), (0, 30)], rows_per_head=256,
                     seed=30 + budget)
+
+
+def test_full_size_gqa_32k_group_select(ssa):
+    """Group-shared selection at the 32K launch configuration: every index,
+    sampled rows of two heads of one group and one of another."""
+    cfg = CONFIGS["gqa_32k_sweep"].with_budget(16)
+    say(f"[parity] full size group select {cfg}")
+    x = make_inputs(cfg, workers=16)
+    got = gpu_run(ssa, x, budget=16, group_select=True)
+    sampled_compare(cfg, x, got, budget=16, heads=[(0, 4), (0, 6), (0, 29)], rows_per_head=256,
+                    seed=77, group_select=True)
 
 
 def test_full_size_decode_64k(ssa):

@@ -163,6 +163,46 @@ def run_prefill(ssa, torch, cfg, steps, warmup, budgets):
     return res
 
 
+def run_paper_shape(ssa, torch, cfg, steps):
+    """The pages' model shape (16-token blocks, D 64, 32 q / 2 kv heads):
+    selection and dual-mode attention time, plus sparse-only attention."""
+    from ssa_inputs import make_inputs
+    dev = torch.device("cuda:0")
+    x = make_inputs(cfg, workers=16)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    del x
+    p = ssa.problem_for(q, k, budget=cfg.budget, n_sink=cfg.n_sink, n_local=cfg.n_local,
+                        block_size=cfg.block)
+    ws = ssa.alloc_workspace(p, dev)
+    idx, cnt = ssa.select_blocks(p, q, k, ws=ws)
+    out = ssa.attn_fwd(p, q, k, v, idx, cnt, ws=ws)
+    tsel, tatt, tsp = EventTimer(torch), EventTimer(torch), EventTimer(torch)
+    for _ in range(max(3, steps // 2)):
+        tsel.start()
+        ssa.select_blocks(p, q, k, ws=ws, idx=idx, cnt=cnt)
+        tsel.stop()
+        tatt.start()
+        ssa.attn_fwd(p, q, k, v, idx, cnt, ws=ws, out=out)
+        tatt.stop()
+        tsp.start()
+        ssa.attn_fwd(p, q, k, v, idx, cnt, ws=ws, out={"h_sparse": out["h_sparse"]},
+                     sparse_only=True)
+        tsp.stop()
+    torch.cuda.synchronize()
+    tiles = cfg.N // 64
+    flops = 4.0 * cfg.D * 64 * 64 * (tiles * (tiles + 1) / 2) * cfg.B * cfg.Hq
+    res = {"workload": f"paper shape prefill: B {cfg.B}, {cfg.Hq} q heads / {cfg.Hkv} kv heads, "
+                       f"N {cfg.N}, D {cfg.D}, block {cfg.block}, budget {cfg.budget}",
+           "select_ms": round(tsel.mean_ms(), 4), "dual_attn_ms": round(tatt.mean_ms(), 4),
+           "attn_tflops": round(flops / (tatt.mean_ms() * 1e-3) / 1e12, 2),
+           "attn_mfma_frac": round(flops / (tatt.mean_ms() * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "sparse_only_attn_ms": round(tsp.mean_ms(), 4),
+           "delta_mean": round(float(out["delta"].mean()), 4)}
+    del q, k, v, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_decode(ssa, torch, cfg, steps, warmup):
     from ssa_inputs import make_inputs
     dev = torch.device("cuda:0")
@@ -371,6 +411,8 @@ def main():
         "budget_sweep": pre.get("sweep"),
         "group_select": pre.get("group_select"),
     }
+    if not args.no_sweep:
+        result["paper_shape"] = run_paper_shape(ssa, torch, CONFIGS["paper_16k_b16"], args.steps)
     if not args.no_decode:
         dec = run_decode(ssa, torch, CONFIGS["gqa_decode_64k"], max(5, args.steps // 2),
                          args.warmup)

@@ -52,7 +52,7 @@ Layout layout_of(const Problem& P) {
   if (P.bf16 && !P.decode) off += align256((size_t)d.B * d.Hkv * d.D * d.Nk * sizeof(uint16_t));
   L.partials = off;
   if (P.bf16 && P.decode) {
-    int ns = ssa::decode_splits(d.nKB);
+    int ns = ssa::decode_splits(d.nT);
     if (ns < ssa::kDecSparseParts) ns = ssa::kDecSparseParts;
     off += align256((size_t)d.B * d.Hq * ns * ssa::decode_partial_floats(d.D) * sizeof(float));
   }
@@ -82,12 +82,15 @@ ssa_status build(const ssa_problem* p, Problem* P) {
   if (p->dtype != SSA_F32 && p->dtype != SSA_BF16)
     return fail(SSA_ERR_UNSUPPORTED, "dtype %d is not SSA_F32 or SSA_BF16", p->dtype);
   if (p->D != 64 && p->D != 128) return fail(SSA_ERR_UNSUPPORTED, "D must be 64 or 128; got %d", p->D);
-  if (p->block_size != ssa::kBlock)
-    return fail(SSA_ERR_UNSUPPORTED, "block_size must be 64; got %d", p->block_size);
+  if (p->block_size != 64 && p->block_size != 16)
+    return fail(SSA_ERR_UNSUPPORTED, "block_size must be 64 or 16; got %d", p->block_size);
   if (p->Nk % ssa::kBlock != 0)
     return fail(SSA_ERR_UNSUPPORTED, "Nk (%d) must be a multiple of 64", p->Nk);
-  if (p->Nk / ssa::kBlock > ssa::kMaxKeyBlocks)
-    return fail(SSA_ERR_UNSUPPORTED, "Nk (%d) exceeds %d key blocks", p->Nk, ssa::kMaxKeyBlocks);
+  if (p->Nk / p->block_size > ssa::kMaxKeyBlocks)
+    return fail(SSA_ERR_UNSUPPORTED, "Nk (%d) exceeds %d key blocks of %d", p->Nk,
+                ssa::kMaxKeyBlocks, p->block_size);
+  if (p->block_size == 16 && p->dtype == SSA_F32)
+    return fail(SSA_ERR_UNSUPPORTED, "block_size 16 needs bf16 inputs");
   if (p->Hq > ssa::kMaxHq) return fail(SSA_ERR_UNSUPPORTED, "Hq (%d) exceeds %d", p->Hq, ssa::kMaxHq);
   const int G = p->Hq / p->Hkv;
   if (G > ssa::kMaxGroup)
@@ -103,7 +106,7 @@ ssa_status build(const ssa_problem* p, Problem* P) {
   const double total = (double)p->B * p->Hq * p->Nq * p->D;
   const double kv = (double)p->B * p->Hkv * p->Nk * p->D;
   if (total > 1.0e12 || kv > 1.0e12) return fail(SSA_ERR_UNSUPPORTED, "problem too large");
-  if ((double)p->B * p->Hq * (p->Nq == 1 ? 1 : p->Nq / ssa::kBlock) > 2.0e9)
+  if ((double)p->B * p->Hq * (p->Nq == 1 ? 1 : p->Nq / p->block_size) > 2.0e9)
     return fail(SSA_ERR_UNSUPPORTED, "too many query blocks");
 
   ssa::HeadMap& hm = P->hm;
@@ -124,13 +127,17 @@ ssa_status build(const ssa_problem* p, Problem* P) {
   ssa::Dims& d = P->d;
   d.B = p->B; d.Hq = p->Hq; d.Hkv = p->Hkv; d.Nq = p->Nq; d.Nk = p->Nk; d.D = p->D;
   d.budget = p->budget; d.n_sink = p->n_sink; d.n_local = p->n_local;
-  d.nKB = p->Nk / ssa::kBlock;
+  d.bs = p->block_size;
+  d.nKB = p->Nk / d.bs;
+  d.nT = p->Nk / ssa::kBlock;
   if (p->Nq == p->Nk) {
     if (p->Nq % ssa::kBlock != 0)
       return fail(SSA_ERR_UNSUPPORTED, "Nq (%d) must be a multiple of 64", p->Nq);
-    d.nQB = p->Nq / ssa::kBlock;
+    d.nQB = p->Nq / d.bs;
+    d.nQT = p->Nq / ssa::kBlock;
   } else {
     d.nQB = 1;
+    d.nQT = 1;
   }
   d.G = G;
   d.group_select = p->selection == SSA_SELECT_GROUP ? 1 : 0;
@@ -173,7 +180,7 @@ ssa_status ssa_pool_blocks(const ssa_problem* p, const void* x, int32_t H, float
   if (x == nullptr || pooled == nullptr) return fail(SSA_ERR_INVALID_ARG, "x or pooled is NULL");
   if (H <= 0) return fail(SSA_ERR_INVALID_ARG, "H must be positive; got %d", H);
   const long nblk = (long)P.d.B * H * P.d.nKB;
-  return hip_status(ssa::launch_pool(x, P.bf16, pooled, nblk, ssa::kBlock, P.d.D,
+  return hip_status(ssa::launch_pool(x, P.bf16, pooled, nblk, P.d.bs, P.d.D,
                                      (hipStream_t)stream), "pool");
 }
 
@@ -197,12 +204,12 @@ ssa_status ssa_select_blocks(const ssa_problem* p, const void* q, const void* k,
   if (P.decode)  // the query is its own block representation
     e = ssa::launch_pool(q, P.bf16, qbar, (long)d.B * d.Hq, 1, d.D, st);
   else
-    e = ssa::launch_pool(q, P.bf16, qbar, (long)d.B * d.Hq * d.nQB, ssa::kBlock, d.D, st);
+    e = ssa::launch_pool(q, P.bf16, qbar, (long)d.B * d.Hq * d.nQB, d.bs, d.D, st);
   if (e != hipSuccess) return hip_status(e, "pool q");
   const float* kbar = k_pooled;
   if (kbar == nullptr) {
     float* kb = (float*)(w + L.kbar);
-    e = ssa::launch_pool(k, P.bf16, kb, (long)d.B * d.Hkv * d.nKB, ssa::kBlock, d.D, st);
+    e = ssa::launch_pool(k, P.bf16, kb, (long)d.B * d.Hkv * d.nKB, d.bs, d.D, st);
     if (e != hipSuccess) return hip_status(e, "pool k");
     kbar = kb;
   }

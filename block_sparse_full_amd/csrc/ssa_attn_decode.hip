@@ -13,10 +13,12 @@
 // workgroup owns one (b, kv head) and a range of key blocks; the q heads of
 // that kv head (the GQA group) all use every K/V load. Per head it keeps the
 // running max m, l_sel / l_drop and two accumulators: acc_full over every key
-// and acc_sel over the head's selected blocks only (a block's PV goes into
-// acc_sel in addition only when that head selected it, so the extra work is
-// proportional to the budget). Dual mode walks every block; sparse-only mode
-// walks only the union of the group's selected blocks and skips acc_full.
+// and acc_sel over the head's selected blocks only (a key's PV goes into
+// acc_sel in addition only when that head selected its block, so the extra
+// work is proportional to the budget). Work is cut into 64-key tiles; with
+// 16-token selection blocks each 16-key quarter of a tile follows its own
+// block. Dual mode walks every tile; sparse-only mode walks only the tiles
+// holding a block selected by some head of the group and skips acc_full.
 #include "ssa_common.h"
 #include "ssa_kernels.h"
 
@@ -27,6 +29,14 @@ __device__ __forceinline__ float dexp2(float x) { return __builtin_amdgcn_exp2f(
 // Bit kb of head n in the selection bitmap.
 __device__ __forceinline__ bool sel_bit(const unsigned* bits, int words, int n, int kb) {
   return (bits[n * words + (kb >> 5)] >> (kb & 31)) & 1u;
+}
+// Selected 16-key quarters of 64-key tile t for head n, as 4 bits: with
+// 64-token selection blocks all four follow block t, with 16-token blocks
+// quarter j is block 4t + j.
+__device__ __forceinline__ unsigned tile_quarters(const unsigned* bits, int words, int n, int t,
+                                                  int bs) {
+  if (bs == kBlock) return sel_bit(bits, words, n, t) ? 0xFu : 0u;
+  return (bits[n * words + ((4 * t) >> 5)] >> ((4 * t) & 31)) & 0xFu;
 }
 
 template <int D, int GP>
@@ -49,8 +59,8 @@ __global__ __launch_bounds__(256) void attn_decode_bf16_kernel(
   extern __shared__ __align__(16) unsigned char smem[];
   const int words = (d.nKB + 31) >> 5;
   unsigned* bits = (unsigned*)smem;                          // [GP][words] selection bitmaps
-  int* ulist = (int*)(bits + GP * words);                    // [nKB] union list (sparse-only)
-  float* ps = (float*)(ulist + d.nKB);                       // [kDecWaves][kBlock][GP]
+  int* ulist = (int*)(bits + GP * words);                    // [nT] union tile list (sparse-only)
+  float* ps = (float*)(ulist + d.nT);                        // [kDecWaves][kBlock][GP]
   float* als = ps + kDecWaves * kBlock * GP;                 // [kDecWaves][GP]
   float* red = als + kDecWaves * GP;                         // [kDecWaves][GP][PF]
   __shared__ int s_nunion;
@@ -72,7 +82,7 @@ __global__ __launch_bounds__(256) void attn_decode_bf16_kernel(
   }
   __syncthreads();
 
-  // ---- the blocks this workgroup walks
+  // ---- the 64-key tiles this workgroup walks
   int blk_begin, blk_count, blk_stride;
   if (sparse_only) {
     if (tid == 0) {
@@ -83,7 +93,8 @@ __global__ __launch_bounds__(256) void attn_decode_bf16_kernel(
         while (u) {
           const int bit = __ffs(u) - 1;
           u &= u - 1u;
-          ulist[nu++] = w * 32 + bit;
+          const int t = (w * 32 + bit) * d.bs / kBlock;   // tile of that block
+          if (nu == 0 || ulist[nu - 1] != t) ulist[nu++] = t;
         }
       }
       s_nunion = nu;
@@ -96,7 +107,7 @@ __global__ __launch_bounds__(256) void attn_decode_bf16_kernel(
     blk_stride = kDecWaves;  // wave w takes entries w, w+4, ...
   } else {
     blk_begin = split * kDecWaves * kDecWaveBlocks;
-    blk_count = max(0, min(kDecWaves * kDecWaveBlocks, d.nKB - blk_begin));
+    blk_count = max(0, min(kDecWaves * kDecWaveBlocks, d.nT - blk_begin));
     blk_stride = kDecWaves;
   }
 
@@ -156,36 +167,40 @@ __global__ __launch_bounds__(256) void attn_decode_bf16_kernel(
         s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], s[kt], 0, 0, 0);
       }
     }
-    // Softmax statistics of head n_col over this block.
-    const bool mine = n_col < G && sel_bit(bits, words, n_col, kb);
-    const bool active = !sparse_only || mine;
+    // Softmax statistics of head n_col over this tile; key tile kt (16
+    // keys) is selection quarter kt.
+    const unsigned mine = n_col < G ? tile_quarters(bits, words, n_col, kb, d.bs) : 0u;
     float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < 4; ++kt) {
+      const bool active = !sparse_only || ((mine >> kt) & 1u);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float x = active ? s[kt][r] * sl2 : -INFINITY;
         s[kt][r] = x;
         mx = fmaxf(mx, x);
       }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
     const bool live = m_new != -INFINITY;
     const float alpha = live ? dexp2(m_run - m_new) : 1.f;
     m_run = m_new;
-    float lsum = 0.f;
+    float lsum_sel = 0.f, lsum_drop = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < 4; ++kt) {
+      float lsum = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float p = live ? dexp2(s[kt][r] - m_new) : 0.f;
         lsum += p;
         if (n_col < GP) wps[(16 * kt + 4 * kgrp + r) * GP + n_col] = p;
       }
-    l_sel *= alpha;
-    l_drop *= alpha;
-    if (mine) l_sel += lsum; else l_drop += lsum;
+      if ((mine >> kt) & 1u) lsum_sel += lsum; else lsum_drop += lsum;
+    }
+    l_sel = l_sel * alpha + lsum_sel;
+    l_drop = l_drop * alpha + lsum_drop;
     if (lane < GP) wal[lane] = alpha;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -197,9 +212,9 @@ __global__ __launch_bounds__(256) void attn_decode_bf16_kernel(
     for (int n = 0; n < GP; ++n)
 #pragma unroll
       for (int e = 0; e < 8; ++e) { acc_full[n][e] *= al[n]; acc_sel[n][e] *= al[n]; }
-    bool hsel[GP];
+    unsigned hsel[GP];
 #pragma unroll
-    for (int n = 0; n < GP; ++n) hsel[n] = n < G && sel_bit(bits, words, n, kb);
+    for (int n = 0; n < GP; ++n) hsel[n] = n < G ? tile_quarters(bits, words, n, kb, d.bs) : 0u;
 #pragma unroll
     for (int i = 0; i < L::KPL; ++i) {
       const int key = L::RPI * i + pv_k0;
@@ -221,7 +236,7 @@ __global__ __launch_bounds__(256) void attn_decode_bf16_kernel(
       }
 #pragma unroll
       for (int n = 0; n < GP; ++n) {
-        if (hsel[n]) {
+        if ((hsel[n] >> (key >> 4)) & 1u) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc_sel[n][e] = fmaf(p[n], vv[e], acc_sel[n][e]);
         }
@@ -342,7 +357,7 @@ static hipError_t launch_dec(const uint16_t* q, const uint16_t* k, const uint16_
                              const int* idx, const int* cnt, float* partials, const Dims& d,
                              const HeadMap& hm, int sparse_only, int nsplit, hipStream_t stream) {
   const int words = (d.nKB + 31) >> 5;
-  const size_t smem = (size_t)GP * words * 4 + (size_t)d.nKB * 4 +
+  const size_t smem = (size_t)GP * words * 4 + (size_t)d.nT * 4 +
                       (size_t)kDecWaves * kBlock * GP * 4 + (size_t)kDecWaves * GP * 4 +
                       (size_t)kDecWaves * GP * (2 * D + 4) * 4;
   hipLaunchKernelGGL((attn_decode_bf16_kernel<D, GP>), dim3(nsplit, d.Hkv, d.B), dim3(256), smem,
@@ -366,7 +381,7 @@ hipError_t launch_attn_decode_bf16(const uint16_t* q, const uint16_t* k, const u
                                    float* delta, float* lse, float* partials, const Dims& d,
                                    const HeadMap& hm, hipStream_t stream) {
   const int sparse_only = hf == nullptr ? 1 : 0;
-  const int nsplit = sparse_only ? kDecSparseParts : decode_splits(d.nKB);
+  const int nsplit = sparse_only ? kDecSparseParts : decode_splits(d.nT);
   hipError_t e = d.D == 128
                      ? launch_dec_g<128>(q, k, v, idx, cnt, partials, d, hm, sparse_only, nsplit, stream)
                      : launch_dec_g<64>(q, k, v, idx, cnt, partials, d, hm, sparse_only, nsplit, stream);

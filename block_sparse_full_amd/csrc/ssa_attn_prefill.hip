@@ -404,6 +404,272 @@ __global__ __launch_bounds__(256, 4) void attn_prefill_bf16_kernel(
   }
 }
 
+// 16-token selection blocks (bs = 16): one workgroup = one (b, q head,
+// 64-row query tile), four waves of 16 rows, so each wave's rows are exactly
+// one query block with its own selection. Every 64-key tile splits into four
+// 16-key quarters; in the S^T layout the keys a lane holds for MFMA tile kt
+// all sit in quarter 2*(kt/2) + (g4/2), so masking a quarter is per (lane,
+// kt). The waves walk the causal tiles in ascending order (sparse-only: the
+// tiles where some wave selected a quarter) with two accumulators sharing one
+// running max: o_all over every causal key and o_sel over the selected
+// quarters (its PV runs only for tiles where the wave selected something);
+// l_sel and l_drop partition the weights. Then
+//     h_full = o_all / (l_sel + l_drop),  h_sparse = o_sel / l_sel,
+//     delta = l_drop / (l_sel + l_drop).
+template <int D>
+__global__ __launch_bounds__(256, 3) void attn_prefill_bf16_q16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ Vt, const int* __restrict__ idx, const int* __restrict__ cnt,
+    uint16_t* __restrict__ Hf, uint16_t* __restrict__ Hs, float* __restrict__ delta,
+    float* __restrict__ lse, Dims d, HeadMap hm) {
+  constexpr int KSPR = D / 8;
+  constexpr int VSPR = kBlock / 8;
+  constexpr int NKS = D / 32;
+  constexpr int NDT = D / 16;
+  constexpr float kTau = 8.0f;
+  constexpr int kPrefetch = 4;
+  constexpr int kWords16 = kMaxKeyBlocks / 32;     // 16-key blocks bitmap words
+  __shared__ __align__(16) uint16_t Ks[kBlock * D];
+  __shared__ __align__(16) uint16_t Vs[D * kBlock];
+  __shared__ uint32_t sel16[4][kWords16];           // per wave: selected 16-key blocks
+  __shared__ uint32_t tiles[kMaxKeyBlocks / 32];    // sparse-only: tiles some wave needs
+
+  const int total = d.B * d.Hq * d.nQT;
+  const int lin = xcd_remap(blockIdx.x, total);
+  const int per_group = d.G * d.nQT;
+  const int grp = lin / per_group;
+  const int rem = lin - grp * per_group;
+  const int qt = d.nQT - 1 - rem / d.G;
+  const int hi = rem - (rem / d.G) * d.G;
+  const int b = grp / d.Hkv;
+  const int g = grp - b * d.Hkv;
+  const int h = hm.q_of_kv[g * d.G + hi];
+  const int bh = b * d.Hq + h;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g4 = lane >> 4;
+  const int qq = wave * 16 + n;
+  const int qrow = qt * kBlock + qq;
+  const int qb16 = 4 * qt + wave;                    // this wave's query block
+  const float sl2 = d.scale_log2;
+  const bool sparse_only = (Hf == nullptr);
+
+  const uint16_t* kbase = K + ((size_t)(b * d.Hkv + g) * d.Nk) * D;
+  const uint16_t* vbase = Vt + ((size_t)(b * d.Hkv + g) * D) * d.Nk;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)((size_t)d.Nk * D * 2));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)((size_t)d.Nk * D * 2));
+  const uint32_t k_row_bytes = D * 2, v_row_bytes = (uint32_t)d.Nk * 2;
+  auto load_k = [&](int t) __attribute__((always_inline)) {
+    tile_to_lds<KSPR, kBlock, 4, true>(krs, (uint32_t)t * kBlock * k_row_bytes, k_row_bytes, Ks,
+                                       wave, lane);
+  };
+  auto load_v = [&](int t) __attribute__((always_inline)) {
+    tile_to_lds<VSPR, D, 4, false>(vrs, (uint32_t)t * kBlock * 2, v_row_bytes, Vs, wave, lane);
+  };
+  auto kchunk = [&](int row, int ch) { return kswz<KSPR>(row, ch); };
+
+  // ---- selection bitmaps (16-key blocks, up to this tile's diagonal)
+  const int nwords16 = ((4 * qt + 3) >> 5) + 1;
+  const int nwords_t = (qt >> 5) + 1;
+  for (int w = tid; w < 4 * kWords16; w += 256) (&sel16[0][0])[w] = 0u;
+  for (int w = tid; w < nwords_t; w += 256) tiles[w] = 0u;
+  __syncthreads();
+  for (int u = 0; u < 4; ++u) {
+    const size_t row = (size_t)bh * d.nQB + 4 * qt + u;
+    const int ns = min(max(cnt[row], 0), d.budget);
+    for (int e = tid; e < ns; e += 256) {
+      const int kb = idx[row * d.budget + e];
+      if (kb >= 0 && kb <= 4 * qt + u) {
+        atomicOr(&sel16[u][kb >> 5], 1u << (kb & 31));
+        if (sparse_only) atomicOr(&tiles[kb >> 7], 1u << ((kb >> 2) & 31));
+      }
+    }
+  }
+  __syncthreads();
+  (void)nwords16;
+
+  // tiles walked: every causal tile, or (sparse-only) those some wave needs
+  int wcur = 0;
+  uint32_t tbits = sparse_only ? __builtin_amdgcn_readfirstlane(tiles[0]) : 0u;
+  int tnext_dual = 0;
+  auto next_tile = [&]() __attribute__((always_inline)) -> int {
+    if (!sparse_only) return tnext_dual <= qt ? tnext_dual++ : -1;
+    while (true) {
+      if (tbits != 0u) {
+        const int t = (wcur << 5) + __builtin_ctz(tbits);
+        tbits &= tbits - 1u;
+        return t <= qt ? t : -1;
+      }
+      if (++wcur < nwords_t) { tbits = __builtin_amdgcn_readfirstlane(tiles[wcur]); continue; }
+      return -1;
+    }
+  };
+  auto quarters = [&](int t) __attribute__((always_inline)) -> uint32_t {   // this wave's selected quarters of tile t
+    return (__builtin_amdgcn_readfirstlane(sel16[wave][t >> 3]) >> ((4 * t) & 31)) & 0xFu;
+  };
+
+  bf16x8_t qf[NKS];
+  {
+    const uint16_t* qp = Q + ((size_t)bh * d.Nq + qrow) * D + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8_t*)(qp + 32 * ks);
+  }
+  f32x4_t oa[NDT], os[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) { oa[i] = f32x4_t{0.f, 0.f, 0.f, 0.f}; os[i] = oa[i]; }
+  float m_ref = -INFINITY, l_sel = 0.f, l_drop = 0.f;
+
+  auto store = [&](uint16_t* H, const f32x4_t* o, float inv) __attribute__((always_inline)) {
+    uint16_t* hp = H + ((size_t)bh * d.Nq + qrow) * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int d0 = 16 * dt + 4 * g4;
+      const uint32_t lo = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+      const uint32_t hi2 = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
+      *(uint2*)(hp + d0) = make_uint2(lo, hi2);
+    }
+  };
+  auto pv = [&](f32x4_t* o, const uint32_t* pwv) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    bf16x8_t fr[2 * NDT];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int r = 16 * dt + n;
+        fr[j * NDT + dt] = *(const bf16x8_t*)(Vs + (r * VSPR + vswz(r, 4 * j + g4)) * 8);
+      }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint4 w = make_uint4(pwv[4 * j], pwv[4 * j + 1], pwv[4 * j + 2], pwv[4 * j + 3]);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, w);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[j * NDT + dt], pb, o[dt], 0, 0, 0);
+    }
+    pipeline_reads<2 * NDT, kPrefetch>();
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  auto body = [&](int t, int t_next) __attribute__((always_inline)) {
+    const uint32_t qm = quarters(t);
+    // sparse-only: a wave with no selected quarter in this tile only keeps
+    // the workgroup's copy/barrier rhythm
+    const bool work = !sparse_only || qm != 0u;
+    uint32_t pw[8], pws[8];
+    if (work) {
+    f32x4_t s[4];
+    {
+      __builtin_amdgcn_s_setprio(1);
+      bf16x8_t fr[4 * NKS];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const int row = kperm16(kt, n);
+          fr[ks * 4 + kt] = *(const bf16x8_t*)(Ks + (row * KSPR + kchunk(row, 4 * ks + g4)) * 8);
+        }
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[ks * 4 + kt], qf[ks], s[kt], 0, 0, 0);
+      pipeline_reads<4 * NKS, kPrefetch>();
+      __builtin_amdgcn_s_setprio(0);
+    }
+    // quarter of the keys this lane holds for MFMA tile kt
+    bool qsel[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) qsel[kt] = (qm >> (2 * (kt >> 1) + (g4 >> 1))) & 1u;
+    if (t == qt) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kperm16(kt, 4 * g4 + r) > qq) s[kt][r] = -INFINITY;
+    }
+    if (sparse_only) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        if (!qsel[kt]) s[kt] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kt][r]);
+    const float m_blk = quad_max(mx) * sl2;
+    if (__builtin_amdgcn_ballot_w64(m_blk > m_ref + kTau) != 0) {
+      const float m_new = fmaxf(m_ref, m_blk);
+      const float alpha = fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) { oa[i][v] *= alpha; os[i][v] *= alpha; }
+      l_sel *= alpha;
+      l_drop *= alpha;
+    }
+    float ls = 0.f, ld = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const float p0 = fast_exp2(fmaf(s[kt][0], sl2, -m_ref));
+      const float p1 = fast_exp2(fmaf(s[kt][1], sl2, -m_ref));
+      const float p2 = fast_exp2(fmaf(s[kt][2], sl2, -m_ref));
+      const float p3 = fast_exp2(fmaf(s[kt][3], sl2, -m_ref));
+      pw[2 * kt] = pack_bf16x2(p0, p1);
+      pw[2 * kt + 1] = pack_bf16x2(p2, p3);
+      pws[2 * kt] = qsel[kt] ? pw[2 * kt] : 0u;
+      pws[2 * kt + 1] = qsel[kt] ? pw[2 * kt + 1] : 0u;
+      float part = add_bf16x2(pw[2 * kt], 0.f);
+      part = add_bf16x2(pw[2 * kt + 1], part);
+      if (qsel[kt]) ls += part; else ld += part;
+    }
+    l_sel += ls;
+    l_drop += ld;
+    }
+
+    wait_vm();
+    __syncthreads();
+    if (t_next >= 0) load_k(t_next);
+    if (!sparse_only) pv(oa, pw);
+    if (qm != 0u) pv(os, pws);
+    wait_vm();
+    __syncthreads();
+    if (t_next >= 0) load_v(t_next);
+  };
+
+  int t = next_tile();
+  if (t >= 0) {
+    load_k(t);
+    load_v(t);
+    wait_vm();
+    __syncthreads();
+  }
+  while (t >= 0) {
+    const int t_next = next_tile();
+    body(t, t_next);
+    t = t_next;
+  }
+  const size_t plane = (size_t)d.B * d.Hq * d.Nq;
+  const float ls_t = quad_sum(l_sel);
+  store(Hs, os, 1.f / ls_t);
+  if (lse != nullptr && g4 == 0)
+    lse[plane + (size_t)bh * d.Nq + qrow] = (m_ref + __log2f(ls_t)) * kLn2;
+  if (sparse_only) return;
+  const float ld_t = quad_sum(l_drop);
+  const float lt = ls_t + ld_t;
+  store(Hf, oa, 1.f / lt);
+  if (g4 == 0) {
+    if (delta != nullptr) delta[(size_t)bh * d.Nq + qrow] = ld_t / lt;
+    if (lse != nullptr) lse[(size_t)bh * d.Nq + qrow] = (m_ref + __log2f(lt)) * kLn2;
+  }
+}
+
 // Row of the K tile that 32x32 MFMA row c reads: the S^T output register v
 // of lane half gl then holds key 16*(v/8) + 8*gl + (v%8) of its 32-key tile,
 // exactly the 8 consecutive keys of the PV B operand.
@@ -867,6 +1133,16 @@ hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const 
                                     const int* idx, const int* cnt, uint16_t* hf, uint16_t* hs,
                                     float* delta, float* lse, const Dims& d, const HeadMap& hm,
                                     hipStream_t stream) {
+  if (d.bs == 16) {
+    const int tiles = d.B * d.Hq * d.nQT;
+    if (d.D == 128)
+      hipLaunchKernelGGL(attn_prefill_bf16_q16_kernel<128>, dim3(tiles), dim3(256), 0, stream, q,
+                         k, vt, idx, cnt, hf, hs, delta, lse, d, hm);
+    else
+      hipLaunchKernelGGL(attn_prefill_bf16_q16_kernel<64>, dim3(tiles), dim3(256), 0, stream, q,
+                         k, vt, idx, cnt, hf, hs, delta, lse, d, hm);
+    return hipGetLastError();
+  }
   // dual mode with four q heads per workgroup; sparse-only calls go to the
   // per-head kernel, which walks only each head's own selected blocks
   if (d.D == 128 && d.G % 4 == 0 && hf != nullptr) {

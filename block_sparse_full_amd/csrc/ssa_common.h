@@ -11,7 +11,7 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kBlock = 64;      // tokens per block (the only supported size)
+constexpr int kBlock = 64;      // tokens per key tile / query tile of the attention kernels
 constexpr int kMaxHq = 256;
 constexpr int kMaxGroup = 16;   // q heads per kv head
 constexpr float kLog2e = 1.4426950408889634f;
@@ -21,7 +21,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 struct Dims {
   int B, Hq, Hkv, Nq, Nk, D;
   int budget, n_sink, n_local;
-  int nQB, nKB, G;     // query row blocks, key blocks, q heads per kv head
+  int nQB, nKB, G;     // query row blocks, key blocks (of bs tokens), q heads per kv head
+  int bs;              // selection block size in tokens (16 or 64)
+  int nQT, nT;         // 64-row query tiles (1 in decode) and 64-key tiles
   int group_select;    // 1: one selection per GQA group (summed head scores)
   float scale;         // logit scale
   float scale_log2;    // scale * log2(e)
@@ -50,7 +52,7 @@ __device__ __forceinline__ float load_as_f32(const float* p) { return *p; }
 // Key block holding the last query of row block qb (queries are aligned to
 // the end of the keys).
 __device__ __forceinline__ int row_block_diag(const Dims& d, int qb) {
-  return (d.Nq == d.Nk) ? qb : (d.Nk - 1) / kBlock;
+  return (d.Nq == d.Nk) ? qb : (d.Nk - 1) / d.bs;
 }
 
 // XCD-aware remap of a linear workgroup id: workgroups are dispatched

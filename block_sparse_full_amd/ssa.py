@@ -269,11 +269,12 @@ def align_loss(p: Problem, h_full, h_sparse, *, want_grads: bool = False,
 def dual_attention(q, k, v, *, budget: int, n_sink: int = 1, n_local: int = 1,
                    scale: float = 0.0, head_map=None, k_pooled=None, sparse_only: bool = False,
                    want_lse: bool = False, want_grads: bool = False, ws=None,
-                   group_select: bool = False):
+                   group_select: bool = False, block_size: int = 64):
     """Selection, both attention streams, dropped mass and alignment losses.
-    group_select: one block list per GQA group (SSA_SELECT_GROUP)."""
+    group_select: one block list per GQA group (SSA_SELECT_GROUP);
+    block_size: selection block in tokens (64 or 16)."""
     p = problem_for(q, k, budget=budget, n_sink=n_sink, n_local=n_local, scale=scale,
-                    head_map=head_map, group_select=group_select)
+                    head_map=head_map, group_select=group_select, block_size=block_size)
     ws = ws if ws is not None else alloc_workspace(p, q.device)
     idx, cnt = select_blocks(p, q, None if k_pooled is not None else k, k_pooled, ws=ws)
     out = attn_fwd(p, q, k, v, idx, cnt, sparse_only=sparse_only, want_lse=want_lse, ws=ws)

@@ -70,7 +70,7 @@ class Config:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads. Sink = first block, local = the block holding the
+# The workloads. Sink = first block, local = the block holding the
 # query (the diagonal block in prefill, the most recent block in decode).
 CONFIGS: Dict[str, Config] = {
     "tiny_f32": Config("tiny_f32", "f32", 1, 1, 1, 512, 64, 64, 4, 1, 1,
@@ -83,9 +83,13 @@ CONFIGS: Dict[str, Config] = {
                             16, 1, 1, False, True, 3, budgets=(4, 8, 16, 32)),
     "gqa_decode_64k": Config("gqa_decode_64k", "bf16", 64, 32, 8, 65536, 128,
                              64, 32, 1, 1, True, True, 4),
+    # the pages' own model shape: 16-token blocks, 16 selected blocks (a
+    # 256-token receptive field), head dim 64, 32 q heads over 2 kv heads
+    "paper_16k_b16": Config("paper_16k_b16", "bf16", 1, 32, 2, 16384, 64, 16,
+                            16, 1, 1, False, True, 5),
 }
 CONFIG_ORDER = ["tiny_f32", "mha_4k", "gqa_8k_peaked", "gqa_32k_sweep",
-                "gqa_decode_64k"]
+                "gqa_decode_64k", "paper_16k_b16"]
 
 
 def stream_seed(seed: int, tensor_id: int, b: int, h: int) -> int:

@@ -22,16 +22,18 @@ def to_np64(t: torch.Tensor) -> np.ndarray:
 
 
 def gpu_run(ssa, x, *, budget, n_sink=1, n_local=1, head_map=None, want_lse=False,
-            want_grads=False, sparse_only=False, k_pooled=False, group_select=False):
+            want_grads=False, sparse_only=False, k_pooled=False, group_select=False, block=64):
     dev = torch.device("cuda:0")
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
     kp = None
     if k_pooled:
-        p = ssa.problem_for(q, k, budget=budget, n_sink=n_sink, n_local=n_local, head_map=head_map)
+        p = ssa.problem_for(q, k, budget=budget, n_sink=n_sink, n_local=n_local, head_map=head_map,
+                            block_size=block)
         kp = ssa.pool_blocks(p, k)
     out = ssa.dual_attention(q, k, v, budget=budget, n_sink=n_sink, n_local=n_local,
                              head_map=head_map, want_lse=want_lse, want_grads=want_grads,
-                             sparse_only=sparse_only, k_pooled=kp, group_select=group_select)
+                             sparse_only=sparse_only, k_pooled=kp, group_select=group_select,
+                             block_size=block)
     torch.cuda.synchronize()
     res = {}
     for key, val in out.items():

@@ -62,6 +62,9 @@ def _status_of(lib, prob, fn="ssa_select_blocks"):
     (dict(Nq=7), 2), (dict(dtype=5), 2), (dict(Hq=64, Hkv=2), 2), (dict(scale=-1.0), 1),
     (dict(Nq=1, Nk=4096, Hq=32, Hkv=2), 2),        # bf16 decode with 16 q heads per kv head
     (dict(selection=2), 1), (dict(selection=-1), 1),
+    (dict(block_size=16), 3),                       # 16-token blocks: valid (bf16), no workspace
+    (dict(block_size=16, dtype=0), 2),              # 16-token blocks need bf16
+    (dict(block_size=16, Nk=200, Nq=200), 2),       # Nk must still be a multiple of 64
     (dict(selection=1), 3),                         # group selection, no workspace
     (dict(), 3),                                    # valid problem, no workspace
 ])

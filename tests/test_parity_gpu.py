@@ -210,6 +210,38 @@ def test_group_select_parity(ssa, name, kw, budget, n_sink, n_local, hm):
         assert np.array_equal(idx[:, h], idx[:, first]), h
 
 
+# 16-token selection blocks (the pages' model shape): prefill with D 64 and
+# 128, GQA 1:1 to 16:1, no forced blocks, iid inputs; decode; sparse-only
+BLOCK16 = [
+    ("paper_16k_b16", dict(Hq=4, Hkv=1, N=1024), 16, 1, 1, False),
+    ("paper_16k_b16", dict(Hq=2, Hkv=2, N=640, D=128), 6, 0, 0, False),
+    ("paper_16k_b16", dict(B=2, Hq=32, Hkv=2, N=512), 16, 1, 1, False),
+    ("paper_16k_b16", dict(Hq=4, Hkv=2, N=2048, planted=False), 12, 2, 2, False),
+    ("paper_16k_b16", dict(Hq=4, Hkv=1, N=1024, D=128), 16, 1, 1, True),
+    ("paper_16k_b16", dict(decode=True, B=3, Hq=8, Hkv=2, N=2048), 16, 1, 1, False),
+    ("paper_16k_b16", dict(decode=True, B=2, Hq=4, Hkv=1, N=4096, D=128), 9, 1, 1, False),
+]
+
+
+@pytest.mark.parametrize("name,kw,budget,n_sink,n_local,sparse", BLOCK16,
+                         ids=[f"b16-{i}" for i in range(len(BLOCK16))])
+def test_block16_parity(ssa, name, kw, budget, n_sink, n_local, sparse):
+    cfg = CONFIGS[name].with_sizes(budget=budget, n_sink=n_sink, n_local=n_local, **kw)
+    say(f"[parity] block 16 {cfg} sparse_only={sparse}")
+    x = make_inputs(cfg)
+    got = gpu_run(ssa, x, budget=budget, n_sink=n_sink, n_local=n_local, want_lse=not sparse,
+                  sparse_only=sparse, block=16)
+    full_compare(cfg, x, got, budget=budget, n_sink=n_sink, n_local=n_local, lse=not sparse,
+                 sparse_only=sparse)
+
+
+def test_block16_group_select(ssa):
+    cfg = CONFIGS["paper_16k_b16"].with_sizes(Hq=8, Hkv=2, N=1024)
+    x = make_inputs(cfg)
+    got = gpu_run(ssa, x, budget=16, want_lse=True, group_select=True, block=16)
+    full_compare(cfg, x, got, budget=16, lse=True, group_select=True)
+
+
 def test_run_to_run_determinism(ssa):
     cfg = CONFIGS["gqa_8k_peaked"].with_sizes(B=1, Hq=8, Hkv=2, N=2048, budget=6)
     x = make_inputs(cfg)
@@ -339,6 +371,17 @@ def test_full_size_gqa_32k_group_select(ssa):
     got = gpu_run(ssa, x, budget=16, group_select=True)
     sampled_compare(cfg, x, got, budget=16, heads=[(0, 4), (0, 6), (0, 29)], rows_per_head=256,
                     seed=77, group_select=True)
+
+
+def test_full_size_paper_16k_b16(ssa):
+    """The pages' model shape at its launch configuration: 16-token blocks,
+    D 64, 32 q heads over 2 kv heads, 16K tokens."""
+    cfg = CONFIGS["paper_16k_b16"]
+    say(f"[parity] full size {cfg}")
+    x = make_inputs(cfg, workers=16)
+    got = gpu_run(ssa, x, budget=cfg.budget, block=16)
+    sampled_compare(cfg, x, got, budget=cfg.budget, heads=[(0, 0), (0, 17)], rows_per_head=256,
+                    seed=91)
 
 
 def test_full_size_decode_64k(ssa):

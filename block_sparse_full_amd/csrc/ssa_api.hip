@@ -96,8 +96,6 @@ ssa_status build(const ssa_problem* p, Problem* P) {
   if (G > ssa::kMaxGroup)
     return fail(SSA_ERR_UNSUPPORTED, "Hq/Hkv (%d) exceeds %d", G, ssa::kMaxGroup);
   const bool decode = p->Nq == 1 && p->Nk != 1;
-  if (decode && p->dtype == SSA_BF16 && G > ssa::kDecMaxGroup)
-    return fail(SSA_ERR_UNSUPPORTED, "bf16 decode supports Hq/Hkv <= %d; got %d", ssa::kDecMaxGroup, G);
   if (p->selection != SSA_SELECT_PER_HEAD && p->selection != SSA_SELECT_GROUP)
     return fail(SSA_ERR_INVALID_ARG, "selection must be SSA_SELECT_PER_HEAD (0) or SSA_SELECT_GROUP (1); "
                 "got %d", p->selection);

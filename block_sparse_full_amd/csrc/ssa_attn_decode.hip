@@ -53,7 +53,7 @@ template <int D, int GP>
 __global__ __launch_bounds__(256) void attn_decode_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int* __restrict__ idx, const int* __restrict__ cnt,
-    float* __restrict__ partials, Dims d, HeadMap hm, int sparse_only, int nsplit) {
+    float* __restrict__ partials, Dims d, HeadMap hm, int sparse_only, int nsplit, int nsub) {
   using L = DecLayout<D, GP>;
   constexpr int PF = 2 * D + 4;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -65,9 +65,12 @@ __global__ __launch_bounds__(256) void attn_decode_bf16_kernel(
   float* red = als + kDecWaves * GP;                         // [kDecWaves][GP][PF]
   __shared__ int s_nunion;
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // a group of more than GP q heads is split over nsub workgroups of GP
+  const int split = blockIdx.x, b = blockIdx.z;
+  const int g = blockIdx.y / nsub, hoff = (blockIdx.y % nsub) * GP;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int G = d.G;
+  const int G = min(GP, d.G - hoff);                         // heads of this workgroup
+  const uint8_t* qmap = hm.q_of_kv + g * d.G + hoff;         // their q head indices
   const float sl2 = d.scale_log2;
 
   // ---- selection bitmaps of the group's heads
@@ -75,7 +78,7 @@ __global__ __launch_bounds__(256) void attn_decode_bf16_kernel(
   __syncthreads();
   for (int i = tid; i < G * d.budget; i += 256) {
     const int n = i / d.budget, e = i - n * d.budget;
-    const int h = hm.q_of_kv[g * G + n];
+    const int h = qmap[n];
     const int c = cnt[b * d.Hq + h];
     const int kb = idx[(size_t)(b * d.Hq + h) * d.budget + e];
     if (e < c && kb >= 0 && kb < d.nKB) atomicOr(&bits[n * words + (kb >> 5)], 1u << (kb & 31));
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(256) void attn_decode_bf16_kernel(
   bf16x8_t qf[L::NKS];
   {
     const bool valid = n_col < G;
-    const int h = valid ? hm.q_of_kv[g * G + n_col] : 0;
+    const int h = valid ? qmap[n_col] : 0;
     const uint16_t* qp = Q + (size_t)(b * d.Hq + h) * D + 8 * kgrp;
 #pragma unroll
     for (int ks = 0; ks < L::NKS; ++ks) {
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(256) void attn_decode_bf16_kernel(
     const int n = i / (D + 1), j = i - n * (D + 1);
     float M = -INFINITY;
     for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, red[(w * GP + n) * PF]);
-    const int h = hm.q_of_kv[g * G + n];
+    const int h = qmap[n];
     float* out = partials + ((size_t)(b * d.Hq + h) * nsplit + split) * PF;
     if (j == D) {
       float ls = 0.f, ld = 0.f;
@@ -360,8 +363,9 @@ static hipError_t launch_dec(const uint16_t* q, const uint16_t* k, const uint16_
   const size_t smem = (size_t)GP * words * 4 + (size_t)d.nT * 4 +
                       (size_t)kDecWaves * kBlock * GP * 4 + (size_t)kDecWaves * GP * 4 +
                       (size_t)kDecWaves * GP * (2 * D + 4) * 4;
-  hipLaunchKernelGGL((attn_decode_bf16_kernel<D, GP>), dim3(nsplit, d.Hkv, d.B), dim3(256), smem,
-                     stream, q, k, v, idx, cnt, partials, d, hm, sparse_only, nsplit);
+  const int nsub = (d.G + GP - 1) / GP;
+  hipLaunchKernelGGL((attn_decode_bf16_kernel<D, GP>), dim3(nsplit, d.Hkv * nsub, d.B), dim3(256),
+                     smem, stream, q, k, v, idx, cnt, partials, d, hm, sparse_only, nsplit, nsub);
   return hipGetLastError();
 }
 

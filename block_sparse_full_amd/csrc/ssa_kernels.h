@@ -17,7 +17,7 @@ constexpr size_t kSelKeyBytes = 32 * 1024; // LDS for the selection keys
 constexpr int kDecWaves = 4;
 constexpr int kDecWaveBlocks = 8;
 constexpr int kDecSparseParts = 4;         // workgroups per (b, kv head), sparse-only
-constexpr int kDecMaxGroup = 8;            // q heads per kv head in bf16 decode
+constexpr int kDecMaxGroup = 8;            // q heads per bf16 decode workgroup (larger groups split)
 
 inline int decode_splits(int nKB) {        // partial results per (b, q head), dual mode
   const int per_wg = kDecWaves * kDecWaveBlocks;

@@ -24,8 +24,9 @@
  *     position Nk - Nq + i. Prefill has Nq == Nk; decode has Nq == 1.
  *   - Element type: SSA_BF16 (bfloat16) or SSA_F32 for Q, K, V and the two
  *     attention outputs. delta, lse, pooled vectors and losses are float32.
- *   - Supported (else SSA_ERR_UNSUPPORTED): D in {64, 128}; block_size 64;
- *     Nk a multiple of 64; Nq in {Nk, 1}; Hq <= 256; Hq/Hkv <= 16.
+ *   - Supported (else SSA_ERR_UNSUPPORTED): D in {64, 128}; block_size 64,
+ *     or 16 with SSA_BF16; Nk a multiple of 64 with at most 4096 blocks;
+ *     Nq in {Nk, 1}; Hq <= 256; Hq/Hkv <= 16.
  *   - Ownership: the caller owns every buffer; the library never allocates
  *     device or host memory. Scratch memory is the caller's workspace of
  *     ssa_workspace_bytes() bytes (device memory, 256-byte aligned).

@@ -60,7 +60,7 @@ def _status_of(lib, prob, fn="ssa_select_blocks"):
     (dict(head_map=[0, 0, 0, 0, 0, 1, 1, 1]), 1), (dict(head_map=[0, 1, 2, 0, 1, 0, 1, 0]), 1),
     (dict(D=96), 2), (dict(block_size=32), 2), (dict(Nk=4000, Nq=4000), 2),
     (dict(Nq=7), 2), (dict(dtype=5), 2), (dict(Hq=64, Hkv=2), 2), (dict(scale=-1.0), 1),
-    (dict(Nq=1, Nk=4096, Hq=32, Hkv=2), 2),        # bf16 decode with 16 q heads per kv head
+    (dict(Nq=1, Nk=4096, Hq=32, Hkv=2), 3),        # bf16 decode, 16 q heads per kv head: valid
     (dict(selection=2), 1), (dict(selection=-1), 1),
     (dict(block_size=16), 3),                       # 16-token blocks: valid (bf16), no workspace
     (dict(block_size=16, dtype=0), 2),              # 16-token blocks need bf16

@@ -86,6 +86,7 @@ def full_compare(cfg, x, got, *, budget, n_sink=1, n_local=1, head_map=None, lse
 # ---------------------------------------------------------------- small, full comparison
 
 SMALL = [
+    ("gqa_decode_64k", dict(B=2, Hq=16, Hkv=1, N=2048), 5, 1, 1),   # 16 q heads per kv head
     ("tiny_f32", {}, 4, 1, 1),
     ("tiny_f32", {}, 2, 1, 1),
     ("tiny_f32", dict(Hq=2, Hkv=1, N=1024), 5, 2, 1),
@@ -220,6 +221,9 @@ BLOCK16 = [
     ("paper_16k_b16", dict(Hq=4, Hkv=1, N=1024, D=128), 16, 1, 1, True),
     ("paper_16k_b16", dict(decode=True, B=3, Hq=8, Hkv=2, N=2048), 16, 1, 1, False),
     ("paper_16k_b16", dict(decode=True, B=2, Hq=4, Hkv=1, N=4096, D=128), 9, 1, 1, False),
+    # decode with 16 q heads per kv head (two workgroups of 8 per group)
+    ("paper_16k_b16", dict(decode=True, B=2, Hq=32, Hkv=2, N=2048), 16, 1, 1, False),
+    ("paper_16k_b16", dict(decode=True, B=2, Hq=32, Hkv=2, N=2048), 16, 1, 1, True),
 ]
 
 

@@ -35,8 +35,8 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 # HBM-counter summary under profiles/), keyed by the SHA-256 of the kernel
 # source they were taken on; any other source reports traffic as null.
 PREFILL_TRAFFIC = {
-    # 773338 KiB x 2.000 read + 528444 KiB x 1.000 written per dispatch
-    "8cf5dca899277ab1e449c7dca790d59285f7b5264226489d5fe99b7eada8633c": int(773338 * 2.0 * 1024 + 528444 * 1.0 * 1024),
+    # 773423 KiB x 2.000 read + 528461 KiB x 1.000 written per dispatch
+    "346e52aca89d980131600c1a22a6a0818c7046cb2341fd1402bcd3ab31ccc740": int(773423 * 2.0 * 1024 + 528461 * 1.0 * 1024),
 }
 PREFILL_SRC = os.path.join(ROOT, "block_sparse_full_amd", "csrc", "ssa_attn_prefill.hip")
 

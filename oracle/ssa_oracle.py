@@ -41,11 +41,20 @@ reason in the design notes):
 * token-level causal masking j <= t inside the query's own block, in both
   streams; logit scale 1/sqrt(D) unless given;
 * losses are mean squared errors over all B*Hq*Nq*D elements; their forward
-  values coincide, stop-gradient only changes which gradient each one feeds.
+  values coincide, stop-gradient only changes which gradient each one feeds;
+* backward: the stop-gradient of "Bidirectional Attention Alignment" blocks
+  each loss's gradient at its target side, so the sparsity loss feeds only
+  h_full and the commitment loss only h_sparse, and the auxiliary output,
+  which is not passed on to later layers ("2. Methodologie"), receives only
+  that gradient; both streams therefore run their own attention backward
+  from the caller's upstream gradient of each output, and dq, dk, dv are the
+  sums over the two streams; the hard top-k selection contributes no
+  gradient.
 
 Every function is pinned by the CPU tests against closed forms, exact special
-cases, torch's scaled-dot-product attention in float64 and brute force on tiny
-inputs; none is "parity unpinned".
+cases, torch's scaled-dot-product attention in float64 (and its autograd for
+the backward), central finite differences of the forward, and brute force on
+tiny inputs; none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -285,6 +294,97 @@ def dual_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray,
             hf[s0:s0 + chunk], hs[s0:s0 + chunk], dl[s0:s0 + chunk] = a, c, d
         out[(b, h)] = (r_all, hf, hs, dl)
     return out
+
+
+# --------------------------------------------------------------------------
+# Backward pass of both streams
+# --------------------------------------------------------------------------
+
+def softmax_vjp(p: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """Gradient with respect to the logits of a row-wise softmax, given its
+    output p and the gradient g with respect to p: the softmax Jacobian
+    diag(p) - p p^T applied to g, i.e. p * (g - sum_j p_j g_j) per row.
+    Entries where p is 0 (masked keys) get 0."""
+    p = np.asarray(p, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    return p * (g - (p * g).sum(axis=1, keepdims=True))
+
+
+def dual_attention_rows_backward(q_rows: np.ndarray, positions: np.ndarray, k: np.ndarray,
+                                 v: np.ndarray, row_selected: np.ndarray,
+                                 d_full: Optional[np.ndarray], d_sparse: Optional[np.ndarray],
+                                 *, block: int, scale: float):
+    """Gradients of <d_full, h_full> + <d_sparse, h_sparse> for a set of query
+    rows of one head, with the block selection held fixed.
+
+    The two streams are those of dual_attention_rows: h_full = P_f v and
+    h_sparse = P_s v with P_f, P_s the softmax of z = scale q k^T over the
+    causal keys and over the causal keys of the selected blocks. Chain rule,
+    stream by stream ("SSA: Achieving Sparser Attention ...", section
+    "Bidirectional Attention Alignment": the sparse and the full stream both
+    receive gradient, each from the loss term whose target side is not
+    stopped):
+        dv  = P_f^T d_full + P_s^T d_sparse
+        dz  = softmax_vjp(P_f, d_full v^T) + softmax_vjp(P_s, d_sparse v^T)
+        dq  = scale dz k,   dk = scale dz^T q.
+    The top-k selection is piecewise constant in q and k, so it contributes
+    no gradient. d_full or d_sparse None means zero. Returns float64
+    dq [R, D], dk [Nk, D], dv [Nk, D] (dk, dv from these rows only).
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    nk = k.shape[0]
+    z = scale * (q_rows @ k.T)
+    j = np.arange(nk)
+    causal = j[None, :] <= np.asarray(positions)[:, None]
+    sel_tok = causal & np.asarray(row_selected)[:, j // block]
+    dz = np.zeros_like(z)
+    dv = np.zeros_like(v)
+    for mask, g in ((causal, d_full), (sel_tok, d_sparse)):
+        if g is None:
+            continue
+        g = np.asarray(g, dtype=np.float64)
+        _, p = _masked_softmax_attend(z, mask, v)
+        dv += p.T @ g
+        dz += softmax_vjp(p, g @ v.T)
+    return scale * (dz @ k), scale * (dz.T @ q_rows), dv
+
+
+def dual_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray,
+                            d_full: Optional[np.ndarray], d_sparse: Optional[np.ndarray],
+                            *, block: int, scale: float, head_map: Sequence[int],
+                            chunk: int = 256):
+    """dq [B, Hq, Nq, D], dk and dv [B, Hkv, Nk, D] (float64) of
+    sum(d_full * h_full) + sum(d_sparse * h_sparse) for a whole problem, with
+    the selection idx [B, Hq, nQB, budget] held fixed. d_full / d_sparse are
+    [B, Hq, Nq, D] upstream gradients of the two outputs, or None for zero.
+    Each kv head's dk, dv add the contributions of all q heads mapped to it.
+    """
+    B, Hq, nq, D = q.shape
+    Hkv, nk = k.shape[1], k.shape[2]
+    n_kb = nk // block
+    dq = np.zeros((B, Hq, nq, D))
+    dk = np.zeros((B, Hkv, nk, D))
+    dv = np.zeros((B, Hkv, nk, D))
+    for b in range(B):
+        for h in range(Hq):
+            g = head_map[h]
+            kk = np.asarray(k[b, g], dtype=np.float64)
+            vv = np.asarray(v[b, g], dtype=np.float64)
+            for r0 in range(0, nq, chunk):
+                r = np.arange(r0, min(nq, r0 + chunk))
+                qb = r // block if nq > 1 else np.zeros_like(r)
+                sel = np.stack([selected_mask(idx[b, h, x], n_kb) for x in qb])
+                gf = None if d_full is None else d_full[b, h, r]
+                gs = None if d_sparse is None else d_sparse[b, h, r]
+                a, c, e = dual_attention_rows_backward(
+                    np.asarray(q[b, h, r], dtype=np.float64), nk - nq + r, kk, vv, sel,
+                    gf, gs, block=block, scale=scale)
+                dq[b, h, r] = a
+                dk[b, g] += c
+                dv[b, g] += e
+    return dq, dk, dv
 
 
 # --------------------------------------------------------------------------

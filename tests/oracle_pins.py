@@ -421,6 +421,144 @@ def check_worked_example():
     assert res["loss_commitment"] == res["loss_sparsity"]
 
 
+# ---------------------------------------------------------------- backward
+
+def _bwd_problem(seed, B=1, Hq=2, Hkv=1, bs=3, nb=4, D=3, budget=2, hm=None):
+    """Tiny GQA problem with a selection that drops blocks, and random
+    upstream gradients of both outputs."""
+    r = _rng(seed)
+    n = bs * nb
+    q = r.standard_normal((B, Hq, n, D))
+    k = r.standard_normal((B, Hkv, n, D)) * 1.3
+    v = r.standard_normal((B, Hkv, n, D))
+    hm = hm if hm is not None else [h // (Hq // Hkv) for h in range(Hq)]
+    idx, _ = O.select_blocks(q, k, block=bs, budget=budget, n_sink=1, n_local=1, head_map=hm)
+    gf = r.standard_normal((B, Hq, n, D))
+    gs = r.standard_normal((B, Hq, n, D))
+    return q, k, v, idx, gf, gs, hm, bs
+
+
+def _streams(q, k, v, idx, bs, scale, hm):
+    res = O.dual_attention(q, k, v, idx, block=bs, scale=scale, head_map=hm)
+    hf = np.zeros(q.shape); hs = np.zeros(q.shape)
+    for (b, h), (r, a, c, _) in res.items():
+        hf[b, h, r], hs[b, h, r] = a, c
+    return hf, hs
+
+
+def check_backward_finite_differences(seed=13):
+    """Central differences (step 1e-6) of F = <d_full, h_full> +
+    <d_sparse, h_sparse>, evaluated with the oracle's forward over a fixed
+    selection, equal the backward's dq, dk, dv for every input element of a
+    two-head GQA group (both heads feed the one kv head)."""
+    q, k, v, idx, gf, gs, hm, bs = _bwd_problem(seed)
+    scale = 0.8
+    dq, dk, dv = O.dual_attention_backward(q, k, v, idx, gf, gs, block=bs, scale=scale, head_map=hm)
+
+    def F(inputs):
+        hf, hs = _streams(inputs[0], inputs[1], inputs[2], idx, bs, scale, hm)
+        return float((gf * hf).sum() + (gs * hs).sum())
+
+    eps = 1e-6
+    for which, grad in enumerate((dq, dk, dv)):
+        for pos in np.ndindex(grad.shape):
+            plus = [q.copy(), k.copy(), v.copy()]
+            minus = [q.copy(), k.copy(), v.copy()]
+            plus[which][pos] += eps
+            minus[which][pos] -= eps
+            fd = (F(plus) - F(minus)) / (2 * eps)
+            assert abs(fd - grad[pos]) < 1e-7, ("qkv"[which], pos, fd, grad[pos])
+
+
+def _torch_streams_grad(q, k, v, sel_tok, gf, gs, scale, hm, sg_loss_alpha=None):
+    """torch float64 autograd through SDPA: full stream under the causal mask,
+    sparse stream under the selected-token mask, K/V gathered per q head so
+    that autograd sums the group's contributions."""
+    t = lambda x: torch.tensor(np.ascontiguousarray(x, dtype=np.float64), requires_grad=True)
+    tq, tk, tv = t(q), t(k), t(v)
+    kk, vv = tk[:, hm], tv[:, hm]
+    n = q.shape[2]
+    causal = torch.from_numpy(np.tril(np.ones((n, n), dtype=bool)))
+    hf = torch.nn.functional.scaled_dot_product_attention(tq, kk, vv, attn_mask=causal, scale=scale)
+    hs = torch.nn.functional.scaled_dot_product_attention(tq, kk, vv, attn_mask=torch.from_numpy(sel_tok),
+                                                          scale=scale)
+    if sg_loss_alpha is None:
+        L = (torch.from_numpy(gf) * hf).sum() + (torch.from_numpy(gs) * hs).sum()
+    else:
+        mse = torch.nn.functional.mse_loss
+        L = sg_loss_alpha * (mse(hf, hs.detach()) + mse(hs, hf.detach()))
+    L.backward()
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy(), hf.detach().numpy(), hs.detach().numpy()
+
+
+def _sel_tok_masks(idx, n, bs):
+    B, Hq = idx.shape[:2]
+    causal = np.tril(np.ones((n, n), dtype=bool))
+    m = np.zeros((B, Hq, n, n), dtype=bool)
+    for b in range(B):
+        for h in range(Hq):
+            for t in range(n):
+                blk = O.selected_mask(idx[b, h, t // bs], n // bs)
+                m[b, h, t] = causal[t] & blk[np.arange(n) // bs]
+    return m
+
+
+def check_backward_vs_torch_autograd(seed=14):
+    """dq, dk, dv equal torch autograd through float64 SDPA of both streams,
+    for B 2, a permuted head map and each stream alone."""
+    q, k, v, idx, gf, gs, hm, bs = _bwd_problem(seed, B=2, Hq=4, Hkv=2, bs=4, nb=5, D=5, budget=3,
+                                                hm=[1, 0, 0, 1])
+    n = q.shape[2]
+    sel_tok = _sel_tok_masks(idx, n, bs)
+    for a, c in ((gf, gs), (gf, None), (None, gs)):
+        ta = np.zeros_like(gf) if a is None else a
+        tc = np.zeros_like(gs) if c is None else c
+        wq, wk, wv, _, _ = _torch_streams_grad(q, k, v, sel_tok, ta, tc, 0.45, hm)
+        dq, dk, dv = O.dual_attention_backward(q, k, v, idx, a, c, block=bs, scale=0.45, head_map=hm)
+        for got, want in ((dq, wq), (dk, wk), (dv, wv)):
+            assert np.allclose(got, want, atol=1e-12, rtol=1e-11), np.abs(got - want).max()
+
+
+def check_backward_invariants(seed=15):
+    """Softmax is unchanged when one vector is added to every key, so dk sums
+    to zero over the keys of each kv head; every softmax row sums to one, so
+    dv summed over keys equals the upstream gradients summed over the rows of
+    the group's q heads. With every causal block selected both streams are
+    the same function, so a gradient fed to either stream gives the same
+    dq, dk, dv."""
+    q, k, v, idx, gf, gs, hm, bs = _bwd_problem(seed, B=2, Hq=4, Hkv=2, nb=5)
+    dq, dk, dv = O.dual_attention_backward(q, k, v, idx, gf, gs, block=bs, scale=0.6, head_map=hm)
+    for b in range(2):
+        for g in range(2):
+            assert np.allclose(dk[b, g].sum(axis=0), 0.0, atol=1e-12)
+            heads = [h for h in range(4) if hm[h] == g]
+            want = sum((gf[b, h] + gs[b, h]).sum(axis=0) for h in heads)
+            assert np.allclose(dv[b, g].sum(axis=0), want, atol=1e-12)
+    nb = q.shape[2] // bs
+    full_idx = np.tile(np.arange(nb), idx.shape[:3] + (1,))
+    a = O.dual_attention_backward(q, k, v, full_idx, gf, None, block=bs, scale=0.6, head_map=hm)
+    c = O.dual_attention_backward(q, k, v, full_idx, None, gf, block=bs, scale=0.6, head_map=hm)
+    for x, y in zip(a, c):
+        assert np.allclose(x, y, atol=1e-13)
+
+
+def check_backward_alignment_seeds(seed=16):
+    """Stop-gradient composition: backward fed with alpha times the loss
+    seeds (sparsity loss -> h_full, commitment loss -> h_sparse) equals torch
+    autograd of alpha (MSE(h_full, sg[h_sparse]) + MSE(h_sparse, sg[h_full]))
+    through float64 SDPA, with sg = detach."""
+    q, k, v, idx, _, _, hm, bs = _bwd_problem(seed, Hq=2, Hkv=1, bs=4, nb=4, D=4)
+    n = q.shape[2]
+    alpha = 10.0
+    wq, wk, wv, hf, hs = _torch_streams_grad(q, k, v, _sel_tok_masks(idx, n, bs), None, None, 0.5, hm,
+                                             sg_loss_alpha=alpha)
+    _, _, sf, ss = O.align_loss(hf, hs)
+    dq, dk, dv = O.dual_attention_backward(q, k, v, idx, alpha * sf, alpha * ss, block=bs,
+                                           scale=0.5, head_map=hm)
+    for got, want in ((dq, wq), (dk, wk), (dv, wv)):
+        assert np.allclose(got, want, atol=1e-12, rtol=1e-10), np.abs(got - want).max()
+
+
 ALL_CHECKS = [
     check_pool_closed_form, check_pool_mean_identity, check_scores_exact_integers,
     check_select_constant_scores, check_select_duplicate_lower_index,
@@ -429,4 +567,6 @@ ALL_CHECKS = [
     check_full_budget_equals_full, check_decomposition_and_bound, check_nested_budgets,
     check_gqa_equals_replicated, check_decode_vs_sdpa, check_loss_vs_torch,
     check_worked_example, check_group_shared_selection,
+    check_backward_finite_differences, check_backward_vs_torch_autograd,
+    check_backward_invariants, check_backward_alignment_seeds,
 ]

@@ -9,6 +9,7 @@ import oracle_pins as P
 _pool, _scores, _select_row, _rows, _loss = (O.pool_blocks, O.block_score_matrix,
                                              O.select_row, O.dual_attention_rows, O.align_loss)
 _group = O.group_score_matrix
+_vjp, _rows_bwd, _bwd = O.softmax_vjp, O.dual_attention_rows_backward, O.dual_attention_backward
 
 
 def m_pool_sum(x, block):                      # sum instead of mean
@@ -77,6 +78,37 @@ def m_group_max(per_head):                     # max over heads instead of the s
     return np.maximum.reduce([np.asarray(x, dtype=np.float64) for x in per_head])
 
 
+def m_vjp_uncentred(p, g):                      # softmax Jacobian without the -p p^T part
+    return np.asarray(p) * np.asarray(g)
+
+
+def m_rows_bwd_no_sparse_dv(q, pos, k, v, sel, gf, gs, *, block, scale):  # P_s^T d_sparse dropped
+    dq, dk, dv = _rows_bwd(q, pos, k, v, sel, gf, gs, block=block, scale=scale)
+    if gs is not None:
+        dv = dv - _rows_bwd(q, pos, k, v, sel, None, gs, block=block, scale=scale)[2]
+    return dq, dk, dv
+
+
+def m_rows_bwd_dk_unscaled(q, pos, k, v, sel, gf, gs, *, block, scale):  # logit scale left off dk
+    dq, dk, dv = _rows_bwd(q, pos, k, v, sel, gf, gs, block=block, scale=scale)
+    return dq, dk / scale, dv
+
+
+def m_rows_bwd_streams_swapped(q, pos, k, v, sel, gf, gs, *, block, scale):  # seeds to the wrong stream
+    return _rows_bwd(q, pos, k, v, sel, gs, gf, block=block, scale=scale)
+
+
+def m_bwd_gqa_overwrite(q, k, v, idx, gf, gs, *, block, scale, head_map, chunk=256):
+    # dk, dv of a kv head overwritten by each q head instead of summed
+    dq, _, _ = _bwd(q, k, v, idx, gf, gs, block=block, scale=scale, head_map=head_map)
+    Hq = q.shape[1]
+    last = {g: max(h for h in range(Hq) if head_map[h] == g) for g in set(head_map)}
+    keep = np.array([last[head_map[h]] == h for h in range(Hq)], dtype=float)[None, :, None, None]
+    _, dk, dv = _bwd(q, k, v, idx, None if gf is None else gf * keep,
+                     None if gs is None else gs * keep, block=block, scale=scale, head_map=head_map)
+    return dq, dk, dv
+
+
 MUTATIONS = [
     ("pool_blocks", m_pool_sum), ("pool_blocks", m_pool_strided),
     ("block_score_matrix", m_scores_transposed),
@@ -85,6 +117,11 @@ MUTATIONS = [
     ("dual_attention_rows", m_rows_no_scale), ("dual_attention_rows", m_rows_delta_kept),
     ("align_loss", m_loss_row_mean), ("align_loss", m_loss_grad_sign),
     ("group_score_matrix", m_group_first_head), ("group_score_matrix", m_group_max),
+    ("softmax_vjp", m_vjp_uncentred),
+    ("dual_attention_rows_backward", m_rows_bwd_no_sparse_dv),
+    ("dual_attention_rows_backward", m_rows_bwd_dk_unscaled),
+    ("dual_attention_rows_backward", m_rows_bwd_streams_swapped),
+    ("dual_attention_backward", m_bwd_gqa_overwrite),
 ]
 
 

@@ -18,10 +18,10 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libssa.so")
 SOURCES = ["ssa_select.hip", "ssa_attn_prefill.hip", "ssa_attn_decode.hip", "ssa_loss.hip",
-           "ssa_api.hip"]
+           "ssa_attn_backward.hip", "ssa_api.hip"]
 # The attention kernels never see NaNs (finite inputs; masked logits are
 # -inf), so let max() skip NaN canonicalisation.
-FILE_FLAGS = {"ssa_attn_prefill.hip": ["-fno-honor-nans"]}
+FILE_FLAGS = {"ssa_attn_prefill.hip": ["-fno-honor-nans"], "ssa_attn_backward.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-function",

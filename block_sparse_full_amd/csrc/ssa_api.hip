@@ -146,6 +146,37 @@ ssa_status build(const ssa_problem* p, Problem* P) {
   return SSA_OK;
 }
 
+// Backward workspace: per-row statistics (float32 [B,Hq,Nq,4]); for bf16
+// also the transposed copies Q^T, dO_f^T, dO_s^T ([B,Hq,D,Nq]) and K^T
+// ([B,Hkv,D,Nk]) and the selection bits (uint16 [B,Hq,key tiles,Nq/32]).
+struct BwdLayout {
+  size_t stats, qt, gft, gst, kt, bits, total;
+};
+
+BwdLayout bwd_layout_of(const Problem& P) {
+  const ssa::Dims& d = P.d;
+  BwdLayout L;
+  size_t off = 0;
+  const size_t qe = (size_t)d.B * d.Hq * d.Nq * d.D;
+  L.stats = off;
+  off += align256((size_t)d.B * d.Hq * d.Nq * 4 * sizeof(float));
+  L.qt = L.gft = L.gst = L.kt = L.bits = off;
+  if (P.bf16) {
+    L.qt = off;
+    off += align256(qe * sizeof(uint16_t));
+    L.gft = off;
+    off += align256(qe * sizeof(uint16_t));
+    L.gst = off;
+    off += align256(qe * sizeof(uint16_t));
+    L.kt = off;
+    off += align256((size_t)d.B * d.Hkv * d.Nk * d.D * sizeof(uint16_t));
+    L.bits = off;
+    off += align256((size_t)d.B * d.Hq * ssa::bwd_key_tiles(d) * (d.Nq / 32) * sizeof(uint16_t));
+  }
+  L.total = off;
+  return L;
+}
+
 ssa_status check_ws(const Problem& P, const void* ws, size_t ws_bytes, Layout* L) {
   *L = layout_of(P);
   if (ws == nullptr) return fail(SSA_ERR_WORKSPACE, "workspace is NULL");
@@ -264,6 +295,74 @@ ssa_status ssa_align_loss(const ssa_problem* p, const void* h_full, const void* 
                                            grad_sparse, (double*)((char*)ws + L.loss),
                                            (hipStream_t)stream),
                     "align loss");
+}
+
+size_t ssa_bwd_workspace_bytes(const ssa_problem* p) {
+  Problem P;
+  if (build(p, &P) != SSA_OK || P.decode) return 0;
+  return bwd_layout_of(P).total;
+}
+
+ssa_status ssa_attn_bwd(const ssa_problem* p, const void* q, const void* k, const void* v,
+                        const int32_t* idx, const int32_t* cnt, const void* h_full,
+                        const void* h_sparse, const float* lse, const void* d_full,
+                        const void* d_sparse, void* dq, void* dk, void* dv, void* ws,
+                        size_t ws_bytes, void* stream) {
+  Problem P;
+  ssa_status s = build(p, &P);
+  if (s != SSA_OK) return s;
+  if (P.decode)
+    return fail(SSA_ERR_UNSUPPORTED, "the backward pass needs a prefill problem (Nq == Nk)");
+  if (q == nullptr || k == nullptr || v == nullptr || idx == nullptr || cnt == nullptr ||
+      lse == nullptr)
+    return fail(SSA_ERR_INVALID_ARG, "q, k, v, idx, cnt or lse is NULL");
+  if (dq == nullptr || dk == nullptr || dv == nullptr)
+    return fail(SSA_ERR_INVALID_ARG, "dq, dk or dv is NULL");
+  if (d_full == nullptr && d_sparse == nullptr)
+    return fail(SSA_ERR_INVALID_ARG, "d_full and d_sparse are both NULL");
+  if (d_full != nullptr && h_full == nullptr)
+    return fail(SSA_ERR_INVALID_ARG, "d_full needs h_full");
+  if (d_sparse != nullptr && h_sparse == nullptr)
+    return fail(SSA_ERR_INVALID_ARG, "d_sparse needs h_sparse");
+  const BwdLayout L = bwd_layout_of(P);
+  if (ws == nullptr) return fail(SSA_ERR_WORKSPACE, "workspace is NULL");
+  if (((uintptr_t)ws & 255u) != 0) return fail(SSA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (ws_bytes < L.total)
+    return fail(SSA_ERR_WORKSPACE, "workspace has %zu bytes; %zu needed (ssa_bwd_workspace_bytes)",
+                ws_bytes, L.total);
+  const ssa::Dims& d = P.d;
+  hipStream_t st = (hipStream_t)stream;
+  char* w = (char*)ws;
+  float* stats = (float*)(w + L.stats);
+  hipError_t e = ssa::launch_attn_bwd_stats(h_full, h_sparse, d_full, d_sparse, lse, stats, P.bf16,
+                                            d, st);
+  if (e != hipSuccess) return hip_status(e, "backward statistics");
+  if (!P.bf16)
+    return hip_status(ssa::launch_attn_bwd_f32((const float*)q, (const float*)k, (const float*)v,
+                                               (const float*)d_full, (const float*)d_sparse, idx,
+                                               cnt, stats, (float*)dq, (float*)dk, (float*)dv, d,
+                                               P.hm, st),
+                      "backward (f32)");
+  uint16_t* qt = (uint16_t*)(w + L.qt);
+  uint16_t* gft = d_full != nullptr ? (uint16_t*)(w + L.gft) : nullptr;
+  uint16_t* gst = d_sparse != nullptr ? (uint16_t*)(w + L.gst) : nullptr;
+  uint16_t* kt = (uint16_t*)(w + L.kt);
+  const int BHq = d.B * d.Hq;
+  if ((e = ssa::launch_transpose((const uint16_t*)q, qt, BHq, d.Nq, d.D, st)) != hipSuccess)
+    return hip_status(e, "transpose q");
+  if (gft && (e = ssa::launch_transpose((const uint16_t*)d_full, gft, BHq, d.Nq, d.D, st)) != hipSuccess)
+    return hip_status(e, "transpose d_full");
+  if (gst && (e = ssa::launch_transpose((const uint16_t*)d_sparse, gst, BHq, d.Nq, d.D, st)) != hipSuccess)
+    return hip_status(e, "transpose d_sparse");
+  if ((e = ssa::launch_transpose((const uint16_t*)k, kt, d.B * d.Hkv, d.Nk, d.D, st)) != hipSuccess)
+    return hip_status(e, "transpose k");
+  return hip_status(ssa::launch_attn_bwd_bf16((const uint16_t*)q, (const uint16_t*)k,
+                                              (const uint16_t*)v, qt, kt,
+                                              (const uint16_t*)d_full, gft,
+                                              (const uint16_t*)d_sparse, gst, idx, cnt, stats,
+                                              (uint16_t*)(w + L.bits), (uint16_t*)dq,
+                                              (uint16_t*)dk, (uint16_t*)dv, d, P.hm, st),
+                    "backward (bf16)");
 }
 
 const char* ssa_status_string(ssa_status s) {

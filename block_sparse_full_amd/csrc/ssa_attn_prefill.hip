@@ -20,22 +20,13 @@
 // Every key block's QK^T and PV run exactly once, so the executed MFMA work
 // equals that of full causal attention alone.
 #include "ssa_common.h"
+#include "ssa_device.h"
 #include "ssa_kernels.h"
 
 #include <type_traits>
 
 namespace ssa {
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// Two floats -> two bfloat16 (round to nearest even) in one instruction.
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const bf16x2_t r = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
-  return __builtin_bit_cast(uint32_t, r);
-}
 // c + a.x + a.y for two packed bfloat16 values, in one instruction. The row
 // sums of both bf16 kernels add the bfloat16 weights that the PV MFMAs
 // apply to V, so each output row is normalised by exactly its own weights.
@@ -51,8 +42,6 @@ __device__ __forceinline__ float add_bf16x2(uint32_t a, float c) {
 // chunk ^ ((row >> 1) & 7) separates them.
 __device__ __forceinline__ int vswz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 // Buffer resource over [base, base + bytes): loads past the end read 0. The
 // base is made wave-uniform explicitly so the descriptor lives in SGPRs.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -62,8 +51,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   void* u = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
   return __builtin_amdgcn_make_buffer_rsrc(u, 0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
-
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Largest of x over the four lanes n, n+16, n+32, n+48 (one query column of
 // a 16x16 MFMA tile), and the same for sums.
@@ -90,15 +77,7 @@ __device__ __forceinline__ float quad_sum(float x) {
 __device__ __forceinline__ int kperm16(int kt, int m) {
   return 32 * (kt >> 1) + 8 * (m >> 2) + 4 * (kt & 1) + (m & 3);
 }
-// K-tile swizzles under that permutation: the 16 rows one ds_read_b128 phase
-// touches land on 16 distinct 16-byte bank groups. 256-byte rows (D = 128,
-// 16 chunks) use chunk ^ f(row) with f taking row bits 0,1,3,4; 128-byte rows
-// (D = 64, 8 chunks, two rows per 256 bytes) use row bits 1,3,4.
-template <int SPR>
-__device__ __forceinline__ int kswz(int row, int chunk) {
-  if constexpr (SPR == 16) return chunk ^ ((row & 3) | ((row >> 1) & 12));
-  else return chunk ^ (((row >> 1) & 1) | ((row >> 2) & 6));
-}
+// K-tile swizzle under that permutation: kswz (shared header).
 
 // Asynchronous global -> LDS copy of one tile of ROWS rows x SPR 16-byte
 // chunks, starting `tile_off` bytes into the buffer, rows `row_bytes` apart,
@@ -452,7 +431,6 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_bf16_q16_kernel(
   const int n = lane & 15, g4 = lane >> 4;
   const int qq = wave * 16 + n;
   const int qrow = qt * kBlock + qq;
-  const int qb16 = 4 * qt + wave;                    // this wave's query block
   const float sl2 = d.scale_log2;
   const bool sparse_only = (Hf == nullptr);
 
@@ -691,33 +669,6 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-// Buffer descriptor words for [base, base + bytes) (stride 0, raw buffer).
-__device__ __forceinline__ i32x4_t make_rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t p = (uint64_t)(uintptr_t)base;
-  return i32x4_t{(int)__builtin_amdgcn_readfirstlane((uint32_t)p),
-                 (int)(__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) & 0xffffu),
-                 (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
-}
-// One 16-byte-per-lane global -> LDS copy (buffer_load_dwordx4 ... lds),
-// issued from inline assembly so that the compiler inserts no wait of its
-// own before later LDS reads: the caller orders every copy against the
-// reads of its stage with explicit vmcnt waits and barriers. m0 (the LDS
-// destination of lane 0) is saved and restored around the copy.
-__device__ __forceinline__ void copy16_to_lds(i32x4_t rsrc, uint32_t soff, uint32_t voff,
-                                              uint32_t lds_addr) {
-  uint32_t keep;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-      "s_nop 0\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(keep)
-      : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
-      : "memory");
-}
 template <int SPR, int ROWS, int NWAVES, bool KMAP>
 __device__ __forceinline__ void tile_to_lds_asm(i32x4_t rsrc, uint32_t tile_off,
                                                 uint32_t row_bytes, uint16_t* lds, int wave,

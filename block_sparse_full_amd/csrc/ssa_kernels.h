@@ -47,4 +47,20 @@ hipError_t launch_align_loss(const void* hf, const void* hs, bool bf16, long n, 
                              void* gf, void* gs, double* partials, hipStream_t stream);
 constexpr int kLossPartials = 1024;
 
+// Backward pass (ssa_attn_backward.hip).
+int bwd_key_tiles(const Dims& d);   // 128-key tiles of the dK/dV kernel
+hipError_t launch_attn_bwd_stats(const void* hf, const void* hs, const void* gf, const void* gs,
+                                 const float* lse, float* stats, bool bf16, const Dims& d,
+                                 hipStream_t stream);
+hipError_t launch_attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const uint16_t* qt, const uint16_t* kt, const uint16_t* gf,
+                                const uint16_t* gft, const uint16_t* gs, const uint16_t* gst,
+                                const int* idx, const int* cnt, const float* stats,
+                                uint16_t* bits, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                                const Dims& d, const HeadMap& hm, hipStream_t stream);
+hipError_t launch_attn_bwd_f32(const float* q, const float* k, const float* v, const float* gf,
+                               const float* gs, const int* idx, const int* cnt,
+                               const float* stats, float* dq, float* dk, float* dv,
+                               const Dims& d, const HeadMap& hm, hipStream_t stream);
+
 }  // namespace ssa

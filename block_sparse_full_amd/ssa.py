@@ -73,6 +73,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ssa_attn_fwd.restype = ctypes.c_int
     lib.ssa_align_loss.argtypes = [P, vp, vp, f32p, vp, vp, vp, sz, vp]
     lib.ssa_align_loss.restype = ctypes.c_int
+    lib.ssa_bwd_workspace_bytes.argtypes = [P]
+    lib.ssa_bwd_workspace_bytes.restype = sz
+    lib.ssa_attn_bwd.argtypes = [P, vp, vp, vp, i32p, i32p, vp, vp, f32p, vp, vp, vp, vp, vp, vp,
+                                 sz, vp]
+    lib.ssa_attn_bwd.restype = ctypes.c_int
     lib.ssa_status_string.argtypes = [ctypes.c_int]
     lib.ssa_status_string.restype = ctypes.c_char_p
     lib.ssa_last_error_message.argtypes = []
@@ -264,6 +269,51 @@ def align_loss(p: Problem, h_full, h_sparse, *, want_grads: bool = False,
         _dev(h_sparse, "h_sparse", p.torch_dtype, shp), loss.data_ptr(),
         _dev(gf, "grad_full"), _dev(gs, "grad_sparse"), wp, wn, _stream()))
     return loss, gf, gs
+
+
+def bwd_workspace_bytes(p: Problem) -> int:
+    c, keep = p.to_c()
+    n = load_library().ssa_bwd_workspace_bytes(ctypes.byref(c))
+    if n == 0:
+        st = load_library().ssa_attn_bwd(ctypes.byref(c), *([None] * 14), 0, None)
+        _check(st if st != 0 else 1)
+    return n
+
+
+def alloc_bwd_workspace(p: Problem, device) -> torch.Tensor:
+    return torch.empty(bwd_workspace_bytes(p) + 256, dtype=torch.uint8, device=device)
+
+
+def attn_bwd(p: Problem, q, k, v, idx, cnt, lse, *, h_full=None, h_sparse=None, d_full=None,
+             d_sparse=None, ws: Optional[torch.Tensor] = None,
+             out: Optional[Dict[str, torch.Tensor]] = None) -> Dict[str, torch.Tensor]:
+    """Backward of both streams: dict with dq [B,Hq,Nq,D], dk and dv
+    [B,Hkv,Nk,D] for upstream gradients d_full / d_sparse (either may be
+    None for zero) of h_full / h_sparse."""
+    dev = q.device
+    o = dict(out or {})
+    shp = (p.B, p.Hq, p.Nq, p.D)
+    kshp = (p.B, p.Hkv, p.Nk, p.D)
+    if "dq" not in o:
+        o["dq"] = torch.empty(shp, dtype=p.torch_dtype, device=dev)
+    for name in ("dk", "dv"):
+        if name not in o:
+            o[name] = torch.empty(kshp, dtype=p.torch_dtype, device=dev)
+    ws = ws if ws is not None else alloc_bwd_workspace(p, dev)
+    wp, wn = _ws_ptr(ws)
+    c, keep = p.to_c()
+    nqb = p.n_qblocks
+    _check(load_library().ssa_attn_bwd(
+        ctypes.byref(c), _dev(q, "q", p.torch_dtype, shp), _dev(k, "k", p.torch_dtype, kshp),
+        _dev(v, "v", p.torch_dtype, kshp),
+        _dev(idx, "idx", torch.int32, (p.B, p.Hq, nqb, p.budget)),
+        _dev(cnt, "cnt", torch.int32, (p.B, p.Hq, nqb)),
+        _dev(h_full, "h_full", p.torch_dtype, shp), _dev(h_sparse, "h_sparse", p.torch_dtype, shp),
+        _dev(lse, "lse", torch.float32, (2, p.B, p.Hq, p.Nq)),
+        _dev(d_full, "d_full", p.torch_dtype, shp), _dev(d_sparse, "d_sparse", p.torch_dtype, shp),
+        _dev(o["dq"], "dq", p.torch_dtype, shp), _dev(o["dk"], "dk", p.torch_dtype, kshp),
+        _dev(o["dv"], "dv", p.torch_dtype, kshp), wp, wn, _stream()))
+    return o
 
 
 def dual_attention(q, k, v, *, budget: int, n_sink: int = 1, n_local: int = 1,

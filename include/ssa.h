@@ -1,6 +1,6 @@
 /*
- * ssa.h - C ABI of the SSA dual-stream block-sparse attention forward for
- * AMD Instinct MI355X (gfx950).
+ * ssa.h - C ABI of the SSA dual-stream block-sparse attention (forward and
+ * backward) for AMD Instinct MI355X (gfx950).
  *
  * What the library computes (the method is described on the pages on SSA,
  * "Sparse Sparse Attention"):
@@ -29,7 +29,8 @@
  *     Nq in {Nk, 1}; Hq <= 256; Hq/Hkv <= 16.
  *   - Ownership: the caller owns every buffer; the library never allocates
  *     device or host memory. Scratch memory is the caller's workspace of
- *     ssa_workspace_bytes() bytes (device memory, 256-byte aligned).
+ *     ssa_workspace_bytes() bytes (ssa_bwd_workspace_bytes() for the
+ *     backward; device memory, 256-byte aligned).
  *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
  *     stream). Every call only enqueues kernels on it and returns without
  *     synchronising. Calls are reentrant; calls that share a workspace must
@@ -93,9 +94,9 @@ typedef struct {
   int32_t selection;
 } ssa_problem;
 
-/* Device workspace bytes needed by every call below for problem p (the
- * largest of their needs, so one workspace serves them all). Returns 0 when
- * p is invalid or unsupported. */
+/* Device workspace bytes needed by every forward call below for problem p
+ * (the largest of their needs, so one workspace serves them all; the
+ * backward has its own query). Returns 0 when p is invalid or unsupported. */
 size_t ssa_workspace_bytes(const ssa_problem* p);
 
 /* Block mean-pool ("Practical Implementation of SSA": mean pooling of each
@@ -167,6 +168,50 @@ ssa_status ssa_align_loss(const ssa_problem* p, const void* h_full,
                           const void* h_sparse, float* loss, void* grad_full,
                           void* grad_sparse, void* ws, size_t ws_bytes,
                           void* stream);
+
+/* Device workspace bytes needed by ssa_attn_bwd for problem p: per-row
+ * statistics and, for SSA_BF16, transposed copies of Q, both upstream
+ * gradients and K plus the selection bits. A separate query because the
+ * backward's scratch is several times the forward's. Returns 0 when p is
+ * invalid, unsupported or a decode problem. */
+size_t ssa_bwd_workspace_bytes(const ssa_problem* p);
+
+/* Backward pass of both attention streams ("Bidirectional Attention
+ * Alignment": the stop-gradient sends the sparsity loss's gradient to
+ * h_full only and the commitment loss's to h_sparse only; "2. Methodologie":
+ * the auxiliary output is not passed to later layers). The caller adds the
+ * task-loss gradient of the primary stream and alpha times the alignment
+ * seeds of ssa_align_loss into one upstream gradient per stream; this call
+ * returns the gradients of sum(d_full * h_full) + sum(d_sparse * h_sparse)
+ * with the block selection held fixed (top-k passes no gradient):
+ *   dV = P_f^T d_full + P_s^T d_sparse,
+ *   dS = P_f * (d_full V^T - rowsum(d_full * h_full))
+ *      + P_s * (d_sparse V^T - rowsum(d_sparse * h_sparse)),
+ *   dQ = scale dS K,  dK = scale dS^T Q,
+ * with P_f, P_s recomputed from the forward's log-sum-exp.
+ *   q, k, v      : the forward's inputs; idx, cnt its selection
+ *   h_full       : [B,Hq,Nq,D] p->dtype, the forward's output (needed when
+ *                  d_full is given)
+ *   h_sparse     : [B,Hq,Nq,D] p->dtype (needed when d_sparse is given)
+ *   lse          : [2,B,Hq,Nq] float32 from ssa_attn_fwd (plane 0 read when
+ *                  d_full is given, plane 1 when d_sparse is)
+ *   d_full       : [B,Hq,Nq,D] p->dtype, dL/dh_full, or NULL for zero
+ *   d_sparse     : [B,Hq,Nq,D] p->dtype, dL/dh_sparse, or NULL for zero;
+ *                  not both NULL. With d_full NULL only the selected blocks
+ *                  are visited.
+ *   dq           : out [B,Hq,Nq,D] p->dtype
+ *   dk, dv       : out [B,Hkv,Nk,D] p->dtype, each kv head summed over its
+ *                  q heads (deterministic: no atomics)
+ *   ws, ws_bytes : at least ssa_bwd_workspace_bytes(p) bytes
+ * Prefill problems only (Nq == Nk; decode gives SSA_ERR_UNSUPPORTED).
+ * float32 accumulation; P and dS enter the bf16 products rounded to bf16;
+ * outputs are rounded once. */
+ssa_status ssa_attn_bwd(const ssa_problem* p, const void* q, const void* k,
+                        const void* v, const int32_t* idx, const int32_t* cnt,
+                        const void* h_full, const void* h_sparse,
+                        const float* lse, const void* d_full,
+                        const void* d_sparse, void* dq, void* dk, void* dv,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* Static text of a status code. */
 const char* ssa_status_string(ssa_status s);

@@ -19,7 +19,11 @@ regenerated alone and generation is parallel and thread-count independent):
   gets ``+2.0 * u`` (so the mean-pooled block similarity singles out the
   planted blocks and the softmax mass concentrates there);
 * bf16 configurations round the float32 values to bfloat16 (round to nearest
-  even) as the last step.
+  even) as the last step;
+* backward inputs: the upstream gradients of the two attention outputs
+  (tensor ids 4 = d_full, 5 = d_sparse) are iid N(0, 1) per (batch, q head),
+  rounded the same way. The backward is linear in them, so their scale
+  (1/n-sized alignment seeds in training) does not change relative errors.
 
 The attention logit scale 1/sqrt(D) is applied inside the attention, not to
 the entries.
@@ -33,7 +37,7 @@ from typing import Dict, Optional, Tuple
 
 import torch
 
-T_Q, T_K, T_V, T_PLANT = 0, 1, 2, 3
+T_Q, T_K, T_V, T_PLANT, T_DFULL, T_DSPARSE = 0, 1, 2, 3, 4, 5
 _MASK63 = (1 << 63) - 1
 
 
@@ -176,6 +180,18 @@ def make_inputs(cfg: Config, workers: int = 8, head_map=None,
     _fill(k, cfg, T_K, cfg.N, hm, workers)
     _fill(v, cfg, T_V, cfg.N, hm, workers)
     return {"q": q, "k": k, "v": v}
+
+
+def make_grads(cfg: Config, workers: int = 8) -> Dict[str, torch.Tensor]:
+    """Upstream gradients d_full, d_sparse [B,Hq,Nq,D] (CPU, config dtype)."""
+    dt = torch_dtype(cfg)
+    hm = default_head_map(cfg.Hq, cfg.Hkv)
+    out = {}
+    for name, tid in (("d_full", T_DFULL), ("d_sparse", T_DSPARSE)):
+        t = torch.empty(cfg.B, cfg.Hq, cfg.Nq, cfg.D, dtype=dt)
+        _fill(t, cfg, tid, cfg.Nq, hm, workers)
+        out[name] = t
+    return out
 
 
 def make_head(cfg: Config, b: int, hq: int, head_map=None) -> Dict[str, torch.Tensor]:

@@ -128,3 +128,42 @@ def test_missing_library_fails_loudly(tmp_path):
     from block_sparse_full_amd import ssa
     with pytest.raises(RuntimeError, match="no fallback"):
         ssa.load_library(str(tmp_path / "libssa.so"))
+
+
+def _bwd(lib, c, *, q=16, lse=16, hf=16, hs=16, gf=16, gs=16, dq=16, ws=None, wn=0):
+    return lib.ssa_attn_bwd(ctypes.byref(c), q, 16, 16, 16, 16, hf, hs, lse, gf, gs, dq, 16, 16,
+                            ws, wn, None)
+
+
+def test_backward_argument_checks(lib):
+    c, keep = _p().to_c()
+    assert _bwd(lib, c) == 3                       # valid, no workspace
+    assert _bwd(lib, c, q=None) == 1
+    assert _bwd(lib, c, lse=None) == 1
+    assert _bwd(lib, c, dq=None) == 1
+    assert _bwd(lib, c, gf=None, gs=None) == 1     # no upstream gradient at all
+    assert _bwd(lib, c, hf=None) == 1              # d_full without h_full
+    assert _bwd(lib, c, hs=None) == 1              # d_sparse without h_sparse
+    assert _bwd(lib, c, hf=None, gf=None) == 3     # sparse stream only: valid
+    assert _bwd(lib, c, hs=None, gs=None) == 3     # full stream only: valid
+    dec, keep2 = _p(Nq=1).to_c()
+    assert _bwd(lib, dec) == 2                     # decode has no backward here
+    assert lib.ssa_bwd_workspace_bytes(ctypes.byref(dec)) == 0
+    bad, keep3 = _p(D=96).to_c()
+    assert _bwd(lib, bad) == 2
+
+
+def test_backward_workspace_size(lib):
+    from block_sparse_full_amd.ssa import bwd_workspace_bytes
+    p = _p()                        # B1 Hq8 Hkv2 N4096 D128 bf16
+    need = bwd_workspace_bytes(p)
+    stats = 8 * 4096 * 4 * 4
+    qt = 8 * 128 * 4096 * 2         # also d_full^T and d_sparse^T
+    kt = 2 * 128 * 4096 * 2
+    bits = 8 * (4096 // 128) * (4096 // 32) * 2
+    assert need == stats + 3 * qt + kt + bits
+    c, keep = p.to_c()
+    assert _bwd(lib, c, ws=4096, wn=need - 256) == 3
+    assert _bwd(lib, c, ws=4096 + 8, wn=need) == 3   # not 256-byte aligned
+    f32 = _p(dtype=0)
+    assert bwd_workspace_bytes(f32) == stats        # float32 path keeps statistics only

@@ -203,6 +203,73 @@ def run_paper_shape(ssa, torch, cfg, steps):
     return res
 
 
+def run_backward(ssa, torch, cfg, steps, warmup):
+    """Backward pass of both streams on the prefill workload, with seeded
+    upstream gradients of both outputs (dual mode, as in alignment training),
+    plus the full-stream-only and sparse-stream-only backward. FLOPs are
+    algorithmic: per causal 64x64 (query block, key block) pair five D-deep
+    products for the full stream (S recompute, dP, dV, dQ, dK) and per
+    selected pair two more for the sparse stream (dP_s, dV_s)."""
+    from ssa_inputs import make_grads, make_inputs
+    dev = torch.device("cuda:0")
+    x = make_inputs(cfg, workers=16)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    del x
+    g = make_grads(cfg, workers=16)
+    gf, gs = g["d_full"].to(dev), g["d_sparse"].to(dev)
+    del g
+    p = ssa.problem_for(q, k, budget=cfg.budget, n_sink=cfg.n_sink, n_local=cfg.n_local,
+                        block_size=cfg.block)
+    ws = ssa.alloc_workspace(p, dev)
+    idx, cnt = ssa.select_blocks(p, q, k, ws=ws)
+    fwd = ssa.attn_fwd(p, q, k, v, idx, cnt, want_lse=True, ws=ws)
+    bws = ssa.alloc_bwd_workspace(p, dev)
+    out = ssa.attn_bwd(p, q, k, v, idx, cnt, fwd["lse"], h_full=fwd["h_full"],
+                       h_sparse=fwd["h_sparse"], d_full=gf, d_sparse=gs, ws=bws)
+
+    def timed(n, **kw):
+        for _ in range(warmup):
+            ssa.attn_bwd(p, q, k, v, idx, cnt, fwd["lse"], ws=bws, out=out, **kw)
+        t = EventTimer(torch)
+        for _ in range(n):
+            t.start()
+            ssa.attn_bwd(p, q, k, v, idx, cnt, fwd["lse"], ws=bws, out=out, **kw)
+            t.stop()
+        torch.cuda.synchronize()
+        return t.mean_ms()
+
+    dual_ms = timed(steps, h_full=fwd["h_full"], h_sparse=fwd["h_sparse"], d_full=gf, d_sparse=gs)
+    full_ms = timed(max(3, steps // 2), h_full=fwd["h_full"], d_full=gf)
+    sparse_ms = timed(max(3, steps // 2), h_sparse=fwd["h_sparse"], d_sparse=gs)
+    fwd_t = EventTimer(torch)
+    for _ in range(max(3, steps // 2)):
+        fwd_t.start()
+        ssa.attn_fwd(p, q, k, v, idx, cnt, want_lse=True, ws=ws, out=fwd)
+        fwd_t.stop()
+    torch.cuda.synchronize()
+    nkb = cfg.N // 64
+    pair = 2.0 * cfg.D * 64 * 64                     # one 64x64xD product
+    full_pairs = nkb * (nkb + 1) / 2 * cfg.B * cfg.Hq
+    sel_pairs = float(cnt.sum()) * (cfg.block / 64) ** 2
+    flops_full = 5 * pair * full_pairs
+    flops_dual = flops_full + 2 * pair * sel_pairs
+    res = {"workload": f"prefill backward: B {cfg.B}, {cfg.Hq} q heads / {cfg.Hkv} kv heads, "
+                       f"N {cfg.N}, D {cfg.D}, block {cfg.block}, budget {cfg.budget}; "
+                       f"upstream gradients of both outputs",
+           "dual_ms": round(dual_ms, 4),
+           "dual_tflops": round(flops_dual / (dual_ms * 1e-3) / 1e12, 2),
+           "dual_mfma_frac": round(flops_dual / (dual_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "full_only_ms": round(full_ms, 4),
+           "full_only_tflops": round(flops_full / (full_ms * 1e-3) / 1e12, 2),
+           "sparse_only_ms": round(sparse_ms, 4),
+           "fwd_dual_ms": round(fwd_t.mean_ms(), 4),
+           "train_step_attn_ms": round(fwd_t.mean_ms() + dual_ms, 4),
+           "sparse_stream_overhead": round((fwd_t.mean_ms() + dual_ms) / (fwd_t.mean_ms() + full_ms) - 1, 4)}
+    del q, k, v, gf, gs, fwd, out, ws, bws
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_decode(ssa, torch, cfg, steps, warmup):
     from ssa_inputs import make_inputs
     dev = torch.device("cuda:0")
@@ -348,6 +415,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only time the backward pass (prints one JSON object)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (x3), the reference for "
                          "scaling HBM byte counters")
@@ -372,6 +442,10 @@ def main():
     ssa.load_library()
 
     cfg = CONFIGS["gqa_32k_sweep"].with_budget(args.budget)
+    if args.backward_only:
+        print(json.dumps({"backward": run_backward(ssa, torch, cfg, args.steps, args.warmup)}),
+              flush=True)
+        return
     if args.no_prefill:
         dec = run_decode(ssa, torch, CONFIGS["gqa_decode_64k"], args.steps, args.warmup)
         print(json.dumps({"decode": dec}), flush=True)
@@ -411,6 +485,8 @@ def main():
         "budget_sweep": pre.get("sweep"),
         "group_select": pre.get("group_select"),
     }
+    if not args.no_backward:
+        result["backward"] = run_backward(ssa, torch, cfg, max(5, args.steps // 2), args.warmup)
     if not args.no_sweep:
         result["paper_shape"] = run_paper_shape(ssa, torch, CONFIGS["paper_16k_b16"], args.steps)
     if not args.no_decode:

@@ -146,32 +146,30 @@ ssa_status build(const ssa_problem* p, Problem* P) {
   return SSA_OK;
 }
 
-// Backward workspace: per-row statistics (float32 [B,Hq,Nq,4]); for bf16
-// also the transposed copies Q^T, dO_f^T, dO_s^T ([B,Hq,D,Nq]) and K^T
-// ([B,Hkv,D,Nk]) and the selection bits (uint16 [B,Hq,key tiles,Nq/32]).
+// Backward workspace: per-row statistics (float32 [B,Hq,Nq,4]) and, for
+// bf16, the selection bits (uint16 [B*Hkv, key tiles, Nq/32, Hq/Hkv]) and
+// the float32 partial sums that the full-stream pass hands to the
+// sparse-stream pass (dQ [B,Hq,Nq,D], dK and dV [B,Hkv,Nk,D]).
 struct BwdLayout {
-  size_t stats, qt, gft, gst, kt, bits, total;
+  size_t stats, bits, pq, pk, pv, total;
 };
 
 BwdLayout bwd_layout_of(const Problem& P) {
   const ssa::Dims& d = P.d;
   BwdLayout L;
   size_t off = 0;
-  const size_t qe = (size_t)d.B * d.Hq * d.Nq * d.D;
   L.stats = off;
   off += align256((size_t)d.B * d.Hq * d.Nq * 4 * sizeof(float));
-  L.qt = L.gft = L.gst = L.kt = L.bits = off;
+  L.bits = L.pq = L.pk = L.pv = off;
   if (P.bf16) {
-    L.qt = off;
-    off += align256(qe * sizeof(uint16_t));
-    L.gft = off;
-    off += align256(qe * sizeof(uint16_t));
-    L.gst = off;
-    off += align256(qe * sizeof(uint16_t));
-    L.kt = off;
-    off += align256((size_t)d.B * d.Hkv * d.Nk * d.D * sizeof(uint16_t));
     L.bits = off;
     off += align256((size_t)d.B * d.Hq * ssa::bwd_key_tiles(d) * (d.Nq / 32) * sizeof(uint16_t));
+    L.pq = off;
+    off += align256((size_t)d.B * d.Hq * d.Nq * d.D * sizeof(float));
+    L.pk = off;
+    off += align256((size_t)d.B * d.Hkv * d.Nk * d.D * sizeof(float));
+    L.pv = off;
+    off += align256((size_t)d.B * d.Hkv * d.Nk * d.D * sizeof(float));
   }
   L.total = off;
   return L;
@@ -343,24 +341,11 @@ ssa_status ssa_attn_bwd(const ssa_problem* p, const void* q, const void* k, cons
                                                cnt, stats, (float*)dq, (float*)dk, (float*)dv, d,
                                                P.hm, st),
                       "backward (f32)");
-  uint16_t* qt = (uint16_t*)(w + L.qt);
-  uint16_t* gft = d_full != nullptr ? (uint16_t*)(w + L.gft) : nullptr;
-  uint16_t* gst = d_sparse != nullptr ? (uint16_t*)(w + L.gst) : nullptr;
-  uint16_t* kt = (uint16_t*)(w + L.kt);
-  const int BHq = d.B * d.Hq;
-  if ((e = ssa::launch_transpose((const uint16_t*)q, qt, BHq, d.Nq, d.D, st)) != hipSuccess)
-    return hip_status(e, "transpose q");
-  if (gft && (e = ssa::launch_transpose((const uint16_t*)d_full, gft, BHq, d.Nq, d.D, st)) != hipSuccess)
-    return hip_status(e, "transpose d_full");
-  if (gst && (e = ssa::launch_transpose((const uint16_t*)d_sparse, gst, BHq, d.Nq, d.D, st)) != hipSuccess)
-    return hip_status(e, "transpose d_sparse");
-  if ((e = ssa::launch_transpose((const uint16_t*)k, kt, d.B * d.Hkv, d.Nk, d.D, st)) != hipSuccess)
-    return hip_status(e, "transpose k");
   return hip_status(ssa::launch_attn_bwd_bf16((const uint16_t*)q, (const uint16_t*)k,
-                                              (const uint16_t*)v, qt, kt,
-                                              (const uint16_t*)d_full, gft,
-                                              (const uint16_t*)d_sparse, gst, idx, cnt, stats,
-                                              (uint16_t*)(w + L.bits), (uint16_t*)dq,
+                                              (const uint16_t*)v, (const uint16_t*)d_full,
+                                              (const uint16_t*)d_sparse, idx, cnt, stats,
+                                              (uint16_t*)(w + L.bits), (float*)(w + L.pq),
+                                              (float*)(w + L.pk), (float*)(w + L.pv), (uint16_t*)dq,
                                               (uint16_t*)dk, (uint16_t*)dv, d, P.hm, st),
                     "backward (bf16)");
 }

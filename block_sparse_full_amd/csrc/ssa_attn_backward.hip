@@ -16,20 +16,23 @@
 // constant in Q and K and passes no gradient.
 //
 // Walk. The dK/dV kernel owns 128 keys of one kv head (32 per wave) and
-// visits the 32-row query steps of every q head of the GQA group that reach
-// those keys; the sparse stream's extra products run only on (step, wave)
-// pairs whose blocks are selected. The dQ kernel owns 128 query rows of one q
-// head (32 per wave) and visits 32-key steps up to the diagonal. In dual mode
-// both kernels walk every causal step (the full stream needs them all); in
-// sparse-only mode (no full-stream gradient) only steps with a selected block.
+// visits the 32-row query steps that reach those keys, for every q head of
+// the GQA group, from the last step down, heads innermost; all workgroups of
+// one kv head start at the last step, so they stream the same Q / dO rows
+// through L2 at about the same time. The sparse stream's extra products run
+// only on (step, wave) pairs whose blocks are selected. The dQ kernel owns 128
+// query rows of one q head (32 per wave) and visits 32-key steps up to the
+// diagonal. In dual mode both kernels walk every causal step (the full
+// stream needs them all); in sparse-only mode (no full-stream gradient) only
+// steps with a selected block.
 //
 // MFMA 16x16x32 bf16 throughout. The dK/dV kernel computes S = Q K^T and
 // dP = dO V^T with query rows on the output's register index, so P and dS
 // sit in the B-operand layout of dV^T = dO^T P and dK^T = Q^T dS once the
 // A rows of the first products are read in the kperm16 order; the dQ kernel
-// does the same with keys: S^T = K Q^T, dQ^T = K^T dS^T. Contractions over
-// query rows (dK/dV) and over keys (dQ) read the transposed copies Q^T, dO^T
-// and K^T, which the host path makes before the kernels run.
+// does the same with keys: S^T = K Q^T, dQ^T = K^T dS^T. The transposed A
+// operands (dO^T, Q^T, K^T) come from the same row-major LDS tiles through
+// the LDS transpose read (ds_read_b64_tr_b16), so every tile crosses L2 once.
 #include "ssa_common.h"
 #include "ssa_device.h"
 #include "ssa_kernels.h"
@@ -42,6 +45,17 @@ constexpr int kStep = 32;        // query rows per dK/dV step, keys per dQ step
 constexpr int kKeysPerWg = 128;  // keys per dK/dV workgroup (32 per wave)
 constexpr int kRowsPerWg = 128;  // query rows per dQ workgroup (32 per wave)
 constexpr int kMaxSteps = 8192;  // 32-row (32-key) steps per head: N <= 262144
+constexpr int kStages = 4;       // LDS stages of the dK/dV and dQ pipelines
+
+// Wait until at most N vector memory operations of this wave are in flight
+// (loads complete in issue order, so every older one has landed).
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0xF70 | N);
+}
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -53,41 +67,78 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, 
 // consecutive rows 8*g .. 8*g+7 that a 32-deep B operand slot range needs.
 __device__ __forceinline__ int rho(int mb, int m) { return 8 * (m >> 2) + 4 * mb + (m & 3); }
 
-// Transposed tiles are D rows of 32 bf16 (64 bytes, 4 chunks); a read phase
-// touches 16 consecutive rows at one logical chunk.
-__device__ __forceinline__ int tswz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+// 16-byte chunk swizzle of the 32-row tiles. Two read patterns must be free
+// of bank conflicts: the kperm16 row reads (16 lanes, rows differing in bits
+// 0, 1, 3 and 4, one logical chunk: the swizzle must be injective on those
+// bits) and the transpose reads (32 lanes, rows differing in bits 0, 1 and 3,
+// two adjacent logical chunks: the swizzle shifted right by one must be
+// injective on those bits). 256-byte rows (16 chunks):
+// f = b4 | b0<<1 | b1<<2 | b3<<3; 128-byte rows (8 chunks, two rows per 256
+// bytes, so bit 0 already separates rows): f = b4 | b1<<1 | b3<<2.
+template <int SPR>
+__device__ __forceinline__ int bswz(int row, int chunk) {
+  if constexpr (SPR == 16)
+    return chunk ^ (((row >> 4) & 1) | ((row & 3) << 1) | (((row >> 3) & 1) << 3));
+  else
+    return chunk ^ (((row >> 4) & 1) | (((row >> 1) & 1) << 1) | (((row >> 3) & 1) << 2));
+}
 
-// One tile copy, global -> LDS, of ROWS rows x SPR 16-byte chunks shared by
+// One 32-row tile copy, global -> LDS, SPR 16-byte chunks per row, shared by
 // four waves. Lane i of a wave instruction fills LDS slot slot0 + i and
-// fetches the global chunk the tile's swizzle maps to it.
-template <int SPR, int ROWS, bool TRANSPOSED>
-__device__ __forceinline__ void copy_tile(i32x4_t rsrc, uint32_t tile_off, uint32_t row_bytes,
-                                          uint16_t* lds, int wave, int lane) {
-  constexpr int SLOTS = ROWS * SPR;
-  constexpr int PER_WAVE = SLOTS / 4;
+// fetches the global chunk that the swizzle (an involution) maps to it.
+template <int SPR>
+__device__ __forceinline__ void copy_tile(i32x4_t rsrc, uint32_t tile_off, uint32_t lds,
+                                          int wave, int lane) {
+  constexpr int PER_WAVE = kStep * SPR / 4;
   static_assert(PER_WAVE % 64 == 0, "tile slots per wave");
 #pragma unroll
   for (int j = 0; j < PER_WAVE / 64; ++j) {
     const int slot0 = wave * PER_WAVE + j * 64;
     const int r0 = slot0 / SPR;
     const int rl = lane / SPR, sl = lane % SPR;
-    const int c = TRANSPOSED ? tswz(r0 + rl, sl) : kswz<SPR>(r0 + rl, sl);
-    const uint32_t voff = (uint32_t)rl * row_bytes + (uint32_t)c * 16u;
-    const uint32_t soff = __builtin_amdgcn_readfirstlane(tile_off + (uint32_t)r0 * row_bytes);
-    const uint32_t la = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(lds_ptr_t)(lds + slot0 * 8));
-    copy16_to_lds(rsrc, soff, voff, la);
+    const uint32_t voff = (uint32_t)rl * SPR * 16u + (uint32_t)bswz<SPR>(r0 + rl, sl) * 16u;
+    const uint32_t soff = __builtin_amdgcn_readfirstlane(tile_off + (uint32_t)r0 * SPR * 16u);
+    copy16_to_lds(rsrc, soff, voff, __builtin_amdgcn_readfirstlane(lds + slot0 * 16u));
   }
 }
 
-// 16-byte fragment of a row-major tile (SPR chunks per row, kswz layout).
-template <int SPR>
-__device__ __forceinline__ bf16x8_t frag_rows(const uint16_t* t, int row, int chunk) {
-  return *(const bf16x8_t*)(t + row * SPR * 8 + kswz<SPR>(row, chunk) * 8);
+// LDS byte address of a __shared__ object. Tiles are addressed by these
+// integers: a generic -> LDS cast of a pointer chosen at run time (a stage)
+// would need a null check.
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr_t)p;
 }
-// 16-byte fragment of a transposed tile (4 chunks per row, tswz layout).
-__device__ __forceinline__ bf16x8_t frag_t(const uint16_t* t, int row, int chunk) {
-  return *(const bf16x8_t*)(t + row * 32 + tswz(row, chunk) * 8);
+
+// A-operand fragment T[row][chunk] (rows of SPR 16-byte chunks): MFMA row m
+// of a 16x32 A block reading 8 consecutive columns of one tile row.
+template <int SPR>
+__device__ __forceinline__ bf16x8_t frag_rows(uint32_t t, int row, int chunk) {
+  typedef __attribute__((address_space(3))) const bf16x8_t* lp;
+  return *(lp)(uintptr_t)(t + 2u * (uint32_t)(row * SPR * 8 + bswz<SPR>(row, chunk) * 8));
+}
+
+// Transposed A-operand fragment: A[m][k] = T[k][c0 + m] for the 16 columns
+// c0 .. c0+15 (c0 a multiple of 16) and the 32 tile rows, so lane (m, g)
+// gets T[8g + j][c0 + m], j = 0..7. ds_read_b64_tr_b16 hands lane i of a
+// 16-lane group element M[4j + i/4][i%4] (j = 0..3) of the 4-element pieces
+// M[L] its lanes L address; lane L therefore addresses row 8g + 4h + L/4,
+// columns c0 + 4(L%4) .. +3, once for each half h of the eight rows.
+template <int SPR>
+__device__ __forceinline__ bf16x8_t frag_tr(uint32_t base, int c0, int lane) {
+  typedef __attribute__((address_space(3))) i16x4_t* lp;
+  const int L = lane & 15, g = lane >> 4;
+  const int col = c0 + 4 * (L & 3);
+  const int chunk = col >> 3, half = (col >> 2) & 1;
+  i16x4_t r[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 8 * g + 4 * h + (L >> 2);
+    const uint32_t a = base + 2u * (uint32_t)(row * SPR * 8 + bswz<SPR>(row, chunk) * 8 + half * 4);
+    r[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(uintptr_t)a);
+  }
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t v{r[0][0], r[0][1], r[0][2], r[0][3], r[1][0], r[1][1], r[1][2], r[1][3]};
+  return __builtin_bit_cast(bf16x8_t, v);
 }
 
 __device__ __forceinline__ bf16x8_t pack8(const float* x) {
@@ -102,9 +153,25 @@ __device__ __forceinline__ void store4_bf16(uint16_t* p, float a, float b, float
   *(u32x2_t*)p = u32x2_t{pack_bf16x2(a, b), pack_bf16x2(c, e)};
 }
 
-// First step s' > s of a head whose selection bits are nonzero (sparse-only
-// walks), or `end`. `bits(i)` reads the bit word of step i; the 64 lanes
-// test 64 candidates at a time, so every wave gets the same answer.
+// Scheduling pattern for NR LDS reads feeding MPR MFMAs each, in order: PF
+// reads first (at most NR), then (MPR MFMAs, one read) pairs, then the remaining MFMAs,
+// so every read runs PF / MPR MFMA groups ahead of its use instead of each
+// MFMA waiting for its own read.
+template <int NR, int MPR, int PF_>
+__device__ __forceinline__ void pipeline_mix() {
+  constexpr int PF = PF_ < NR ? PF_ : NR;
+  __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);      // DS reads
+#pragma unroll
+  for (int k = 0; k < NR - PF; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, MPR * PF, 0);
+}
+
+// First step s' > s whose selection bits are nonzero (sparse-only walks), or
+// `end`. `bits(i)` reads the bit word of step i; the 64 lanes test 64
+// candidates at a time, so every wave gets the same answer.
 template <typename F>
 __device__ __forceinline__ int next_selected(int s, int end, int lane, F bits) {
   for (int base = s + 1; base < end; base += 64) {
@@ -123,7 +190,27 @@ __device__ __forceinline__ int next_selected(int s, int end, int lane, F bits) {
 // full stream, 1 rowsum(dO_f * h_full), 2 lse of the sparse stream, 3
 // rowsum(dO_s * h_sparse); float32 products of the stored outputs and
 // gradients, summed in float32. One workgroup per (step, b*q head); eight
-// lanes per row.
+// lanes per row, each over D/8 contiguous elements.
+__device__ __forceinline__ float dot8(const uint16_t* a, const uint16_t* b, float acc) {
+  const uint4 x = *(const uint4*)a, y = *(const uint4*)b;
+  const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = fmaf(__uint_as_float(xs[i] << 16), __uint_as_float(ys[i] << 16), acc);
+    acc = fmaf(__uint_as_float(xs[i] & 0xffff0000u), __uint_as_float(ys[i] & 0xffff0000u), acc);
+  }
+  return acc;
+}
+__device__ __forceinline__ float dot8(const float* a, const float* b, float acc) {
+  const float4 x0 = *(const float4*)a, x1 = *(const float4*)(a + 4);
+  const float4 y0 = *(const float4*)b, y1 = *(const float4*)(b + 4);
+  acc = fmaf(x0.x, y0.x, acc); acc = fmaf(x0.y, y0.y, acc);
+  acc = fmaf(x0.z, y0.z, acc); acc = fmaf(x0.w, y0.w, acc);
+  acc = fmaf(x1.x, y1.x, acc); acc = fmaf(x1.y, y1.y, acc);
+  acc = fmaf(x1.z, y1.z, acc); acc = fmaf(x1.w, y1.w, acc);
+  return acc;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_stats_kernel(const T* __restrict__ hf,
                                                         const T* __restrict__ hs,
@@ -137,10 +224,10 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const T* __restrict__ hf
   const size_t row = bh * d.Nq + (size_t)s * kStep + r;
   const int per = d.D / 8;
   float df = 0.f, ds = 0.f;
-  for (int i = 0; i < per; ++i) {
+  for (int i = 0; i < per; i += 8) {
     const size_t e = row * d.D + (size_t)part * per + i;
-    if (gf != nullptr) df = fmaf(load_as_f32(gf + e), load_as_f32(hf + e), df);
-    if (gs != nullptr) ds = fmaf(load_as_f32(gs + e), load_as_f32(hs + e), ds);
+    if (gf != nullptr) df = dot8(gf + e, hf + e, df);
+    if (gs != nullptr) ds = dot8(gs + e, hs + e, ds);
   }
 #pragma unroll
   for (int o = 1; o < 8; o <<= 1) {
@@ -158,23 +245,29 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const T* __restrict__ hf
 }
 
 // ---------------------------------------------------------------- selection bits
-// bits[bh][kt][s]: 16 bits per (b*q head, 128-key tile kt, 32-row step s);
-// nibble w covers the 32 keys of wave w, bit 2*qsub + ksub the 16x16 quarter
-// (query rows 16*qsub.., keys 16*ksub..) of that 32x32 block. A bit is set
-// when the quarter's query block selected the quarter's key block. One thread
-// per (b*q head, step) owns its column entries, so no two threads write one
-// word.
+// bits[b*kv head][kt][s][hi]: 16 bits per (128-key tile kt, 32-row step s,
+// q head hi of the GQA group); nibble w covers the 32 keys of wave w, bit
+// 2*qsub + ksub the 16x16 quarter (query rows 16*qsub.., keys 16*ksub..) of
+// that 32x32 block. A bit is set when the quarter's query block selected the
+// quarter's key block. One thread per (b*q head, step) owns its entries, so
+// no two threads write one word.
 __global__ __launch_bounds__(256) void bwd_bits_kernel(const int* __restrict__ idx,
                                                        const int* __restrict__ cnt,
                                                        uint16_t* __restrict__ bits, Dims d,
-                                                       int nKT) {
+                                                       HeadMap hm, int nKT) {
   const int nS = d.Nq / kStep;
   const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= (long)d.B * d.Hq * nS) return;
   const int s = (int)(t % nS);
   const size_t bh = (size_t)(t / nS);
-  uint16_t* col = bits + bh * nKT * nS + s;
-  for (int kt = 0; kt < nKT; ++kt) col[(size_t)kt * nS] = 0;
+  const int b = (int)(bh / d.Hq), h = (int)(bh % d.Hq);
+  const int g = hm.kv_of_q[h];
+  int hi = 0;
+  while (hi < d.G - 1 && hm.q_of_kv[g * d.G + hi] != h) ++hi;
+  const size_t bg = (size_t)b * d.Hkv + g;
+  uint16_t* col = bits + (bg * nKT * nS + s) * d.G + hi;    // entry kt at col[kt * nS * G]
+  const size_t kstride = (size_t)nS * d.G;
+  for (int kt = 0; kt < nKT; ++kt) col[kt * kstride] = 0;
   const int nq = d.bs == 16 ? 2 : 1;
   for (int qs = 0; qs < nq; ++qs) {
     const int qb = d.bs == 16 ? 2 * s + qs : s >> 1;
@@ -186,49 +279,64 @@ __global__ __launch_bounds__(256) void bwd_bits_kernel(const int* __restrict__ i
       if (d.bs == 16) {
         const int kw = kb >> 1;
         const int bit = 4 * (kw & 3) + 2 * qs + (kb & 1);
-        col[(size_t)(kw >> 2) * nS] |= (uint16_t)(1u << bit);
+        col[(kw >> 2) * kstride] |= (uint16_t)(1u << bit);
       } else {
         for (int kw = 2 * kb; kw < 2 * kb + 2; ++kw)
-          col[(size_t)(kw >> 2) * nS] |= (uint16_t)(0xFu << (4 * (kw & 3)));
+          col[(kw >> 2) * kstride] |= (uint16_t)(0xFu << (4 * (kw & 3)));
       }
     }
   }
 }
 
 // ---------------------------------------------------------------- dK / dV
-// One workgroup per (b, kv head, 128-key tile); four waves of 32 keys. For
-// every q head of the group and every 32-row step reaching the tile: S and
-// dP_f (and dP_s on selected blocks) from LDS tiles of Q and dO with K and V
-// in registers, P and dS in registers, then dV^T += dO_f^T P_f (+ dO_s^T P_s)
-// and dK^T += Q^T dS from the transposed tiles. The step tiles (Q, Q^T, dO_f,
-// dO_f^T, dO_s, dO_s^T and the row statistics) are double-buffered in LDS;
-// the copy of the next step overlaps the compute of the current one.
-template <int D>
+// One workgroup per (b, kv head, 128-key tile); four waves of 32 keys. Items
+// are (32-row step s, q head hi) pairs, s from the last step down to the
+// tile's first, hi innermost. Per item, three phases:
+//   A: S = Q K^T and dP_f = dO_f V^T (and dP_s on selected blocks) from the
+//      LDS tiles of Q and dO, K and V in registers;
+//   B: P and dS in registers (exp2, products, bf16 packing);
+//   C: dV^T += dO_f^T P_f (+ dO_s^T P_s), dK^T += Q^T dS, the transposed
+//      operands read from the same tiles.
+// The LDS fragment reads of A and C run a few MFMAs ahead of their use. Item
+// tiles (Q, dO_f, dO_s, row statistics) sit in four LDS stages; the copies
+// run three items ahead of the compute. The items' bit
+// words arrive 64 at a time (lane i holds item 64c + i), one chunk ahead.
+// MODE 0: both streams; 1: full stream only; 2: sparse stream only (items
+// without a selected block are skipped).
+template <int D, int MODE, int IO>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ QT, const uint16_t* __restrict__ GF,
-    const uint16_t* __restrict__ GFT, const uint16_t* __restrict__ GS,
-    const uint16_t* __restrict__ GST, const float* __restrict__ stats,
-    const uint16_t* __restrict__ bits, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-    Dims d, HeadMap hm, int nKT) {
-  constexpr int SPR = D / 8;          // 16-byte chunks per row-major row
+    const uint16_t* __restrict__ GF, const uint16_t* __restrict__ GS,
+    const float* __restrict__ stats, const uint16_t* __restrict__ bits,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ pK,
+    float* __restrict__ pV, Dims d, HeadMap hm, int nKT) {
+  constexpr bool FULL = MODE != 2, SPARSE = MODE != 1;
+  constexpr int SPR = D / 8;          // 16-byte chunks per row
   constexpr int KK = D / 32;          // 32-deep k-steps over D
-  constexpr int MB = D / 16;          // 16-row blocks over D
+  constexpr int MB = D / 16;          // 16-column blocks over D
   constexpr int TILE = kStep * D;     // bf16 elements per step tile
-  __shared__ __align__(16) uint16_t sQ[2][TILE], sQT[2][TILE], sGF[2][TILE], sGFT[2][TILE];
-  __shared__ __align__(16) uint16_t sGS[2][TILE], sGST[2][TILE];
-  __shared__ __align__(16) float sStat[2][8 * kStep];
-  __shared__ uint16_t sBits[kMaxSteps];
+  constexpr int CT = kStep * SPR / 4 / 64;   // copy instructions per tile per wave
+  constexpr int CPI = CT * (1 + (FULL ? 1 : 0) + (SPARSE ? 1 : 0)) + 1;   // per item per wave
+  static_assert(2 * CPI < 16, "vmcnt immediate");
+  __shared__ __align__(16) uint16_t sQ[kStages][TILE];
+  __shared__ __align__(16) uint16_t sGF[FULL ? kStages : 1][FULL ? TILE : 8];
+  __shared__ __align__(16) uint16_t sGS[SPARSE ? kStages : 1][SPARSE ? TILE : 8];
+  __shared__ __align__(16) float sStat[kStages][4 * kStep];
+  constexpr uint32_t TB = TILE * 2u, SB = 4u * kStep * 4u;   // stage strides in bytes
+  const uint32_t aQ = lds_u32(&sQ[0][0]), aGF = lds_u32(&sGF[0][0]);
+  const uint32_t aGS = lds_u32(&sGS[0][0]), aSt = lds_u32(&sStat[0][0]);
 
-  const bool has_full = GF != nullptr, has_sparse = GS != nullptr;
   const int nBG = d.B * d.Hkv;
   const int bg = blockIdx.x % nBG, kt = blockIdx.x / nBG;   // heaviest tiles first
   const int b = bg / d.Hkv, g = bg % d.Hkv;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, gq = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, gq = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nS = d.Nq / kStep;
+  const int G = d.G;
   const int kw0 = kt * kKeysPerWg + kStep * w;   // first key of this wave
   const bool wave_keys = kw0 < d.Nk;
   const int s_first = kt * (kKeysPerWg / kStep);  // first step whose rows reach the tile
+  const int nItems = G * (nS - s_first);
   const float sl2 = d.scale_log2;
 
   bf16x8_t kreg[2][KK], vreg[2][KK];
@@ -243,171 +351,271 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
         vreg[nb][kk] = wave_keys ? *(const bf16x8_t*)(V + off) : bf16x8_t{};
       }
   }
+  const size_t obase = ((size_t)bg * d.Nk) * D;
+  auto out_off = [&](int mb, int nb) {
+    return obase + (size_t)(kw0 + 16 * nb + n) * D + 16 * mb + 4 * gq;
+  };
   f32x4_t accK[MB][2], accV[MB][2];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) accK[mb][nb] = accV[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < 2; ++nb) {
+      if (IO == 2 && wave_keys) {   // continue the full-stream pass's partial sums
+        accK[mb][nb] = *(const f32x4_t*)(pK + out_off(mb, nb));
+        accV[mb][nb] = *(const f32x4_t*)(pV + out_off(mb, nb));
+      } else {
+        accK[mb][nb] = accV[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+
+  // item e -> (step, head index)
+  auto item_s = [&](int e) { return nS - 1 - e / G; };
+  auto item_h = [&](int e) { return e % G; };
+  const uint16_t* tile_bits = bits + (size_t)(bg * nKT + kt) * nS * G;
+  auto load_chunk = [&](int c) -> uint32_t {
+    const int e = 64 * c + lane;
+    if (!SPARSE || e >= nItems) return 0u;
+    return tile_bits[(size_t)item_s(e) * G + item_h(e)];
+  };
+  int chunk = 0;
+  uint32_t chA = load_chunk(0), chB = load_chunk(1);
+  // next item >= from that has work (every item unless sparse-only), with
+  // its bit word; nItems when none is left
+  auto find = [&](int from, uint32_t& word) -> int {
+    while (from < nItems) {
+      while ((from >> 6) > chunk) {
+        chA = chB;
+        chB = load_chunk(chunk + 2);
+        ++chunk;
+      }
+      const uint64_t act = MODE == 2 ? __ballot(chA != 0u) : ~0ull;
+      const uint64_t m = act & (~0ull << (from & 63));
+      if (m) {
+        const int e = (chunk << 6) + __builtin_ctzll(m);
+        word = __builtin_amdgcn_readlane(chA, e & 63);
+        return e;
+      }
+      from = (chunk + 1) << 6;
+    }
+    return nItems;
+  };
 
   const uint32_t head_bytes = (uint32_t)d.Nq * D * 2u;
   const uint32_t stat_bytes = (uint32_t)nS * 4u * kStep * 4u;
 
-  for (int hi = 0; hi < d.G; ++hi) {
-    const int h = hm.q_of_kv[g * d.G + hi];
-    const size_t bh = (size_t)b * d.Hq + h;
-    const i32x4_t rq = make_rsrc_words(Q + bh * d.Nq * D, head_bytes);
-    const i32x4_t rqt = make_rsrc_words(QT + bh * d.Nq * D, head_bytes);
-    const i32x4_t rgf = make_rsrc_words(has_full ? GF + bh * d.Nq * D : Q, has_full ? head_bytes : 0u);
-    const i32x4_t rgft = make_rsrc_words(has_full ? GFT + bh * d.Nq * D : Q, has_full ? head_bytes : 0u);
-    const i32x4_t rgs = make_rsrc_words(has_sparse ? GS + bh * d.Nq * D : Q, has_sparse ? head_bytes : 0u);
-    const i32x4_t rgst = make_rsrc_words(has_sparse ? GST + bh * d.Nq * D : Q, has_sparse ? head_bytes : 0u);
-    const i32x4_t rst = make_rsrc_words(stats + bh * nS * 4 * kStep, stat_bytes);
-
-    __syncthreads();   // every wave is done with the previous head's tiles and bits
-    if (has_sparse) {
-      const uint16_t* bc = bits + ((size_t)bh * nKT + kt) * nS;
-      for (int i = s_first + tid; i < nS; i += 256) sBits[i] = bc[i];
+  auto issue = [&](int e, uint32_t word, int st) __attribute__((always_inline)) {
+    const int s = item_s(e);
+    const size_t bh = (size_t)b * d.Hq + hm.q_of_kv[g * G + item_h(e)];
+    const uint32_t toff = (uint32_t)s * kStep * D * 2u;
+    copy_tile<SPR>(make_rsrc_words(Q + bh * d.Nq * D, head_bytes), toff, aQ + st * TB, w, lane);
+    if (FULL)
+      copy_tile<SPR>(make_rsrc_words(GF + bh * d.Nq * D, head_bytes), toff, aGF + st * TB, w, lane);
+    if (SPARSE)   // a record count of 0 turns an unneeded copy into zero fills, so
+                  // every item issues the same number of copies
+      copy_tile<SPR>(make_rsrc_words(GS + bh * d.Nq * D, word != 0u ? head_bytes : 0u), toff,
+                     aGS + st * TB, w, lane);
+    if (lane < 8) {   // wave w brings statistics array w of the item's 32 rows
+      const uint32_t la = __builtin_amdgcn_readfirstlane(aSt + st * SB + kStep * 4u * w);
+      copy16_to_lds(make_rsrc_words(stats + bh * nS * 4 * kStep, stat_bytes),
+                    __builtin_amdgcn_readfirstlane((uint32_t)(s * 4 + w) * kStep * 4u),
+                    (uint32_t)lane * 16u, la);
     }
-    __syncthreads();
-    auto step_bits = [&](int s) -> uint32_t { return has_sparse ? sBits[s] : 0u; };
+  };
 
-    auto issue = [&](int s, int st) __attribute__((always_inline)) {
-      const uint32_t toff = (uint32_t)s * kStep * D * 2u;     // row-major tile offset
-      const uint32_t tcol = (uint32_t)s * kStep * 2u;         // transposed tile column offset
-      const uint32_t trow = (uint32_t)d.Nq * 2u;              // transposed row stride
-      copy_tile<SPR, kStep, false>(rq, toff, D * 2u, sQ[st], w, lane);
-      copy_tile<4, D, true>(rqt, tcol, trow, sQT[st], w, lane);
-      if (has_full) {
-        copy_tile<SPR, kStep, false>(rgf, toff, D * 2u, sGF[st], w, lane);
-        copy_tile<4, D, true>(rgft, tcol, trow, sGFT[st], w, lane);
-      }
-      if (has_sparse && step_bits(s) != 0) {
-        copy_tile<SPR, kStep, false>(rgs, toff, D * 2u, sGS[st], w, lane);
-        copy_tile<4, D, true>(rgst, tcol, trow, sGST[st], w, lane);
-      }
-      if (w == 0) {
-        const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)s * 4u * kStep * 4u);
-        const uint32_t la = __builtin_amdgcn_readfirstlane(
-            (uint32_t)(uintptr_t)(lds_ptr_t)(&sStat[st][0]));
-        copy16_to_lds(rst, soff, (uint32_t)lane * 16u, la);
-      }
-    };
-
-    auto compute = [&](int s, int st) __attribute__((always_inline)) {
-      if (!wave_keys || kStep * s + kStep - 1 < kw0) return;   // every key after every row
-      const bool diag = kStep * s == kw0;
-      const uint32_t nib = (step_bits(s) >> (4 * w)) & 0xFu;
-      const bool sp = nib != 0;
-      const uint16_t* tq = sQ[st];
-      f32x4_t sa[2][2], pf[2][2], ps[2][2];
+  // No early exit and no branch around the dK / dV updates: a wave whose keys
+  // all follow the item's rows gets P = dS = 0 from the causal mask, so the
+  // loop-carried accumulators never pass through a control-flow merge (which
+  // would copy them between register files every item).
+  auto compute = [&](int e, uint32_t word, int st) __attribute__((always_inline)) {
+    const int s = item_s(e);
+    const int rel = kStep * s - kw0;   // row position minus key position of (0, 0)
+    const uint32_t nib = SPARSE ? (word >> (4 * w)) & 0xFu : 0u;
+    const bool sp = nib != 0u;
+    typedef __attribute__((address_space(3))) const f32x4_t* lpf;
+    auto stat = [&](int a, int r0) { return *(lpf)(uintptr_t)(aSt + st * SB + 4u * (a * kStep + r0)); };
+    // statistics of the lane's rows 8*gq + 4*mb + r, read ahead of use
+    f32x4_t lf[2], df[2], ls[2], dd[2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb) {
+      const int r0 = 8 * gq + 4 * mb;
+      if (FULL) {
+        lf[mb] = stat(0, r0);
+        df[mb] = stat(1, r0);
+      }
+      if (sp) {
+        ls[mb] = stat(2, r0);
+        dd[mb] = stat(3, r0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // A: S and dP_f
+    f32x4_t sa[2][2], pf[2][2], ps[2][2];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) sa[mb][nb] = pf[mb][nb] = ps[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) sa[mb][nb] = pf[mb][nb] = ps[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    {
+      constexpr int NR = (FULL ? 2 : 1) * 2 * KK;   // fragment reads
+      bf16x8_t fr[NR];
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const int row = rho(mb, n);
-          const bf16x8_t a = frag_rows<SPR>(tq, row, 4 * kk + gq);
+          const int i = (FULL ? 2 : 1) * (2 * kk + mb);
+          fr[i] = frag_rows<SPR>(aQ + st * TB, rho(mb, n), 4 * kk + gq);
+          if (FULL) fr[i + 1] = frag_rows<SPR>(aGF + st * TB, rho(mb, n), 4 * kk + gq);
+        }
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) sa[mb][nb] = mfma16(a, kreg[nb][kk], sa[mb][nb]);
-          if (has_full) {
-            const bf16x8_t af = frag_rows<SPR>(sGF[st], row, 4 * kk + gq);
+      for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) pf[mb][nb] = mfma16(af, vreg[nb][kk], pf[mb][nb]);
-          }
-          if (sp) {
-            const bf16x8_t as = frag_rows<SPR>(sGS[st], row, 4 * kk + gq);
+        for (int mb = 0; mb < 2; ++mb) {
+          const int i = (FULL ? 2 : 1) * (2 * kk + mb);
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) ps[mb][nb] = mfma16(as, vreg[nb][kk], ps[mb][nb]);
+          for (int nb = 0; nb < 2; ++nb) sa[mb][nb] = mfma16(fr[i], kreg[nb][kk], sa[mb][nb]);
+          if (FULL) {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) pf[mb][nb] = mfma16(fr[i + 1], vreg[nb][kk], pf[mb][nb]);
           }
         }
-      // P and dS, in the B-operand layout: slot j of lane group gq is row 8*gq + j
-      float xf[2][8], xs[2][8], xd[2][8];
-      const float* stt = sStat[st];
+      pipeline_mix<NR, 2, 6>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (sp) {
+      bf16x8_t fr[2 * KK];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int r0 = 8 * gq + 4 * mb;
-        const f32x4_t lf = *(const f32x4_t*)(stt + 0 * kStep + r0);
-        const f32x4_t df = *(const f32x4_t*)(stt + 1 * kStep + r0);
-        const f32x4_t ls = *(const f32x4_t*)(stt + 2 * kStep + r0);
-        const f32x4_t dd = *(const f32x4_t*)(stt + 3 * kStep + r0);
+      for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const bool sel = sp && ((nib >> (2 * (gq >> 1) + nb)) & 1u);
+        for (int mb = 0; mb < 2; ++mb) fr[2 * kk + mb] = frag_rows<SPR>(aGS + st * TB, rho(mb, n), 4 * kk + gq);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool masked = diag && (16 * nb + n > r0 + i);
-            const float x = sa[mb][nb][i] * sl2;
-            float p = 0.f, dsv = 0.f, q = 0.f;
-            if (has_full) {
-              p = masked ? 0.f : fast_exp2(x - lf[i]);
-              dsv = p * (pf[mb][nb][i] - df[i]);
-            }
-            if (sel) {
-              q = masked ? 0.f : fast_exp2(x - ls[i]);
-              dsv = fmaf(q, ps[mb][nb][i] - dd[i], dsv);
-            }
-            xf[nb][4 * mb + i] = p;
-            xs[nb][4 * mb + i] = q;
-            xd[nb][4 * mb + i] = dsv;
-          }
-        }
-      }
-      bf16x8_t bP[2], bS[2], bD[2];
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) ps[mb][nb] = mfma16(fr[2 * kk + mb], vreg[nb][kk], ps[mb][nb]);
+      pipeline_mix<2 * KK, 2, 4>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // B: P and dS in the B-operand layout (slot j of lane group gq is row 8*gq + j)
+    float xf[2][8], xs[2][8], xd[2][8];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int r0 = 8 * gq + 4 * mb;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        bP[nb] = pack8(xf[nb]);
-        bS[nb] = pack8(xs[nb]);
-        bD[nb] = pack8(xd[nb]);
+        const bool sel = sp && ((nib >> (2 * (gq >> 1) + nb)) & 1u);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool keep = 16 * nb + n <= rel + r0 + r;   // key <= row
+          float p = 0.f, dsv = 0.f, q = 0.f;
+          if (FULL) {
+            p = fast_exp2(fmaf(sa[mb][nb][r], sl2, -lf[mb][r]));
+            p = keep ? p : 0.f;
+            dsv = p * (pf[mb][nb][r] - df[mb][r]);
+          }
+          if (sp) {
+            q = fast_exp2(fmaf(sa[mb][nb][r], sl2, -ls[mb][r]));
+            q = (keep && sel) ? q : 0.f;
+            dsv = fmaf(q, ps[mb][nb][r] - dd[mb][r], dsv);
+          }
+          xf[nb][4 * mb + r] = p;
+          xs[nb][4 * mb + r] = q;
+          xd[nb][4 * mb + r] = dsv;
+        }
+      }
+    }
+    bf16x8_t bP[2], bS[2], bD[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      bP[nb] = pack8(xf[nb]);
+      bS[nb] = pack8(xs[nb]);
+      bD[nb] = pack8(xd[nb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // C: dV^T += dO^T P (+ dO_s^T P_s), dK^T += Q^T dS
+    {
+      constexpr int NR = (FULL ? 2 : 1) * MB;
+      bf16x8_t tr[NR];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int i = (FULL ? 2 : 1) * mb;
+        tr[i] = frag_tr<SPR>(aQ + st * TB, 16 * mb, lane);
+        if (FULL) tr[i + 1] = frag_tr<SPR>(aGF + st * TB, 16 * mb, lane);
+      }
+      bf16x8_t ts[SPARSE ? MB : 1];
+      if (SPARSE) {
+        // the sparse products run on every item; without a selected block
+        // P_s is 0 and the Q^T fragments stand in for dO_s^T
+        if (sp) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) ts[mb] = frag_tr<SPR>(aGS + st * TB, 16 * mb, lane);
+        } else {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) ts[mb] = tr[(FULL ? 2 : 1) * mb];
+        }
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const int row = 16 * mb + n;
-        if (has_full) {
-          const bf16x8_t a = frag_t(sGFT[st], row, gq);
+        const int i = (FULL ? 2 : 1) * mb;
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) accV[mb][nb] = mfma16(a, bP[nb], accV[mb][nb]);
+        for (int nb = 0; nb < 2; ++nb) accK[mb][nb] = mfma16(tr[i], bD[nb], accK[mb][nb]);
+        if (FULL) {
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) accV[mb][nb] = mfma16(tr[i + 1], bP[nb], accV[mb][nb]);
         }
-        if (sp) {
-          const bf16x8_t a = frag_t(sGST[st], row, gq);
+        if (SPARSE) {
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) accV[mb][nb] = mfma16(a, bS[nb], accV[mb][nb]);
+          for (int nb = 0; nb < 2; ++nb) accV[mb][nb] = mfma16(ts[mb], bS[nb], accV[mb][nb]);
         }
-        const bf16x8_t aq = frag_t(sQT[st], row, gq);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) accK[mb][nb] = mfma16(aq, bD[nb], accK[mb][nb]);
       }
-    };
+      pipeline_mix<2 * NR, (FULL ? 1 : 2) + (SPARSE ? 1 : 0), 8>();   // two transpose reads per fragment
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 
-    int s = has_full ? s_first : next_selected(s_first - 1, nS, lane, step_bits);
-    if (s >= nS) continue;
-    int st = 0;
-    issue(s, st);
+  // items x0 (current) .. x3, with their bit words; copies run three items
+  // ahead of the compute, each into the stage the item four back used
+  int x0, x1, x2, x3;
+  uint32_t w0 = 0u, w1 = 0u, w2 = 0u, w3 = 0u;
+  x0 = find(0, w0);
+  x1 = x0 < nItems ? find(x0 + 1, w1) : nItems;
+  x2 = x1 < nItems ? find(x1 + 1, w2) : nItems;
+  if (x0 < nItems) {
+    issue(x0, w0, 0);
+    if (x1 < nItems) issue(x1, w1, 1);
+    if (x2 < nItems) issue(x2, w2, 2);
+    int e = 0;   // ordinal of x0 in the walk; its stage is e % kStages
     while (true) {
-      const int sn = has_full ? s + 1 : next_selected(s, nS, lane, step_bits);
-      wait_vm();
-      __syncthreads();   // step s landed for every wave; stage st^1 is free
-      if (sn < nS) issue(sn, st ^ 1);
-      compute(s, st);
-      if (sn >= nS) break;
-      s = sn;
-      st ^= 1;
+      x3 = x2 < nItems ? find(x2 + 1, w3) : nItems;
+      // item x0 has landed once at most the copies of x1 and x2 are in flight
+      if (x2 < nItems) wait_vm_n<2 * CPI>();
+      else if (x1 < nItems) wait_vm_n<CPI>();
+      else wait_vm();
+      __syncthreads();   // x0 visible to every wave; stage (e + 3) % 4 is free
+      if (x3 < nItems) issue(x3, w3, (e + 3) % kStages);
+      compute(x0, w0, e % kStages);
+      if (x1 >= nItems) break;
+      x0 = x1; w0 = w1;
+      x1 = x2; w1 = w2;
+      x2 = x3; w2 = w3;
+      ++e;
     }
   }
   wait_vm();
 
   if (!wave_keys) return;
-  const size_t obase = ((size_t)bg * d.Nk) * D;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const size_t off = obase + (size_t)(kw0 + 16 * nb + n) * D + 16 * mb + 4 * gq;
+      const size_t off = out_off(mb, nb);
       const f32x4_t kv = accK[mb][nb], vv = accV[mb][nb];
-      store4_bf16(dK + off, kv[0] * d.scale, kv[1] * d.scale, kv[2] * d.scale, kv[3] * d.scale);
-      store4_bf16(dV + off, vv[0], vv[1], vv[2], vv[3]);
+      if (IO == 1) {   // float32 partial sums (dK unscaled) for the sparse pass
+        *(f32x4_t*)(pK + off) = kv;
+        *(f32x4_t*)(pV + off) = vv;
+      } else {
+        store4_bf16(dK + off, kv[0] * d.scale, kv[1] * d.scale, kv[2] * d.scale, kv[3] * d.scale);
+        store4_bf16(dV + off, vv[0], vv[1], vv[2], vv[3]);
+      }
     }
 }
 
@@ -415,30 +623,38 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
 // One workgroup per (b, q head, 128-row query tile); four waves of 32 rows.
 // Q and both upstream gradients of the wave's rows stay in registers; per
 // 32-key step, S^T = K Q^T and dP^T = V dO^T from LDS tiles of K and V, then
-// dQ^T += K^T dS^T from the K^T tile. The selection bits of the workgroup's
-// rows are built in LDS from idx at the start.
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
+// dQ^T += K^T dS^T with K^T read from the K tile by transpose reads. The
+// selection bits of the workgroup's rows are built in LDS from idx at the
+// start. Workgroups are ordered heaviest first, the q heads of one kv head
+// next to each other.
+template <int D, int MODE, int IO>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ KT, const uint16_t* __restrict__ GF,
-    const uint16_t* __restrict__ GS, const float* __restrict__ stats,
-    const int* __restrict__ idx, const int* __restrict__ cnt, uint16_t* __restrict__ dQ, Dims d,
-    HeadMap hm) {
+    const uint16_t* __restrict__ GF, const uint16_t* __restrict__ GS,
+    const float* __restrict__ stats, const int* __restrict__ idx, const int* __restrict__ cnt,
+    uint16_t* __restrict__ dQ, float* __restrict__ pQ, Dims d, HeadMap hm) {
   constexpr int SPR = D / 8;
   constexpr int KK = D / 32;
   constexpr int MB = D / 16;
   constexpr int TILE = kStep * D;
-  __shared__ __align__(16) uint16_t sK[2][TILE], sV[2][TILE], sKT[2][TILE];
+  constexpr int CT = kStep * SPR / 4 / 64;   // copy instructions per tile per wave
+  constexpr int CPS = 2 * CT;                 // per key step per wave
+  __shared__ __align__(16) uint16_t sK[kStages][TILE], sV[kStages][TILE];
   __shared__ uint32_t sNib[kMaxSteps / 2];   // 16 bits per key step: nibble w for wave w
+  constexpr uint32_t TB = TILE * 2u;
+  const uint32_t aK = lds_u32(&sK[0][0]), aV = lds_u32(&sV[0][0]);
 
-  const bool has_full = GF != nullptr, has_sparse = GS != nullptr;
-  const int nBH = d.B * d.Hq;
+  constexpr bool has_full = MODE != 2, has_sparse = MODE != 1;
+  const int nBG = d.B * d.Hkv;
   const int nQT = (d.Nq + kRowsPerWg - 1) / kRowsPerWg;
-  const int bh = blockIdx.x % nBH, qt = nQT - 1 - (int)(blockIdx.x / nBH);   // heaviest first
-  const int b = bh / d.Hq, h = bh % d.Hq;
-  const int g = hm.kv_of_q[h];
-  const size_t bgk = (size_t)b * d.Hkv + g;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, gq = lane >> 4;
+  const int bg = blockIdx.x % nBG;
+  const int hi = (blockIdx.x / nBG) % d.G;
+  const int qt = nQT - 1 - (int)(blockIdx.x / (nBG * d.G));   // heaviest first
+  const int b = bg / d.Hkv, g = bg % d.Hkv;
+  const int h = hm.q_of_kv[g * d.G + hi];
+  const size_t bh = (size_t)b * d.Hq + h;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, gq = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r0w = qt * kRowsPerWg + kStep * w;     // first row of this wave
   const bool wave_rows = r0w < d.Nq;
   const int last_row = min(qt * kRowsPerWg + kRowsPerWg, d.Nq) - 1;
@@ -454,8 +670,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
       const int nq = d.bs == 16 ? 2 : 1;
       for (int qs = 0; qs < nq; ++qs) {
         const int qb = d.bs == 16 ? r0w / 16 + qs : r0w / 64;
-        const int* list = idx + ((size_t)bh * d.nQB + qb) * d.budget;
-        const int cn = min(max(cnt[(size_t)bh * d.nQB + qb], 0), d.budget);
+        const int* list = idx + (bh * d.nQB + qb) * d.budget;
+        const int cn = min(max(cnt[bh * d.nQB + qb], 0), d.budget);
         for (int e = lane; e < cn; e += 64) {
           const int kb = list[e];
           if (kb < 0 || kb > qb) continue;
@@ -477,47 +693,53 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   };
 
   // wave operands in registers
-  bf16x8_t qreg[2][KK], freg[2][KK], sreg[2][KK];
+  bf16x8_t qreg[2][KK], freg[has_full ? 2 : 1][KK], sreg[has_sparse ? 2 : 1][KK];
   float lf[2], dfv[2], ls[2], dsv_[2];
   {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int row = wave_rows ? r0w + 16 * nb + n : 0;
-      const size_t base = ((size_t)bh * d.Nq + row) * D + 8 * gq;
+      const size_t base = (bh * d.Nq + row) * D + 8 * gq;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         qreg[nb][kk] = *(const bf16x8_t*)(Q + base + 32 * kk);
-        freg[nb][kk] = has_full ? *(const bf16x8_t*)(GF + base + 32 * kk) : bf16x8_t{};
-        sreg[nb][kk] = has_sparse ? *(const bf16x8_t*)(GS + base + 32 * kk) : bf16x8_t{};
+        if (has_full) freg[nb][kk] = *(const bf16x8_t*)(GF + base + 32 * kk);
+        if (has_sparse) sreg[nb][kk] = *(const bf16x8_t*)(GS + base + 32 * kk);
       }
-      const float* st = stats + (((size_t)bh * nS + row / kStep) * 4) * kStep + row % kStep;
+      const float* st = stats + ((bh * nS + row / kStep) * 4) * kStep + row % kStep;
       lf[nb] = st[0];
       dfv[nb] = st[kStep];
       ls[nb] = st[2 * kStep];
       dsv_[nb] = st[3 * kStep];
     }
   }
+  auto out_off = [&](int mb, int nb) {
+    return (bh * d.Nq + r0w + 16 * nb + n) * D + 16 * mb + 4 * gq;
+  };
   f32x4_t acc[MB][2];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < 2; ++nb)
+      acc[mb][nb] = (IO == 2 && wave_rows) ? *(const f32x4_t*)(pQ + out_off(mb, nb))
+                                           : f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  const size_t bgk = (size_t)bg;
   const uint32_t kv_bytes = (uint32_t)d.Nk * D * 2u;
   const i32x4_t rk = make_rsrc_words(K + bgk * d.Nk * D, kv_bytes);
   const i32x4_t rv = make_rsrc_words(V + bgk * d.Nk * D, kv_bytes);
-  const i32x4_t rkt = make_rsrc_words(KT + bgk * d.Nk * D, kv_bytes);
 
   auto issue = [&](int t, int st) __attribute__((always_inline)) {
     const uint32_t toff = (uint32_t)t * kStep * D * 2u;
-    copy_tile<SPR, kStep, false>(rk, toff, D * 2u, sK[st], w, lane);
-    copy_tile<SPR, kStep, false>(rv, toff, D * 2u, sV[st], w, lane);
-    copy_tile<4, D, true>(rkt, (uint32_t)t * kStep * 2u, (uint32_t)d.Nk * 2u, sKT[st], w, lane);
+    copy_tile<SPR>(rk, toff, aK + st * TB, w, lane);
+    copy_tile<SPR>(rv, toff, aV + st * TB, w, lane);
   };
 
+  // No early exit and no branch around the dQ update: keys after the rows
+  // (and rows past the end) get dS = 0 from the mask, so the loop-carried
+  // accumulators never pass through a control-flow merge.
   auto compute = [&](int t, int st) __attribute__((always_inline)) {
-    if (!wave_rows || kStep * t > r0w + kStep - 1) return;   // every key after every row
-    const bool diag = kStep * t == r0w;
+    const int rel = r0w - kStep * t;   // row position minus key position of (0, 0)
     const uint32_t nib = (step_bits(t) >> (4 * w)) & 0xFu;
     const bool sp = nib != 0;
     f32x4_t sa[2][2], pf[2][2], ps[2][2];
@@ -525,41 +747,57 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) sa[mb][nb] = pf[mb][nb] = ps[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    {
+      bf16x8_t fr[4 * KK];   // K and V fragments, read ahead of their MFMAs
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
+      for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int key = rho(mb, n);
-        const bf16x8_t a = frag_rows<SPR>(sK[st], key, 4 * kk + gq);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) sa[mb][nb] = mfma16(a, qreg[nb][kk], sa[mb][nb]);
-        const bf16x8_t av = frag_rows<SPR>(sV[st], key, 4 * kk + gq);
-        if (has_full) {
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) pf[mb][nb] = mfma16(av, freg[nb][kk], pf[mb][nb]);
+        for (int mb = 0; mb < 2; ++mb) {
+          fr[2 * (2 * kk + mb)] = frag_rows<SPR>(aK + st * TB, rho(mb, n), 4 * kk + gq);
+          fr[2 * (2 * kk + mb) + 1] = frag_rows<SPR>(aV + st * TB, rho(mb, n), 4 * kk + gq);
         }
-        if (sp) {
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) ps[mb][nb] = mfma16(av, sreg[nb][kk], ps[mb][nb]);
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const int i = 2 * (2 * kk + mb);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) sa[mb][nb] = mfma16(fr[i], qreg[nb][kk], sa[mb][nb]);
+          if (has_full) {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) pf[mb][nb] = mfma16(fr[i + 1], freg[nb][kk], pf[mb][nb]);
+          }
         }
+      if (has_sparse && sp) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+              ps[mb][nb] = mfma16(fr[2 * (2 * kk + mb) + 1], sreg[nb][kk], ps[mb][nb]);
       }
+      pipeline_mix<4 * KK, 2, 6>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
     float xd[2][8];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const bool sel = sp && ((nib >> (2 * nb + (gq >> 1))) & 1u);
+      const bool sel = (nib >> (2 * nb + (gq >> 1))) & 1u;   // per lane
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool masked = diag && (8 * gq + 4 * mb + i > 16 * nb + n);
-          const float x = sa[mb][nb][i] * sl2;
+          const bool keep = wave_rows && 8 * gq + 4 * mb + i <= rel + 16 * nb + n;   // key <= row
           float dsv = 0.f;
           if (has_full) {
-            const float p = masked ? 0.f : fast_exp2(x - lf[nb]);
+            float p = fast_exp2(fmaf(sa[mb][nb][i], sl2, -lf[nb]));
+            p = keep ? p : 0.f;
             dsv = p * (pf[mb][nb][i] - dfv[nb]);
           }
-          if (sel) {
-            const float q = masked ? 0.f : fast_exp2(x - ls[nb]);
+          if (has_sparse && sp) {   // wave-uniform branch; the lane's own bit masks
+            float q = fast_exp2(fmaf(sa[mb][nb][i], sl2, -ls[nb]));
+            q = (keep && sel) ? q : 0.f;
             dsv = fmaf(q, ps[mb][nb][i] - dsv_[nb], dsv);
           }
           xd[nb][4 * mb + i] = dsv;
@@ -568,27 +806,43 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     bf16x8_t bD[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) bD[nb] = pack8(xd[nb]);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      bf16x8_t tr[MB];   // K^T fragments by transpose reads of the K tile
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const bf16x8_t a = frag_t(sKT[st], 16 * mb + n, gq);
+      for (int mb = 0; mb < MB; ++mb) tr[mb] = frag_tr<SPR>(aK + st * TB, 16 * mb, lane);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma16(a, bD[nb], acc[mb][nb]);
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma16(tr[mb], bD[nb], acc[mb][nb]);
+      pipeline_mix<2 * MB, 1, 8>();
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  int t = has_full ? 0 : next_selected(-1, nT, lane, step_bits);
-  if (t < nT) {
-    int st = 0;
-    issue(t, st);
+  // key steps t0 (current) .. t3; copies run three steps ahead
+  auto next = [&](int t) { return has_full ? t + 1 : next_selected(t, nT, lane, step_bits); };
+  int t0 = has_full ? 0 : next_selected(-1, nT, lane, step_bits);
+  int t1 = t0 < nT ? next(t0) : nT;
+  int t2 = t1 < nT ? next(t1) : nT;
+  if (t0 < nT) {
+    issue(t0, 0);
+    if (t1 < nT) issue(t1, 1);
+    if (t2 < nT) issue(t2, 2);
+    int e = 0;
     while (true) {
-      const int tn = has_full ? t + 1 : next_selected(t, nT, lane, step_bits);
-      wait_vm();
+      const int t3 = t2 < nT ? next(t2) : nT;
+      if (t2 < nT) wait_vm_n<2 * CPS>();
+      else if (t1 < nT) wait_vm_n<CPS>();
+      else wait_vm();
       __syncthreads();
-      if (tn < nT) issue(tn, st ^ 1);
-      compute(t, st);
-      if (tn >= nT) break;
-      t = tn;
-      st ^= 1;
+      if (t3 < nT) issue(t3, (e + 3) % kStages);
+      compute(t0, e % kStages);
+      if (t1 >= nT) break;
+      t0 = t1;
+      t1 = t2;
+      t2 = t3;
+      ++e;
     }
   }
   wait_vm();
@@ -598,9 +852,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const size_t off = ((size_t)bh * d.Nq + r0w + 16 * nb + n) * D + 16 * mb + 4 * gq;
+      const size_t off = out_off(mb, nb);
       const f32x4_t a = acc[mb][nb];
-      store4_bf16(dQ + off, a[0] * d.scale, a[1] * d.scale, a[2] * d.scale, a[3] * d.scale);
+      if (IO == 1) *(f32x4_t*)(pQ + off) = a;   // unscaled partial sums for the sparse pass
+      else store4_bf16(dQ + off, a[0] * d.scale, a[1] * d.scale, a[2] * d.scale, a[3] * d.scale);
     }
 }
 
@@ -762,31 +1017,43 @@ hipError_t launch_attn_bwd_stats(const void* hf, const void* hs, const void* gf,
 int bwd_key_tiles(const Dims& d) { return (d.Nk + kKeysPerWg - 1) / kKeysPerWg; }
 
 hipError_t launch_attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                const uint16_t* qt, const uint16_t* kt, const uint16_t* gf,
-                                const uint16_t* gft, const uint16_t* gs, const uint16_t* gst,
-                                const int* idx, const int* cnt, const float* stats,
-                                uint16_t* bits, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                                const uint16_t* gf, const uint16_t* gs, const int* idx,
+                                const int* cnt, const float* stats, uint16_t* bits, float* pq,
+                                float* pk, float* pv, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                                 const Dims& d, const HeadMap& hm, hipStream_t stream) {
   const int nKT = bwd_key_tiles(d);
   if (gs != nullptr) {
     const long threads = (long)d.B * d.Hq * (d.Nq / kStep);
     hipLaunchKernelGGL(bwd_bits_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       stream, idx, cnt, bits, d, nKT);
+                       stream, idx, cnt, bits, d, hm, nKT);
   }
   const dim3 g1((unsigned)(nKT * d.B * d.Hkv));
   const int nQT = (d.Nq + kRowsPerWg - 1) / kRowsPerWg;
   const dim3 g2((unsigned)(nQT * d.B * d.Hq));
-  if (d.D == 128) {
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, g1, dim3(256), 0, stream, q, k, v, qt, gf, gft,
-                       gs, gst, stats, bits, dk, dv, d, hm, nKT);
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, g2, dim3(256), 0, stream, q, k, v, kt, gf, gs,
-                       stats, idx, cnt, dq, d, hm);
-  } else {
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, g1, dim3(256), 0, stream, q, k, v, qt, gf, gft,
-                       gs, gst, stats, bits, dk, dv, d, hm, nKT);
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, g2, dim3(256), 0, stream, q, k, v, kt, gf, gs,
-                       stats, idx, cnt, dq, d, hm);
+#define SSA_DKDV(DD, MM, IO)                                                                 \
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DD, MM, IO>), g1, dim3(256), 0, stream, q, k, v, gf, \
+                     gs, stats, bits, dk, dv, pk, pv, d, hm, nKT)
+#define SSA_DQ(DD, MM, IO)                                                                   \
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DD, MM, IO>), g2, dim3(256), 0, stream, q, k, v, gf, \
+                     gs, stats, idx, cnt, dq, pq, d, hm)
+  // Both streams: a full-stream pass leaves float32 partial sums, a
+  // sparse-stream pass over the selected blocks only adds to them and rounds.
+#define SSA_PASSES(DD)                                                                       \
+  if (gf != nullptr && gs != nullptr) {                                                      \
+    SSA_DKDV(DD, 1, 1); SSA_DKDV(DD, 2, 2); SSA_DQ(DD, 1, 1); SSA_DQ(DD, 2, 2);              \
+  } else if (gs == nullptr) {                                                                \
+    SSA_DKDV(DD, 1, 0); SSA_DQ(DD, 1, 0);                                                    \
+  } else {                                                                                   \
+    SSA_DKDV(DD, 2, 0); SSA_DQ(DD, 2, 0);                                                    \
   }
+  if (d.D == 128) {
+    SSA_PASSES(128)
+  } else {
+    SSA_PASSES(64)
+  }
+#undef SSA_PASSES
+#undef SSA_DKDV
+#undef SSA_DQ
   return hipGetLastError();
 }
 

@@ -170,10 +170,11 @@ ssa_status ssa_align_loss(const ssa_problem* p, const void* h_full,
                           void* stream);
 
 /* Device workspace bytes needed by ssa_attn_bwd for problem p: per-row
- * statistics and, for SSA_BF16, transposed copies of Q, both upstream
- * gradients and K plus the selection bits. A separate query because the
- * backward's scratch is several times the forward's. Returns 0 when p is
- * invalid, unsupported or a decode problem. */
+ * statistics (16 bytes per query row) and, for SSA_BF16, the selection bits
+ * of the dK/dV walk (2 bytes per q head, 128-key tile and 32-row step) and
+ * float32 copies of dQ, dK and dV (the full-stream pass hands its partial
+ * sums to the sparse-stream pass). Returns 0 when p is invalid, unsupported
+ * or a decode problem. */
 size_t ssa_bwd_workspace_bytes(const ssa_problem* p);
 
 /* Backward pass of both attention streams ("Bidirectional Attention

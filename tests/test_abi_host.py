@@ -158,10 +158,9 @@ def test_backward_workspace_size(lib):
     p = _p()                        # B1 Hq8 Hkv2 N4096 D128 bf16
     need = bwd_workspace_bytes(p)
     stats = 8 * 4096 * 4 * 4
-    qt = 8 * 128 * 4096 * 2         # also d_full^T and d_sparse^T
-    kt = 2 * 128 * 4096 * 2
     bits = 8 * (4096 // 128) * (4096 // 32) * 2
-    assert need == stats + 3 * qt + kt + bits
+    partials = (8 + 2 * 2) * 4096 * 128 * 4     # float32 dQ, dK, dV between the two passes
+    assert need == stats + bits + partials
     c, keep = p.to_c()
     assert _bwd(lib, c, ws=4096, wn=need - 256) == 3
     assert _bwd(lib, c, ws=4096 + 8, wn=need) == 3   # not 256-byte aligned

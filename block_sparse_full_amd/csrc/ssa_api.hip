@@ -149,9 +149,10 @@ ssa_status build(const ssa_problem* p, Problem* P) {
 // Backward workspace: per-row statistics (float32 [B,Hq,Nq,4]) and, for
 // bf16, the selection bits (uint16 [B*Hkv, key tiles, Nq/32, Hq/Hkv]) and
 // the float32 partial sums that the full-stream pass hands to the
-// sparse-stream pass (dQ [B,Hq,Nq,D], dK and dV [B,Hkv,Nk,D]).
+// sparse-stream pass (dQ [B,Hq,Nq,D], dK and dV [B,Hkv,Nk,D]), plus the
+// sparse dK / dV pass's per-q-head slots ([Hq/Hkv] x [B,Hkv,Nk,D] each).
 struct BwdLayout {
-  size_t stats, bits, pq, pk, pv, total;
+  size_t stats, bits, pq, pk, pv, sk, sv, total;
 };
 
 BwdLayout bwd_layout_of(const Problem& P) {
@@ -160,7 +161,7 @@ BwdLayout bwd_layout_of(const Problem& P) {
   size_t off = 0;
   L.stats = off;
   off += align256((size_t)d.B * d.Hq * d.Nq * 4 * sizeof(float));
-  L.bits = L.pq = L.pk = L.pv = off;
+  L.bits = L.pq = L.pk = L.pv = L.sk = L.sv = off;
   if (P.bf16) {
     L.bits = off;
     off += align256((size_t)d.B * d.Hq * ssa::bwd_key_tiles(d) * (d.Nq / 32) * sizeof(uint16_t));
@@ -170,6 +171,10 @@ BwdLayout bwd_layout_of(const Problem& P) {
     off += align256((size_t)d.B * d.Hkv * d.Nk * d.D * sizeof(float));
     L.pv = off;
     off += align256((size_t)d.B * d.Hkv * d.Nk * d.D * sizeof(float));
+    L.sk = off;   // per-q-head slots of the sparse dK / dV pass
+    off += align256((size_t)d.G * d.B * d.Hkv * d.Nk * d.D * sizeof(float));
+    L.sv = off;
+    off += align256((size_t)d.G * d.B * d.Hkv * d.Nk * d.D * sizeof(float));
   }
   L.total = off;
   return L;
@@ -345,7 +350,8 @@ ssa_status ssa_attn_bwd(const ssa_problem* p, const void* q, const void* k, cons
                                               (const uint16_t*)v, (const uint16_t*)d_full,
                                               (const uint16_t*)d_sparse, idx, cnt, stats,
                                               (uint16_t*)(w + L.bits), (float*)(w + L.pq),
-                                              (float*)(w + L.pk), (float*)(w + L.pv), (uint16_t*)dq,
+                                              (float*)(w + L.pk), (float*)(w + L.pv),
+                                              (float*)(w + L.sk), (float*)(w + L.sv), (uint16_t*)dq,
                                               (uint16_t*)dk, (uint16_t*)dv, d, P.hm, st),
                     "backward (bf16)");
 }

@@ -327,16 +327,23 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
   const uint32_t aGS = lds_u32(&sGS[0][0]), aSt = lds_u32(&sStat[0][0]);
 
   const int nBG = d.B * d.Hkv;
-  const int bg = blockIdx.x % nBG, kt = blockIdx.x / nBG;   // heaviest tiles first
+  // the sparse stream (MODE 2) runs one workgroup per (tile, q head): a block
+  // that every query selects (the sink) would otherwise make one workgroup
+  // walk every step of every head alone
+  constexpr bool SPLIT = MODE == 2;
+  const int bg = blockIdx.x % nBG;
+  const int kt = (blockIdx.x / nBG) % nKT;                  // heaviest tiles first
+  const int h0 = SPLIT ? blockIdx.x / (nBG * nKT) : 0;      // the q head of a split workgroup
   const int b = bg / d.Hkv, g = bg % d.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, gq = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nS = d.Nq / kStep;
   const int G = d.G;
+  const int GW = SPLIT ? 1 : G;                             // q heads walked by this workgroup
   const int kw0 = kt * kKeysPerWg + kStep * w;   // first key of this wave
   const bool wave_keys = kw0 < d.Nk;
   const int s_first = kt * (kKeysPerWg / kStep);  // first step whose rows reach the tile
-  const int nItems = G * (nS - s_first);
+  const int nItems = GW * (nS - s_first);
   const float sl2 = d.scale_log2;
 
   bf16x8_t kreg[2][KK], vreg[2][KK];
@@ -351,7 +358,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
         vreg[nb][kk] = wave_keys ? *(const bf16x8_t*)(V + off) : bf16x8_t{};
       }
   }
-  const size_t obase = ((size_t)bg * d.Nk) * D;
+  // float32 outputs go to pK / pV, a split workgroup's to its head's slot
+  const size_t obase = (SPLIT ? (size_t)h0 * d.B * d.Hkv * d.Nk * D : 0) + ((size_t)bg * d.Nk) * D;
   auto out_off = [&](int mb, int nb) {
     return obase + (size_t)(kw0 + 16 * nb + n) * D + 16 * mb + 4 * gq;
   };
@@ -359,18 +367,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      if (IO == 2 && wave_keys) {   // continue the full-stream pass's partial sums
-        accK[mb][nb] = *(const f32x4_t*)(pK + out_off(mb, nb));
-        accV[mb][nb] = *(const f32x4_t*)(pV + out_off(mb, nb));
-      } else {
-        accK[mb][nb] = accV[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-    }
+    for (int nb = 0; nb < 2; ++nb) accK[mb][nb] = accV[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // item e -> (step, head index)
-  auto item_s = [&](int e) { return nS - 1 - e / G; };
-  auto item_h = [&](int e) { return e % G; };
+  auto item_s = [&](int e) { return nS - 1 - e / GW; };
+  auto item_h = [&](int e) { return SPLIT ? h0 : e % G; };
   const uint16_t* tile_bits = bits + (size_t)(bg * nKT + kt) * nS * G;
   auto load_chunk = [&](int c) -> uint32_t {
     const int e = 64 * c + lane;
@@ -609,7 +610,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     for (int nb = 0; nb < 2; ++nb) {
       const size_t off = out_off(mb, nb);
       const f32x4_t kv = accK[mb][nb], vv = accV[mb][nb];
-      if (IO == 1) {   // float32 partial sums (dK unscaled) for the sparse pass
+      if (IO == 1) {   // float32 partial sums (dK unscaled), summed by bwd_reduce_kernel
         *(f32x4_t*)(pK + off) = kv;
         *(f32x4_t*)(pV + off) = vv;
       } else {
@@ -617,6 +618,29 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
         store4_bf16(dV + off, vv[0], vv[1], vv[2], vv[3]);
       }
     }
+}
+
+// dK = scale (pK + sum_h sK[h]), dV = pV + sum_h sV[h] in bfloat16, four
+// elements per thread; pK / pV (the full-stream pass) may be absent. The
+// heads are added in ascending order, so the result does not depend on
+// scheduling.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ pK,
+                                                         const float* __restrict__ pV,
+                                                         const float* __restrict__ sK,
+                                                         const float* __restrict__ sV, int G,
+                                                         size_t n4, float scale,
+                                                         uint16_t* __restrict__ dK,
+                                                         uint16_t* __restrict__ dV) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  f32x4_t k = pK != nullptr ? ((const f32x4_t*)pK)[i] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t v = pV != nullptr ? ((const f32x4_t*)pV)[i] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int h = 0; h < G; ++h) {
+    k += ((const f32x4_t*)sK)[(size_t)h * n4 + i];
+    v += ((const f32x4_t*)sV)[(size_t)h * n4 + i];
+  }
+  store4_bf16(dK + 4 * i, k[0] * scale, k[1] * scale, k[2] * scale, k[3] * scale);
+  store4_bf16(dV + 4 * i, v[0], v[1], v[2], v[3]);
 }
 
 // ---------------------------------------------------------------- dQ
@@ -1019,8 +1043,9 @@ int bwd_key_tiles(const Dims& d) { return (d.Nk + kKeysPerWg - 1) / kKeysPerWg; 
 hipError_t launch_attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const uint16_t* gf, const uint16_t* gs, const int* idx,
                                 const int* cnt, const float* stats, uint16_t* bits, float* pq,
-                                float* pk, float* pv, uint16_t* dq, uint16_t* dk, uint16_t* dv,
-                                const Dims& d, const HeadMap& hm, hipStream_t stream) {
+                                float* pk, float* pv, float* sk, float* sv, uint16_t* dq,
+                                uint16_t* dk, uint16_t* dv, const Dims& d, const HeadMap& hm,
+                                hipStream_t stream) {
   const int nKT = bwd_key_tiles(d);
   if (gs != nullptr) {
     const long threads = (long)d.B * d.Hq * (d.Nq / kStep);
@@ -1030,26 +1055,35 @@ hipError_t launch_attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint
   const dim3 g1((unsigned)(nKT * d.B * d.Hkv));
   const int nQT = (d.Nq + kRowsPerWg - 1) / kRowsPerWg;
   const dim3 g2((unsigned)(nQT * d.B * d.Hq));
-#define SSA_DKDV(DD, MM, IO)                                                                 \
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DD, MM, IO>), g1, dim3(256), 0, stream, q, k, v, gf, \
-                     gs, stats, bits, dk, dv, pk, pv, d, hm, nKT)
+#define SSA_DKDV(DD, MM, IO, PK, PV, GRID)                                                   \
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DD, MM, IO>), GRID, dim3(256), 0, stream, q, k, v,   \
+                     gf, gs, stats, bits, dk, dv, PK, PV, d, hm, nKT)
 #define SSA_DQ(DD, MM, IO)                                                                   \
   hipLaunchKernelGGL((attn_bwd_dq_kernel<DD, MM, IO>), g2, dim3(256), 0, stream, q, k, v, gf, \
                      gs, stats, idx, cnt, dq, pq, d, hm)
   // Both streams: a full-stream pass leaves float32 partial sums, a
   // sparse-stream pass over the selected blocks only adds to them and rounds.
+  // The sparse dK/dV pass runs per (tile, q head) into per-head slots.
+  const dim3 g1s((unsigned)(nKT * d.B * d.Hkv * d.G));
 #define SSA_PASSES(DD)                                                                       \
   if (gf != nullptr && gs != nullptr) {                                                      \
-    SSA_DKDV(DD, 1, 1); SSA_DKDV(DD, 2, 2); SSA_DQ(DD, 1, 1); SSA_DQ(DD, 2, 2);              \
+    SSA_DKDV(DD, 1, 1, pk, pv, g1); SSA_DKDV(DD, 2, 1, sk, sv, g1s);                         \
+    SSA_DQ(DD, 1, 1); SSA_DQ(DD, 2, 2);                                                      \
   } else if (gs == nullptr) {                                                                \
-    SSA_DKDV(DD, 1, 0); SSA_DQ(DD, 1, 0);                                                    \
+    SSA_DKDV(DD, 1, 0, pk, pv, g1); SSA_DQ(DD, 1, 0);                                        \
   } else {                                                                                   \
-    SSA_DKDV(DD, 2, 0); SSA_DQ(DD, 2, 0);                                                    \
+    SSA_DKDV(DD, 2, 1, sk, sv, g1s); SSA_DQ(DD, 2, 0);                                       \
   }
   if (d.D == 128) {
     SSA_PASSES(128)
   } else {
     SSA_PASSES(64)
+  }
+  if (gs != nullptr) {
+    const size_t n4 = (size_t)d.B * d.Hkv * d.Nk * d.D / 4;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
+                       stream, gf != nullptr ? pk : nullptr, gf != nullptr ? pv : nullptr, sk, sv,
+                       d.G, n4, d.scale, dk, dv);
   }
 #undef SSA_PASSES
 #undef SSA_DKDV

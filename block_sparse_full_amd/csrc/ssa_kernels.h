@@ -55,8 +55,9 @@ hipError_t launch_attn_bwd_stats(const void* hf, const void* hs, const void* gf,
 hipError_t launch_attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const uint16_t* gf, const uint16_t* gs, const int* idx,
                                 const int* cnt, const float* stats, uint16_t* bits, float* pq,
-                                float* pk, float* pv, uint16_t* dq, uint16_t* dk, uint16_t* dv,
-                                const Dims& d, const HeadMap& hm, hipStream_t stream);
+                                float* pk, float* pv, float* sk, float* sv, uint16_t* dq,
+                                uint16_t* dk, uint16_t* dv, const Dims& d, const HeadMap& hm,
+                                hipStream_t stream);
 hipError_t launch_attn_bwd_f32(const float* q, const float* k, const float* v, const float* gf,
                                const float* gs, const int* idx, const int* cnt,
                                const float* stats, float* dq, float* dk, float* dv,

@@ -173,8 +173,9 @@ ssa_status ssa_align_loss(const ssa_problem* p, const void* h_full,
  * statistics (16 bytes per query row) and, for SSA_BF16, the selection bits
  * of the dK/dV walk (2 bytes per q head, 128-key tile and 32-row step) and
  * float32 copies of dQ, dK and dV (the full-stream pass hands its partial
- * sums to the sparse-stream pass). Returns 0 when p is invalid, unsupported
- * or a decode problem. */
+ * sums to the sparse-stream pass) and Hq/Hkv float32 copies of dK and dV
+ * (one per q head of a group for the sparse pass). Returns 0 when p is
+ * invalid, unsupported or a decode problem. */
 size_t ssa_bwd_workspace_bytes(const ssa_problem* p);
 
 /* Backward pass of both attention streams ("Bidirectional Attention

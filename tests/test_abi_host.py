@@ -160,7 +160,8 @@ def test_backward_workspace_size(lib):
     stats = 8 * 4096 * 4 * 4
     bits = 8 * (4096 // 128) * (4096 // 32) * 2
     partials = (8 + 2 * 2) * 4096 * 128 * 4     # float32 dQ, dK, dV between the two passes
-    assert need == stats + bits + partials
+    slots = 2 * 4 * 2 * 4096 * 128 * 4           # sparse dK, dV per q head of a group (4)
+    assert need == stats + bits + partials + slots
     c, keep = p.to_c()
     assert _bwd(lib, c, ws=4096, wn=need - 256) == 3
     assert _bwd(lib, c, ws=4096 + 8, wn=need) == 3   # not 256-byte aligned

@@ -33,19 +33,28 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 # HBM bytes per launch of the prefill attention kernel, from two rocprofv3
 # --pmc runs (FETCH_SIZE, WRITE_SIZE) scaled by a plain 1 GiB copy (see the
 # HBM-counter summary under profiles/), keyed by the SHA-256 of the kernel
-# source they were taken on; any other source reports traffic as null.
+# sources they were taken on (the prefill file and the headers it includes);
+# any other source reports traffic as null.
 PREFILL_TRAFFIC = {
     # 773423 KiB x 2.000 read + 528461 KiB x 1.000 written per dispatch
     "346e52aca89d980131600c1a22a6a0818c7046cb2341fd1402bcd3ab31ccc740": int(773423 * 2.0 * 1024 + 528461 * 1.0 * 1024),
 }
-PREFILL_SRC = os.path.join(ROOT, "block_sparse_full_amd", "csrc", "ssa_attn_prefill.hip")
+PREFILL_SRCS = [os.path.join(ROOT, "block_sparse_full_amd", "csrc", f)
+                for f in ("ssa_attn_prefill.hip", "ssa_device.h", "ssa_common.h")]
+
+
+def prefill_source_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for p in PREFILL_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def prefill_traffic():
-    import hashlib
     try:
-        with open(PREFILL_SRC, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = prefill_source_sha()
     except OSError:
         return None
     return PREFILL_TRAFFIC.get(sha)

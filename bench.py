@@ -36,8 +36,8 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 # sources they were taken on (the prefill file and the headers it includes);
 # any other source reports traffic as null.
 PREFILL_TRAFFIC = {
-    # 773423 KiB x 2.000 read + 528461 KiB x 1.000 written per dispatch
-    "346e52aca89d980131600c1a22a6a0818c7046cb2341fd1402bcd3ab31ccc740": int(773423 * 2.0 * 1024 + 528461 * 1.0 * 1024),
+    # 778645 KiB x 2.000 read + 531409 KiB x 1.000 written per dispatch
+    "d1dcaeba6b33669a55644c34bab33916b177abaa501c2967049c339ccff9b864": int(778645 * 2.0 * 1024 + 531409 * 1.0 * 1024),
 }
 PREFILL_SRCS = [os.path.join(ROOT, "block_sparse_full_amd", "csrc", f)
                 for f in ("ssa_attn_prefill.hip", "ssa_device.h", "ssa_common.h")]

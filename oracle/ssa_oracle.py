@@ -38,6 +38,11 @@ reason in the design notes):
   score ties go to the lower block index;
 * optionally (group-shared selection) one list per GQA group, ranked by the
   sum of the group's per-head scores, added in ascending head order;
+* optionally (per-token selection) one list per query row: the row's own
+  query vector, taken as float32, is scored against the pooled key blocks
+  (the page's identity Mean(qK^T) = q Mean(K)^T is written for a single
+  query q); candidates and forced blocks are those of the row's own block,
+  so a row of a block and its block-mode list see the same causal range;
 * token-level causal masking j <= t inside the query's own block, in both
   streams; logit scale 1/sqrt(D) unless given;
 * losses are mean squared errors over all B*Hq*Nq*D elements; their forward
@@ -150,6 +155,30 @@ def select_row(scores: np.ndarray, diag: int, budget: int, n_sink: int,
     return sorted(forced + [int(x) for x in picks])
 
 
+def token_representations(q_rows: np.ndarray) -> np.ndarray:
+    """Per-token selection: each query row represents itself, rounded once to
+    float32 (exact for bfloat16 and float32 inputs). "Practical
+    Implementation of SSA" scores the query q against the pooled keys,
+    q Mean(K)^T."""
+    return np.asarray(q_rows, dtype=np.float64).astype(np.float32)
+
+
+def token_row_diag(nq: int, nk: int, block: int, t: int) -> int:
+    """Key block holding query row t (at key position nk - nq + t): the
+    causal range and the forced blocks of a per-token list."""
+    if nq != nk and nq != 1:
+        raise ValueError("only Nq == Nk (prefill) and Nq == 1 (decode) are defined")
+    return (nk - nq + t) // block
+
+
+def list_row(r: int, block: int, nq: int, per_token: bool) -> int:
+    """Selection list that query row r reads: its own list (per-token
+    selection), else its row block's list; decode has one list."""
+    if nq == 1:
+        return 0
+    return r if per_token else r // block
+
+
 def row_block_diag(nq: int, nk: int, block: int, qb: int) -> int:
     """Key block that holds the last query of row block qb (queries are
     aligned to the end of the keys: query i sits at position nk - nq + i)."""
@@ -162,7 +191,8 @@ def row_block_diag(nq: int, nk: int, block: int, qb: int) -> int:
 
 def select_blocks(q: np.ndarray, k: np.ndarray, *, block: int, budget: int,
                   n_sink: int, n_local: int, head_map: Sequence[int],
-                  k_pooled: Optional[np.ndarray] = None, group_shared: bool = False):
+                  k_pooled: Optional[np.ndarray] = None, group_shared: bool = False,
+                  per_token: bool = False):
     """Selection for every (b, q head, row block).
 
     q [B, Hq, Nq, D], k [B, Hkv, Nk, D]. Returns idx [B, Hq, nQB, budget]
@@ -175,10 +205,31 @@ def select_blocks(q: np.ndarray, k: np.ndarray, *, block: int, budget: int,
     the pooled key against the sum of the heads' pooled queries. This is the
     GQA-group-shared reading of "the query" in "Practical Implementation of
     SSA" (the pages select per query; a GQA group reads one kv head).
+
+    per_token: one list per (b, q head, query row), idx [B, Hq, Nq, budget]:
+    row t scores its own float32 query vector against the pooled keys, with
+    the causal range and forced blocks of its block (token_row_diag). In
+    decode the single query already represents itself, so per-token and
+    per-block selection coincide.
     """
     B, Hq, nq, D = q.shape
     nk = k.shape[2]
     kbar = pool_blocks(k, block) if k_pooled is None else np.asarray(k_pooled, np.float32)
+    if per_token:
+        if group_shared:
+            raise ValueError("per-token selection is per q head")
+        qrep = token_representations(q)
+        idx = np.full((B, Hq, nq, budget), -1, dtype=np.int32)
+        cnt = np.zeros((B, Hq, nq), dtype=np.int32)
+        for b in range(B):
+            for h in range(Hq):
+                s = block_score_matrix(qrep[b, h], kbar[b, head_map[h]])
+                for t in range(nq):
+                    sel = select_row(s[t], token_row_diag(nq, nk, block, t), budget,
+                                     n_sink, n_local)
+                    idx[b, h, t, :len(sel)] = sel
+                    cnt[b, h, t] = len(sel)
+        return idx, cnt
     if nq == 1:
         qbar = np.asarray(q, dtype=np.float64).astype(np.float32)
     else:
@@ -264,10 +315,11 @@ def selected_mask(idx_row: np.ndarray, n_kb: int) -> np.ndarray:
 
 def dual_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray,
                    *, block: int, scale: float, head_map: Sequence[int],
-                   rows: Optional[Dict] = None, chunk: int = 256):
+                   rows: Optional[Dict] = None, chunk: int = 256, per_token: bool = False):
     """Both streams for every (b, q head) and row, or for a subset of rows.
 
-    q [B, Hq, Nq, D]; k, v [B, Hkv, Nk, D]; idx [B, Hq, nQB, budget].
+    q [B, Hq, Nq, D]; k, v [B, Hkv, Nk, D]; idx [B, Hq, nQB, budget], or
+    [B, Hq, Nq, budget] with per_token (row r reads list list_row(r)).
     `rows` maps (b, h) -> array of row indices; default: all rows of all
     heads. Returns dicts keyed by (b, h) of (rows, h_full, h_sparse, delta).
     """
@@ -286,8 +338,8 @@ def dual_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray,
         dl = np.zeros(len(r_all))
         for s0 in range(0, len(r_all), chunk):
             r = r_all[s0:s0 + chunk]
-            qb = r // block if nq > 1 else np.zeros_like(r)
-            sel = np.stack([selected_mask(idx[b, h, x], n_kb) for x in qb])
+            sel = np.stack([selected_mask(idx[b, h, list_row(int(x), block, nq, per_token)], n_kb)
+                            for x in r])
             pos = nk - nq + r
             a, c, d = dual_attention_rows(np.asarray(q[b, h, r], dtype=np.float64),
                                           pos, kk, vv, sel, block=block, scale=scale)
@@ -354,12 +406,13 @@ def dual_attention_rows_backward(q_rows: np.ndarray, positions: np.ndarray, k: n
 def dual_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray,
                             d_full: Optional[np.ndarray], d_sparse: Optional[np.ndarray],
                             *, block: int, scale: float, head_map: Sequence[int],
-                            chunk: int = 256):
+                            chunk: int = 256, per_token: bool = False):
     """dq [B, Hq, Nq, D], dk and dv [B, Hkv, Nk, D] (float64) of
     sum(d_full * h_full) + sum(d_sparse * h_sparse) for a whole problem, with
     the selection idx [B, Hq, nQB, budget] held fixed. d_full / d_sparse are
     [B, Hq, Nq, D] upstream gradients of the two outputs, or None for zero.
     Each kv head's dk, dv add the contributions of all q heads mapped to it.
+    per_token: idx is [B, Hq, Nq, budget], one list per query row.
     """
     B, Hq, nq, D = q.shape
     Hkv, nk = k.shape[1], k.shape[2]
@@ -374,8 +427,8 @@ def dual_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np
             vv = np.asarray(v[b, g], dtype=np.float64)
             for r0 in range(0, nq, chunk):
                 r = np.arange(r0, min(nq, r0 + chunk))
-                qb = r // block if nq > 1 else np.zeros_like(r)
-                sel = np.stack([selected_mask(idx[b, h, x], n_kb) for x in qb])
+                sel = np.stack([selected_mask(idx[b, h, list_row(int(x), block, nq, per_token)],
+                                              n_kb) for x in r])
                 gf = None if d_full is None else d_full[b, h, r]
                 gs = None if d_sparse is None else d_sparse[b, h, r]
                 a, c, e = dual_attention_rows_backward(
@@ -417,7 +470,8 @@ def align_loss(h_full: np.ndarray, h_sparse: np.ndarray):
 
 def ssa_forward(q, k, v, *, block: int, budget: int, n_sink: int, n_local: int,
                 scale: Optional[float] = None, head_map: Optional[Sequence[int]] = None,
-                k_pooled: Optional[np.ndarray] = None, group_shared: bool = False):
+                k_pooled: Optional[np.ndarray] = None, group_shared: bool = False,
+                per_token: bool = False):
     """Selection, both streams, dropped mass and losses for a whole problem.
 
     q [B, Hq, Nq, D], k and v [B, Hkv, Nk, D] (any float dtype; used at their
@@ -435,8 +489,9 @@ def ssa_forward(q, k, v, *, block: int, budget: int, n_sink: int, n_local: int,
         scale = 1.0 / math.sqrt(D)
     idx, cnt = select_blocks(q, k, block=block, budget=budget, n_sink=n_sink,
                              n_local=n_local, head_map=head_map, k_pooled=k_pooled,
-                             group_shared=group_shared)
-    res = dual_attention(q, k, v, idx, block=block, scale=scale, head_map=head_map)
+                             group_shared=group_shared, per_token=per_token)
+    res = dual_attention(q, k, v, idx, block=block, scale=scale, head_map=head_map,
+                         per_token=per_token)
     h_full = np.zeros((B, Hq, nq, D))
     h_sparse = np.zeros((B, Hq, nq, D))
     delta = np.zeros((B, Hq, nq))

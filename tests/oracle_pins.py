@@ -559,6 +559,168 @@ def check_backward_alignment_seeds(seed=16):
         assert np.allclose(got, want, atol=1e-12, rtol=1e-10), np.abs(got - want).max()
 
 
+# ---------------------------------------------------------------- per-token selection
+
+def _brute_token_selection(q, k, bs, budget, n_sink, n_local, head_map):
+    """Per-token lists from exact rational arithmetic on the raw inputs: the
+    row's own query and the block means of K as Fractions, ranked by
+    (-score, index); the forced blocks of the row's block (first n_sink
+    blocks, n_local blocks ending at the block holding the row) are added."""
+    B, Hq, nq, D = q.shape
+    nk = k.shape[2]
+    nkb = nk // bs
+    out = {}
+    for b in range(B):
+        for h in range(Hq):
+            g = head_map[h]
+            kbar = [[sum(Fraction(float(k[b, g, j * bs + t, d])) for t in range(bs)) / bs
+                     for d in range(D)] for j in range(nkb)]
+            for t in range(nq):
+                diag = (nk - nq + t) // bs
+                qv = [Fraction(float(q[b, h, t, d])) for d in range(D)]
+                score = [sum(qv[d] * kbar[j][d] for d in range(D)) for j in range(nkb)]
+                forced = set(range(min(n_sink, diag + 1)))
+                forced |= set(range(max(0, diag - n_local + 1), diag + 1))
+                cands = [j for j in range(diag + 1) if j not in forced]
+                free = budget - len(forced)
+                picks = cands if len(cands) <= free else \
+                    sorted(cands, key=lambda j: (-score[j], j))[:free]
+                out[(b, h, t)] = sorted(forced | set(picks))
+    return out
+
+
+def check_token_selection_brute(seed=17):
+    """Per-token selection against exact rational brute force (small integer
+    inputs keep every float step exact), for a permuted GQA head map and
+    several forced-block settings; rows of one block must get lists of their
+    own (the data are chosen so that some do differ). In decode the single
+    query represents itself, so per-token equals per-block selection."""
+    r = _rng(seed)
+    B, Hq, Hkv, bs, nb, D = 2, 4, 2, 2, 7, 3
+    n = bs * nb
+    q = r.integers(-4, 5, size=(B, Hq, n, D)).astype(np.float64)
+    k = r.integers(-4, 5, size=(B, Hkv, n, D)).astype(np.float64)
+    hm = [1, 0, 0, 1]
+    differs = 0
+    for budget, n_sink, n_local in ((3, 1, 1), (4, 0, 1), (5, 1, 0), (2, 0, 0)):
+        idx, cnt = O.select_blocks(q, k, block=bs, budget=budget, n_sink=n_sink,
+                                   n_local=n_local, head_map=hm, per_token=True)
+        assert idx.shape == (B, Hq, n, budget) and cnt.shape == (B, Hq, n)
+        want = _brute_token_selection(q, k, bs, budget, n_sink, n_local, hm)
+        for (b, h, t), sel in want.items():
+            assert int(cnt[b, h, t]) == len(sel), (budget, b, h, t)
+            assert idx[b, h, t, :len(sel)].tolist() == sel, (budget, b, h, t, sel)
+            assert (idx[b, h, t, len(sel):] == -1).all()
+            if t % bs and want[(b, h, t - 1)] != sel:
+                differs += 1
+    assert differs > 0
+    qd = r.standard_normal((1, 2, 1, 4)).astype(np.float32)
+    kd = r.standard_normal((1, 1, 24, 4)).astype(np.float32)
+    a = O.select_blocks(qd, kd, block=4, budget=3, n_sink=1, n_local=1, head_map=[0, 0])
+    c = O.select_blocks(qd, kd, block=4, budget=3, n_sink=1, n_local=1, head_map=[0, 0],
+                        per_token=True)
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
+
+
+def check_token_float32_query():
+    """The row's query enters the scores as float32, hand-derived: pooled keys
+    (0, 1), (1, 0), (0, 1/2) for blocks 0-2, the last row forces its own block
+    3 and has one free slot. q = (1 + 2^-10, 1) scores 1, 1 + 2^-10, 1/2 and
+    takes block 1 (a bfloat16 copy of q would tie blocks 0 and 1 and take 0);
+    q = (1 + 2^-30, 1) rounds to (1, 1) in float32, ties, and takes block 0."""
+    k = np.array([[0, 1], [0, 1], [1, 0], [1, 0], [0, 0.5], [0, 0.5], [0, 0], [0, 0]],
+                 dtype=np.float64)[None, None]
+    for eps, want in ((2.0 ** -10, [1, 3]), (2.0 ** -30, [0, 3])):
+        q = np.zeros((1, 1, 8, 2))
+        q[0, 0, 7] = [1.0 + eps, 1.0]
+        idx, cnt = O.select_blocks(q, k, block=2, budget=2, n_sink=0, n_local=1, head_map=[0],
+                                   per_token=True)
+        assert idx[0, 0, 7].tolist() == want and int(cnt[0, 0, 7]) == 2, (eps, idx[0, 0, 7])
+
+
+def check_token_constant_rows(seed=18):
+    """When every row of a query block carries the same float32 vector, the
+    block's pooled query is that vector exactly, so each row's per-token list
+    is its block's per-block list (random float data, ties unlikely)."""
+    r = _rng(seed)
+    B, Hq, Hkv, bs, nb, D = 1, 2, 1, 4, 9, 5
+    base = r.standard_normal((B, Hq, nb, D)).astype(np.float32)
+    q = np.repeat(base, bs, axis=2)
+    k = r.standard_normal((B, Hkv, nb * bs, D)).astype(np.float32)
+    for budget, n_sink, n_local in ((3, 1, 1), (4, 0, 2)):
+        ib, cb = O.select_blocks(q, k, block=bs, budget=budget, n_sink=n_sink, n_local=n_local,
+                                 head_map=[0, 0])
+        it, ct = O.select_blocks(q, k, block=bs, budget=budget, n_sink=n_sink, n_local=n_local,
+                                 head_map=[0, 0], per_token=True)
+        rows = np.arange(nb * bs)
+        assert np.array_equal(it, ib[:, :, rows // bs]), budget
+        assert np.array_equal(ct, cb[:, :, rows // bs]), budget
+
+
+def _token_masks(idx, n, bs):
+    """[B, Hq, n, n] selected-token masks of per-token lists, built directly:
+    key j is in row t's sparse set when j <= t and j's block is in idx[t]."""
+    B, Hq = idx.shape[:2]
+    m = np.zeros((B, Hq, n, n), dtype=bool)
+    for b in range(B):
+        for h in range(Hq):
+            for t in range(n):
+                blocks = {int(x) for x in idx[b, h, t] if x >= 0}
+                for j in range(t + 1):
+                    m[b, h, t, j] = (j // bs) in blocks
+    return m
+
+
+def check_token_attention_vs_sdpa(seed=19):
+    """Both streams and the dropped mass with per-token lists: h_full is
+    float64 SDPA under the causal mask, h_sparse SDPA under each row's own
+    selected-token mask, delta the full softmax weight outside that mask."""
+    r = _rng(seed)
+    B, Hq, Hkv, bs, nb, D = 1, 2, 1, 4, 6, 4
+    n = bs * nb
+    q = r.standard_normal((B, Hq, n, D)); k = r.standard_normal((B, Hkv, n, D)) * 1.5
+    v = r.standard_normal((B, Hkv, n, D))
+    hm = [0, 0]
+    idx, _ = O.select_blocks(q, k, block=bs, budget=3, n_sink=1, n_local=1, head_map=hm,
+                             per_token=True)
+    sel = _token_masks(idx, n, bs)
+    res = O.dual_attention(q, k, v, idx, block=bs, scale=0.4, head_map=hm, per_token=True)
+    causal = np.tril(np.ones((n, n), dtype=bool))
+    rows_differ = False
+    for h in range(Hq):
+        _, hf, hs, dl = res[(0, h)]
+        assert np.allclose(hf, _sdpa(q[0, h], k[0, 0], v[0, 0], causal, 0.4), atol=1e-13)
+        assert np.allclose(hs, _sdpa(q[0, h], k[0, 0], v[0, 0], sel[0, h], 0.4), atol=1e-13)
+        z = 0.4 * q[0, h] @ k[0, 0].T
+        z = np.where(causal, z, -np.inf)
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        assert np.allclose(dl, np.where(causal & ~sel[0, h], p, 0).sum(axis=1), atol=1e-14)
+        for t in range(1, n):
+            if t % bs and not np.array_equal(sel[0, h, t, :t], sel[0, h, t - 1, :t]):
+                rows_differ = True
+    assert rows_differ
+
+
+def check_token_backward_vs_torch_autograd(seed=20):
+    """Backward with per-token lists equals torch autograd through float64
+    SDPA of both streams under each row's own selected-token mask."""
+    r = _rng(seed)
+    B, Hq, Hkv, bs, nb, D = 1, 2, 1, 4, 5, 4
+    n = bs * nb
+    q = r.standard_normal((B, Hq, n, D)); k = r.standard_normal((B, Hkv, n, D)) * 1.3
+    v = r.standard_normal((B, Hkv, n, D))
+    gf = r.standard_normal((B, Hq, n, D)); gs = r.standard_normal((B, Hq, n, D))
+    hm = [0, 0]
+    idx, _ = O.select_blocks(q, k, block=bs, budget=2, n_sink=1, n_local=1, head_map=hm,
+                             per_token=True)
+    wq, wk, wv, _, _ = _torch_streams_grad(q, k, v, _token_masks(idx, n, bs), gf, gs, 0.5, hm)
+    dq, dk, dv = O.dual_attention_backward(q, k, v, idx, gf, gs, block=bs, scale=0.5,
+                                           head_map=hm, per_token=True)
+    for got, want in ((dq, wq), (dk, wk), (dv, wv)):
+        assert np.allclose(got, want, atol=1e-12, rtol=1e-11), np.abs(got - want).max()
+
+
 ALL_CHECKS = [
     check_pool_closed_form, check_pool_mean_identity, check_scores_exact_integers,
     check_select_constant_scores, check_select_duplicate_lower_index,
@@ -569,4 +731,6 @@ ALL_CHECKS = [
     check_worked_example, check_group_shared_selection,
     check_backward_finite_differences, check_backward_vs_torch_autograd,
     check_backward_invariants, check_backward_alignment_seeds,
+    check_token_selection_brute, check_token_float32_query, check_token_constant_rows, check_token_attention_vs_sdpa,
+    check_token_backward_vs_torch_autograd,
 ]

@@ -10,6 +10,7 @@ _pool, _scores, _select_row, _rows, _loss = (O.pool_blocks, O.block_score_matrix
                                              O.select_row, O.dual_attention_rows, O.align_loss)
 _group = O.group_score_matrix
 _vjp, _rows_bwd, _bwd = O.softmax_vjp, O.dual_attention_rows_backward, O.dual_attention_backward
+_tok_rep, _tok_diag = O.token_representations, O.token_row_diag
 
 
 def m_pool_sum(x, block):                      # sum instead of mean
@@ -109,6 +110,23 @@ def m_bwd_gqa_overwrite(q, k, v, idx, gf, gs, *, block, scale, head_map, chunk=2
     return dq, dk, dv
 
 
+def m_token_prev_row(q_rows):                 # row t scored with row t-1's query
+    return np.roll(_tok_rep(q_rows), 1, axis=-2)
+
+
+def m_token_rep_bf16(q_rows):                 # representation truncated to bfloat16
+    x = _tok_rep(q_rows).view(np.uint32) & np.uint32(0xFFFF0000)
+    return x.view(np.float32)
+
+
+def m_token_diag_next(nq, nk, block, t):       # causal range of the next token's block
+    return _tok_diag(nq, nk, block, min(t + 1, nq - 1))
+
+
+def m_list_row_block(r, block, nq, per_token):  # per-token rows read the block's list
+    return 0 if nq == 1 else r // block
+
+
 MUTATIONS = [
     ("pool_blocks", m_pool_sum), ("pool_blocks", m_pool_strided),
     ("block_score_matrix", m_scores_transposed),
@@ -122,6 +140,8 @@ MUTATIONS = [
     ("dual_attention_rows_backward", m_rows_bwd_dk_unscaled),
     ("dual_attention_rows_backward", m_rows_bwd_streams_swapped),
     ("dual_attention_backward", m_bwd_gqa_overwrite),
+    ("token_representations", m_token_prev_row), ("token_representations", m_token_rep_bf16),
+    ("token_row_diag", m_token_diag_next), ("list_row", m_list_row_block),
 ]
 
 

@@ -37,7 +37,7 @@ struct Problem {
 };
 
 struct Layout {
-  size_t qbar, kbar, vt, partials, loss, total;
+  size_t qbar, kbar, kc, vt, partials, loss, total;
 };
 
 Layout layout_of(const Problem& P) {
@@ -48,6 +48,8 @@ Layout layout_of(const Problem& P) {
   off += align256((size_t)d.B * d.Hq * d.nQB * d.D * sizeof(float));
   L.kbar = off;
   off += align256((size_t)d.B * d.Hkv * d.nKB * d.D * sizeof(float));
+  L.kc = off;   // per-token selection: float64 pooled keys, 16-block chunks
+  if (d.tok) off += align256(ssa::tok_kc_bytes(d));
   L.vt = off;
   if (P.bf16 && !P.decode) off += align256((size_t)d.B * d.Hkv * d.D * d.Nk * sizeof(uint16_t));
   L.partials = off;
@@ -96,16 +98,22 @@ ssa_status build(const ssa_problem* p, Problem* P) {
   if (G > ssa::kMaxGroup)
     return fail(SSA_ERR_UNSUPPORTED, "Hq/Hkv (%d) exceeds %d", G, ssa::kMaxGroup);
   const bool decode = p->Nq == 1 && p->Nk != 1;
-  if (p->selection != SSA_SELECT_PER_HEAD && p->selection != SSA_SELECT_GROUP)
-    return fail(SSA_ERR_INVALID_ARG, "selection must be SSA_SELECT_PER_HEAD (0) or SSA_SELECT_GROUP (1); "
-                "got %d", p->selection);
+  if (p->selection != SSA_SELECT_PER_HEAD && p->selection != SSA_SELECT_GROUP &&
+      p->selection != SSA_SELECT_TOKEN)
+    return fail(SSA_ERR_INVALID_ARG, "selection must be SSA_SELECT_PER_HEAD (0), SSA_SELECT_GROUP (1) "
+                "or SSA_SELECT_TOKEN (2); got %d", p->selection);
+  // in decode the single query is its own representation: per token = per head
+  const bool tok = p->selection == SSA_SELECT_TOKEN && !decode;
+  if (tok && p->budget > ssa::kTokMaxBudget)
+    return fail(SSA_ERR_UNSUPPORTED, "per-token selection supports budget <= %d; got %d",
+                ssa::kTokMaxBudget, p->budget);
   if (!(p->scale >= 0.f) || isinf(p->scale))
     return fail(SSA_ERR_INVALID_ARG, "scale must be finite and >= 0 (0 selects 1/sqrt(D))");
   const double total = (double)p->B * p->Hq * p->Nq * p->D;
   const double kv = (double)p->B * p->Hkv * p->Nk * p->D;
   if (total > 1.0e12 || kv > 1.0e12) return fail(SSA_ERR_UNSUPPORTED, "problem too large");
-  if ((double)p->B * p->Hq * (p->Nq == 1 ? 1 : p->Nq / p->block_size) > 2.0e9)
-    return fail(SSA_ERR_UNSUPPORTED, "too many query blocks");
+  if ((double)p->B * p->Hq * (p->Nq == 1 ? 1 : tok ? p->Nq : p->Nq / p->block_size) > 2.0e9)
+    return fail(SSA_ERR_UNSUPPORTED, "too many selection lists");
 
   ssa::HeadMap& hm = P->hm;
   memset(&hm, 0, sizeof(hm));
@@ -139,6 +147,9 @@ ssa_status build(const ssa_problem* p, Problem* P) {
   }
   d.G = G;
   d.group_select = p->selection == SSA_SELECT_GROUP ? 1 : 0;
+  d.tok = tok ? 1 : 0;
+  d.nL = tok ? d.Nq : d.nQB;
+  d.lrows = tok ? 1 : d.bs;
   d.scale = p->scale > 0.f ? p->scale : (float)(1.0 / sqrt((double)p->D));
   d.scale_log2 = d.scale * ssa::kLog2e;
   P->bf16 = p->dtype == SSA_BF16;
@@ -233,6 +244,17 @@ ssa_status ssa_select_blocks(const ssa_problem* p, const void* q, const void* k,
   char* w = (char*)ws;
   float* qbar = (float*)(w + L.qbar);
   hipError_t e;
+  if (d.tok) {   // each row scores its own query: pool K only
+    const float* kbar = k_pooled;
+    if (kbar == nullptr) {
+      float* kb = (float*)(w + L.kbar);
+      e = ssa::launch_pool(k, P.bf16, kb, (long)d.B * d.Hkv * d.nKB, d.bs, d.D, st);
+      if (e != hipSuccess) return hip_status(e, "pool k");
+      kbar = kb;
+    }
+    return hip_status(ssa::launch_select_tok(q, P.bf16, kbar, (double*)(w + L.kc), idx, cnt, d,
+                                             P.hm, st), "select (per token)");
+  }
   if (P.decode)  // the query is its own block representation
     e = ssa::launch_pool(q, P.bf16, qbar, (long)d.B * d.Hq, 1, d.D, st);
   else
@@ -316,6 +338,8 @@ ssa_status ssa_attn_bwd(const ssa_problem* p, const void* q, const void* k, cons
   if (s != SSA_OK) return s;
   if (P.decode)
     return fail(SSA_ERR_UNSUPPORTED, "the backward pass needs a prefill problem (Nq == Nk)");
+  if (P.d.tok && P.bf16)
+    return fail(SSA_ERR_UNSUPPORTED, "the bf16 backward pass does not take per-token selection lists");
   if (q == nullptr || k == nullptr || v == nullptr || idx == nullptr || cnt == nullptr ||
       lse == nullptr)
     return fail(SSA_ERR_INVALID_ARG, "q, k, v, idx, cnt or lse is NULL");

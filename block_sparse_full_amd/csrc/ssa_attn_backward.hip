@@ -913,9 +913,9 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(
   const int nS = d.Nq / kStep;
   const float* st = stats + ((bh * nS + row / kStep) * 4) * kStep + row % kStep;
   const float lf = st[0], df = st[kStep], ls = st[2 * kStep], dd = st[3 * kStep];
-  const int qb = row / d.bs;
-  const int* list = idx + (bh * d.nQB + qb) * d.budget;
-  const int ncnt = min(max(cnt[bh * d.nQB + qb], 0), d.budget);
+  const int lr = row / d.lrows;   // this row's selection list
+  const int* list = idx + (bh * d.nL + lr) * d.budget;
+  const int ncnt = min(max(cnt[bh * d.nL + lr], 0), d.budget);
   float q[E], gf[E], gs[E], acc[E];
   const size_t ro = (bh * d.Nq + row) * D;
 #pragma unroll
@@ -980,10 +980,10 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_f32_kernel(
     const int h = hm.q_of_kv[g * d.G + hi];
     const size_t bh = (size_t)b * d.Hq + h;
     for (int row = j; row < d.Nq; ++row) {
-      const int qb = row / d.bs;
+      const int lr = row / d.lrows;
       const bool sel = GS != nullptr &&
-                       block_selected(idx + (bh * d.nQB + qb) * d.budget,
-                                      min(max(cnt[bh * d.nQB + qb], 0), d.budget), kb);
+                       block_selected(idx + (bh * d.nL + lr) * d.budget,
+                                      min(max(cnt[bh * d.nL + lr], 0), d.budget), kb);
       if (GF == nullptr && !sel) continue;
       const size_t ro = (bh * d.Nq + row) * D;
       float qv[E], gf[E], gs[E];

@@ -395,7 +395,15 @@ __global__ __launch_bounds__(256, 4) void attn_prefill_bf16_kernel(
 // l_sel and l_drop partition the weights. Then
 //     h_full = o_all / (l_sel + l_drop),  h_sparse = o_sel / l_sel,
 //     delta = l_drop / (l_sel + l_drop).
-template <int D>
+//
+// TOK > 0 (per-token selection with blocks of TOK tokens): every query row
+// has its own list. The workgroup stages the 64 rows' lists in LDS (kept
+// ascending and causal), and each lane walks its row's list alongside the
+// tiles, so the selected quarters of a tile are a per-lane nibble (a 64-token
+// block is a whole tile: 0xF or 0). The accumulator split is unchanged; the
+// selected-stream PV runs for a tile when any row of the wave selected part
+// of it.
+template <int D, int TOK>
 __global__ __launch_bounds__(256, 3) void attn_prefill_bf16_q16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vt, const int* __restrict__ idx, const int* __restrict__ cnt,
@@ -408,9 +416,13 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_bf16_q16_kernel(
   constexpr float kTau = 8.0f;
   constexpr int kPrefetch = 4;
   constexpr int kWords16 = kMaxKeyBlocks / 32;     // 16-key blocks bitmap words
+  constexpr int kTokLd = kTokMaxBudget + 1;        // padded per-row list stride
+  static_assert(TOK == 0 || TOK == 16 || TOK == 64, "per-token block size");
   __shared__ __align__(16) uint16_t Ks[kBlock * D];
   __shared__ __align__(16) uint16_t Vs[D * kBlock];
-  __shared__ uint32_t sel16[4][kWords16];           // per wave: selected 16-key blocks
+  __shared__ uint32_t sel16[TOK ? 1 : 4][TOK ? 1 : kWords16];   // per wave: selected 16-key blocks
+  __shared__ int rl[TOK ? 64 : 1][TOK ? kTokLd : 1];            // per row: its list (TOK)
+  __shared__ int rn[TOK ? 64 : 1];
   __shared__ uint32_t tiles[kMaxKeyBlocks / 32];    // sparse-only: tiles some wave needs
 
   const int total = d.B * d.Hq * d.nQT;
@@ -448,25 +460,50 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_bf16_q16_kernel(
   };
   auto kchunk = [&](int row, int ch) { return kswz<KSPR>(row, ch); };
 
-  // ---- selection bitmaps (16-key blocks, up to this tile's diagonal)
-  const int nwords16 = ((4 * qt + 3) >> 5) + 1;
+  // ---- selection: bitmaps of 16-key blocks up to this tile's diagonal
+  // (TOK == 0), or the rows' own lists (TOK)
   const int nwords_t = (qt >> 5) + 1;
-  for (int w = tid; w < 4 * kWords16; w += 256) (&sel16[0][0])[w] = 0u;
   for (int w = tid; w < nwords_t; w += 256) tiles[w] = 0u;
-  __syncthreads();
-  for (int u = 0; u < 4; ++u) {
-    const size_t row = (size_t)bh * d.nQB + 4 * qt + u;
-    const int ns = min(max(cnt[row], 0), d.budget);
-    for (int e = tid; e < ns; e += 256) {
-      const int kb = idx[row * d.budget + e];
-      if (kb >= 0 && kb <= 4 * qt + u) {
-        atomicOr(&sel16[u][kb >> 5], 1u << (kb & 31));
-        if (sparse_only) atomicOr(&tiles[kb >> 7], 1u << ((kb >> 2) & 31));
+  if constexpr (TOK == 0) {
+    for (int w = tid; w < 4 * kWords16; w += 256) (&sel16[0][0])[w] = 0u;
+    __syncthreads();
+    for (int u = 0; u < 4; ++u) {
+      const size_t row = (size_t)bh * d.nQB + 4 * qt + u;
+      const int ns = min(max(cnt[row], 0), d.budget);
+      for (int e = tid; e < ns; e += 256) {
+        const int kb = idx[row * d.budget + e];
+        if (kb >= 0 && kb <= 4 * qt + u) {
+          atomicOr(&sel16[u][kb >> 5], 1u << (kb & 31));
+          if (sparse_only) atomicOr(&tiles[kb >> 7], 1u << ((kb >> 2) & 31));
+        }
       }
+    }
+  } else {
+    const size_t lrow0 = (size_t)bh * d.Nq + (size_t)qt * kBlock;   // this tile's 64 lists
+    for (int i = tid; i < kBlock * d.budget; i += 256) {
+      const int r = i / d.budget, e = i - r * d.budget;
+      rl[r][e] = idx[lrow0 * d.budget + i];
+    }
+    if (tid < kBlock) rn[tid] = min(max(cnt[lrow0 + tid], 0), d.budget);
+    __syncthreads();
+    if (tid < kBlock) {   // keep the ascending entries within the row's causal blocks
+      const int limit = (qt * kBlock + tid) / TOK;
+      int m = 0, last = -1;
+      for (int e = 0; e < rn[tid]; ++e) {
+        const int kb = rl[tid][e];
+        if (kb > last && kb <= limit) {
+          rl[tid][m++] = kb;
+          last = kb;
+          if (sparse_only) {
+            const int tt = TOK == 64 ? kb : kb >> 2;
+            atomicOr(&tiles[tt >> 5], 1u << (tt & 31));
+          }
+        }
+      }
+      rn[tid] = m;
     }
   }
   __syncthreads();
-  (void)nwords16;
 
   // tiles walked: every causal tile, or (sparse-only) those some wave needs
   int wcur = 0;
@@ -484,8 +521,29 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_bf16_q16_kernel(
       return -1;
     }
   };
-  auto quarters = [&](int t) __attribute__((always_inline)) -> uint32_t {   // this wave's selected quarters of tile t
-    return (__builtin_amdgcn_readfirstlane(sel16[wave][t >> 3]) >> ((4 * t) & 31)) & 0xFu;
+  // selected 16-key quarters of tile t: this wave's (TOK == 0) or this
+  // lane's row's (TOK; tiles are visited in ascending order)
+  int lptr = 0;
+  const int lcnt = TOK ? rn[TOK ? qq : 0] : 0;
+  auto quarters = [&](int t) __attribute__((always_inline)) -> uint32_t {
+    if constexpr (TOK == 0) {
+      return (__builtin_amdgcn_readfirstlane(sel16[wave][t >> 3]) >> ((4 * t) & 31)) & 0xFu;
+    } else if constexpr (TOK == 64) {
+      const int e = lptr < lcnt ? rl[qq][lptr] : -1;
+      const bool hit = e == t;
+      lptr += hit ? 1 : 0;
+      return hit ? 0xFu : 0u;
+    } else {
+      uint32_t nib = 0u;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = lptr < lcnt ? rl[qq][lptr] : -1;
+        const bool hit = e >= 0 && (e >> 2) == t;
+        nib |= hit ? 1u << (e & 3) : 0u;
+        lptr += hit ? 1 : 0;
+      }
+      return nib;
+    }
   };
 
   bf16x8_t qf[NKS];
@@ -533,9 +591,10 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_bf16_q16_kernel(
 
   auto body = [&](int t, int t_next) __attribute__((always_inline)) {
     const uint32_t qm = quarters(t);
+    const bool any_sel = TOK ? __builtin_amdgcn_ballot_w64(qm != 0u) != 0ull : qm != 0u;
     // sparse-only: a wave with no selected quarter in this tile only keeps
     // the workgroup's copy/barrier rhythm
-    const bool work = !sparse_only || qm != 0u;
+    const bool work = !sparse_only || any_sel;
     uint32_t pw[8], pws[8];
     if (work) {
     f32x4_t s[4];
@@ -615,7 +674,7 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_bf16_q16_kernel(
     __syncthreads();
     if (t_next >= 0) load_k(t_next);
     if (!sparse_only) pv(oa, pw);
-    if (qm != 0u) pv(os, pws);
+    if (any_sel) pv(os, pws);
     wait_vm();
     __syncthreads();
     if (t_next >= 0) load_v(t_next);
@@ -1084,14 +1143,27 @@ hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const 
                                     const int* idx, const int* cnt, uint16_t* hf, uint16_t* hs,
                                     float* delta, float* lse, const Dims& d, const HeadMap& hm,
                                     hipStream_t stream) {
+  if (d.tok) {   // per-token lists
+    const int tiles = d.B * d.Hq * d.nQT;
+#define SSA_TOK_LAUNCH(DD, TT)                                                                  \
+  hipLaunchKernelGGL((attn_prefill_bf16_q16_kernel<DD, TT>), dim3(tiles), dim3(256), 0, stream, \
+                     q, k, vt, idx, cnt, hf, hs, delta, lse, d, hm)
+    if (d.D == 128) {
+      if (d.bs == 16) SSA_TOK_LAUNCH(128, 16); else SSA_TOK_LAUNCH(128, 64);
+    } else {
+      if (d.bs == 16) SSA_TOK_LAUNCH(64, 16); else SSA_TOK_LAUNCH(64, 64);
+    }
+#undef SSA_TOK_LAUNCH
+    return hipGetLastError();
+  }
   if (d.bs == 16) {
     const int tiles = d.B * d.Hq * d.nQT;
     if (d.D == 128)
-      hipLaunchKernelGGL(attn_prefill_bf16_q16_kernel<128>, dim3(tiles), dim3(256), 0, stream, q,
-                         k, vt, idx, cnt, hf, hs, delta, lse, d, hm);
+      hipLaunchKernelGGL((attn_prefill_bf16_q16_kernel<128, 0>), dim3(tiles), dim3(256), 0, stream,
+                         q, k, vt, idx, cnt, hf, hs, delta, lse, d, hm);
     else
-      hipLaunchKernelGGL(attn_prefill_bf16_q16_kernel<64>, dim3(tiles), dim3(256), 0, stream, q,
-                         k, vt, idx, cnt, hf, hs, delta, lse, d, hm);
+      hipLaunchKernelGGL((attn_prefill_bf16_q16_kernel<64, 0>), dim3(tiles), dim3(256), 0, stream,
+                         q, k, vt, idx, cnt, hf, hs, delta, lse, d, hm);
     return hipGetLastError();
   }
   // dual mode with four q heads per workgroup; sparse-only calls go to the
@@ -1115,7 +1187,11 @@ hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const 
 // ---------------------------------------------------------------- float32
 // Plain VALU kernel for float32 problems (prefill and decode): one wave per
 // (b, q head, row block); lane r owns query row r of the block. Same walk:
-// selected blocks, snapshot, remaining causal blocks.
+// selected blocks, snapshot, remaining causal blocks. With per-token lists
+// the rows of a block select different blocks, so the sparse stream runs as
+// its own pass over the blocks some row selected (each lane masks the blocks
+// its row did not select), and the full stream as a second pass over every
+// causal block.
 template <int D>
 __global__ __launch_bounds__(64) void attn_rows_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
@@ -1145,7 +1221,7 @@ __global__ __launch_bounds__(64) void attn_rows_f32_kernel(
   const float* kbase = K + ((size_t)(b * d.Hkv + g) * d.Nk) * D;
   const float* vbase = V + ((size_t)(b * d.Hkv + g) * d.Nk) * D;
 
-  auto process = [&](int kb, bool selected) {
+  auto process = [&](int kb, bool selected, bool use) {
     const float* kg = kbase + (size_t)kb * kBlock * D;
     const float* vg = vbase + (size_t)kb * kBlock * D;
     for (int i = lane; i < kBlock * D / 4; i += 64) {
@@ -1161,7 +1237,7 @@ __global__ __launch_bounds__(64) void attn_rows_f32_kernel(
         float a = 0.f;
 #pragma unroll
         for (int i = 0; i < D; ++i) a = fmaf(q[i], Ks[j0 + j][i], a);
-        if (kb * kBlock + j0 + j > pos) a = -INFINITY;
+        if (kb * kBlock + j0 + j > pos || !use) a = -INFINITY;
         s[j] = a;
         mx = fmaxf(mx, a);
       }
@@ -1186,13 +1262,49 @@ __global__ __launch_bounds__(64) void attn_rows_f32_kernel(
     __syncthreads();
   };
 
+  const size_t plane = (size_t)d.B * d.Hq * d.Nq;
+  if (d.tok) {
+    const size_t lrow = (size_t)bh * d.Nq + row;
+    const int* mine = idx + lrow * d.budget;
+    const int nm = min(max(cnt[lrow], 0), d.budget);
+    auto has = [&](int kb) {
+      bool f = false;
+      for (int i = 0; i < nm; ++i) f |= mine[i] == kb;
+      return f;
+    };
+    for (int kb = 0; kb <= diag; ++kb) {   // sparse stream
+      const bool sel = has(kb);
+      if (__builtin_amdgcn_ballot_w64(sel) == 0ull) continue;
+      process(kb, true, sel);
+    }
+    if (active) {
+      float* hp = Hs + ((size_t)bh * d.Nq + row) * D;
+      const float inv = 1.f / l_sel;
+      for (int i = 0; i < D; ++i) hp[i] = acc[i] * inv;
+      if (lse != nullptr) lse[plane + (size_t)bh * d.Nq + row] = (m_run + log2f(l_sel)) * kLn2;
+    }
+    if (Hf == nullptr) return;
+    m_run = -INFINITY;
+    l_sel = l_drop = 0.f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) acc[i] = 0.f;
+    for (int kb = 0; kb <= diag; ++kb) process(kb, has(kb), true);   // full stream
+    if (active) {
+      const float lt = l_sel + l_drop;
+      float* hp = Hf + ((size_t)bh * d.Nq + row) * D;
+      const float inv = 1.f / lt;
+      for (int i = 0; i < D; ++i) hp[i] = acc[i] * inv;
+      if (delta != nullptr) delta[(size_t)bh * d.Nq + row] = l_drop / lt;
+      if (lse != nullptr) lse[(size_t)bh * d.Nq + row] = (m_run + log2f(lt)) * kLn2;
+    }
+    return;
+  }
   const int* my_idx = idx + ((size_t)bh * d.nQB + qb) * d.budget;
   const int n_sel = min(max(cnt[(size_t)bh * d.nQB + qb], 0), d.budget);
   for (int it = 0; it < n_sel; ++it) {
     const int kb = my_idx[it];
-    if (kb >= 0 && kb <= diag) process(kb, true);
+    if (kb >= 0 && kb <= diag) process(kb, true, true);
   }
-  const size_t plane = (size_t)d.B * d.Hq * d.Nq;
   if (active) {
     float* hp = Hs + ((size_t)bh * d.Nq + row) * D;
     const float inv = 1.f / l_sel;
@@ -1204,7 +1316,7 @@ __global__ __launch_bounds__(64) void attn_rows_f32_kernel(
   for (int kb = 0; kb <= diag; ++kb) {
     while (j < n_sel && my_idx[j] < kb) ++j;
     if (j < n_sel && my_idx[j] == kb) continue;
-    process(kb, false);
+    process(kb, false, true);
   }
   if (active) {
     const float lt = l_sel + l_drop;

@@ -14,6 +14,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kBlock = 64;      // tokens per key tile / query tile of the attention kernels
 constexpr int kMaxHq = 256;
 constexpr int kMaxGroup = 16;   // q heads per kv head
+constexpr int kTokMaxBudget = 64;  // list length limit of per-token selection
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -25,6 +26,9 @@ struct Dims {
   int bs;              // selection block size in tokens (16 or 64)
   int nQT, nT;         // 64-row query tiles (1 in decode) and 64-key tiles
   int group_select;    // 1: one selection per GQA group (summed head scores)
+  int tok;             // 1: one selection list per query row (prefill)
+  int nL;              // selection lists per (b, q head): nQB, or Nq per token
+  int lrows;           // query rows per selection list: bs, or 1 per token
   float scale;         // logit scale
   float scale_log2;    // scale * log2(e)
 };

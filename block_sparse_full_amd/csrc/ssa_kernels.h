@@ -29,6 +29,15 @@ hipError_t launch_pool(const void* x, bool bf16, float* out, long nblk_total, in
                        hipStream_t stream);
 hipError_t launch_select(const float* qbar, const float* kbar, int* idx, int* cnt,
                          const Dims& d, const HeadMap& hm, hipStream_t stream);
+// Per-token selection: float64 copy of the pooled keys in chunks of
+// kTokChunk blocks ([B*Hkv][chunk][D][kTokChunk]), read as scalar operands.
+constexpr int kTokChunk = 16;
+inline size_t tok_kc_bytes(const Dims& d) {
+  const size_t chunks = (size_t)(d.nKB + kTokChunk - 1) / kTokChunk;
+  return (size_t)d.B * d.Hkv * chunks * kTokChunk * d.D * sizeof(double);
+}
+hipError_t launch_select_tok(const void* q, bool bf16, const float* kbar, double* kc, int* idx,
+                             int* cnt, const Dims& d, const HeadMap& hm, hipStream_t stream);
 hipError_t launch_transpose(const uint16_t* v, uint16_t* vt, int BH, int N, int D,
                             hipStream_t stream);
 

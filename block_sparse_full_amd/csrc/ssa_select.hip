@@ -293,6 +293,193 @@ hipError_t launch_select(const float* qbar, const float* kbar, int* idx, int* cn
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- per-token selection
+// Every query row scores its own query vector (as float32) against the
+// pooled key blocks and keeps the top `free` candidates of the causal range
+// of the block holding it; contract as above (float64 dot products in
+// ascending d, ties to the lower block index).
+//
+// Lane = one query row (64 consecutive rows per wave, four independent waves
+// per workgroup). The wave walks the key blocks in chunks of kTokChunk: the
+// pooled keys of a chunk are wave-uniform, so they come as float64 scalar
+// operands (from the chunked float64 copy kc), while the query stays in the
+// lane's registers; one v_fma_f64 per (row, block, d). Each lane keeps its
+// best candidates in a register list sorted by (key descending, block
+// ascending) of KCAP entries; a new candidate is inserted below every entry
+// with an equal or larger key, so among equal keys the earlier (lower) block
+// stays ahead. At the end the lane sorts its `free` picks by block index and
+// writes sink blocks, picks and local blocks in ascending order.
+
+// kc[bg][c][d][i] = (double)kbar[bg][kTokChunk*c + i][d], 0 past the last block.
+__global__ __launch_bounds__(256) void kbar_f64_kernel(const float* __restrict__ kbar,
+                                                       double* __restrict__ kc, int nKB, int nC,
+                                                       int D, long total) {
+  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= total) return;
+  const int i = (int)(t % kTokChunk);
+  long r = t / kTokChunk;
+  const int dd = (int)(r % D);
+  r /= D;
+  const int c = (int)(r % nC);
+  const long bg = r / nC;
+  const int kb = c * kTokChunk + i;
+  kc[t] = kb < nKB ? (double)kbar[(bg * nKB + kb) * D + dd] : 0.0;
+}
+
+// Eight consecutive query values of a lane's row as float32.
+__device__ __forceinline__ void load_q8(const uint16_t* p, float out[8]) { load8(p, out); }
+__device__ __forceinline__ void load_q8(const float* p, float out[8]) { load8(p, out); }
+
+template <int D, int KCAP, typename T>
+__global__ __launch_bounds__(256) void select_tok_kernel(const T* __restrict__ q,
+                                                         const double* __restrict__ kc,
+                                                         int* __restrict__ idx,
+                                                         int* __restrict__ cnt, Dims d,
+                                                         HeadMap hm) {
+  __shared__ uint64_t keys[4][kTokChunk][64];   // one chunk of keys per wave
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.y, b = blockIdx.z;
+  // heavier (later) rows first
+  const int row0 = ((gridDim.x - 1 - blockIdx.x) * 4 + wave) * 64;
+  if (row0 >= d.Nq) return;   // wave-uniform; Nq is a multiple of 64, no barrier below
+  const int t = row0 + lane;
+  const int g = hm.kv_of_q[h];
+  const size_t bh = (size_t)b * d.Hq + h;
+  const int nC = (d.nKB + kTokChunk - 1) / kTokChunk;
+  const double* kg = kc + (size_t)(b * d.Hkv + g) * nC * D * kTokChunk;
+  const T* qrow = q + (bh * d.Nq + t) * D;
+
+  const int diag = (d.Nk - d.Nq + t) / d.bs;
+  const int ncausal = diag + 1;
+  const int a_end = min(d.n_sink, ncausal);
+  const int l_begin = max(0, ncausal - d.n_local);
+  const int n_forced = a_end + (ncausal - l_begin) - max(0, a_end - l_begin);
+  const int free_slots = d.budget - n_forced;   // >= 0: budget >= n_sink + n_local
+  // candidates: a_end <= kb < l_begin; the last row has the widest range
+  const int wave_end = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(l_begin, 63));
+
+  uint64_t lk[KCAP];
+  int lb[KCAP];
+#pragma unroll
+  for (int j = 0; j < KCAP; ++j) { lk[j] = 0ull; lb[j] = 0; }
+  uint64_t* wk = &keys[wave][0][0];
+
+  for (int c0 = 0; c0 < wave_end; c0 += kTokChunk) {
+    double acc[kTokChunk];
+#pragma unroll
+    for (int i = 0; i < kTokChunk; ++i) acc[i] = 0.0;
+    const double* kp = kg + (size_t)(c0 / kTokChunk) * D * kTokChunk;
+#pragma unroll 2
+    for (int d8 = 0; d8 < D; d8 += 8) {
+      float qv[8];
+      load_q8(qrow + d8, qv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double qd = (double)qv[e];
+#pragma unroll
+        for (int i = 0; i < kTokChunk; ++i)
+          acc[i] = __fma_rn(qd, kp[(d8 + e) * kTokChunk + i], acc[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kTokChunk; ++i) {
+      const int kb = c0 + i;
+      wk[i * 64 + lane] = (kb >= a_end && kb < l_begin) ? orderable_key(acc[i]) : 0ull;
+    }
+    wave_lds_fence();
+#pragma unroll 1
+    for (int i = 0; i < kTokChunk; ++i) {
+      const uint64_t key = wk[i * 64 + lane];
+      if (__builtin_amdgcn_ballot_w64(key > lk[KCAP - 1]) == 0ull) continue;
+      const int kb = c0 + i;
+      // insert below every entry with key >= this one (bottom-up, in place)
+#pragma unroll
+      for (int j = KCAP - 1; j >= 0; --j) {
+        const int jp = j > 0 ? j - 1 : 0;
+        const bool here = key > lk[j];
+        const bool above = j > 0 && key > lk[jp];
+        const uint64_t nk = above ? lk[jp] : key;
+        const int nb = above ? lb[jp] : kb;
+        lk[j] = here ? nk : lk[j];
+        lb[j] = here ? nb : lb[j];
+      }
+    }
+    wave_lds_fence();
+  }
+
+  // picks: the first free_slots entries that hold a candidate, by block index
+  int pk[KCAP];
+  int np = 0;
+#pragma unroll
+  for (int j = 0; j < KCAP; ++j) {
+    const bool use = j < free_slots && lk[j] != 0ull;
+    pk[j] = use ? lb[j] : 0x7FFFFFFF;
+    np += use ? 1 : 0;
+  }
+#pragma unroll 1
+  for (int round = 0; round < KCAP; round += 2) {   // odd-even transposition sort
+#pragma unroll
+    for (int j = 0; j + 1 < KCAP; j += 2) {
+      const int lo = min(pk[j], pk[j + 1]), hi = max(pk[j], pk[j + 1]);
+      pk[j] = lo;
+      pk[j + 1] = hi;
+    }
+#pragma unroll
+    for (int j = 1; j + 1 < KCAP; j += 2) {
+      const int lo = min(pk[j], pk[j + 1]), hi = max(pk[j], pk[j + 1]);
+      pk[j] = lo;
+      pk[j + 1] = hi;
+    }
+  }
+
+  int* out = idx + (bh * d.Nq + t) * d.budget;
+  int pos = 0;
+  for (int kb = 0; kb < a_end; ++kb) out[pos++] = kb;
+#pragma unroll
+  for (int j = 0; j < KCAP; ++j)
+    if (j < np) out[pos + j] = pk[j];
+  pos += np;
+  for (int kb = max(l_begin, a_end); kb <= diag; ++kb) out[pos++] = kb;
+  const int n_out = pos;
+  for (; pos < d.budget; ++pos) out[pos] = -1;
+  cnt[bh * d.Nq + t] = n_out;
+}
+
+template <int D, typename T>
+static void launch_tok(const void* q, const double* kc, int* idx, int* cnt, const Dims& d,
+                       const HeadMap& hm, hipStream_t stream) {
+  const dim3 grid((d.Nq + 255) / 256, d.Hq, d.B);
+  const T* qt = (const T*)q;
+  if (d.budget <= 16)
+    hipLaunchKernelGGL((select_tok_kernel<D, 16, T>), grid, dim3(256), 0, stream, qt, kc, idx,
+                       cnt, d, hm);
+  else if (d.budget <= 32)
+    hipLaunchKernelGGL((select_tok_kernel<D, 32, T>), grid, dim3(256), 0, stream, qt, kc, idx,
+                       cnt, d, hm);
+  else
+    hipLaunchKernelGGL((select_tok_kernel<D, 64, T>), grid, dim3(256), 0, stream, qt, kc, idx,
+                       cnt, d, hm);
+}
+
+hipError_t launch_select_tok(const void* q, bool bf16, const float* kbar, double* kc, int* idx,
+                             int* cnt, const Dims& d, const HeadMap& hm, hipStream_t stream) {
+  const int nC = (d.nKB + kTokChunk - 1) / kTokChunk;
+  const long total = (long)d.B * d.Hkv * nC * d.D * kTokChunk;
+  hipLaunchKernelGGL(kbar_f64_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                     kbar, kc, d.nKB, nC, d.D, total);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (d.D == 128) {
+    if (bf16) launch_tok<128, uint16_t>(q, kc, idx, cnt, d, hm, stream);
+    else launch_tok<128, float>(q, kc, idx, cnt, d, hm, stream);
+  } else {
+    if (bf16) launch_tok<64, uint16_t>(q, kc, idx, cnt, d, hm, stream);
+    else launch_tok<64, float>(q, kc, idx, cnt, d, hm, stream);
+  }
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- V transpose
 // vt[bh][d][n] = v[bh][n][d] for bf16, 64x64 tiles through LDS.
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ v,

@@ -24,7 +24,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssa.so"
 _lib = None
 
 SSA_F32, SSA_BF16 = 0, 1
-SSA_SELECT_PER_HEAD, SSA_SELECT_GROUP = 0, 1
+SSA_SELECT_PER_HEAD, SSA_SELECT_GROUP, SSA_SELECT_TOKEN = 0, 1, 2
 STATUS = {0: "SSA_OK", 1: "SSA_ERR_INVALID_ARG", 2: "SSA_ERR_UNSUPPORTED",
           3: "SSA_ERR_WORKSPACE", 4: "SSA_ERR_HIP"}
 EXPORTS = ("ssa_workspace_bytes", "ssa_pool_blocks", "ssa_select_blocks", "ssa_attn_fwd",
@@ -118,7 +118,11 @@ class Problem:
 
     @property
     def n_qblocks(self) -> int:
-        return 1 if self.Nq == 1 else self.Nq // self.block_size
+        """Selection lists per (b, q head): one per query block, one per
+        query row with SSA_SELECT_TOKEN, one in decode."""
+        if self.Nq == 1:
+            return 1
+        return self.Nq if self.selection == SSA_SELECT_TOKEN else self.Nq // self.block_size
 
     @property
     def torch_dtype(self):
@@ -127,7 +131,8 @@ class Problem:
 
 def problem_for(q: torch.Tensor, k: torch.Tensor, *, budget: int, n_sink: int = 1,
                 n_local: int = 1, block_size: int = 64, scale: float = 0.0,
-                head_map: Optional[Sequence[int]] = None, group_select: bool = False) -> Problem:
+                head_map: Optional[Sequence[int]] = None, group_select: bool = False,
+                token_select: bool = False) -> Problem:
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be 4-D [B, H, N, D]")
     dt = {torch.bfloat16: SSA_BF16, torch.float32: SSA_F32}.get(q.dtype)
@@ -136,7 +141,8 @@ def problem_for(q: torch.Tensor, k: torch.Tensor, *, budget: int, n_sink: int = 
     return Problem(B=q.shape[0], Hq=q.shape[1], Hkv=k.shape[1], Nq=q.shape[2], Nk=k.shape[2],
                    D=q.shape[3], budget=budget, n_sink=n_sink, n_local=n_local,
                    block_size=block_size, scale=scale, dtype=dt, head_map=head_map,
-                   selection=SSA_SELECT_GROUP if group_select else SSA_SELECT_PER_HEAD)
+                   selection=(SSA_SELECT_TOKEN if token_select else
+                              SSA_SELECT_GROUP if group_select else SSA_SELECT_PER_HEAD))
 
 
 def _check(status: int):
@@ -319,12 +325,15 @@ def attn_bwd(p: Problem, q, k, v, idx, cnt, lse, *, h_full=None, h_sparse=None, 
 def dual_attention(q, k, v, *, budget: int, n_sink: int = 1, n_local: int = 1,
                    scale: float = 0.0, head_map=None, k_pooled=None, sparse_only: bool = False,
                    want_lse: bool = False, want_grads: bool = False, ws=None,
-                   group_select: bool = False, block_size: int = 64):
+                   group_select: bool = False, block_size: int = 64,
+                   token_select: bool = False):
     """Selection, both attention streams, dropped mass and alignment losses.
     group_select: one block list per GQA group (SSA_SELECT_GROUP);
+    token_select: one block list per query row (SSA_SELECT_TOKEN);
     block_size: selection block in tokens (64 or 16)."""
     p = problem_for(q, k, budget=budget, n_sink=n_sink, n_local=n_local, scale=scale,
-                    head_map=head_map, group_select=group_select, block_size=block_size)
+                    head_map=head_map, group_select=group_select, block_size=block_size,
+                    token_select=token_select)
     ws = ws if ws is not None else alloc_workspace(p, q.device)
     idx, cnt = select_blocks(p, q, None if k_pooled is not None else k, k_pooled, ws=ws)
     out = attn_fwd(p, q, k, v, idx, cnt, sparse_only=sparse_only, want_lse=want_lse, ws=ws)

@@ -69,8 +69,19 @@ typedef enum { SSA_F32 = 0, SSA_BF16 = 1 } ssa_dtype;
  *                         score is the sum of its q heads' scores (float64,
  *                         q heads in ascending index order). The pages select
  *                         per query ("Practical Implementation of SSA"); the
- *                         group reading lets a GQA group share one list. */
-typedef enum { SSA_SELECT_PER_HEAD = 0, SSA_SELECT_GROUP = 1 } ssa_selection;
+ *                         group reading lets a GQA group share one list.
+ *   SSA_SELECT_TOKEN    : one list per (b, q head, query row): each row
+ *                         scores its own query vector (as float32) against
+ *                         the pooled key blocks, the page's q Mean(K)^T for
+ *                         a single query; candidates and forced blocks are
+ *                         those of the block holding the row. idx is then
+ *                         [B,Hq,Nq,budget] and cnt [B,Hq,Nq]; budget <= 64.
+ *                         In decode (Nq == 1) it is SSA_SELECT_PER_HEAD. */
+typedef enum {
+  SSA_SELECT_PER_HEAD = 0,
+  SSA_SELECT_GROUP = 1,
+  SSA_SELECT_TOKEN = 2
+} ssa_selection;
 
 /* One attention problem (one layer's attention of one batch).
  *   B, Hq, Hkv : batch, query heads, key/value heads (Hq % Hkv == 0)
@@ -117,10 +128,13 @@ ssa_status ssa_pool_blocks(const ssa_problem* p, const void* x, int32_t H,
  *              or NULL to pool k here
  *   idx      : out [B,Hq,nQB,budget] int32, nQB = Nq/block_size (prefill) or
  *              1 (decode); the selected key blocks of each (b, h, query
- *              block) in ascending order, padded with -1
- *   cnt      : out [B,Hq,nQB] int32, the number of valid idx entries
- * The query block's representation is its mean-pooled Q (decode: the query
- * itself). Scores are float64 dot products of the float32 pooled vectors,
+ *              block) in ascending order, padded with -1. With
+ *              SSA_SELECT_TOKEN (prefill) one list per query row:
+ *              [B,Hq,Nq,budget]
+ *   cnt      : out [B,Hq,nQB] int32 ([B,Hq,Nq] per token), the number of
+ *              valid idx entries
+ * The query block's representation is its mean-pooled Q (decode, and every
+ * row with SSA_SELECT_TOKEN: the query itself, as float32). Scores are float64 dot products of the float32 pooled vectors,
  * summed over d in ascending order, unscaled. With p->selection ==
  * SSA_SELECT_GROUP every q head of a GQA group receives the group's list,
  * ranked by the float64 sum of the heads' scores (ascending q head order). Forced blocks (the first
@@ -137,6 +151,8 @@ ssa_status ssa_select_blocks(const ssa_problem* p, const void* q, const void* k,
  * sparse stream over the tokens of the selected blocks; "2. Methodologie":
  * the counterpart output and the dropped mass).
  *   q, k, v  : device inputs as above; idx, cnt from ssa_select_blocks
+ *              (laid out for p->selection; with SSA_SELECT_TOKEN each row's
+ *              list must be ascending, as ssa_select_blocks writes it)
  *   h_full   : out [B,Hq,Nq,D] p->dtype: softmax(scale q k^T) v over keys
  *              j <= position of the query; NULL selects sparse-only mode
  *              (only the selected blocks are read)
@@ -205,7 +221,9 @@ size_t ssa_bwd_workspace_bytes(const ssa_problem* p);
  *   dk, dv       : out [B,Hkv,Nk,D] p->dtype, each kv head summed over its
  *                  q heads (deterministic: no atomics)
  *   ws, ws_bytes : at least ssa_bwd_workspace_bytes(p) bytes
- * Prefill problems only (Nq == Nk; decode gives SSA_ERR_UNSUPPORTED).
+ * Prefill problems only (Nq == Nk; decode gives SSA_ERR_UNSUPPORTED);
+ * SSA_SELECT_TOKEN lists are supported for SSA_F32 only (SSA_BF16 gives
+ * SSA_ERR_UNSUPPORTED).
  * float32 accumulation; P and dS enter the bf16 products rounded to bf16;
  * outputs are rounded once. */
 ssa_status ssa_attn_bwd(const ssa_problem* p, const void* q, const void* k,

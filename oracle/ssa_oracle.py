@@ -192,7 +192,7 @@ def row_block_diag(nq: int, nk: int, block: int, qb: int) -> int:
 def select_blocks(q: np.ndarray, k: np.ndarray, *, block: int, budget: int,
                   n_sink: int, n_local: int, head_map: Sequence[int],
                   k_pooled: Optional[np.ndarray] = None, group_shared: bool = False,
-                  per_token: bool = False):
+                  per_token: bool = False, rows: Optional[Dict] = None):
     """Selection for every (b, q head, row block).
 
     q [B, Hq, Nq, D], k [B, Hkv, Nk, D]. Returns idx [B, Hq, nQB, budget]
@@ -210,7 +210,8 @@ def select_blocks(q: np.ndarray, k: np.ndarray, *, block: int, budget: int,
     row t scores its own float32 query vector against the pooled keys, with
     the causal range and forced blocks of its block (token_row_diag). In
     decode the single query already represents itself, so per-token and
-    per-block selection coincide.
+    per-block selection coincide. `rows` (per_token only) maps (b, h) to the
+    query rows to select for; the other lists are left at -1 / 0.
     """
     B, Hq, nq, D = q.shape
     nk = k.shape[2]
@@ -221,14 +222,14 @@ def select_blocks(q: np.ndarray, k: np.ndarray, *, block: int, budget: int,
         qrep = token_representations(q)
         idx = np.full((B, Hq, nq, budget), -1, dtype=np.int32)
         cnt = np.zeros((B, Hq, nq), dtype=np.int32)
-        for b in range(B):
-            for h in range(Hq):
-                s = block_score_matrix(qrep[b, h], kbar[b, head_map[h]])
-                for t in range(nq):
-                    sel = select_row(s[t], token_row_diag(nq, nk, block, t), budget,
-                                     n_sink, n_local)
-                    idx[b, h, t, :len(sel)] = sel
-                    cnt[b, h, t] = len(sel)
+        keys = rows.keys() if rows is not None else [(b, h) for b in range(B) for h in range(Hq)]
+        for (b, h) in keys:
+            ts = np.arange(nq) if rows is None else np.asarray(rows[(b, h)], dtype=np.int64)
+            s = block_score_matrix(qrep[b, h, ts], kbar[b, head_map[h]])
+            for i, t in enumerate(ts.tolist()):
+                sel = select_row(s[i], token_row_diag(nq, nk, block, t), budget, n_sink, n_local)
+                idx[b, h, t, :len(sel)] = sel
+                cnt[b, h, t] = len(sel)
         return idx, cnt
     if nq == 1:
         qbar = np.asarray(q, dtype=np.float64).astype(np.float32)

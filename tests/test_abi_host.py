@@ -61,7 +61,11 @@ def _status_of(lib, prob, fn="ssa_select_blocks"):
     (dict(D=96), 2), (dict(block_size=32), 2), (dict(Nk=4000, Nq=4000), 2),
     (dict(Nq=7), 2), (dict(dtype=5), 2), (dict(Hq=64, Hkv=2), 2), (dict(scale=-1.0), 1),
     (dict(Nq=1, Nk=4096, Hq=32, Hkv=2), 3),        # bf16 decode, 16 q heads per kv head: valid
-    (dict(selection=2), 1), (dict(selection=-1), 1),
+    (dict(selection=3), 1), (dict(selection=-1), 1),
+    (dict(selection=2), 3),                         # per-token selection: valid, no workspace
+    (dict(selection=2, budget=64), 3),              # longest per-token list
+    (dict(selection=2, budget=65), 2),              # per-token lists hold at most 64 blocks
+    (dict(selection=2, budget=65, Nq=1), 3),        # decode: per token is per head, no limit
     (dict(block_size=16), 3),                       # 16-token blocks: valid (bf16), no workspace
     (dict(block_size=16, dtype=0), 2),              # 16-token blocks need bf16
     (dict(block_size=16, Nk=200, Nq=200), 2),       # Nk must still be a multiple of 64
@@ -151,6 +155,23 @@ def test_backward_argument_checks(lib):
     assert lib.ssa_bwd_workspace_bytes(ctypes.byref(dec)) == 0
     bad, keep3 = _p(D=96).to_c()
     assert _bwd(lib, bad) == 2
+
+
+def test_token_selection_host(lib):
+    """Per-token lists: bf16 backward refused, float32 backward accepted;
+    the workspace adds the float64 chunked copy of the pooled keys."""
+    from block_sparse_full_amd.ssa import SSA_SELECT_TOKEN, workspace_bytes
+    c, keep = _p(selection=SSA_SELECT_TOKEN).to_c()
+    assert _bwd(lib, c) == 2
+    assert "per-token" in lib.ssa_last_error_message().decode()
+    c32, keep2 = _p(selection=SSA_SELECT_TOKEN, dtype=0, D=64).to_c()
+    assert _bwd(lib, c32) == 3                     # valid, no workspace
+    base = workspace_bytes(_p())
+    tok = workspace_bytes(_p(selection=SSA_SELECT_TOKEN))
+    assert tok - base == 2 * 64 * 128 * 8          # Hkv 2, 64 blocks (4 chunks of 16), D 128
+    p = _p(selection=SSA_SELECT_TOKEN)
+    assert p.n_qblocks == 4096
+    assert _p(selection=SSA_SELECT_TOKEN, Nq=1).n_qblocks == 1
 
 
 def test_backward_workspace_size(lib):

@@ -43,11 +43,12 @@ def say(*a):
 
 
 def gpu_bwd(ssa, cfg, x, grads, *, budget, use_full=True, use_sparse=True, head_map=None,
-            group_select=False):
+            group_select=False, token_select=False):
     dev = torch.device("cuda:0")
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
     p = ssa.problem_for(q, k, budget=budget, n_sink=cfg.n_sink, n_local=cfg.n_local,
-                        head_map=head_map, group_select=group_select, block_size=cfg.block)
+                        head_map=head_map, group_select=group_select, block_size=cfg.block,
+                        token_select=token_select)
     ws = ssa.alloc_workspace(p, dev)
     idx, cnt = ssa.select_blocks(p, q, k, ws=ws)
     fwd = ssa.attn_fwd(p, q, k, v, idx, cnt, want_lse=True, ws=ws)
@@ -75,25 +76,27 @@ def check_grad(name, got, want, dtype):
 
 
 def full_compare(ssa, cfg, *, budget=None, use_full=True, use_sparse=True, head_map=None,
-                 group_select=False):
+                 group_select=False, token_select=False):
     budget = budget or cfg.budget
     say(f"[bwd] {cfg.name} B{cfg.B} Hq{cfg.Hq} Hkv{cfg.Hkv} N{cfg.N} D{cfg.D} bs{cfg.block} "
-        f"budget {budget} full={use_full} sparse={use_sparse} group={group_select}")
+        f"budget {budget} full={use_full} sparse={use_sparse} group={group_select} "
+        f"token={token_select}")
     x = make_inputs(cfg, head_map=head_map)
     grads = make_grads(cfg)
     got = gpu_bwd(ssa, cfg, x, grads, budget=budget, use_full=use_full, use_sparse=use_sparse,
-                  head_map=head_map, group_select=group_select)
+                  head_map=head_map, group_select=group_select, token_select=token_select)
     hm = head_map or default_head_map(cfg.Hq, cfg.Hkv)
     xn = {n: t.double().numpy() for n, t in x.items()}
     idx, cnt = O.select_blocks(xn["q"], xn["k"], block=cfg.block, budget=budget,
                                n_sink=cfg.n_sink, n_local=cfg.n_local, head_map=hm,
-                               group_shared=group_select)
+                               group_shared=group_select, per_token=token_select)
     assert np.array_equal(got["idx"].numpy(), idx), "selected blocks differ"
     assert np.array_equal(got["cnt"].numpy(), cnt), "block counts differ"
     gf = grads["d_full"].double().numpy() if use_full else None
     gs = grads["d_sparse"].double().numpy() if use_sparse else None
     dq, dk, dv = O.dual_attention_backward(xn["q"], xn["k"], xn["v"], idx, gf, gs, block=cfg.block,
-                                           scale=scale_for(cfg), head_map=hm)
+                                           scale=scale_for(cfg), head_map=hm,
+                                           per_token=token_select)
     for name, want in (("dq", dq), ("dk", dk), ("dv", dv)):
         check_grad(name, to_np64(got[name]), want, cfg.dtype)
 
@@ -111,6 +114,9 @@ SMALL = [
     ("paper_16k_b16", dict(Hq=4, Hkv=1, N=1024), dict(budget=16, use_full=False)),
     ("paper_16k_b16", dict(Hq=2, Hkv=1, N=576, D=128), dict(budget=8)),
     ("tiny_f32", dict(Hq=2, Hkv=1, N=256, D=128), dict(budget=2, use_full=False)),
+    # per-token lists (float32 path)
+    ("tiny_f32", dict(Hq=2, Hkv=1, N=512), dict(budget=3, token_select=True)),
+    ("tiny_f32", dict(Hq=2, Hkv=2, N=256, D=128), dict(budget=2, token_select=True, use_full=False)),
 ]
 
 

@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+FP64_PEAK_TFLOPS = 78.6          # MI355X float64 vector FMA
 
 # HBM bytes per launch of the prefill attention kernel, from two rocprofv3
 # --pmc runs (FETCH_SIZE, WRITE_SIZE) scaled by a plain 1 GiB copy (see the
@@ -62,6 +63,57 @@ def prefill_traffic():
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def token_select_flops(cfg, budget) -> float:
+    """float64 FLOPs of per-token selection: one D-long dot product (2 D
+    FLOPs) per (query row, candidate block); candidates are the causal
+    blocks of the row's block minus the sink and local blocks."""
+    nkb = cfg.N // cfg.block
+    pairs = 0
+    for qb in range(nkb):
+        forced = len(set(range(min(cfg.n_sink, qb + 1))) |
+                     set(range(max(0, qb - cfg.n_local + 1), qb + 1)))
+        pairs += (qb + 1 - forced) * cfg.block
+    return 2.0 * cfg.D * pairs * cfg.B * cfg.Hq
+
+
+def run_token_select(ssa, torch, cfg, q, k, v, steps):
+    """Per-token selection (one list per query row) at cfg.budget: selection
+    time with its float64 roofline, dual-mode and sparse-only attention."""
+    dev = q.device
+    p = ssa.problem_for(q, k, budget=cfg.budget, n_sink=cfg.n_sink, n_local=cfg.n_local,
+                        block_size=cfg.block, token_select=True)
+    ws = ssa.alloc_workspace(p, dev)
+    idx, cnt = ssa.select_blocks(p, q, k, ws=ws)
+    out = ssa.attn_fwd(p, q, k, v, idx, cnt, ws=ws)
+    tsel, tatt, tsp = EventTimer(torch), EventTimer(torch), EventTimer(torch)
+    for _ in range(max(3, steps // 4)):
+        tsel.start()
+        ssa.select_blocks(p, q, k, ws=ws, idx=idx, cnt=cnt)
+        tsel.stop()
+        tatt.start()
+        ssa.attn_fwd(p, q, k, v, idx, cnt, ws=ws, out=out)
+        tatt.stop()
+        tsp.start()
+        ssa.attn_fwd(p, q, k, v, idx, cnt, ws=ws, out={"h_sparse": out["h_sparse"]},
+                     sparse_only=True)
+        tsp.stop()
+    torch.cuda.synchronize()
+    sel_tf = token_select_flops(cfg, cfg.budget) / (tsel.mean_ms() * 1e-3) / 1e12
+    att_tf = prefill_flops(cfg) / (tatt.mean_ms() * 1e-3) / 1e12
+    res = {"budget": cfg.budget, "block": cfg.block,
+           "select_ms": round(tsel.mean_ms(), 4),
+           "select_fp64_tflops": round(sel_tf, 2),
+           "select_fp64_frac": round(sel_tf / FP64_PEAK_TFLOPS, 4),
+           "dual_attn_ms": round(tatt.mean_ms(), 4),
+           "attn_tflops": round(att_tf, 2),
+           "attn_mfma_frac": round(att_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+           "sparse_only_attn_ms": round(tsp.mean_ms(), 4),
+           "delta_mean": round(float(out["delta"].mean()), 4)}
+    del out, ws, idx, cnt
+    torch.cuda.empty_cache()
+    return res
 
 
 def prefill_flops(cfg) -> float:
@@ -167,7 +219,10 @@ def run_prefill(ssa, torch, cfg, steps, warmup, budgets):
     res["group_select"] = {"budget": cfg.budget, "select_ms": round(tsel.mean_ms(), 4),
                            "dual_attn_ms": round(tg.mean_ms(), 4),
                            "delta_mean": round(float(out["delta"].mean()), 4)}
-    del q, k, v, out, ws
+    del out, ws
+    torch.cuda.empty_cache()
+    res["token_select"] = run_token_select(ssa, torch, cfg, q, k, v, steps)
+    del q, k, v
     torch.cuda.empty_cache()
     return res
 
@@ -207,7 +262,10 @@ def run_paper_shape(ssa, torch, cfg, steps):
            "attn_mfma_frac": round(flops / (tatt.mean_ms() * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
            "sparse_only_attn_ms": round(tsp.mean_ms(), 4),
            "delta_mean": round(float(out["delta"].mean()), 4)}
-    del q, k, v, out, ws
+    del out, ws
+    torch.cuda.empty_cache()
+    res["token_select"] = run_token_select(ssa, torch, cfg, q, k, v, steps)
+    del q, k, v
     torch.cuda.empty_cache()
     return res
 
@@ -493,6 +551,7 @@ def main():
         "delta_mean": round(pre["delta_mean"], 4),
         "budget_sweep": pre.get("sweep"),
         "group_select": pre.get("group_select"),
+        "token_select": pre.get("token_select"),
     }
     if not args.no_backward:
         result["backward"] = run_backward(ssa, torch, cfg, max(5, args.steps // 2), args.warmup)

@@ -332,6 +332,26 @@ def run_backward(ssa, torch, cfg, steps, warmup):
            "fwd_dual_ms": round(fwd_t.mean_ms(), 4),
            "train_step_attn_ms": round(fwd_t.mean_ms() + dual_ms, 4),
            "sparse_stream_overhead": round((fwd_t.mean_ms() + dual_ms) / (fwd_t.mean_ms() + full_ms) - 1, 4)}
+    del fwd, out, ws, bws
+    torch.cuda.empty_cache()
+    # per-token lists (one per query row): dual-mode backward
+    pt = ssa.problem_for(q, k, budget=cfg.budget, n_sink=cfg.n_sink, n_local=cfg.n_local,
+                         block_size=cfg.block, token_select=True)
+    ws = ssa.alloc_workspace(pt, dev)
+    it, ct = ssa.select_blocks(pt, q, k, ws=ws)
+    fwd = ssa.attn_fwd(pt, q, k, v, it, ct, want_lse=True, ws=ws)
+    bws = ssa.alloc_bwd_workspace(pt, dev)
+    kw = dict(h_full=fwd["h_full"], h_sparse=fwd["h_sparse"], d_full=gf, d_sparse=gs)
+    out = ssa.attn_bwd(pt, q, k, v, it, ct, fwd["lse"], ws=bws, **kw)
+    tt = EventTimer(torch)
+    for _ in range(max(3, steps // 2)):
+        tt.start()
+        ssa.attn_bwd(pt, q, k, v, it, ct, fwd["lse"], ws=bws, out=out, **kw)
+        tt.stop()
+    torch.cuda.synchronize()
+    tok_flops = flops_full + 2 * pair * float(ct.sum()) * (cfg.block / 64) / 64
+    res["token_select_dual_ms"] = round(tt.mean_ms(), 4)
+    res["token_select_dual_tflops"] = round(tok_flops / (tt.mean_ms() * 1e-3) / 1e12, 2)
     del q, k, v, gf, gs, fwd, out, ws, bws
     torch.cuda.empty_cache()
     return res

@@ -161,9 +161,11 @@ ssa_status build(const ssa_problem* p, Problem* P) {
 // bf16, the selection bits (uint16 [B*Hkv, key tiles, Nq/32, Hq/Hkv]) and
 // the float32 partial sums that the full-stream pass hands to the
 // sparse-stream pass (dQ [B,Hq,Nq,D], dK and dV [B,Hkv,Nk,D]), plus the
-// sparse dK / dV pass's per-q-head slots ([Hq/Hkv] x [B,Hkv,Nk,D] each).
+// sparse dK / dV pass's per-q-head slots ([Hq/Hkv] x [B,Hkv,Nk,D] each);
+// with per-token lists also one 64-bit row mask per (kv head, 128-key tile,
+// 32-row step, q head of the group, 32-key wave block).
 struct BwdLayout {
-  size_t stats, bits, pq, pk, pv, sk, sv, total;
+  size_t stats, bits, rowbits, pq, pk, pv, sk, sv, total;
 };
 
 BwdLayout bwd_layout_of(const Problem& P) {
@@ -172,10 +174,13 @@ BwdLayout bwd_layout_of(const Problem& P) {
   size_t off = 0;
   L.stats = off;
   off += align256((size_t)d.B * d.Hq * d.Nq * 4 * sizeof(float));
-  L.bits = L.pq = L.pk = L.pv = L.sk = L.sv = off;
+  L.bits = L.rowbits = L.pq = L.pk = L.pv = L.sk = L.sv = off;
   if (P.bf16) {
     L.bits = off;
     off += align256((size_t)d.B * d.Hq * ssa::bwd_key_tiles(d) * (d.Nq / 32) * sizeof(uint16_t));
+    L.rowbits = off;   // per-token lists: one 64-bit row mask per 32-key wave block
+    if (d.tok)
+      off += align256((size_t)d.B * d.Hq * ssa::bwd_key_tiles(d) * (d.Nq / 32) * 4 * sizeof(uint64_t));
     L.pq = off;
     off += align256((size_t)d.B * d.Hq * d.Nq * d.D * sizeof(float));
     L.pk = off;
@@ -338,8 +343,6 @@ ssa_status ssa_attn_bwd(const ssa_problem* p, const void* q, const void* k, cons
   if (s != SSA_OK) return s;
   if (P.decode)
     return fail(SSA_ERR_UNSUPPORTED, "the backward pass needs a prefill problem (Nq == Nk)");
-  if (P.d.tok && P.bf16)
-    return fail(SSA_ERR_UNSUPPORTED, "the bf16 backward pass does not take per-token selection lists");
   if (q == nullptr || k == nullptr || v == nullptr || idx == nullptr || cnt == nullptr ||
       lse == nullptr)
     return fail(SSA_ERR_INVALID_ARG, "q, k, v, idx, cnt or lse is NULL");
@@ -373,7 +376,8 @@ ssa_status ssa_attn_bwd(const ssa_problem* p, const void* q, const void* k, cons
   return hip_status(ssa::launch_attn_bwd_bf16((const uint16_t*)q, (const uint16_t*)k,
                                               (const uint16_t*)v, (const uint16_t*)d_full,
                                               (const uint16_t*)d_sparse, idx, cnt, stats,
-                                              (uint16_t*)(w + L.bits), (float*)(w + L.pq),
+                                              (uint16_t*)(w + L.bits),
+                                              (uint64_t*)(w + L.rowbits), (float*)(w + L.pq),
                                               (float*)(w + L.pk), (float*)(w + L.pv),
                                               (float*)(w + L.sk), (float*)(w + L.sv), (uint16_t*)dq,
                                               (uint16_t*)dk, (uint16_t*)dv, d, P.hm, st),

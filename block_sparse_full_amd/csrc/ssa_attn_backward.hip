@@ -253,7 +253,8 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const T* __restrict__ hf
 // no two threads write one word.
 __global__ __launch_bounds__(256) void bwd_bits_kernel(const int* __restrict__ idx,
                                                        const int* __restrict__ cnt,
-                                                       uint16_t* __restrict__ bits, Dims d,
+                                                       uint16_t* __restrict__ bits,
+                                                       uint64_t* __restrict__ rowbits, Dims d,
                                                        HeadMap hm, int nKT) {
   const int nS = d.Nq / kStep;
   const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -268,6 +269,36 @@ __global__ __launch_bounds__(256) void bwd_bits_kernel(const int* __restrict__ i
   uint16_t* col = bits + (bg * nKT * nS + s) * d.G + hi;    // entry kt at col[kt * nS * G]
   const size_t kstride = (size_t)nS * d.G;
   for (int kt = 0; kt < nKT; ++kt) col[kt * kstride] = 0;
+  if (d.tok) {
+    // per-token lists: the rows of the step select on their own; the nibbles
+    // say whether any row of a 16-row half selected a 16-key half, and
+    // rowbits[bg][kt][s][hi][wave] holds bit 32*(key half) + row of each
+    // 32-key wave block
+    uint64_t* rb = rowbits + ((bg * nKT * nS + s) * d.G + hi) * 4;   // entry kt at rb[kt * kstride * 4]
+    for (int kt = 0; kt < nKT; ++kt)
+      for (int wv = 0; wv < 4; ++wv) rb[kt * kstride * 4 + wv] = 0ull;
+    for (int j = 0; j < kStep; ++j) {
+      const int row = kStep * s + j;
+      const size_t lr = bh * d.nL + row;
+      const int* list = idx + lr * d.budget;
+      const int n = min(max(cnt[lr], 0), d.budget);
+      const int diag = row / d.bs;
+      for (int e = 0; e < n; ++e) {
+        const int kb = list[e];
+        if (kb < 0 || kb > diag) continue;
+        for (int kw = kb * d.bs / kStep; kw < (kb * d.bs + d.bs + kStep - 1) / kStep; ++kw) {
+          const int kt = kw >> 2, wv = kw & 3;
+          // key halves of the wave block covered by this block
+          const int h0 = d.bs == 16 ? (kb & 1) : 0, h1 = d.bs == 16 ? (kb & 1) : 1;
+          for (int kh = h0; kh <= h1; ++kh) {
+            col[kt * kstride] |= (uint16_t)(1u << (4 * wv + 2 * (j >> 4) + kh));
+            rb[kt * kstride * 4 + wv] |= 1ull << (32 * kh + j);
+          }
+        }
+      }
+    }
+    return;
+  }
   const int nq = d.bs == 16 ? 2 : 1;
   for (int qs = 0; qs < nq; ++qs) {
     const int qb = d.bs == 16 ? 2 * s + qs : s >> 1;
@@ -303,13 +334,15 @@ __global__ __launch_bounds__(256) void bwd_bits_kernel(const int* __restrict__ i
 // words arrive 64 at a time (lane i holds item 64c + i), one chunk ahead.
 // MODE 0: both streams; 1: full stream only; 2: sparse stream only (items
 // without a selected block are skipped).
-template <int D, int MODE, int IO>
+// TOK: per-token lists; the selection of each of the item's rows comes from
+// rowbits (one 64-bit word per wave: bit 32*(key half) + row).
+template <int D, int MODE, int IO, bool TOK>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ GF, const uint16_t* __restrict__ GS,
     const float* __restrict__ stats, const uint16_t* __restrict__ bits,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ pK,
-    float* __restrict__ pV, Dims d, HeadMap hm, int nKT) {
+    const uint64_t* __restrict__ rowbits, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+    float* __restrict__ pK, float* __restrict__ pV, Dims d, HeadMap hm, int nKT) {
   constexpr bool FULL = MODE != 2, SPARSE = MODE != 1;
   constexpr int SPR = D / 8;          // 16-byte chunks per row
   constexpr int KK = D / 32;          // 32-deep k-steps over D
@@ -432,6 +465,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     const int rel = kStep * s - kw0;   // row position minus key position of (0, 0)
     const uint32_t nib = SPARSE ? (word >> (4 * w)) & 0xFu : 0u;
     const bool sp = nib != 0u;
+    // per-token lists: bits of the lane's rows 8*gq .. 8*gq+7, per key half
+    uint32_t rsel[2] = {0u, 0u};
+    if (TOK && SPARSE) {
+      const uint64_t rm = rowbits[(((size_t)bg * nKT + kt) * nS + s) * G * 4 + (size_t)item_h(e) * 4 + w];
+      rsel[0] = (uint32_t)(rm >> (8 * gq)) & 0xFFu;
+      rsel[1] = (uint32_t)(rm >> (32 + 8 * gq)) & 0xFFu;
+    }
     typedef __attribute__((address_space(3))) const f32x4_t* lpf;
     auto stat = [&](int a, int r0) { return *(lpf)(uintptr_t)(aSt + st * SB + 4u * (a * kStep + r0)); };
     // statistics of the lane's rows 8*gq + 4*mb + r, read ahead of use
@@ -503,9 +543,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
       const int r0 = 8 * gq + 4 * mb;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const bool sel = sp && ((nib >> (2 * (gq >> 1) + nb)) & 1u);
+        const bool selb = sp && ((nib >> (2 * (gq >> 1) + nb)) & 1u);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+          const bool sel = TOK ? ((rsel[nb] >> (4 * mb + r)) & 1u) != 0u : selb;
           const bool keep = 16 * nb + n <= rel + r0 + r;   // key <= row
           float p = 0.f, dsv = 0.f, q = 0.f;
           if (FULL) {
@@ -651,12 +692,13 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict
 // selection bits of the workgroup's rows are built in LDS from idx at the
 // start. Workgroups are ordered heaviest first, the q heads of one kv head
 // next to each other.
-template <int D, int MODE, int IO>
+template <int D, int MODE, int IO, bool TOK>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ GF, const uint16_t* __restrict__ GS,
     const float* __restrict__ stats, const int* __restrict__ idx, const int* __restrict__ cnt,
-    uint16_t* __restrict__ dQ, float* __restrict__ pQ, Dims d, HeadMap hm) {
+    const uint64_t* __restrict__ rowbits, uint16_t* __restrict__ dQ, float* __restrict__ pQ,
+    Dims d, HeadMap hm, int nKT) {
   constexpr int SPR = D / 8;
   constexpr int KK = D / 32;
   constexpr int MB = D / 16;
@@ -690,7 +732,27 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
   if (has_sparse) {
     for (int i = tid; i < (nT + 1) / 2; i += 256) sNib[i] = 0u;
     __syncthreads();
-    if (wave_rows) {
+    if (TOK && wave_rows) {   // per-token lists: any row of each 16-row half
+      for (int j = 0; j < kStep; ++j) {
+        const int row = r0w + j;
+        const size_t lr = bh * d.nL + row;
+        const int* list = idx + lr * d.budget;
+        const int cn = min(max(cnt[lr], 0), d.budget);
+        const int diag = row / d.bs;
+        for (int e = lane; e < cn; e += 64) {
+          const int kb = list[e];
+          if (kb < 0 || kb > diag) continue;
+          if (d.bs == 16) {
+            const int t = kb >> 1;
+            const uint32_t bit = 1u << (2 * (j >> 4) + (kb & 1));
+            atomicOr(&sNib[t >> 1], bit << (16 * (t & 1) + 4 * w));
+          } else {
+            for (int t = 2 * kb; t < 2 * kb + 2; ++t)
+              atomicOr(&sNib[t >> 1], (3u << (2 * (j >> 4))) << (16 * (t & 1) + 4 * w));
+          }
+        }
+      }
+    } else if (wave_rows) {
       const int nq = d.bs == 16 ? 2 : 1;
       for (int qs = 0; qs < nq; ++qs) {
         const int qb = d.bs == 16 ? r0w / 16 + qs : r0w / 64;
@@ -766,6 +828,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
     const int rel = r0w - kStep * t;   // row position minus key position of (0, 0)
     const uint32_t nib = (step_bits(t) >> (4 * w)) & 0xFu;
     const bool sp = nib != 0;
+    // per-token lists: bits of the lane's rows 16*nb + n in its key half
+    uint32_t rsel = 0u;
+    if (TOK && has_sparse) {
+      const int sw = min(r0w / kStep, nS - 1);
+      const uint64_t rm = rowbits[(((size_t)bg * nKT + (t >> 2)) * nS + sw) * d.G * 4 + (size_t)hi * 4 + (t & 3)];
+      rsel = (uint32_t)(rm >> (32 * (gq >> 1) + n));
+    }
     f32x4_t sa[2][2], pf[2][2], ps[2][2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -807,7 +876,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
     float xd[2][8];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const bool sel = (nib >> (2 * nb + (gq >> 1))) & 1u;   // per lane
+      const bool sel = TOK ? ((rsel >> (16 * nb)) & 1u) != 0u
+                           : ((nib >> (2 * nb + (gq >> 1))) & 1u) != 0u;   // per lane
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -1042,7 +1112,8 @@ int bwd_key_tiles(const Dims& d) { return (d.Nk + kKeysPerWg - 1) / kKeysPerWg; 
 
 hipError_t launch_attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const uint16_t* gf, const uint16_t* gs, const int* idx,
-                                const int* cnt, const float* stats, uint16_t* bits, float* pq,
+                                const int* cnt, const float* stats, uint16_t* bits,
+                                uint64_t* rowbits, float* pq,
                                 float* pk, float* pv, float* sk, float* sv, uint16_t* dq,
                                 uint16_t* dk, uint16_t* dv, const Dims& d, const HeadMap& hm,
                                 hipStream_t stream) {
@@ -1050,17 +1121,24 @@ hipError_t launch_attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint
   if (gs != nullptr) {
     const long threads = (long)d.B * d.Hq * (d.Nq / kStep);
     hipLaunchKernelGGL(bwd_bits_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       stream, idx, cnt, bits, d, hm, nKT);
+                       stream, idx, cnt, bits, rowbits, d, hm, nKT);
   }
   const dim3 g1((unsigned)(nKT * d.B * d.Hkv));
   const int nQT = (d.Nq + kRowsPerWg - 1) / kRowsPerWg;
   const dim3 g2((unsigned)(nQT * d.B * d.Hq));
+  // the full-stream pass never reads the selection; the sparse-stream
+  // kernels come in a per-block and a per-token (per-row masks) form
+#define SSA_DKDV_T(DD, MM, IO, TK, PK, PV, GRID)                                             \
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DD, MM, IO, TK>), GRID, dim3(256), 0, stream, q, k, \
+                     v, gf, gs, stats, bits, rowbits, dk, dv, PK, PV, d, hm, nKT)
+#define SSA_DQ_T(DD, MM, IO, TK)                                                             \
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DD, MM, IO, TK>), g2, dim3(256), 0, stream, q, k, v,  \
+                     gf, gs, stats, idx, cnt, rowbits, dq, pq, d, hm, nKT)
 #define SSA_DKDV(DD, MM, IO, PK, PV, GRID)                                                   \
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DD, MM, IO>), GRID, dim3(256), 0, stream, q, k, v,   \
-                     gf, gs, stats, bits, dk, dv, PK, PV, d, hm, nKT)
+  if (MM == 2 && d.tok) { SSA_DKDV_T(DD, MM, IO, true, PK, PV, GRID); }                      \
+  else { SSA_DKDV_T(DD, MM, IO, false, PK, PV, GRID); }
 #define SSA_DQ(DD, MM, IO)                                                                   \
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<DD, MM, IO>), g2, dim3(256), 0, stream, q, k, v, gf, \
-                     gs, stats, idx, cnt, dq, pq, d, hm)
+  if (MM == 2 && d.tok) { SSA_DQ_T(DD, MM, IO, true); } else { SSA_DQ_T(DD, MM, IO, false); }
   // Both streams: a full-stream pass leaves float32 partial sums, a
   // sparse-stream pass over the selected blocks only adds to them and rounds.
   // The sparse dK/dV pass runs per (tile, q head) into per-head slots.
@@ -1088,6 +1166,8 @@ hipError_t launch_attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint
 #undef SSA_PASSES
 #undef SSA_DKDV
 #undef SSA_DQ
+#undef SSA_DKDV_T
+#undef SSA_DQ_T
   return hipGetLastError();
 }
 

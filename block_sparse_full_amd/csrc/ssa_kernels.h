@@ -63,7 +63,8 @@ hipError_t launch_attn_bwd_stats(const void* hf, const void* hs, const void* gf,
                                  hipStream_t stream);
 hipError_t launch_attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const uint16_t* gf, const uint16_t* gs, const int* idx,
-                                const int* cnt, const float* stats, uint16_t* bits, float* pq,
+                                const int* cnt, const float* stats, uint16_t* bits,
+                                uint64_t* rowbits, float* pq,
                                 float* pk, float* pv, float* sk, float* sv, uint16_t* dq,
                                 uint16_t* dk, uint16_t* dv, const Dims& d, const HeadMap& hm,
                                 hipStream_t stream);

@@ -187,7 +187,8 @@ ssa_status ssa_align_loss(const ssa_problem* p, const void* h_full,
 
 /* Device workspace bytes needed by ssa_attn_bwd for problem p: per-row
  * statistics (16 bytes per query row) and, for SSA_BF16, the selection bits
- * of the dK/dV walk (2 bytes per q head, 128-key tile and 32-row step) and
+ * of the dK/dV walk (2 bytes per q head, 128-key tile and 32-row step; 32
+ * more with SSA_SELECT_TOKEN, the row masks of the four 32-key blocks) and
  * float32 copies of dQ, dK and dV (the full-stream pass hands its partial
  * sums to the sparse-stream pass) and Hq/Hkv float32 copies of dK and dV
  * (one per q head of a group for the sparse pass). Returns 0 when p is
@@ -221,9 +222,8 @@ size_t ssa_bwd_workspace_bytes(const ssa_problem* p);
  *   dk, dv       : out [B,Hkv,Nk,D] p->dtype, each kv head summed over its
  *                  q heads (deterministic: no atomics)
  *   ws, ws_bytes : at least ssa_bwd_workspace_bytes(p) bytes
- * Prefill problems only (Nq == Nk; decode gives SSA_ERR_UNSUPPORTED);
- * SSA_SELECT_TOKEN lists are supported for SSA_F32 only (SSA_BF16 gives
- * SSA_ERR_UNSUPPORTED).
+ * Prefill problems only (Nq == Nk; decode gives SSA_ERR_UNSUPPORTED).
+ * With SSA_SELECT_TOKEN each row's own list selects its sparse keys.
  * float32 accumulation; P and dS enter the bf16 products rounded to bf16;
  * outputs are rounded once. */
 ssa_status ssa_attn_bwd(const ssa_problem* p, const void* q, const void* k,

@@ -158,12 +158,15 @@ def test_backward_argument_checks(lib):
 
 
 def test_token_selection_host(lib):
-    """Per-token lists: bf16 backward refused, float32 backward accepted;
-    the workspace adds the float64 chunked copy of the pooled keys."""
-    from block_sparse_full_amd.ssa import SSA_SELECT_TOKEN, workspace_bytes
+    """Per-token lists: the backward accepts them (bf16 and float32); the
+    forward workspace adds the float64 chunked copy of the pooled keys and
+    the bf16 backward workspace one 64-bit row mask per (q head, 128-key
+    tile, 32-row step, 32-key block)."""
+    from block_sparse_full_amd.ssa import SSA_SELECT_TOKEN, bwd_workspace_bytes, workspace_bytes
     c, keep = _p(selection=SSA_SELECT_TOKEN).to_c()
-    assert _bwd(lib, c) == 2
-    assert "per-token" in lib.ssa_last_error_message().decode()
+    assert _bwd(lib, c) == 3                       # valid, no workspace
+    extra = bwd_workspace_bytes(_p(selection=SSA_SELECT_TOKEN)) - bwd_workspace_bytes(_p())
+    assert extra == 8 * (4096 // 128) * (4096 // 32) * 4 * 8
     c32, keep2 = _p(selection=SSA_SELECT_TOKEN, dtype=0, D=64).to_c()
     assert _bwd(lib, c32) == 3                     # valid, no workspace
     base = workspace_bytes(_p())

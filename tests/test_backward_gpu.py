@@ -114,9 +114,18 @@ SMALL = [
     ("paper_16k_b16", dict(Hq=4, Hkv=1, N=1024), dict(budget=16, use_full=False)),
     ("paper_16k_b16", dict(Hq=2, Hkv=1, N=576, D=128), dict(budget=8)),
     ("tiny_f32", dict(Hq=2, Hkv=1, N=256, D=128), dict(budget=2, use_full=False)),
-    # per-token lists (float32 path)
+    # per-token lists: float32, and bf16 (row masks) with blocks 64 and 16,
+    # both streams and each alone, GQA, a permuted head map, D 64 and 128
     ("tiny_f32", dict(Hq=2, Hkv=1, N=512), dict(budget=3, token_select=True)),
     ("tiny_f32", dict(Hq=2, Hkv=2, N=256, D=128), dict(budget=2, token_select=True, use_full=False)),
+    ("gqa_8k_peaked", dict(B=1, Hq=8, Hkv=2, N=1024), dict(budget=4, token_select=True)),
+    ("gqa_8k_peaked", dict(B=1, Hq=4, Hkv=1, N=1024, planted=False), dict(budget=5, token_select=True, use_full=False)),
+    ("gqa_8k_peaked", dict(B=1, Hq=4, Hkv=1, N=768, planted=False), dict(budget=5, token_select=True, use_sparse=False)),
+    ("gqa_8k_peaked", dict(B=2, Hq=4, Hkv=2, N=576), dict(budget=3, token_select=True, head_map=[1, 0, 0, 1])),
+    ("gqa_8k_peaked", dict(B=1, Hq=4, Hkv=1, N=704, D=64, planted=False), dict(budget=4, token_select=True)),
+    ("paper_16k_b16", dict(Hq=4, Hkv=1, N=1024), dict(budget=16, token_select=True)),
+    ("paper_16k_b16", dict(Hq=4, Hkv=1, N=1024, planted=False), dict(budget=12, token_select=True, use_full=False)),
+    ("paper_16k_b16", dict(Hq=2, Hkv=1, N=576, D=128, planted=False), dict(budget=8, token_select=True)),
 ]
 
 
@@ -144,17 +153,19 @@ def test_backward_full_budget_streams_agree(ssa):
         assert err <= 1e-2 * np.abs(ref).max(), (n, err)
 
 
-def test_backward_full_size_gqa_32k(ssa):
+@pytest.mark.parametrize("token_select", [False, True], ids=["per_block", "per_token"])
+def test_backward_full_size_gqa_32k(ssa, token_select):
     """The 32K GQA workload (budget 16, planted blocks) at full size: dq on
     sampled rows and dk, dv of the last 128 keys of every kv head against the
     oracle restricted to the rows that reach them; over all keys, dk sums to
     zero and dv sums to the upstream gradients summed over rows (per kv
-    head), as softmax's shift invariance and unit row sums require."""
+    head), as softmax's shift invariance and unit row sums require. Per-block
+    lists, and per-token lists (the oracle selects the sampled rows)."""
     cfg = CONFIGS["gqa_32k_sweep"].with_budget(16)
-    say(f"[bwd] full size {cfg.name} budget {cfg.budget}")
+    say(f"[bwd] full size {cfg.name} budget {cfg.budget} token_select={token_select}")
     x = make_inputs(cfg)
     grads = make_grads(cfg)
-    got = gpu_bwd(ssa, cfg, x, grads, budget=cfg.budget)
+    got = gpu_bwd(ssa, cfg, x, grads, budget=cfg.budget, token_select=token_select)
     hm = default_head_map(cfg.Hq, cfg.Hkv)
     G = cfg.Hq // cfg.Hkv
     N, nkb = cfg.N, cfg.N // cfg.block
@@ -164,6 +175,12 @@ def test_backward_full_size_gqa_32k(ssa):
     tail = np.arange(N - 128, N)
     dq = to_np64(got["dq"]); dk = to_np64(got["dk"]); dv = to_np64(got["dv"])
     gf_all = grads["d_full"].double().numpy(); gs_all = grads["d_sparse"].double().numpy()
+    if token_select:
+        both = np.union1d(rows, tail)
+        tok_idx, _ = O.select_blocks(x["q"].double().numpy(), x["k"].double().numpy(),
+                                     block=cfg.block, budget=cfg.budget, n_sink=cfg.n_sink,
+                                     n_local=cfg.n_local, head_map=hm, per_token=True,
+                                     rows={(0, h): both for h in range(cfg.Hq)})
     err_q = err_k = err_v = 0.0
     max_q = max_k = max_v = 0.0
     for g in range(cfg.Hkv):
@@ -178,10 +195,14 @@ def test_backward_full_size_gqa_32k(ssa):
                 sel = np.zeros((len(rr), nkb), dtype=bool)
                 for i, r in enumerate(rr):
                     qb = r // cfg.block
-                    lst = O.select_row(scores[qb], qb, cfg.budget, cfg.n_sink, cfg.n_local)
+                    if token_select:
+                        lst = [int(v) for v in tok_idx[0, h, r] if v >= 0]
+                        want = got["idx"][0, h, r].numpy()
+                    else:
+                        lst = O.select_row(scores[qb], qb, cfg.budget, cfg.n_sink, cfg.n_local)
+                        want = got["idx"][0, h, qb].numpy()
                     sel[i, lst] = True
-                    want = got["idx"][0, h, qb].numpy()
-                    assert sorted(x for x in want.tolist() if x >= 0) == sorted(lst), (h, qb)
+                    assert sorted(x for x in want.tolist() if x >= 0) == sorted(lst), (h, r)
                 a, c, e = O.dual_attention_rows_backward(qq[rr], rr, kk, vv, sel, gf_all[0, h, rr],
                                                          gs_all[0, h, rr], block=cfg.block,
                                                          scale=scale)

@@ -307,8 +307,10 @@ hipError_t launch_select(const float* qbar, const float* kbar, int* idx, int* cn
 // best candidates in a register list sorted by (key descending, block
 // ascending) of KCAP entries; a new candidate is inserted below every entry
 // with an equal or larger key, so among equal keys the earlier (lower) block
-// stays ahead. At the end the lane sorts its `free` picks by block index and
-// writes sink blocks, picks and local blocks in ascending order.
+// stays ahead. Per chunk a lane marks the keys above its list's last entry
+// and the wave inserts them in rounds, as many as the busiest lane needs.
+// At the end the lane sorts its `free` picks by block index and writes sink
+// blocks, picks and local blocks in ascending order.
 
 // kc[bg][c][d][i] = (double)kbar[bg][kTokChunk*c + i][d], 0 past the last block.
 __global__ __launch_bounds__(256) void kbar_f64_kernel(const float* __restrict__ kbar,
@@ -382,16 +384,23 @@ __global__ __launch_bounds__(256) void select_tok_kernel(const T* __restrict__ q
           acc[i] = __fma_rn(qd, kp[(d8 + e) * kTokChunk + i], acc[i]);
       }
     }
+    // keys that beat the list's last entry (the list only rises, so the
+    // others cannot enter); the wave runs as many insertion rounds as its
+    // busiest lane needs, each lane taking its next marked key
+    uint32_t todo = 0u;
 #pragma unroll
     for (int i = 0; i < kTokChunk; ++i) {
       const int kb = c0 + i;
-      wk[i * 64 + lane] = (kb >= a_end && kb < l_begin) ? orderable_key(acc[i]) : 0ull;
+      const uint64_t key = (kb >= a_end && kb < l_begin) ? orderable_key(acc[i]) : 0ull;
+      wk[i * 64 + lane] = key;
+      todo |= (key > lk[KCAP - 1]) ? 1u << i : 0u;
     }
     wave_lds_fence();
 #pragma unroll 1
-    for (int i = 0; i < kTokChunk; ++i) {
-      const uint64_t key = wk[i * 64 + lane];
-      if (__builtin_amdgcn_ballot_w64(key > lk[KCAP - 1]) == 0ull) continue;
+    while (__builtin_amdgcn_ballot_w64(todo != 0u) != 0ull) {
+      const int i = todo != 0u ? __builtin_ctz(todo) : 0;
+      const uint64_t key = todo != 0u ? wk[i * 64 + lane] : 0ull;   // key 0 inserts nothing
+      todo &= todo - 1u;
       const int kb = c0 + i;
       // insert below every entry with key >= this one (bottom-up, in place)
 #pragma unroll

@@ -14,8 +14,9 @@ BF16_ABS = 2e-2      # max-abs bar for bf16 inputs, float32 accumulation
 F32_ABS = 1e-5       # max-abs bar for float32 problems
 BF16_REL_L2 = 1e-2   # relative L2 bar (informative, asserted)
 # delta = l_drop / (l_sel + l_drop) from sums of bf16-rounded weights (each
-# relative error <= 2^-9): |d delta| <= delta (1 - delta) * 2 * 2^-9 <= 2^-10
-BF16_DELTA_ABS = 1e-3
+# within the bf16 unit roundoff 2^-8, an 8-bit significand):
+# |d delta| <= delta (1 - delta) * 2 * 2^-8 <= 2^-9
+BF16_DELTA_ABS = 2e-3
 
 
 def to_np64(t: torch.Tensor) -> np.ndarray:
@@ -117,8 +118,9 @@ def full_compare(cfg, x, got, *, budget, n_sink=1, n_local=1, head_map=None, lse
         tokmask = sel[:, :, rb][..., torch.arange(nk) // cfg.block] & causal
         sparse = torch.logsumexp(z.masked_fill(~tokmask, -math.inf), -1)
         # bf16: the row sums add the bfloat16-rounded weights (relative error
-        # <= 2^-9 each), so |d lse| <= ln(1 + 2^-9) ~ 1.95e-3; fp32 exact sums
-        lse_tol = 1e-3 if f32 else 2.5e-3
+        # <= 2^-8 each, the bf16 unit roundoff), so |d lse| <= ln(1 + 2^-8)
+        # ~ 3.9e-3 (reached when one weight dominates a row); fp32 exact sums
+        lse_tol = 1e-3 if f32 else 4e-3
         assert_close("lse_full", got["lse"][0].double().numpy(), full.numpy(), lse_tol)
         assert_close("lse_sparse", got["lse"][1].double().numpy(), sparse.numpy(), lse_tol)
     return ref

@@ -8,9 +8,10 @@ gradients in float64.
 Bars, per gradient tensor: max-abs error at most BWD_NORM times the largest
 |oracle value| of that tensor, and relative L2 error at most BWD_REL_L2.
 bf16: P and dS enter the bf16 products rounded to bf16 (relative error
-2^-9 each), the row sums rowsum(dO * O) use the bf16-rounded forward output,
-and every output is rounded once more (2^-9); summed over a row's keys or a
-key's rows these give errors of a few 2^-9 of the largest terms, well inside
+2^-8 each, the bf16 unit roundoff), the row sums rowsum(dO * O) use the
+bf16-rounded forward output, and every output is rounded once more (2^-8);
+summed over a row's keys or a key's rows these give errors of a few 2^-8 of
+the largest terms, well inside
 2e-2 of the tensor's largest value and 1e-2 in relative L2. float32: exp2,
 float32 sums of up to N terms: 1e-5 of the largest value.
 """
@@ -217,7 +218,7 @@ def test_backward_full_size_gqa_32k(ssa, token_select):
         # invariants over all keys of the kv head
         heads = [hh for hh in range(cfg.Hq) if hm[hh] == g]
         want_v = sum((gf_all[0, h] + gs_all[0, h]).sum(axis=0) for h in heads)
-        # per-element errors of a few 2^-9 of the terms: bound the sums by
+        # per-element errors of a few 2^-8 of the terms: bound the sums by
         # 2e-2 of the summed magnitudes, d by d
         sv = dv[0, g].sum(axis=0)
         assert np.all(np.abs(sv - want_v) <= 2e-2 * np.abs(dv[0, g]).sum(axis=0)), (g, sv[:4], want_v[:4])

@@ -739,7 +739,9 @@ __device__ __forceinline__ void tile_to_lds_asm(i32x4_t rsrc, uint32_t tile_off,
     const int slot0 = wave * PER_WAVE + j * 64;
     const int r0 = slot0 / SPR;
     const int rl = lane / SPR, sl = lane % SPR;
-    const int c = KMAP ? kswz32(r0 + rl, sl) : vswz(r0 + rl, sl);
+    // 256-byte K rows (D = 128) take kswz32; 128-byte rows (V^T, and K for
+    // D = 64) take vswz, which also keeps the kperm32 row reads apart
+    const int c = (KMAP && SPR == 16) ? kswz32(r0 + rl, sl) : vswz(r0 + rl, sl);
     const uint32_t voff = (uint32_t)rl * row_bytes + (uint32_t)c * 16u;
     const uint32_t soff = __builtin_amdgcn_readfirstlane(tile_off + (uint32_t)r0 * row_bytes);
     const uint32_t la = __builtin_amdgcn_readfirstlane(
@@ -1139,6 +1141,325 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
   }
 }
 
+// 16-token selection blocks, D = 64, G % 4 == 0 (the pages' model shape):
+// one workgroup = one (b, kv head, 64-row query tile) serving four q heads,
+// eight waves of 32 rows on MFMA 32x32x16 bf16 in the ping-pong slots of the
+// kernel above (wave w: rows 32*(w/4) .. +31 of head w%4). A wave's rows
+// span two 16-row query blocks with their own selections, so instead of
+// walking selected blocks first, every causal 64-key tile is walked in order
+// with two accumulators sharing one running max: o_all over every causal key
+// and o_sel over the selected 16-key quarters (a lane's row's quarters come
+// from per-(head, query block) bitmaps in LDS; the quarter of a key held in
+// S^T register v is fixed by the kperm32 row order). Both PV products of an
+// entry read the same V^T fragments; the selected one multiplies weights that
+// are zero outside the row's quarters, so no branch touches the accumulators.
+//     h_full = o_all / (l_sel + l_drop),  h_sparse = o_sel / l_sel,
+//     delta = l_drop / (l_sel + l_drop).
+template <int NST>
+__global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ Vt, const int* __restrict__ idx, const int* __restrict__ cnt,
+    uint16_t* __restrict__ Hf, uint16_t* __restrict__ Hs, float* __restrict__ delta,
+    float* __restrict__ lse, Dims d, HeadMap hm) {
+  constexpr int D = 64;
+  constexpr int HPW = 4;
+  constexpr int NW = 8;
+  constexpr int KSPR = D / 8;
+  constexpr int VSPR = kBlock / 8;
+  constexpr int NKS = D / 16;
+  constexpr int NDT = D / 32;
+  constexpr int TILE = kBlock * D;
+  constexpr int LPH = (TILE / 8) / (64 * NW);   // buffer loads per half tile (K or V) per wave
+  constexpr float kTau = 8.0f;
+  constexpr int kWords16 = kMaxKeyBlocks / 32;
+  static_assert(LPH == 1, "copy shape");
+  __shared__ __align__(16) uint16_t K0[TILE], K1[TILE], K2[TILE], K3[NST > 3 ? TILE : 8];
+  __shared__ __align__(16) uint16_t V0[TILE], V1[TILE], V2[TILE], V3[NST > 3 ? TILE : 8];
+  __shared__ uint32_t sel16[HPW][4][kWords16];   // per head and 16-row query block
+
+  const int ngrp = d.G / HPW;
+  const int total = d.B * d.Hkv * ngrp * d.nQT;
+  const int lin = xcd_remap(blockIdx.x, total);
+  const int per_group = ngrp * d.nQT;
+  const int grp = lin / per_group;
+  const int rem = lin - grp * per_group;
+  const int qt = d.nQT - 1 - rem / ngrp;
+  const int hg = rem - (rem / ngrp) * ngrp;
+  const int b = grp / d.Hkv;
+  const int g = grp - b * d.Hkv;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hs = wave & 3;
+  const bool group_a = wave < 4;
+  const int h = hm.q_of_kv[g * d.G + hg * HPW + hs];
+  const int bh = b * d.Hq + h;
+  const int c = lane & 31, gl = lane >> 5;
+  const int qq = (wave >> 2) * 32 + c;   // row within the tile
+  const int qbl = qq >> 4;               // the row's 16-row query block within the tile
+  const int qrow = qt * kBlock + qq;
+  const float sl2 = d.scale_log2;
+  const int n = qt + 1;                  // causal tiles
+
+  // ---- selection bitmaps of the four heads' four query blocks
+  const int nwords16 = ((4 * qt + 3) >> 5) + 1;
+  for (int i = tid; i < HPW * 4 * kWords16; i += 64 * NW) (&sel16[0][0][0])[i] = 0u;
+  {
+    // GEMM(0) multiplies the V stage of the (absent) entry -1 by P = 0
+    uint16_t* vz = (NST - 1) == 1 ? V1 : (NST - 1) == 2 ? V2 : V3;
+    for (int w = tid; w < TILE / 8; w += 64 * NW) ((uint4*)vz)[w] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
+  for (int u = 0; u < HPW; ++u) {
+    const int hu = hm.q_of_kv[g * d.G + hg * HPW + u];
+    for (int qs = 0; qs < 4; ++qs) {
+      const size_t row = (size_t)(b * d.Hq + hu) * d.nQB + 4 * qt + qs;
+      const int ns = min(max(cnt[row], 0), d.budget);
+      for (int e = tid; e < ns; e += 64 * NW) {
+        const int kb = idx[row * d.budget + e];
+        if (kb >= 0 && kb <= 4 * qt + qs) atomicOr(&sel16[u][qs][kb >> 5], 1u << (kb & 31));
+      }
+    }
+  }
+  __syncthreads();
+  (void)nwords16;
+
+  // ---- tiles
+  const uint16_t* kbase = K + ((size_t)(b * d.Hkv + g) * d.Nk) * D;
+  const uint16_t* vbase = Vt + ((size_t)(b * d.Hkv + g) * D) * d.Nk;
+  const i32x4_t krs = make_rsrc_words(kbase, (uint32_t)((size_t)d.Nk * D * 2));
+  const i32x4_t vrs = make_rsrc_words(vbase, (uint32_t)((size_t)d.Nk * D * 2));
+  const uint32_t k_row_bytes = D * 2, v_row_bytes = (uint32_t)d.Nk * 2;
+  // copies past the last tile repeat it: every slot issues the same number
+  // of copies, so the waits are static
+  auto tile_c = [&](int e) __attribute__((always_inline)) { return min(e, n - 1); };
+  auto load_k_kb = [&](auto stc, int kb) __attribute__((always_inline)) {
+    constexpr int st = decltype(stc)::value;
+    uint16_t* kt = st == 0 ? K0 : st == 1 ? K1 : st == 2 ? K2 : K3;
+    tile_to_lds_asm<KSPR, kBlock, NW, true>(krs, (uint32_t)kb * kBlock * k_row_bytes,
+                                           k_row_bytes, kt, wave, lane);
+  };
+  auto load_v_kb = [&](auto stc, int kb) __attribute__((always_inline)) {
+    constexpr int st = decltype(stc)::value;
+    uint16_t* vt = st == 0 ? V0 : st == 1 ? V1 : st == 2 ? V2 : V3;
+    tile_to_lds_asm<VSPR, D, NW, false>(vrs, (uint32_t)kb * kBlock * 2, v_row_bytes, vt,
+                                       wave, lane);
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  bf16x8_t qf[NKS];
+  {
+    const uint16_t* qp = Q + ((size_t)bh * d.Nq + qrow) * D + 8 * gl;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8_t*)(qp + 16 * ks);
+  }
+  // the Q fragments land before any LDS copy is issued: the compiler does
+  // not count the copies, so it must see no load of its own outstanding
+  __builtin_amdgcn_s_waitcnt(0xF70);
+  // prologue = the copies of the virtual slots before slot 0: K(0..NST-2)
+  // and V(0..NST-3), with V(0) standing in for the missing V(-1)
+  load_k_kb(I0{}, tile_c(0));
+  load_v_kb(I0{}, tile_c(0));
+  load_k_kb(I1{}, tile_c(1));
+  load_v_kb(I0{}, tile_c(0));
+  if constexpr (NST > 3) {
+    load_k_kb(I2{}, tile_c(2));
+    load_v_kb(I1{}, tile_c(1));
+  }
+
+  f32x16_t oa[NDT], os[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { oa[i][v] = 0.f; os[i][v] = 0.f; }
+  f32x16_t s0, s1;
+  uint32_t pw[16], pws[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) { pw[k] = 0u; pws[k] = 0u; }
+  float m_ref = -INFINITY, l_sel = 0.f, l_drop = 0.f;
+  const int pr = kperm32(c);
+  const size_t plane = (size_t)d.B * d.Hq * d.Nq;
+
+  auto store = [&](uint16_t* H, const f32x16_t* o, float inv) __attribute__((always_inline)) {
+    uint16_t* hp = H + ((size_t)bh * d.Nq + qrow) * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * dt + 8 * i + 4 * gl;
+        const uint32_t lo = pack_bf16x2(o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv);
+        const uint32_t hi2 = pack_bf16x2(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv);
+        *(uint2*)(hp + d0) = make_uint2(lo, hi2);
+      }
+    }
+  };
+
+  // GEMM(e) = 8 MFMAs S(e) = K(e) Q^T plus 2 x 8 MFMAs O_all += V(e-1) P(e-1)
+  // and O_sel += V(e-1) P_sel(e-1) on the same V^T fragments.
+  auto gemm = [&](auto stc) __attribute__((always_inline)) {
+    constexpr int sk = decltype(stc)::value;
+    constexpr int sv = (sk + NST - 1) % NST;
+    constexpr int PF = 4;
+    const uint16_t* Kt = sk == 0 ? K0 : sk == 1 ? K1 : sk == 2 ? K2 : K3;
+    const uint16_t* Vtl = sv == 0 ? V0 : sv == 1 ? V1 : sv == 2 ? V2 : V3;
+    bf16x8_t fr[2 * NKS + 4 * NDT];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int ch = 2 * ks + gl;
+      fr[2 * ks] = *(const bf16x8_t*)(Kt + (pr * KSPR + vswz(pr, ch)) * 8);
+      fr[2 * ks + 1] = *(const bf16x8_t*)(Kt + ((32 + pr) * KSPR + vswz(32 + pr, ch)) * 8);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int r = 32 * dt + c;
+        fr[2 * NKS + s * NDT + dt] = *(const bf16x8_t*)(Vtl + (r * VSPR + vswz(r, 2 * s + gl)) * 8);
+      }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { s0[v] = 0.f; s1[v] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[2 * ks], qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[2 * ks + 1], qf[ks], s1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 w = make_uint4(pw[4 * s], pw[4 * s + 1], pw[4 * s + 2], pw[4 * s + 3]);
+      const uint4 ws = make_uint4(pws[4 * s], pws[4 * s + 1], pws[4 * s + 2], pws[4 * s + 3]);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, w);
+      const bf16x8_t psb = __builtin_bit_cast(bf16x8_t, ws);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        oa[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[2 * NKS + s * NDT + dt], pb, oa[dt], 0, 0, 0);
+        os[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[2 * NKS + s * NDT + dt], psb, os[dt], 0, 0, 0);
+      }
+    }
+    // schedule: PF reads, then MFMAs interleaved with the remaining reads
+    constexpr int NR = 2 * NKS + 4 * NDT;    // 16 fragment reads
+    constexpr int NM = 2 * NKS + 8 * NDT;    // 24 MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+    for (int k = 0; k < NR - PF; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - (NR - PF), 0);
+  };
+  // softmax(e): P(e) and P_sel(e) from S(e); the row's selected quarters of
+  // tile e, quarter of register v: v / 8 (s0) and 2 + v / 8 (s1)
+  auto softmax = [&](int e) __attribute__((always_inline)) {
+    if (e >= n) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) { pw[k] = 0u; pws[k] = 0u; }
+      return;
+    }
+    const uint32_t nib = (sel16[hs][qbl][e >> 3] >> ((4 * e) & 31)) & 0xFu;
+    if (e == qt) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key0 = 16 * (v >> 3) + 8 * gl + (v & 7);
+        if (key0 > qq) s0[v] = -INFINITY;
+        if (key0 + 32 > qq) s1[v] = -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
+    const float m_blk = pair_max(mx) * sl2;
+    if (__builtin_amdgcn_ballot_w64(m_blk > m_ref + kTau) != 0) {
+      const float m_new = fmaxf(m_ref, m_blk);
+      const float alpha = fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) { oa[i][v] *= alpha; os[i][v] *= alpha; }
+      l_sel *= alpha;
+      l_drop *= alpha;
+    }
+    // row sums of all weights (l_all) and of the selected ones (l_sel), each
+    // one dot2 chain; the dropped mass is their difference at the end
+    float la = 0.f, ls = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      const float a0 = fast_exp2(fmaf(s0[v], sl2, -m_ref));
+      const float a1 = fast_exp2(fmaf(s0[v + 1], sl2, -m_ref));
+      const float e0 = fast_exp2(fmaf(s1[v], sl2, -m_ref));
+      const float e1 = fast_exp2(fmaf(s1[v + 1], sl2, -m_ref));
+      const bool q0 = (nib >> (v >> 3)) & 1u, q1 = (nib >> (2 + (v >> 3))) & 1u;
+      const uint32_t w0 = pack_bf16x2(a0, a1), w1 = pack_bf16x2(e0, e1);
+      pw[v >> 1] = w0;
+      pw[8 + (v >> 1)] = w1;
+      pws[v >> 1] = q0 ? w0 : 0u;
+      pws[8 + (v >> 1)] = q1 ? w1 : 0u;
+      la = add_bf16x2(w0, la);
+      la = add_bf16x2(w1, la);
+      ls = add_bf16x2(pws[v >> 1], ls);
+      ls = add_bf16x2(pws[8 + (v >> 1)], ls);
+    }
+    l_sel += ls;
+    l_drop += la;   // running sum of all weights here; l_all - l_sel at the end
+  };
+  // Slots as in the kernel above: group A runs GEMM(t) in slot 2t and
+  // softmax(t) in slot 2t+1, group B one slot later; each wave requests its
+  // share of K(t+NST-1) and V(t+NST-2) after its GEMM(t).
+  auto issue_tiles = [&](auto stc, int kbk, int kbv) __attribute__((always_inline)) {
+    constexpr int st = decltype(stc)::value;
+    load_k_kb(std::integral_constant<int, (st + NST - 1) % NST>{}, kbk);
+    load_v_kb(std::integral_constant<int, (st + NST - 2) % NST>{}, kbv);
+  };
+  auto slot_barrier = [&]() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  constexpr int kWaitA = 0xF70 | (2 * LPH * (NST - 2));
+  constexpr int kWaitB = 0xF70 | (2 * LPH * (NST - 3));
+  if (!group_a) {
+    __builtin_amdgcn_s_waitcnt(kWaitA);
+    slot_barrier();
+  }
+  auto slots = [&](auto stc, int t) __attribute__((always_inline)) {
+    if (group_a) __builtin_amdgcn_s_waitcnt(kWaitA);
+    else __builtin_amdgcn_s_waitcnt(kWaitB);
+    slot_barrier();
+    __builtin_amdgcn_s_setprio(1);
+    gemm(stc);
+    __builtin_amdgcn_s_setprio(0);
+    issue_tiles(stc, tile_c(t + NST - 1), tile_c(t + NST - 2));
+    slot_barrier();
+    softmax(t);
+  };
+  for (int t = 0; t <= n; t += NST) {
+    slots(I0{}, t);
+    if (t + 1 > n) break;
+    slots(I1{}, t + 1);
+    if (t + 2 > n) break;
+    slots(I2{}, t + 2);
+    if constexpr (NST > 3) {
+      if (t + 3 > n) break;
+      slots(I3{}, t + 3);
+    }
+  }
+  if (group_a) slot_barrier();
+  __builtin_amdgcn_s_waitcnt(0xF70);
+  const float ls_t = pair_sum(l_sel);
+  const float lt = pair_sum(l_drop);   // all weights
+  const float ld_t = fmaxf(lt - ls_t, 0.f);
+  store(Hs, os, 1.f / ls_t);
+  store(Hf, oa, 1.f / lt);
+  if (gl == 0) {
+    if (delta != nullptr) delta[(size_t)bh * d.Nq + qrow] = ld_t / lt;
+    if (lse != nullptr) {
+      lse[(size_t)bh * d.Nq + qrow] = (m_ref + __log2f(lt)) * kLn2;
+      lse[plane + (size_t)bh * d.Nq + qrow] = (m_ref + __log2f(ls_t)) * kLn2;
+    }
+  }
+}
+
 hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* vt,
                                     const int* idx, const int* cnt, uint16_t* hf, uint16_t* hs,
                                     float* delta, float* lse, const Dims& d, const HeadMap& hm,
@@ -1154,6 +1475,13 @@ hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const 
       if (d.bs == 16) SSA_TOK_LAUNCH(64, 16); else SSA_TOK_LAUNCH(64, 64);
     }
 #undef SSA_TOK_LAUNCH
+    return hipGetLastError();
+  }
+  if (d.bs == 16 && d.D == 64 && d.G % 4 == 0 && hf != nullptr) {
+    // dual mode, four q heads per workgroup
+    const int groups = d.B * d.Hkv * (d.G / 4) * d.nQT;
+    hipLaunchKernelGGL((attn_prefill_bf16_pp16_kernel<3>), dim3(groups), dim3(512), 0, stream, q,
+                       k, vt, idx, cnt, hf, hs, delta, lse, d, hm);
     return hipGetLastError();
   }
   if (d.bs == 16) {

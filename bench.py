@@ -116,6 +116,13 @@ def run_token_select(ssa, torch, cfg, q, k, v, steps):
     return res
 
 
+def sparse_flops(cfg, cnt) -> float:
+    """Algorithmic FLOPs of sparse-only attention: 4 D FLOPs (QK^T and PV) per
+    (query row, key) pair of the selected blocks, i.e. 4 D bs^2 per selected
+    (query block, key block) pair; cnt holds the list lengths."""
+    return 4.0 * cfg.D * cfg.block * cfg.block * float(cnt.sum())
+
+
 def prefill_flops(cfg) -> float:
     nkb = cfg.N // cfg.block
     pairs = nkb * (nkb + 1) // 2
@@ -198,8 +205,12 @@ def run_prefill(ssa, torch, cfg, steps, warmup, budgets):
                          sparse_only=True)
             sp.stop()
         torch.cuda.synchronize()
+        sp_flops = sparse_flops(cfg, cb)
         sweep[str(bgt)] = {"dual_attn_ms": round(tm.mean_ms(), 4),
                            "sparse_only_attn_ms": round(sp.mean_ms(), 4),
+                           "sparse_only_tflops": round(sp_flops / (sp.mean_ms() * 1e-3) / 1e12, 2),
+                           "sparse_only_mfma_frac": round(sp_flops / (sp.mean_ms() * 1e-3) / 1e12
+                                                          / MFMA_BF16_PEAK_TFLOPS, 4),
                            "delta_mean": round(float(out["delta"].mean()), 4)}
     res["sweep"] = sweep
     # group-shared selection (one list per GQA group) at the headline budget
@@ -261,6 +272,7 @@ def run_paper_shape(ssa, torch, cfg, steps):
            "attn_tflops": round(flops / (tatt.mean_ms() * 1e-3) / 1e12, 2),
            "attn_mfma_frac": round(flops / (tatt.mean_ms() * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
            "sparse_only_attn_ms": round(tsp.mean_ms(), 4),
+           "sparse_only_tflops": round(sparse_flops(cfg, cnt) / (tsp.mean_ms() * 1e-3) / 1e12, 2),
            "delta_mean": round(float(out["delta"].mean()), 4)}
     del out, ws
     torch.cuda.empty_cache()

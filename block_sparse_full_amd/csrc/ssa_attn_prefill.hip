@@ -1277,9 +1277,10 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
 #pragma unroll
     for (int v = 0; v < 16; ++v) { oa[i][v] = 0.f; os[i][v] = 0.f; }
   f32x16_t s0, s1;
-  uint32_t pw[16], pws[16];
+  uint32_t pw[16];      // P(e) as bf16 pairs; k-step s of the PV product is pw[4s .. 4s+3]
+  uint32_t qmask = 0u;  // the row's selected quarters of the tile pw belongs to
 #pragma unroll
-  for (int k = 0; k < 16; ++k) { pw[k] = 0u; pws[k] = 0u; }
+  for (int k = 0; k < 16; ++k) pw[k] = 0u;
   float m_ref = -INFINITY, l_sel = 0.f, l_drop = 0.f;
   const int pr = kperm32(c);
   const size_t plane = (size_t)d.B * d.Hq * d.Nq;
@@ -1329,8 +1330,11 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      // k-step s covers the tile's keys 16s .. 16s+15: quarter s
+      const uint32_t keep = ((qmask >> s) & 1u) ? 0xFFFFFFFFu : 0u;
       const uint4 w = make_uint4(pw[4 * s], pw[4 * s + 1], pw[4 * s + 2], pw[4 * s + 3]);
-      const uint4 ws = make_uint4(pws[4 * s], pws[4 * s + 1], pws[4 * s + 2], pws[4 * s + 3]);
+      const uint4 ws = make_uint4(pw[4 * s] & keep, pw[4 * s + 1] & keep, pw[4 * s + 2] & keep,
+                                  pw[4 * s + 3] & keep);
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, w);
       const bf16x8_t psb = __builtin_bit_cast(bf16x8_t, ws);
 #pragma unroll
@@ -1355,7 +1359,8 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
   auto softmax = [&](int e) __attribute__((always_inline)) {
     if (e >= n) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) { pw[k] = 0u; pws[k] = 0u; }
+      for (int k = 0; k < 16; ++k) pw[k] = 0u;
+      qmask = 0u;
       return;
     }
     const uint32_t nib = (sel16[hs][qbl][e >> 3] >> ((4 * e) & 31)) & 0xFu;
@@ -1382,28 +1387,28 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
       l_sel *= alpha;
       l_drop *= alpha;
     }
-    // row sums of all weights (l_all) and of the selected ones (l_sel), each
-    // one dot2 chain; the dropped mass is their difference at the end
-    float la = 0.f, ls = 0.f;
+    // row sums per quarter (one dot2 chain each): all weights go to l_all,
+    // the row's selected quarters to l_sel; the dropped mass is their
+    // difference at the end. Register v of s0 holds quarter v / 8, of s1
+    // quarter 2 + v / 8; pw[k] then belongs to quarter k / 4.
+    float qs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int v = 0; v < 16; v += 2) {
       const float a0 = fast_exp2(fmaf(s0[v], sl2, -m_ref));
       const float a1 = fast_exp2(fmaf(s0[v + 1], sl2, -m_ref));
       const float e0 = fast_exp2(fmaf(s1[v], sl2, -m_ref));
       const float e1 = fast_exp2(fmaf(s1[v + 1], sl2, -m_ref));
-      const bool q0 = (nib >> (v >> 3)) & 1u, q1 = (nib >> (2 + (v >> 3))) & 1u;
-      const uint32_t w0 = pack_bf16x2(a0, a1), w1 = pack_bf16x2(e0, e1);
-      pw[v >> 1] = w0;
-      pw[8 + (v >> 1)] = w1;
-      pws[v >> 1] = q0 ? w0 : 0u;
-      pws[8 + (v >> 1)] = q1 ? w1 : 0u;
-      la = add_bf16x2(w0, la);
-      la = add_bf16x2(w1, la);
-      ls = add_bf16x2(pws[v >> 1], ls);
-      ls = add_bf16x2(pws[8 + (v >> 1)], ls);
+      pw[v >> 1] = pack_bf16x2(a0, a1);
+      pw[8 + (v >> 1)] = pack_bf16x2(e0, e1);
+      qs[v >> 3] = add_bf16x2(pw[v >> 1], qs[v >> 3]);
+      qs[2 + (v >> 3)] = add_bf16x2(pw[8 + (v >> 1)], qs[2 + (v >> 3)]);
     }
+    float ls = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ls += ((nib >> u) & 1u) ? qs[u] : 0.f;
+    qmask = nib;
     l_sel += ls;
-    l_drop += la;   // running sum of all weights here; l_all - l_sel at the end
+    l_drop += (qs[0] + qs[1]) + (qs[2] + qs[3]);   // running sum of all weights; l_all - l_sel at the end
   };
   // Slots as in the kernel above: group A runs GEMM(t) in slot 2t and
   // softmax(t) in slot 2t+1, group B one slot later; each wave requests its

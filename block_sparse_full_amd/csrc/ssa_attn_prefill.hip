@@ -1155,7 +1155,7 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
 // are zero outside the row's quarters, so no branch touches the accumulators.
 //     h_full = o_all / (l_sel + l_drop),  h_sparse = o_sel / l_sel,
 //     delta = l_drop / (l_sel + l_drop).
-template <int NST>
+template <int NST, int TPE>
 __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vt, const int* __restrict__ idx, const int* __restrict__ cnt,
@@ -1173,8 +1173,11 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
   constexpr float kTau = 8.0f;
   constexpr int kWords16 = kMaxKeyBlocks / 32;
   static_assert(LPH == 1, "copy shape");
-  __shared__ __align__(16) uint16_t K0[TILE], K1[TILE], K2[TILE], K3[NST > 3 ? TILE : 8];
-  __shared__ __align__(16) uint16_t V0[TILE], V1[TILE], V2[TILE], V3[NST > 3 ? TILE : 8];
+  // each stage holds TPE consecutive 64-key tiles (one list entry)
+  __shared__ __align__(16) uint16_t K0[TPE * TILE], K1[TPE * TILE], K2[TPE * TILE],
+      K3[NST > 3 ? TPE * TILE : 8];
+  __shared__ __align__(16) uint16_t V0[TPE * TILE], V1[TPE * TILE], V2[TPE * TILE],
+      V3[NST > 3 ? TPE * TILE : 8];
   __shared__ uint32_t sel16[HPW][4][kWords16];   // per head and 16-row query block
 
   const int ngrp = d.G / HPW;
@@ -1200,7 +1203,8 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
   const int qbl = qq >> 4;               // the row's 16-row query block within the tile
   const int qrow = qt * kBlock + qq;
   const float sl2 = d.scale_log2;
-  const int n = qt + 1;                  // causal tiles
+  const int ntiles = qt + 1;             // causal tiles
+  const int n = (ntiles + TPE - 1) / TPE;   // entries of TPE tiles
 
   // ---- selection bitmaps of the four heads' four query blocks
   const int nwords16 = ((4 * qt + 3) >> 5) + 1;
@@ -1208,7 +1212,7 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
   {
     // GEMM(0) multiplies the V stage of the (absent) entry -1 by P = 0
     uint16_t* vz = (NST - 1) == 1 ? V1 : (NST - 1) == 2 ? V2 : V3;
-    for (int w = tid; w < TILE / 8; w += 64 * NW) ((uint4*)vz)[w] = make_uint4(0u, 0u, 0u, 0u);
+    for (int w = tid; w < TPE * TILE / 8; w += 64 * NW) ((uint4*)vz)[w] = make_uint4(0u, 0u, 0u, 0u);
   }
   __syncthreads();
   for (int u = 0; u < HPW; ++u) {
@@ -1233,18 +1237,24 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
   const uint32_t k_row_bytes = D * 2, v_row_bytes = (uint32_t)d.Nk * 2;
   // copies past the last tile repeat it: every slot issues the same number
   // of copies, so the waits are static
-  auto tile_c = [&](int e) __attribute__((always_inline)) { return min(e, n - 1); };
-  auto load_k_kb = [&](auto stc, int kb) __attribute__((always_inline)) {
+  auto tile_c = [&](int t) __attribute__((always_inline)) { return min(t, ntiles - 1); };
+  // the TPE tiles of entry e into a stage
+  auto load_k_e = [&](auto stc, int e) __attribute__((always_inline)) {
     constexpr int st = decltype(stc)::value;
     uint16_t* kt = st == 0 ? K0 : st == 1 ? K1 : st == 2 ? K2 : K3;
-    tile_to_lds_asm<KSPR, kBlock, NW, true>(krs, (uint32_t)kb * kBlock * k_row_bytes,
-                                           k_row_bytes, kt, wave, lane);
+#pragma unroll
+    for (int tt = 0; tt < TPE; ++tt)
+      tile_to_lds_asm<KSPR, kBlock, NW, true>(
+          krs, (uint32_t)tile_c(TPE * e + tt) * kBlock * k_row_bytes, k_row_bytes,
+          kt + tt * TILE, wave, lane);
   };
-  auto load_v_kb = [&](auto stc, int kb) __attribute__((always_inline)) {
+  auto load_v_e = [&](auto stc, int e) __attribute__((always_inline)) {
     constexpr int st = decltype(stc)::value;
     uint16_t* vt = st == 0 ? V0 : st == 1 ? V1 : st == 2 ? V2 : V3;
-    tile_to_lds_asm<VSPR, D, NW, false>(vrs, (uint32_t)kb * kBlock * 2, v_row_bytes, vt,
-                                       wave, lane);
+#pragma unroll
+    for (int tt = 0; tt < TPE; ++tt)
+      tile_to_lds_asm<VSPR, D, NW, false>(vrs, (uint32_t)tile_c(TPE * e + tt) * kBlock * 2,
+                                         v_row_bytes, vt + tt * TILE, wave, lane);
   };
 
   using I0 = std::integral_constant<int, 0>;
@@ -1262,13 +1272,13 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
   __builtin_amdgcn_s_waitcnt(0xF70);
   // prologue = the copies of the virtual slots before slot 0: K(0..NST-2)
   // and V(0..NST-3), with V(0) standing in for the missing V(-1)
-  load_k_kb(I0{}, tile_c(0));
-  load_v_kb(I0{}, tile_c(0));
-  load_k_kb(I1{}, tile_c(1));
-  load_v_kb(I0{}, tile_c(0));
+  load_k_e(I0{}, 0);
+  load_v_e(I0{}, 0);
+  load_k_e(I1{}, 1);
+  load_v_e(I0{}, 0);
   if constexpr (NST > 3) {
-    load_k_kb(I2{}, tile_c(2));
-    load_v_kb(I1{}, tile_c(1));
+    load_k_e(I2{}, 2);
+    load_v_e(I1{}, 1);
   }
 
   f32x16_t oa[NDT], os[NDT];
@@ -1276,11 +1286,13 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
   for (int i = 0; i < NDT; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) { oa[i][v] = 0.f; os[i][v] = 0.f; }
-  f32x16_t s0, s1;
-  uint32_t pw[16];      // P(e) as bf16 pairs; k-step s of the PV product is pw[4s .. 4s+3]
-  uint32_t qmask = 0u;  // the row's selected quarters of the tile pw belongs to
+  f32x16_t sc[TPE][2];      // S^T of the entry's tiles (keys 0-31, 32-63 of each)
+  uint32_t pw[TPE][16];     // P as bf16 pairs; k-step s of tile tt's PV is pw[tt][4s .. 4s+3]
+  uint32_t qmask = 0u;      // the row's selected quarters: 4 bits per tile of the entry pw holds
 #pragma unroll
-  for (int k = 0; k < 16; ++k) pw[k] = 0u;
+  for (int tt = 0; tt < TPE; ++tt)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) pw[tt][k] = 0u;
   float m_ref = -INFINITY, l_sel = 0.f, l_drop = 0.f;
   const int pr = kperm32(c);
   const size_t plane = (size_t)d.B * d.Hq * d.Nq;
@@ -1301,51 +1313,70 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
 
   // GEMM(e) = 8 MFMAs S(e) = K(e) Q^T plus 2 x 8 MFMAs O_all += V(e-1) P(e-1)
   // and O_sel += V(e-1) P_sel(e-1) on the same V^T fragments.
+  // GEMM(e) = per tile 8 MFMAs S = K Q^T, plus per tile of entry e-1 2 x 8
+  // MFMAs O_all += V P and O_sel += V P_sel on the same V^T fragments.
   auto gemm = [&](auto stc) __attribute__((always_inline)) {
     constexpr int sk = decltype(stc)::value;
     constexpr int sv = (sk + NST - 1) % NST;
     constexpr int PF = 4;
+    constexpr int RK = 2 * NKS, RV = 4 * NDT;   // fragment reads per tile
     const uint16_t* Kt = sk == 0 ? K0 : sk == 1 ? K1 : sk == 2 ? K2 : K3;
     const uint16_t* Vtl = sv == 0 ? V0 : sv == 1 ? V1 : sv == 2 ? V2 : V3;
-    bf16x8_t fr[2 * NKS + 4 * NDT];
+    bf16x8_t fr[TPE * (RK + RV)];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int ch = 2 * ks + gl;
-      fr[2 * ks] = *(const bf16x8_t*)(Kt + (pr * KSPR + vswz(pr, ch)) * 8);
-      fr[2 * ks + 1] = *(const bf16x8_t*)(Kt + ((32 + pr) * KSPR + vswz(32 + pr, ch)) * 8);
-    }
+    for (int tt = 0; tt < TPE; ++tt) {
+      const uint16_t* kt = Kt + tt * TILE;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int r = 32 * dt + c;
-        fr[2 * NKS + s * NDT + dt] = *(const bf16x8_t*)(Vtl + (r * VSPR + vswz(r, 2 * s + gl)) * 8);
-      }
-#pragma unroll
-    for (int v = 0; v < 16; ++v) { s0[v] = 0.f; s1[v] = 0.f; }
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[2 * ks], qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[2 * ks + 1], qf[ks], s1, 0, 0, 0);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      // k-step s covers the tile's keys 16s .. 16s+15: quarter s
-      const uint32_t keep = ((qmask >> s) & 1u) ? 0xFFFFFFFFu : 0u;
-      const uint4 w = make_uint4(pw[4 * s], pw[4 * s + 1], pw[4 * s + 2], pw[4 * s + 3]);
-      const uint4 ws = make_uint4(pw[4 * s] & keep, pw[4 * s + 1] & keep, pw[4 * s + 2] & keep,
-                                  pw[4 * s + 3] & keep);
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, w);
-      const bf16x8_t psb = __builtin_bit_cast(bf16x8_t, ws);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        oa[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[2 * NKS + s * NDT + dt], pb, oa[dt], 0, 0, 0);
-        os[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[2 * NKS + s * NDT + dt], psb, os[dt], 0, 0, 0);
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int ch = 2 * ks + gl;
+        fr[tt * RK + 2 * ks] = *(const bf16x8_t*)(kt + (pr * KSPR + vswz(pr, ch)) * 8);
+        fr[tt * RK + 2 * ks + 1] = *(const bf16x8_t*)(kt + ((32 + pr) * KSPR + vswz(32 + pr, ch)) * 8);
       }
     }
+#pragma unroll
+    for (int tt = 0; tt < TPE; ++tt) {
+      const uint16_t* vt = Vtl + tt * TILE;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int r = 32 * dt + c;
+          fr[TPE * RK + tt * RV + s * NDT + dt] =
+              *(const bf16x8_t*)(vt + (r * VSPR + vswz(r, 2 * s + gl)) * 8);
+        }
+    }
+#pragma unroll
+    for (int tt = 0; tt < TPE; ++tt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) { sc[tt][0][v] = 0.f; sc[tt][1][v] = 0.f; }
+#pragma unroll
+    for (int tt = 0; tt < TPE; ++tt)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        sc[tt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[tt * RK + 2 * ks], qf[ks], sc[tt][0], 0, 0, 0);
+        sc[tt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[tt * RK + 2 * ks + 1], qf[ks], sc[tt][1], 0, 0, 0);
+      }
+#pragma unroll
+    for (int tt = 0; tt < TPE; ++tt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        // k-step s of tile tt covers its keys 16s .. 16s+15: quarter 4*tt + s
+        const uint32_t keep = ((qmask >> (4 * tt + s)) & 1u) ? 0xFFFFFFFFu : 0u;
+        const uint4 w = make_uint4(pw[tt][4 * s], pw[tt][4 * s + 1], pw[tt][4 * s + 2], pw[tt][4 * s + 3]);
+        const uint4 ws = make_uint4(pw[tt][4 * s] & keep, pw[tt][4 * s + 1] & keep,
+                                    pw[tt][4 * s + 2] & keep, pw[tt][4 * s + 3] & keep);
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, w);
+        const bf16x8_t psb = __builtin_bit_cast(bf16x8_t, ws);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const bf16x8_t vf = fr[TPE * RK + tt * RV + s * NDT + dt];
+          oa[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, oa[dt], 0, 0, 0);
+          os[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, psb, os[dt], 0, 0, 0);
+        }
+      }
     // schedule: PF reads, then MFMAs interleaved with the remaining reads
-    constexpr int NR = 2 * NKS + 4 * NDT;    // 16 fragment reads
-    constexpr int NM = 2 * NKS + 8 * NDT;    // 24 MFMAs
+    constexpr int NR = TPE * (RK + RV);
+    constexpr int NM = TPE * (2 * NKS + 8 * NDT);
     __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
 #pragma unroll
     for (int k = 0; k < NR - PF; ++k) {
@@ -1354,27 +1385,37 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
     }
     __builtin_amdgcn_sched_group_barrier(0x008, NM - (NR - PF), 0);
   };
-  // softmax(e): P(e) and P_sel(e) from S(e); the row's selected quarters of
-  // tile e, quarter of register v: v / 8 (s0) and 2 + v / 8 (s1)
+  // softmax(e): P of the entry's tiles from S; per tile the row's selected
+  // quarters; register v of sc[tt][0] holds quarter v / 8, of sc[tt][1]
+  // quarter 2 + v / 8 (kperm32 order), so pw[tt][k] belongs to quarter k / 4
   auto softmax = [&](int e) __attribute__((always_inline)) {
     if (e >= n) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) pw[k] = 0u;
+      for (int tt = 0; tt < TPE; ++tt)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) pw[tt][k] = 0u;
       qmask = 0u;
       return;
     }
-    const uint32_t nib = (sel16[hs][qbl][e >> 3] >> ((4 * e) & 31)) & 0xFu;
-    if (e == qt) {
+    uint32_t nibs = 0u;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key0 = 16 * (v >> 3) + 8 * gl + (v & 7);
-        if (key0 > qq) s0[v] = -INFINITY;
-        if (key0 + 32 > qq) s1[v] = -INFINITY;
+    for (int tt = 0; tt < TPE; ++tt) {
+      const int t = TPE * e + tt;
+      if (t <= qt) nibs |= ((sel16[hs][qbl][t >> 3] >> ((4 * t) & 31)) & 0xFu) << (4 * tt);
+      if (t >= qt) {   // the diagonal tile: key <= row; tiles past it: nothing
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key0 = 16 * (v >> 3) + 8 * gl + (v & 7);
+          if (t > qt || key0 > qq) sc[tt][0][v] = -INFINITY;
+          if (t > qt || key0 + 32 > qq) sc[tt][1][v] = -INFINITY;
+        }
       }
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
+    for (int tt = 0; tt < TPE; ++tt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, fmaxf(sc[tt][0][v], sc[tt][1][v]));
     const float m_blk = pair_max(mx) * sl2;
     if (__builtin_amdgcn_ballot_w64(m_blk > m_ref + kTau) != 0) {
       const float m_new = fmaxf(m_ref, m_blk);
@@ -1389,40 +1430,46 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
     }
     // row sums per quarter (one dot2 chain each): all weights go to l_all,
     // the row's selected quarters to l_sel; the dropped mass is their
-    // difference at the end. Register v of s0 holds quarter v / 8, of s1
-    // quarter 2 + v / 8; pw[k] then belongs to quarter k / 4.
-    float qs[4] = {0.f, 0.f, 0.f, 0.f};
+    // difference at the end
+    float qs[4 * TPE];
 #pragma unroll
-    for (int v = 0; v < 16; v += 2) {
-      const float a0 = fast_exp2(fmaf(s0[v], sl2, -m_ref));
-      const float a1 = fast_exp2(fmaf(s0[v + 1], sl2, -m_ref));
-      const float e0 = fast_exp2(fmaf(s1[v], sl2, -m_ref));
-      const float e1 = fast_exp2(fmaf(s1[v + 1], sl2, -m_ref));
-      pw[v >> 1] = pack_bf16x2(a0, a1);
-      pw[8 + (v >> 1)] = pack_bf16x2(e0, e1);
-      qs[v >> 3] = add_bf16x2(pw[v >> 1], qs[v >> 3]);
-      qs[2 + (v >> 3)] = add_bf16x2(pw[8 + (v >> 1)], qs[2 + (v >> 3)]);
+    for (int u = 0; u < 4 * TPE; ++u) qs[u] = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < TPE; ++tt)
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const float a0 = fast_exp2(fmaf(sc[tt][0][v], sl2, -m_ref));
+        const float a1 = fast_exp2(fmaf(sc[tt][0][v + 1], sl2, -m_ref));
+        const float e0 = fast_exp2(fmaf(sc[tt][1][v], sl2, -m_ref));
+        const float e1 = fast_exp2(fmaf(sc[tt][1][v + 1], sl2, -m_ref));
+        pw[tt][v >> 1] = pack_bf16x2(a0, a1);
+        pw[tt][8 + (v >> 1)] = pack_bf16x2(e0, e1);
+        qs[4 * tt + (v >> 3)] = add_bf16x2(pw[tt][v >> 1], qs[4 * tt + (v >> 3)]);
+        qs[4 * tt + 2 + (v >> 3)] = add_bf16x2(pw[tt][8 + (v >> 1)], qs[4 * tt + 2 + (v >> 3)]);
+      }
+    float ls = 0.f, la = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4 * TPE; ++u) {
+      ls += ((nibs >> u) & 1u) ? qs[u] : 0.f;
+      la += qs[u];
     }
-    float ls = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) ls += ((nib >> u) & 1u) ? qs[u] : 0.f;
-    qmask = nib;
+    qmask = nibs;
     l_sel += ls;
-    l_drop += (qs[0] + qs[1]) + (qs[2] + qs[3]);   // running sum of all weights; l_all - l_sel at the end
+    l_drop += la;   // running sum of all weights; l_all - l_sel at the end
   };
   // Slots as in the kernel above: group A runs GEMM(t) in slot 2t and
   // softmax(t) in slot 2t+1, group B one slot later; each wave requests its
   // share of K(t+NST-1) and V(t+NST-2) after its GEMM(t).
-  auto issue_tiles = [&](auto stc, int kbk, int kbv) __attribute__((always_inline)) {
+  auto issue_tiles = [&](auto stc, int t) __attribute__((always_inline)) {
     constexpr int st = decltype(stc)::value;
-    load_k_kb(std::integral_constant<int, (st + NST - 1) % NST>{}, kbk);
-    load_v_kb(std::integral_constant<int, (st + NST - 2) % NST>{}, kbv);
+    load_k_e(std::integral_constant<int, (st + NST - 1) % NST>{}, t + NST - 1);
+    load_v_e(std::integral_constant<int, (st + NST - 2) % NST>{}, t + NST - 2);
   };
   auto slot_barrier = [&]() __attribute__((always_inline)) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  constexpr int kWaitA = 0xF70 | (2 * LPH * (NST - 2));
-  constexpr int kWaitB = 0xF70 | (2 * LPH * (NST - 3));
+  constexpr int kWaitA = 0xF70 | (2 * LPH * TPE * (NST - 2));
+  constexpr int kWaitB = 0xF70 | (2 * LPH * TPE * (NST - 3));
   if (!group_a) {
     __builtin_amdgcn_s_waitcnt(kWaitA);
     slot_barrier();
@@ -1434,7 +1481,7 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
     __builtin_amdgcn_s_setprio(1);
     gemm(stc);
     __builtin_amdgcn_s_setprio(0);
-    issue_tiles(stc, tile_c(t + NST - 1), tile_c(t + NST - 2));
+    issue_tiles(stc, t);
     slot_barrier();
     softmax(t);
   };
@@ -1485,8 +1532,8 @@ hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const 
   if (d.bs == 16 && d.D == 64 && d.G % 4 == 0 && hf != nullptr) {
     // dual mode, four q heads per workgroup
     const int groups = d.B * d.Hkv * (d.G / 4) * d.nQT;
-    hipLaunchKernelGGL((attn_prefill_bf16_pp16_kernel<3>), dim3(groups), dim3(512), 0, stream, q,
-                       k, vt, idx, cnt, hf, hs, delta, lse, d, hm);
+    hipLaunchKernelGGL((attn_prefill_bf16_pp16_kernel<3, 2>), dim3(groups), dim3(512), 0, stream,
+                       q, k, vt, idx, cnt, hf, hs, delta, lse, d, hm);
     return hipGetLastError();
   }
   if (d.bs == 16) {

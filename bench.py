@@ -274,7 +274,25 @@ def run_paper_shape(ssa, torch, cfg, steps):
            "sparse_only_attn_ms": round(tsp.mean_ms(), 4),
            "sparse_only_tflops": round(sparse_flops(cfg, cnt) / (tsp.mean_ms() * 1e-3) / 1e12, 2),
            "delta_mean": round(float(out["delta"].mean()), 4)}
-    del out, ws
+    # backward of both streams on this shape (seeded upstream gradients)
+    from ssa_inputs import make_grads
+    gr = make_grads(cfg, workers=16)
+    gf, gs = gr["d_full"].to(dev), gr["d_sparse"].to(dev)
+    del gr
+    fwd = ssa.attn_fwd(p, q, k, v, idx, cnt, want_lse=True, ws=ws)
+    bws = ssa.alloc_bwd_workspace(p, dev)
+    kw = dict(h_full=fwd["h_full"], h_sparse=fwd["h_sparse"], d_full=gf, d_sparse=gs)
+    bo = ssa.attn_bwd(p, q, k, v, idx, cnt, fwd["lse"], ws=bws, **kw)
+    tb = EventTimer(torch)
+    for _ in range(max(3, steps // 4)):
+        tb.start()
+        ssa.attn_bwd(p, q, k, v, idx, cnt, fwd["lse"], ws=bws, out=bo, **kw)
+        tb.stop()
+    torch.cuda.synchronize()
+    bflops = 2.5 * flops + sparse_flops(cfg, cnt)   # 5 products per causal pair, 2 per selected
+    res["backward_dual_ms"] = round(tb.mean_ms(), 4)
+    res["backward_dual_tflops"] = round(bflops / (tb.mean_ms() * 1e-3) / 1e12, 2)
+    del out, ws, fwd, bws, bo, gf, gs
     torch.cuda.empty_cache()
     res["token_select"] = run_token_select(ssa, torch, cfg, q, k, v, steps)
     del q, k, v

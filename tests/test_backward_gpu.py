@@ -154,6 +154,19 @@ def test_backward_full_budget_streams_agree(ssa):
         assert err <= 1e-2 * np.abs(ref).max(), (n, err)
 
 
+@pytest.mark.parametrize("kw", [dict(), dict(token_select=True)], ids=["per_block", "per_token"])
+def test_backward_determinism(ssa, kw):
+    """dK and dV sum the q heads of a group and the two streams in a fixed
+    order (no atomics): two calls give identical bits."""
+    cfg = CONFIGS["gqa_8k_peaked"].with_sizes(B=1, Hq=8, Hkv=2, N=1024)
+    x = make_inputs(cfg)
+    grads = make_grads(cfg)
+    a = gpu_bwd(ssa, cfg, x, grads, budget=4, **kw)
+    b = gpu_bwd(ssa, cfg, x, grads, budget=4, **kw)
+    for name in ("dq", "dk", "dv"):
+        assert torch.equal(a[name], b[name]), name
+
+
 @pytest.mark.parametrize("token_select", [False, True], ids=["per_block", "per_token"])
 def test_backward_full_size_gqa_32k(ssa, token_select):
     """The 32K GQA workload (budget 16, planted blocks) at full size: dq on

@@ -196,11 +196,22 @@ def test_block16_group_select(ssa):
     full_compare(cfg, x, got, budget=16, lse=True, group_select=True)
 
 
-def test_run_to_run_determinism(ssa):
-    cfg = CONFIGS["gqa_8k_peaked"].with_sizes(B=1, Hq=8, Hkv=2, N=2048, budget=6)
+DETERMINISM = [
+    ("gqa_8k_peaked", dict(B=1, Hq=8, Hkv=2, N=2048, budget=6), dict()),
+    ("paper_16k_b16", dict(Hq=8, Hkv=2, N=2048, budget=16), dict(block=16)),
+    ("gqa_8k_peaked", dict(B=1, Hq=8, Hkv=2, N=2048, budget=6), dict(token_select=True)),
+    ("gqa_8k_peaked", dict(B=1, Hq=8, Hkv=2, N=2048, budget=6), dict(group_select=True)),
+]
+
+
+@pytest.mark.parametrize("name,kw,run", DETERMINISM, ids=["per_head", "block16", "per_token", "group"])
+def test_run_to_run_determinism(ssa, name, kw, run):
+    """Two calls on the same inputs give identical bits (fixed-order
+    reductions everywhere)."""
+    cfg = CONFIGS[name].with_sizes(**kw)
     x = make_inputs(cfg)
-    a = gpu_run(ssa, x, budget=6, want_lse=True)
-    b = gpu_run(ssa, x, budget=6, want_lse=True)
+    a = gpu_run(ssa, x, budget=cfg.budget, want_lse=True, **run)
+    b = gpu_run(ssa, x, budget=cfg.budget, want_lse=True, **run)
     for key in ("idx", "cnt", "h_full", "h_sparse", "delta", "loss", "lse"):
         assert torch.equal(a[key], b[key]), key
 

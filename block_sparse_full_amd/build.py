@@ -1,6 +1,8 @@
 """Build the SSA HIP library (libssa.so) for gfx950 with hipcc.
 
 Usage: python -m block_sparse_full_amd.build   (or call build_library()).
+       python -m block_sparse_full_amd.build --host-asan   (C-ABI host code
+       under AddressSanitizer, for the host sanitizer test)
 Objects go to _build/ at the repository root; the shared library lands next
 to this file, where the Python binding loads it.
 """
@@ -67,5 +69,47 @@ def build_library(verbose: bool = False, extra_flags=()) -> str:
     return LIB
 
 
+def build_host_asan_library(verbose: bool = False) -> str:
+    """libssa_asan.so under _build/asan: the C-ABI layer (argument checks,
+    workspace sizing, layout arithmetic, error strings) compiled with
+    AddressSanitizer on its host pass only, linked with the ordinary kernel
+    objects. GPU code is never instrumented. Load it in a process that has the
+    clang ASan runtime preloaded."""
+    cc = hipcc()
+    if not all(os.path.exists(os.path.join(BUILD, os.path.splitext(s)[0] + ".o"))
+               for s in SOURCES):
+        build_library(verbose=verbose)
+    out_dir = os.path.join(BUILD, "asan")
+    os.makedirs(out_dir, exist_ok=True)
+    api = "ssa_api.hip"
+    obj = os.path.join(out_dir, "ssa_api.o")
+    err = _run([cc, *CFLAGS, "-O1", "-g", "-Xarch_host", "-fsanitize=address",
+                "-Xarch_host", "-fno-omit-frame-pointer", "-c", os.path.join(CSRC, api), "-o", obj])
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    objs = [obj] + [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != api]
+    lib = os.path.join(out_dir, "libssa_asan.so")
+    tmp = lib + ".tmp"
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
+    os.replace(tmp, lib)
+    return lib
+
+
+def asan_runtime() -> str | None:
+    """Path of the clang ASan runtime that matches hipcc's host compiler."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    for c in (clang, shutil.which("clang")):
+        if c and os.path.exists(c):
+            r = subprocess.run([c, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                               capture_output=True, text=True)
+            path = r.stdout.strip()
+            if r.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+                return path
+    return None
+
+
 if __name__ == "__main__":
-    print(build_library(verbose="-v" in sys.argv))
+    if "--host-asan" in sys.argv:
+        print(build_host_asan_library(verbose="-v" in sys.argv))
+    else:
+        print(build_library(verbose="-v" in sys.argv))

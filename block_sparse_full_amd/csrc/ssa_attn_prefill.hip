@@ -717,6 +717,8 @@ __device__ __forceinline__ int kperm32(int c) {
 // 256-byte K rows: the 16 rows one ds_read_b128 phase touches have distinct
 // low four bits, so chunk ^ (row & 15) spreads them over all bank groups.
 __device__ __forceinline__ int kswz32(int row, int chunk) { return chunk ^ (row & 15); }
+// Maximum of three floats; a chain of these becomes v_max3_f32 operations.
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 __device__ __forceinline__ float pair_max(float x) {
   const unsigned u = __float_as_uint(x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
@@ -1047,10 +1049,14 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
         if (key0 + 32 > qq) s1[v] = -INFINITY;
       }
     }
-    float mx = -INFINITY;
+    // two chains of three-input maxima: 17 VALU operations for the 32 logits
+    float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
-    const float m_blk = pair_max(mx) * sl2;
+    for (int v = 0; v < 16; v += 2) {
+      mx0 = max3f(mx0, s0[v], s1[v]);
+      mx1 = max3f(mx1, s0[v + 1], s1[v + 1]);
+    }
+    const float m_blk = pair_max(fmaxf(mx0, mx1)) * sl2;
     if (__builtin_amdgcn_ballot_w64(m_blk > m_ref + kTau) != 0) {
       const float m_new = fmaxf(m_ref, m_blk);
       const float alpha = fast_exp2(m_ref - m_new);
@@ -1411,12 +1417,15 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
         }
       }
     }
-    float mx = -INFINITY;
+    float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
     for (int tt = 0; tt < TPE; ++tt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, fmaxf(sc[tt][0][v], sc[tt][1][v]));
-    const float m_blk = pair_max(mx) * sl2;
+      for (int v = 0; v < 16; v += 2) {
+        mx0 = max3f(mx0, sc[tt][0][v], sc[tt][1][v]);
+        mx1 = max3f(mx1, sc[tt][0][v + 1], sc[tt][1][v + 1]);
+      }
+    const float m_blk = pair_max(fmaxf(mx0, mx1)) * sl2;
     if (__builtin_amdgcn_ballot_w64(m_blk > m_ref + kTau) != 0) {
       const float m_new = fmaxf(m_ref, m_blk);
       const float alpha = fast_exp2(m_ref - m_new);

@@ -223,17 +223,25 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
           const int incl = wave_incl_scan(csum);
           const int excl = incl - csum;
           const bool mine = excl < k && k <= incl;
-          int bin = top, rest = k - excl;
-          if (rest > c0) { rest -= c0; bin = top - 1;
-            if (rest > c1) { rest -= c1; bin = top - 2;
-              if (rest > c2) { rest -= c2; bin = top - 3; } } }
+          int bin = top, rest = k - excl, cbin = c0;
+          if (rest > c0) { rest -= c0; bin = top - 1; cbin = c1;
+            if (rest > c1) { rest -= c1; bin = top - 2; cbin = c2;
+              if (rest > c2) { rest -= c2; bin = top - 3; cbin = c3; } } }
           const uint64_t ball = __builtin_amdgcn_ballot_w64(mine);
           const int src = ball ? __builtin_ctzll(ball) : 0;   // ball != 0 always
           const int sbin = __builtin_amdgcn_readlane(bin, src);
+          const int scnt = __builtin_amdgcn_readlane(cbin, src);
           k = __builtin_amdgcn_readlane(rest, src);
           prefix |= (uint64_t)sbin << shift;
           pmask |= 0xFFull << shift;
           wave_lds_fence();
+          // every remaining key of the chosen bin is taken: the selected keys
+          // are exactly those >= prefix, and the lower digits need no pass
+          if (scnt == k && prefix != 0ull) {
+            prefix -= 1ull;
+            k = 0;
+            break;
+          }
         }
         thr = prefix;
         k_eq = k;

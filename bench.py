@@ -124,6 +124,9 @@ def sparse_flops(cfg, cnt) -> float:
 
 
 def prefill_flops(cfg) -> float:
+    """Algorithmic FLOPs of one dual-stream prefill: QK^T and PV over the
+    causal set, 4 D bs^2 per (query block, causal key block) pair; the sparse
+    stream reuses those products."""
     nkb = cfg.N // cfg.block
     pairs = nkb * (nkb + 1) // 2
     return 4.0 * cfg.D * cfg.block * cfg.block * pairs * cfg.B * cfg.Hq
@@ -264,8 +267,7 @@ def run_paper_shape(ssa, torch, cfg, steps):
                      sparse_only=True)
         tsp.stop()
     torch.cuda.synchronize()
-    tiles = cfg.N // 64
-    flops = 4.0 * cfg.D * 64 * 64 * (tiles * (tiles + 1) / 2) * cfg.B * cfg.Hq
+    flops = prefill_flops(cfg)
     res = {"workload": f"paper shape prefill: B {cfg.B}, {cfg.Hq} q heads / {cfg.Hkv} kv heads, "
                        f"N {cfg.N}, D {cfg.D}, block {cfg.block}, budget {cfg.budget}",
            "select_ms": round(tsel.mean_ms(), 4), "dual_attn_ms": round(tatt.mean_ms(), 4),
@@ -296,6 +298,42 @@ def run_paper_shape(ssa, torch, cfg, steps):
     torch.cuda.empty_cache()
     res["token_select"] = run_token_select(ssa, torch, cfg, q, k, v, steps)
     del q, k, v
+    torch.cuda.empty_cache()
+    res["gqa_16to1"] = run_paper_fwd(ssa, torch, cfg.with_sizes(Hq=16, Hkv=1), steps)
+    return res
+
+
+def run_paper_fwd(ssa, torch, cfg, steps):
+    """Dual-mode and sparse-only forward time of a 16-token-block shape."""
+    from ssa_inputs import make_inputs
+    dev = torch.device("cuda:0")
+    x = make_inputs(cfg, workers=16)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    del x
+    p = ssa.problem_for(q, k, budget=cfg.budget, n_sink=cfg.n_sink, n_local=cfg.n_local,
+                        block_size=cfg.block)
+    ws = ssa.alloc_workspace(p, dev)
+    idx, cnt = ssa.select_blocks(p, q, k, ws=ws)
+    out = ssa.attn_fwd(p, q, k, v, idx, cnt, ws=ws)
+    tatt, tsp = EventTimer(torch), EventTimer(torch)
+    for _ in range(max(3, steps // 2)):
+        tatt.start()
+        ssa.attn_fwd(p, q, k, v, idx, cnt, ws=ws, out=out)
+        tatt.stop()
+        tsp.start()
+        ssa.attn_fwd(p, q, k, v, idx, cnt, ws=ws, out={"h_sparse": out["h_sparse"]},
+                     sparse_only=True)
+        tsp.stop()
+    torch.cuda.synchronize()
+    flops = prefill_flops(cfg)
+    res = {"workload": f"B {cfg.B}, {cfg.Hq} q heads / {cfg.Hkv} kv head(s), N {cfg.N}, D {cfg.D}, "
+                       f"block {cfg.block}, budget {cfg.budget}",
+           "dual_attn_ms": round(tatt.mean_ms(), 4),
+           "attn_tflops": round(flops / (tatt.mean_ms() * 1e-3) / 1e12, 2),
+           "attn_mfma_frac": round(flops / (tatt.mean_ms() * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "sparse_only_attn_ms": round(tsp.mean_ms(), 4),
+           "delta_mean": round(float(out["delta"].mean()), 4)}
+    del q, k, v, out, ws, idx, cnt
     torch.cuda.empty_cache()
     return res
 

@@ -169,6 +169,8 @@ BLOCK16 = [
     ("paper_16k_b16", dict(B=2, Hq=32, Hkv=2, N=512), 16, 1, 1, False),
     ("paper_16k_b16", dict(Hq=4, Hkv=2, N=2048, planted=False), 12, 2, 2, False),
     ("paper_16k_b16", dict(Hq=4, Hkv=1, N=1024, D=128), 16, 1, 1, True),
+    # 16 q heads on one kv head: four four-head workgroups share each kv head
+    ("paper_16k_b16", dict(Hq=16, Hkv=1, N=1536), 16, 1, 1, False),
     ("paper_16k_b16", dict(decode=True, B=3, Hq=8, Hkv=2, N=2048), 16, 1, 1, False),
     ("paper_16k_b16", dict(decode=True, B=2, Hq=4, Hkv=1, N=4096, D=128), 9, 1, 1, False),
     # decode with 16 q heads per kv head (two workgroups of 8 per group)

@@ -37,7 +37,7 @@ struct Problem {
 };
 
 struct Layout {
-  size_t qbar, kbar, kc, vt, partials, loss, total;
+  size_t qbar, kbar, kc, vt, queues, partials, loss, total;
 };
 
 Layout layout_of(const Problem& P) {
@@ -52,6 +52,8 @@ Layout layout_of(const Problem& P) {
   if (d.tok) off += align256(ssa::tok_kc_bytes(d));
   L.vt = off;
   if (P.bf16 && !P.decode) off += align256((size_t)d.B * d.Hkv * d.D * d.Nk * sizeof(uint16_t));
+  L.queues = off;   // prefill work queues, zeroed by the V transpose of every call
+  if (P.bf16 && !P.decode) off += align256((size_t)ssa::kNumXcd * ssa::kQueueStride * sizeof(int));
   L.partials = off;
   if (P.bf16 && P.decode) {
     int ns = ssa::decode_splits(d.nT);
@@ -302,11 +304,12 @@ ssa_status ssa_attn_fwd(const ssa_problem* p, const void* q, const void* k, cons
                                                    lse, (float*)(w + L.partials), d, P.hm, st),
                       "attention (decode)");
   uint16_t* vt = (uint16_t*)(w + L.vt);
-  hipError_t e = ssa::launch_transpose((const uint16_t*)v, vt, d.B * d.Hkv, d.Nk, d.D, st);
+  int* queues = (int*)(w + L.queues);
+  hipError_t e = ssa::launch_transpose((const uint16_t*)v, vt, d.B * d.Hkv, d.Nk, d.D, queues, st);
   if (e != hipSuccess) return hip_status(e, "transpose v");
   return hip_status(ssa::launch_attn_prefill_bf16((const uint16_t*)q, (const uint16_t*)k, vt, idx,
                                                   cnt, (uint16_t*)h_full, (uint16_t*)h_sparse,
-                                                  delta, lse, d, P.hm, st),
+                                                  delta, lse, queues, d, P.hm, st),
                     "attention (prefill)");
 }
 

@@ -23,6 +23,7 @@
 #include "ssa_device.h"
 #include "ssa_kernels.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace ssa {
@@ -771,12 +772,26 @@ __device__ __forceinline__ void tile_to_lds_asm(i32x4_t rsrc, uint32_t tile_off,
 // work overlaps the other wave's VALU work. K/V tiles live in NST LDS
 // stages; after its GEMM(e) each wave requests its share of K(e+NST-1) and
 // V(e+NST-2).
+// Takes the next work item for this workgroup: the queues hold items
+// [x * per, (x + 1) * per) for XCD x, in that order (the static mapping of
+// xcd_remap); a workgroup first draws from its own XCD's queue, then from the
+// others. With exactly one workgroup per item every workgroup gets one.
+__device__ __forceinline__ int fetch_work_item(int* queues, int per) {
+  unsigned xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  for (int j = 0; j < kNumXcd; ++j) {
+    const int x = (int)((xcc + j) % kNumXcd);
+    const int i = atomicAdd(&queues[x * kQueueStride], 1);
+    if (i < per) return x * per + i;
+  }
+  return -1;
+}
 template <int D, int NST>
 __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vt, const int* __restrict__ idx, const int* __restrict__ cnt,
     uint16_t* __restrict__ Hf, uint16_t* __restrict__ Hs, float* __restrict__ delta,
-    float* __restrict__ lse, Dims d, HeadMap hm) {
+    float* __restrict__ lse, int* __restrict__ queues, Dims d, HeadMap hm) {
   constexpr int HPW = 4;
   constexpr int NW = 8;
   constexpr int KSPR = D / 8;
@@ -798,7 +813,24 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
 
   const int ngrp = d.G / HPW;
   const int total = d.B * d.Hkv * ngrp * d.nQB;
-  const int lin = xcd_remap(blockIdx.x, total);
+  // Work items: with queues the grid is one workgroup per CU and each
+  // workgroup takes items until every queue is empty, first from its own
+  // XCD's queue, then from the others' (an XCD that runs ahead takes over the
+  // short tail items of a slower one); without queues one item per workgroup
+  // in the static mapping.
+  __shared__ int s_item;
+  const bool dyn = queues != nullptr && total % kNumXcd == 0;
+  for (int pass = 0;; ++pass) {
+  if (dyn) {
+    __syncthreads();   // the previous item no longer reads LDS or s_item
+    if (threadIdx.x == 0) s_item = fetch_work_item(queues, total / kNumXcd);
+  } else {
+    if (pass > 0) break;
+    if (threadIdx.x == 0) s_item = xcd_remap(blockIdx.x, total);
+  }
+  __syncthreads();
+  const int lin = s_item;
+  if (lin < 0) break;   // every queue is empty
   const int per_group = ngrp * d.nQB;
   const int grp = lin / per_group;
   const int rem = lin - grp * per_group;
@@ -1136,15 +1168,17 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
   }
   if (group_a) slot_barrier();
   __builtin_amdgcn_s_waitcnt(0xF70);
-  if (sparse_only) return;
-  const float ls_t = pair_sum(l_sel);
-  const float ld_t = pair_sum(l_drop);
-  const float lt = ls_t + ld_t;
-  store(Hf, 1.f / lt);
-  if (gl == 0) {
-    if (delta != nullptr) delta[(size_t)bh * d.Nq + qrow] = ld_t / lt;
-    if (lse != nullptr) lse[(size_t)bh * d.Nq + qrow] = (m_ref + __log2f(lt)) * kLn2;
+  if (!sparse_only) {
+    const float ls_t = pair_sum(l_sel);
+    const float ld_t = pair_sum(l_drop);
+    const float lt = ls_t + ld_t;
+    store(Hf, 1.f / lt);
+    if (gl == 0) {
+      if (delta != nullptr) delta[(size_t)bh * d.Nq + qrow] = ld_t / lt;
+      if (lse != nullptr) lse[(size_t)bh * d.Nq + qrow] = (m_ref + __log2f(lt)) * kLn2;
+    }
   }
+  }   // work items
 }
 
 // 16-token selection blocks, D = 64, G % 4 == 0 (the pages' model shape):
@@ -1166,7 +1200,7 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vt, const int* __restrict__ idx, const int* __restrict__ cnt,
     uint16_t* __restrict__ Hf, uint16_t* __restrict__ Hs, float* __restrict__ delta,
-    float* __restrict__ lse, Dims d, HeadMap hm) {
+    float* __restrict__ lse, int* __restrict__ queues, Dims d, HeadMap hm) {
   constexpr int D = 64;
   constexpr int HPW = 4;
   constexpr int NW = 8;
@@ -1188,7 +1222,21 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
 
   const int ngrp = d.G / HPW;
   const int total = d.B * d.Hkv * ngrp * d.nQT;
-  const int lin = xcd_remap(blockIdx.x, total);
+  // work items as in the kernel above: persistent workgroups drawing from
+  // per-XCD queues, or one item per workgroup in the static mapping
+  __shared__ int s_item;
+  const bool dyn = queues != nullptr && total % kNumXcd == 0;
+  for (int pass = 0;; ++pass) {
+  if (dyn) {
+    __syncthreads();   // the previous item no longer reads LDS or s_item
+    if (threadIdx.x == 0) s_item = fetch_work_item(queues, total / kNumXcd);
+  } else {
+    if (pass > 0) break;
+    if (threadIdx.x == 0) s_item = xcd_remap(blockIdx.x, total);
+  }
+  __syncthreads();
+  const int lin = s_item;
+  if (lin < 0) break;   // every queue is empty
   const int per_group = ngrp * d.nQT;
   const int grp = lin / per_group;
   const int rem = lin - grp * per_group;
@@ -1519,12 +1567,29 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
       lse[plane + (size_t)bh * d.Nq + qrow] = (m_ref + __log2f(ls_t)) * kLn2;
     }
   }
+  }   // work items
+}
+
+// Compute units of the current device (cached per device).
+static hipError_t compute_units(int* out) {
+  static int cached[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) { *out = cached[dev]; return hipSuccess; }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (n <= 0) n = 1;
+  if (dev >= 0 && dev < 64) cached[dev] = n;
+  *out = n;
+  return hipSuccess;
 }
 
 hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* vt,
                                     const int* idx, const int* cnt, uint16_t* hf, uint16_t* hs,
-                                    float* delta, float* lse, const Dims& d, const HeadMap& hm,
-                                    hipStream_t stream) {
+                                    float* delta, float* lse, int* queues, const Dims& d,
+                                    const HeadMap& hm, hipStream_t stream) {
   if (d.tok) {   // per-token lists
     const int tiles = d.B * d.Hq * d.nQT;
 #define SSA_TOK_LAUNCH(DD, TT)                                                                  \
@@ -1541,8 +1606,16 @@ hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const 
   if (d.bs == 16 && d.D == 64 && d.G % 4 == 0 && hf != nullptr) {
     // dual mode, four q heads per workgroup
     const int groups = d.B * d.Hkv * (d.G / 4) * d.nQT;
-    hipLaunchKernelGGL((attn_prefill_bf16_pp16_kernel<3, 2>), dim3(groups), dim3(512), 0, stream,
-                       q, k, vt, idx, cnt, hf, hs, delta, lse, d, hm);
+    const bool dyn = queues != nullptr && groups % kNumXcd == 0;
+    int grid = groups;
+    if (dyn) {
+      int cus = 0;
+      const hipError_t e = compute_units(&cus);
+      if (e != hipSuccess) return e;
+      grid = std::min(groups, cus);
+    }
+    hipLaunchKernelGGL((attn_prefill_bf16_pp16_kernel<3, 2>), dim3(grid), dim3(512), 0, stream,
+                       q, k, vt, idx, cnt, hf, hs, delta, lse, dyn ? queues : nullptr, d, hm);
     return hipGetLastError();
   }
   if (d.bs == 16) {
@@ -1559,8 +1632,17 @@ hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const 
   // per-head kernel, which walks only each head's own selected blocks
   if (d.D == 128 && d.G % 4 == 0 && hf != nullptr) {
     const int groups = d.B * d.Hkv * (d.G / 4) * d.nQB;
-    hipLaunchKernelGGL((attn_prefill_bf16_pp_kernel<128, 3>), dim3(groups), dim3(512), 0, stream,
-                       q, k, vt, idx, cnt, hf, hs, delta, lse, d, hm);
+    // with queues: one persistent workgroup per CU (one fits per CU)
+    const bool dyn = queues != nullptr && groups % kNumXcd == 0;
+    int grid = groups;
+    if (dyn) {
+      int cus = 0;
+      const hipError_t e = compute_units(&cus);
+      if (e != hipSuccess) return e;
+      grid = std::min(groups, cus);
+    }
+    hipLaunchKernelGGL((attn_prefill_bf16_pp_kernel<128, 3>), dim3(grid), dim3(512), 0, stream,
+                       q, k, vt, idx, cnt, hf, hs, delta, lse, dyn ? queues : nullptr, d, hm);
     return hipGetLastError();
   }
   const int total = d.B * d.Hq * d.nQB;

@@ -15,6 +15,10 @@ constexpr int kBlock = 64;      // tokens per key tile / query tile of the atten
 constexpr int kMaxHq = 256;
 constexpr int kMaxGroup = 16;   // q heads per kv head
 constexpr int kTokMaxBudget = 64;  // list length limit of per-token selection
+// Work queues of the grouped prefill kernels: one counter per XCD, each on
+// its own 256-byte line of the workspace.
+constexpr int kNumXcd = 8;
+constexpr int kQueueStride = 64;   // ints between two counters
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

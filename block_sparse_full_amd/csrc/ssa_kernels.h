@@ -38,13 +38,16 @@ inline size_t tok_kc_bytes(const Dims& d) {
 }
 hipError_t launch_select_tok(const void* q, bool bf16, const float* kbar, double* kc, int* idx,
                              int* cnt, const Dims& d, const HeadMap& hm, hipStream_t stream);
-hipError_t launch_transpose(const uint16_t* v, uint16_t* vt, int BH, int N, int D,
+// Also zeroes the prefill work queues (kNumXcd counters) when queues != NULL.
+hipError_t launch_transpose(const uint16_t* v, uint16_t* vt, int BH, int N, int D, int* queues,
                             hipStream_t stream);
 
+// queues: kNumXcd zeroed counters (see launch_transpose), or NULL for a
+// static workgroup-to-tile mapping.
 hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* vt,
                                     const int* idx, const int* cnt, uint16_t* hf, uint16_t* hs,
-                                    float* delta, float* lse, const Dims& d, const HeadMap& hm,
-                                    hipStream_t stream);
+                                    float* delta, float* lse, int* queues, const Dims& d,
+                                    const HeadMap& hm, hipStream_t stream);
 hipError_t launch_attn_rows_f32(const float* q, const float* k, const float* v, const int* idx,
                                 const int* cnt, float* hf, float* hs, float* delta, float* lse,
                                 const Dims& d, const HeadMap& hm, hipStream_t stream);

@@ -500,8 +500,12 @@ hipError_t launch_select_tok(const void* q, bool bf16, const float* kbar, double
 // ---------------------------------------------------------------- V transpose
 // vt[bh][d][n] = v[bh][n][d] for bf16, 64x64 tiles through LDS.
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ v,
-                                                        uint16_t* __restrict__ vt, int N, int D) {
+                                                        uint16_t* __restrict__ vt, int N, int D,
+                                                        int* __restrict__ queues) {
   __shared__ uint16_t tile[64][66];
+  if (queues != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 &&
+      threadIdx.x < kNumXcd)
+    queues[threadIdx.x * kQueueStride] = 0;
   const int n0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
   const size_t bh = blockIdx.z;
   const uint16_t* src = v + bh * (size_t)N * D;
@@ -512,10 +516,10 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
   for (int r = ty; r < 64; r += 4) dst[(size_t)(d0 + r) * N + n0 + tx] = tile[tx][r];
 }
 
-hipError_t launch_transpose(const uint16_t* v, uint16_t* vt, int BH, int N, int D,
+hipError_t launch_transpose(const uint16_t* v, uint16_t* vt, int BH, int N, int D, int* queues,
                             hipStream_t stream) {
   hipLaunchKernelGGL(transpose_kernel, dim3(N / 64, D / 64, BH), dim3(256), 0, stream, v, vt,
-                     N, D);
+                     N, D, queues);
   return hipGetLastError();
 }
 

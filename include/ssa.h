@@ -107,7 +107,10 @@ typedef struct {
 
 /* Device workspace bytes needed by every forward call below for problem p
  * (the largest of their needs, so one workspace serves them all; the
- * backward has its own query). Returns 0 when p is invalid or unsupported. */
+ * backward has its own query). Returns 0 when p is invalid or unsupported.
+ * Besides intermediates (pooled blocks, V transposed) the workspace holds
+ * the bf16 prefill's work-queue counters, which ssa_attn_fwd resets itself:
+ * no part of the workspace needs clearing by the caller. */
 size_t ssa_workspace_bytes(const ssa_problem* p);
 
 /* Block mean-pool ("Practical Implementation of SSA": mean pooling of each

@@ -185,10 +185,11 @@ BwdLayout bwd_layout_of(const Problem& P) {
       off += align256((size_t)d.B * d.Hq * ssa::bwd_key_tiles(d) * (d.Nq / 32) * 4 * sizeof(uint64_t));
     L.pq = off;
     off += align256((size_t)d.B * d.Hq * d.Nq * d.D * sizeof(float));
-    L.pk = off;
-    off += align256((size_t)d.B * d.Hkv * d.Nk * d.D * sizeof(float));
+    L.pk = off;   // head-group slots of the full dK / dV pass
+    const size_t nslot = (size_t)ssa::bwd_full_split(d);
+    off += align256(nslot * d.B * d.Hkv * d.Nk * d.D * sizeof(float));
     L.pv = off;
-    off += align256((size_t)d.B * d.Hkv * d.Nk * d.D * sizeof(float));
+    off += align256(nslot * d.B * d.Hkv * d.Nk * d.D * sizeof(float));
     L.sk = off;   // per-q-head slots of the sparse dK / dV pass
     off += align256((size_t)d.G * d.B * d.Hkv * d.Nk * d.D * sizeof(float));
     L.sv = off;

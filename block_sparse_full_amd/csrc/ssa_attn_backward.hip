@@ -342,7 +342,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ GF, const uint16_t* __restrict__ GS,
     const float* __restrict__ stats, const uint16_t* __restrict__ bits,
     const uint64_t* __restrict__ rowbits, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-    float* __restrict__ pK, float* __restrict__ pV, Dims d, HeadMap hm, int nKT) {
+    float* __restrict__ pK, float* __restrict__ pV, Dims d, HeadMap hm, int nKT, int hsplit) {
   constexpr bool FULL = MODE != 2, SPARSE = MODE != 1;
   constexpr int SPR = D / 8;          // 16-byte chunks per row
   constexpr int KK = D / 32;          // 32-deep k-steps over D
@@ -360,19 +360,22 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
   const uint32_t aGS = lds_u32(&sGS[0][0]), aSt = lds_u32(&sStat[0][0]);
 
   const int nBG = d.B * d.Hkv;
-  // the sparse stream (MODE 2) runs one workgroup per (tile, q head): a block
+  // The q heads of a kv head are split into hsplit groups of GW heads, one
+  // workgroup per (tile, group), each writing its own float32 slot. The
+  // sparse stream (MODE 2) runs one workgroup per (tile, q head): a block
   // that every query selects (the sink) would otherwise make one workgroup
-  // walk every step of every head alone
-  constexpr bool SPLIT = MODE == 2;
+  // walk every step of every head alone. The full stream splits when there
+  // are too few (tile, kv head) pairs to fill the chip.
   const int bg = blockIdx.x % nBG;
-  const int kt = (blockIdx.x / nBG) % nKT;                  // heaviest tiles first
-  const int h0 = SPLIT ? blockIdx.x / (nBG * nKT) : 0;      // the q head of a split workgroup
+  const int hgi = (blockIdx.x / nBG) % hsplit;              // head group
+  const int kt = blockIdx.x / (nBG * hsplit);               // heaviest tiles first
   const int b = bg / d.Hkv, g = bg % d.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, gq = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nS = d.Nq / kStep;
   const int G = d.G;
-  const int GW = SPLIT ? 1 : G;                             // q heads walked by this workgroup
+  const int GW = G / hsplit;                                // q heads walked by this workgroup
+  const int h0 = hgi * GW;                                  // its first head within the group
   const int kw0 = kt * kKeysPerWg + kStep * w;   // first key of this wave
   const bool wave_keys = kw0 < d.Nk;
   const int s_first = kt * (kKeysPerWg / kStep);  // first step whose rows reach the tile
@@ -392,7 +395,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
       }
   }
   // float32 outputs go to pK / pV, a split workgroup's to its head's slot
-  const size_t obase = (SPLIT ? (size_t)h0 * d.B * d.Hkv * d.Nk * D : 0) + ((size_t)bg * d.Nk) * D;
+  const size_t obase = (size_t)hgi * d.B * d.Hkv * d.Nk * D + ((size_t)bg * d.Nk) * D;
   auto out_off = [&](int mb, int nb) {
     return obase + (size_t)(kw0 + 16 * nb + n) * D + 16 * mb + 4 * gq;
   };
@@ -404,7 +407,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
 
   // item e -> (step, head index)
   auto item_s = [&](int e) { return nS - 1 - e / GW; };
-  auto item_h = [&](int e) { return SPLIT ? h0 : e % G; };
+  auto item_h = [&](int e) { return h0 + e % GW; };
   const uint16_t* tile_bits = bits + (size_t)(bg * nKT + kt) * nS * G;
   auto load_chunk = [&](int c) -> uint32_t {
     const int e = 64 * c + lane;
@@ -661,12 +664,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     }
 }
 
-// dK = scale (pK + sum_h sK[h]), dV = pV + sum_h sV[h] in bfloat16, four
-// elements per thread; pK / pV (the full-stream pass) may be absent. The
-// heads are added in ascending order, so the result does not depend on
-// scheduling.
+// dK = scale (sum_j pK[j] + sum_h sK[h]), dV = sum_j pV[j] + sum_h sV[h] in
+// bfloat16, four elements per thread; pK / pV hold the npk head-group slots
+// of the full-stream pass (npk may be 0). Slots are added in ascending
+// order, so the result does not depend on scheduling.
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ pK,
-                                                         const float* __restrict__ pV,
+                                                         const float* __restrict__ pV, int npk,
                                                          const float* __restrict__ sK,
                                                          const float* __restrict__ sV, int G,
                                                          size_t n4, float scale,
@@ -674,8 +677,11 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict
                                                          uint16_t* __restrict__ dV) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n4) return;
-  f32x4_t k = pK != nullptr ? ((const f32x4_t*)pK)[i] : f32x4_t{0.f, 0.f, 0.f, 0.f};
-  f32x4_t v = pV != nullptr ? ((const f32x4_t*)pV)[i] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t k = f32x4_t{0.f, 0.f, 0.f, 0.f}, v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < npk; ++j) {
+    k += ((const f32x4_t*)pK)[(size_t)j * n4 + i];
+    v += ((const f32x4_t*)pV)[(size_t)j * n4 + i];
+  }
   for (int h = 0; h < G; ++h) {
     k += ((const f32x4_t*)sK)[(size_t)h * n4 + i];
     v += ((const f32x4_t*)sV)[(size_t)h * n4 + i];
@@ -1110,6 +1116,16 @@ hipError_t launch_attn_bwd_stats(const void* hf, const void* hs, const void* gf,
 
 int bwd_key_tiles(const Dims& d) { return (d.Nk + kKeysPerWg - 1) / kKeysPerWg; }
 
+int bwd_full_split(const Dims& d) {
+  // fewest head groups that give the full-stream dK/dV pass at least
+  // kBwdMinWorkgroups workgroups (the heaviest tile then holds 1/hs of the
+  // work it would alone)
+  const long pairs = (long)bwd_key_tiles(d) * d.B * d.Hkv;
+  for (int hs = 1; hs < d.G; ++hs)
+    if (d.G % hs == 0 && pairs * hs >= kBwdMinWorkgroups) return hs;
+  return d.G;
+}
+
 hipError_t launch_attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const uint16_t* gf, const uint16_t* gs, const int* idx,
                                 const int* cnt, const float* stats, uint16_t* bits,
@@ -1128,40 +1144,45 @@ hipError_t launch_attn_bwd_bf16(const uint16_t* q, const uint16_t* k, const uint
   const dim3 g2((unsigned)(nQT * d.B * d.Hq));
   // the full-stream pass never reads the selection; the sparse-stream
   // kernels come in a per-block and a per-token (per-row masks) form
-#define SSA_DKDV_T(DD, MM, IO, TK, PK, PV, GRID)                                             \
+#define SSA_DKDV_T(DD, MM, IO, TK, PK, PV, GRID, HS)                                         \
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DD, MM, IO, TK>), GRID, dim3(256), 0, stream, q, k, \
-                     v, gf, gs, stats, bits, rowbits, dk, dv, PK, PV, d, hm, nKT)
+                     v, gf, gs, stats, bits, rowbits, dk, dv, PK, PV, d, hm, nKT, HS)
 #define SSA_DQ_T(DD, MM, IO, TK)                                                             \
   hipLaunchKernelGGL((attn_bwd_dq_kernel<DD, MM, IO, TK>), g2, dim3(256), 0, stream, q, k, v,  \
                      gf, gs, stats, idx, cnt, rowbits, dq, pq, d, hm, nKT)
-#define SSA_DKDV(DD, MM, IO, PK, PV, GRID)                                                   \
-  if (MM == 2 && d.tok) { SSA_DKDV_T(DD, MM, IO, true, PK, PV, GRID); }                      \
-  else { SSA_DKDV_T(DD, MM, IO, false, PK, PV, GRID); }
+#define SSA_DKDV(DD, MM, IO, PK, PV, GRID, HS)                                               \
+  if (MM == 2 && d.tok) { SSA_DKDV_T(DD, MM, IO, true, PK, PV, GRID, HS); }                  \
+  else { SSA_DKDV_T(DD, MM, IO, false, PK, PV, GRID, HS); }
 #define SSA_DQ(DD, MM, IO)                                                                   \
   if (MM == 2 && d.tok) { SSA_DQ_T(DD, MM, IO, true); } else { SSA_DQ_T(DD, MM, IO, false); }
   // Both streams: a full-stream pass leaves float32 partial sums, a
   // sparse-stream pass over the selected blocks only adds to them and rounds.
   // The sparse dK/dV pass runs per (tile, q head) into per-head slots.
   const dim3 g1s((unsigned)(nKT * d.B * d.Hkv * d.G));
+  // the full-stream pass in hs head groups (one float32 slot each)
+  const int hs = bwd_full_split(d);
+  const dim3 g1f((unsigned)(nKT * d.B * d.Hkv * hs));
 #define SSA_PASSES(DD)                                                                       \
   if (gf != nullptr && gs != nullptr) {                                                      \
-    SSA_DKDV(DD, 1, 1, pk, pv, g1); SSA_DKDV(DD, 2, 1, sk, sv, g1s);                         \
+    SSA_DKDV(DD, 1, 1, pk, pv, g1f, hs); SSA_DKDV(DD, 2, 1, sk, sv, g1s, d.G);               \
     SSA_DQ(DD, 1, 1); SSA_DQ(DD, 2, 2);                                                      \
   } else if (gs == nullptr) {                                                                \
-    SSA_DKDV(DD, 1, 0, pk, pv, g1); SSA_DQ(DD, 1, 0);                                        \
+    if (hs == 1) { SSA_DKDV(DD, 1, 0, pk, pv, g1, 1); }                                      \
+    else { SSA_DKDV(DD, 1, 1, pk, pv, g1f, hs); }                                            \
+    SSA_DQ(DD, 1, 0);                                                                        \
   } else {                                                                                   \
-    SSA_DKDV(DD, 2, 1, sk, sv, g1s); SSA_DQ(DD, 2, 0);                                       \
+    SSA_DKDV(DD, 2, 1, sk, sv, g1s, d.G); SSA_DQ(DD, 2, 0);                                  \
   }
   if (d.D == 128) {
     SSA_PASSES(128)
   } else {
     SSA_PASSES(64)
   }
-  if (gs != nullptr) {
+  if (gs != nullptr || hs > 1) {
     const size_t n4 = (size_t)d.B * d.Hkv * d.Nk * d.D / 4;
+    const int npk = gf != nullptr ? hs : 0;
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
-                       stream, gf != nullptr ? pk : nullptr, gf != nullptr ? pv : nullptr, sk, sv,
-                       d.G, n4, d.scale, dk, dv);
+                       stream, pk, pv, npk, sk, sv, gs != nullptr ? d.G : 0, n4, d.scale, dk, dv);
   }
 #undef SSA_PASSES
 #undef SSA_DKDV

@@ -191,11 +191,13 @@ ssa_status ssa_align_loss(const ssa_problem* p, const void* h_full,
 /* Device workspace bytes needed by ssa_attn_bwd for problem p: per-row
  * statistics (16 bytes per query row) and, for SSA_BF16, the selection bits
  * of the dK/dV walk (2 bytes per q head, 128-key tile and 32-row step; 32
- * more with SSA_SELECT_TOKEN, the row masks of the four 32-key blocks) and
- * float32 copies of dQ, dK and dV (the full-stream pass hands its partial
- * sums to the sparse-stream pass) and Hq/Hkv float32 copies of dK and dV
- * (one per q head of a group for the sparse pass). Returns 0 when p is
- * invalid, unsupported or a decode problem. */
+ * more with SSA_SELECT_TOKEN, the row masks of the four 32-key blocks),
+ * a float32 copy of dQ (the full-stream pass hands its partial sums to the
+ * sparse-stream pass), float32 copies of dK and dV for each head group of
+ * the full-stream pass (one group, or up to Hq/Hkv when there are fewer than
+ * 1024 pairs of 128-key tile and kv head) and Hq/Hkv float32 copies of dK
+ * and dV (one per q head of a group for the sparse pass). Returns 0 when p
+ * is invalid, unsupported or a decode problem. */
 size_t ssa_bwd_workspace_bytes(const ssa_problem* p);
 
 /* Backward pass of both attention streams ("Bidirectional Attention

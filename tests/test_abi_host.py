@@ -184,7 +184,10 @@ def test_backward_workspace_size(lib):
     need = bwd_workspace_bytes(p)
     stats = 8 * 4096 * 4 * 4
     bits = 8 * (4096 // 128) * (4096 // 32) * 2
-    partials = (8 + 2 * 2) * 4096 * 128 * 4     # float32 dQ, dK, dV between the two passes
+    # float32 dQ, and dK, dV per head group of the full-stream pass: 32 key
+    # tiles x 2 kv heads = 64 workgroups, below 1024, so each of the four
+    # heads of a group gets its own workgroup and slot
+    partials = (8 + 4 * 2 * 2) * 4096 * 128 * 4
     slots = 2 * 4 * 2 * 4096 * 128 * 4           # sparse dK, dV per q head of a group (4)
     assert need == stats + bits + partials + slots
     c, keep = p.to_c()

@@ -573,6 +573,9 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--backward-only", action="store_true",
                     help="only time the backward pass (prints one JSON object)")
+    ap.add_argument("--paper-only", action="store_true",
+                    help="only time the pages' shape (16-token blocks, D 64): forward, backward, "
+                         "per-token selection, 16:1 GQA (prints one JSON object)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (x3), the reference for "
                          "scaling HBM byte counters")
@@ -600,6 +603,10 @@ def main():
     if args.backward_only:
         print(json.dumps({"backward": run_backward(ssa, torch, cfg, args.steps, args.warmup)}),
               flush=True)
+        return
+    if args.paper_only:
+        print(json.dumps({"paper_shape": run_paper_shape(ssa, torch, CONFIGS["paper_16k_b16"],
+                                                         args.steps)}), flush=True)
         return
     if args.no_prefill:
         dec = run_decode(ssa, torch, CONFIGS["gqa_decode_64k"], args.steps, args.warmup)

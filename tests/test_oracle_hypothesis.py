@@ -1,8 +1,12 @@
 """The oracle against a pure-Python brute force on Hypothesis-drawn tiny
 problems: explicit loops over rows, keys and dimensions, block selection by a
 full sort of (-score, index), softmax with math.exp. Queries and keys are
-small integers, so every pooled mean and score is exact in float64 and both
-sides must select the same blocks; the attention outputs agree to rounding.
+small integers and block sizes powers of two, so every pooled mean and score
+is a short dyadic fraction, exact in float64 whatever the summation order:
+equal scores are then true ties and both sides must select the same blocks.
+(With a block of 3 the means are thirds, the rounding of two mathematically
+equal scores can differ with the order of operations, and a tie can break
+either way.) The attention outputs agree to rounding.
 Also checks the loss bound of the linear error result (the dropped mass
 bounds |h_full - h_sparse| by 2 delta max |v|, so the MSE is at most the
 mean of 4 delta^2 max|v|^2 / D per row)."""
@@ -88,7 +92,7 @@ def problems(draw):
     Hkv = draw(st.integers(1, 2))
     G = draw(st.integers(1, 3))
     Hq = Hkv * G
-    block = draw(st.integers(1, 4))
+    block = draw(st.sampled_from([1, 2, 4]))
     nb = draw(st.integers(1, 6))
     D = draw(st.integers(1, 4))
     n_sink = draw(st.integers(0, 2))

@@ -365,7 +365,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
   // sparse stream (MODE 2) runs one workgroup per (tile, q head): a block
   // that every query selects (the sink) would otherwise make one workgroup
   // walk every step of every head alone. The full stream splits when there
-  // are too few (tile, kv head) pairs to fill the chip.
+  // are too few (tile, kv head) pairs to balance the chip.
   const int bg = blockIdx.x % nBG;
   const int hgi = (blockIdx.x / nBG) % hsplit;              // head group
   const int kt = blockIdx.x / (nBG * hsplit);               // heaviest tiles first

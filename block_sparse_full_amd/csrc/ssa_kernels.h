@@ -63,7 +63,7 @@ constexpr int kLossPartials = 1024;
 int bwd_key_tiles(const Dims& d);   // 128-key tiles of the dK/dV kernel
 // Head groups of the full-stream dK/dV pass (a divisor of G; its float32
 // partial-sum slots in the backward workspace).
-constexpr long kBwdMinWorkgroups = 1024;
+constexpr long kBwdMinWorkgroups = 4096;
 int bwd_full_split(const Dims& d);
 hipError_t launch_attn_bwd_stats(const void* hf, const void* hs, const void* gf, const void* gs,
                                  const float* lse, float* stats, bool bf16, const Dims& d,

@@ -195,7 +195,7 @@ ssa_status ssa_align_loss(const ssa_problem* p, const void* h_full,
  * a float32 copy of dQ (the full-stream pass hands its partial sums to the
  * sparse-stream pass), float32 copies of dK and dV for each head group of
  * the full-stream pass (one group, or up to Hq/Hkv when there are fewer than
- * 1024 pairs of 128-key tile and kv head) and Hq/Hkv float32 copies of dK
+ * 4096 pairs of 128-key tile and kv head) and Hq/Hkv float32 copies of dK
  * and dV (one per q head of a group for the sparse pass). Returns 0 when p
  * is invalid, unsupported or a decode problem. */
 size_t ssa_bwd_workspace_bytes(const ssa_problem* p);

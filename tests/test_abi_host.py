@@ -185,7 +185,7 @@ def test_backward_workspace_size(lib):
     stats = 8 * 4096 * 4 * 4
     bits = 8 * (4096 // 128) * (4096 // 32) * 2
     # float32 dQ, and dK, dV per head group of the full-stream pass: 32 key
-    # tiles x 2 kv heads = 64 workgroups, below 1024, so each of the four
+    # tiles x 2 kv heads = 64 workgroups, below 4096, so each of the four
     # heads of a group gets its own workgroup and slot
     partials = (8 + 4 * 2 * 2) * 4096 * 128 * 4
     slots = 2 * 4 * 2 * 4096 * 128 * 4           # sparse dK, dV per q head of a group (4)

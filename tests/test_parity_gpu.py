@@ -52,6 +52,9 @@ SMALL = [
     ("gqa_8k_peaked", dict(B=2, Hq=16, Hkv=2, N=1536), 5, 0, 0),
     ("gqa_8k_peaked", dict(B=1, Hq=4, Hkv=1, N=4096), 7, 1, 2),
     ("gqa_8k_peaked", dict(B=1, Hq=8, Hkv=2, N=2048, planted=False), 6, 1, 1),
+    # 9 query blocks: a work-item count that is not a multiple of the 8 XCD
+    # queues, so the grouped kernel takes its static one-item-per-workgroup path
+    ("gqa_8k_peaked", dict(B=1, Hq=4, Hkv=1, N=576), 4, 1, 1),
     ("gqa_decode_64k", dict(B=3, Hq=8, Hkv=2, N=2048), 4, 1, 1),
     ("gqa_decode_64k", dict(B=2, Hq=8, Hkv=1, N=4096, D=64), 5, 1, 1),
     ("gqa_decode_64k", dict(B=2, Hq=2, Hkv=2, N=640), 3, 0, 1),
@@ -171,6 +174,8 @@ BLOCK16 = [
     ("paper_16k_b16", dict(Hq=4, Hkv=1, N=1024, D=128), 16, 1, 1, True),
     # 16 q heads on one kv head: four four-head workgroups share each kv head
     ("paper_16k_b16", dict(Hq=16, Hkv=1, N=1536), 16, 1, 1, False),
+    # 9 query tiles: the static one-item-per-workgroup path of the grouped kernel
+    ("paper_16k_b16", dict(Hq=4, Hkv=1, N=576), 16, 1, 1, False),
     ("paper_16k_b16", dict(decode=True, B=3, Hq=8, Hkv=2, N=2048), 16, 1, 1, False),
     ("paper_16k_b16", dict(decode=True, B=2, Hq=4, Hkv=1, N=4096, D=128), 9, 1, 1, False),
     # decode with 16 q heads per kv head (two workgroups of 8 per group)

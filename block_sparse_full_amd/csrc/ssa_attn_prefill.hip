@@ -24,6 +24,7 @@
 #include "ssa_kernels.h"
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 namespace ssa {
@@ -1570,18 +1571,23 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
   }   // work items
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; threads that race
+// on the first call store the same value).
 static hipError_t compute_units(int* out) {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < 64 && cached[dev] > 0) { *out = cached[dev]; return hipSuccess; }
+  const bool slot = dev >= 0 && dev < 64;
+  if (slot) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) { *out = c; return hipSuccess; }
+  }
   int n = 0;
   e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   if (n <= 0) n = 1;
-  if (dev >= 0 && dev < 64) cached[dev] = n;
+  if (slot) cached[dev].store(n, std::memory_order_relaxed);
   *out = n;
   return hipSuccess;
 }

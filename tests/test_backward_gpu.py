@@ -115,6 +115,11 @@ SMALL = [
     ("paper_16k_b16", dict(Hq=4, Hkv=1, N=1024), dict(budget=16, use_full=False)),
     ("paper_16k_b16", dict(Hq=2, Hkv=1, N=576, D=128), dict(budget=8)),
     ("tiny_f32", dict(Hq=2, Hkv=1, N=256, D=128), dict(budget=2, use_full=False)),
+    # 64 x 32 kv heads x 2 key tiles = 4096 (key tile, kv head) pairs: the
+    # full-stream dK/dV pass runs as one head group, writing bfloat16 directly
+    # (full stream only) or one float32 slot (both streams)
+    ("gqa_8k_peaked", dict(B=64, Hq=32, Hkv=32, N=256, D=64), dict(budget=2, use_sparse=False)),
+    ("gqa_8k_peaked", dict(B=64, Hq=32, Hkv=32, N=256, D=64), dict(budget=2)),
     # per-token lists: float32, and bf16 (row masks) with blocks 64 and 16,
     # both streams and each alone, GQA, a permuted head map, D 64 and 128
     ("tiny_f32", dict(Hq=2, Hkv=1, N=512), dict(budget=3, token_select=True)),

@@ -37,8 +37,8 @@ FP64_PEAK_TFLOPS = 78.6          # MI355X float64 vector FMA
 # sources they were taken on (the prefill file and the headers it includes);
 # any other source reports traffic as null.
 PREFILL_TRAFFIC = {
-    # 784934 KiB x 2.000 read + 531580 KiB x 1.000 written per dispatch
-    "b82835a34e766b3e3bdf586a164d40e16214b6eacfd7d9e508b40e9e9ac0ed6e": int(784934 * 2.0 * 1024 + 531580 * 1.0 * 1024),
+    # 783395 KiB x 2.000 read + 531580 KiB x 1.000 written per dispatch
+    "c4dda059c6a3a2e6be667888f50534ec632faa9235488f0e8741af63d108f84a": int(783395 * 2.0 * 1024 + 531580 * 1.0 * 1024),
 }
 PREFILL_SRCS = [os.path.join(ROOT, "block_sparse_full_amd", "csrc", f)
                 for f in ("ssa_attn_prefill.hip", "ssa_device.h", "ssa_common.h")]

@@ -644,7 +644,9 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_bf16_q16_kernel(
     const float m_blk = quad_max(mx) * sl2;
     if (__builtin_amdgcn_ballot_w64(m_blk > m_ref + kTau) != 0) {
       const float m_new = fmaxf(m_ref, m_blk);
-      const float alpha = fast_exp2(m_ref - m_new);
+      // sparse-only per-token lists: a row that has met none of its
+      // selected keys yet keeps m = -inf and zero sums (no -inf - -inf)
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_ref - m_new);
       m_ref = m_new;
 #pragma unroll
       for (int i = 0; i < NDT; ++i)
@@ -653,13 +655,15 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_bf16_q16_kernel(
       l_sel *= alpha;
       l_drop *= alpha;
     }
+    // such a row's logits are all -inf here: its weights come out 0
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
     float ls = 0.f, ld = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      const float p0 = fast_exp2(fmaf(s[kt][0], sl2, -m_ref));
-      const float p1 = fast_exp2(fmaf(s[kt][1], sl2, -m_ref));
-      const float p2 = fast_exp2(fmaf(s[kt][2], sl2, -m_ref));
-      const float p3 = fast_exp2(fmaf(s[kt][3], sl2, -m_ref));
+      const float p0 = fast_exp2(fmaf(s[kt][0], sl2, -m_use));
+      const float p1 = fast_exp2(fmaf(s[kt][1], sl2, -m_use));
+      const float p2 = fast_exp2(fmaf(s[kt][2], sl2, -m_use));
+      const float p3 = fast_exp2(fmaf(s[kt][3], sl2, -m_use));
       pw[2 * kt] = pack_bf16x2(p0, p1);
       pw[2 * kt + 1] = pack_bf16x2(p2, p3);
       pws[2 * kt] = qsel[kt] ? pw[2 * kt] : 0u;

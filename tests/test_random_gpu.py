@@ -37,7 +37,7 @@ def random_cases(n=14, seed=2024):
     return cases
 
 
-CASES = random_cases()
+CASES = random_cases(24)
 
 
 def random_mode_cases(n=14, seed=2025):
@@ -68,7 +68,7 @@ def random_mode_cases(n=14, seed=2025):
     return cases
 
 
-MODE_CASES = random_mode_cases()
+MODE_CASES = random_mode_cases(24)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"r{i}-{c['base'][:7]}-G{c['Hq'] // c['Hkv']}-"

@@ -144,6 +144,35 @@ def test_backward_parity(ssa, name, sizes, kw):
     full_compare(ssa, cfg, **kw)
 
 
+def test_backward_mid_size_full_compare(ssa):
+    """8192 tokens, 8 q heads over 2 kv heads, budget 16, planted blocks,
+    compared element by element in full. The sink block is selected by every
+    query row, so its dK and dV sum all 8192 rows of four q heads in both
+    streams; they are checked on their own against the largest value of that
+    block, not only through the whole tensor's bar."""
+    cfg = CONFIGS["gqa_8k_peaked"].with_sizes(B=1, Hq=8, Hkv=2, N=8192)
+    say(f"[bwd] mid size {cfg.name} B{cfg.B} Hq{cfg.Hq} Hkv{cfg.Hkv} N{cfg.N} budget 16")
+    x = make_inputs(cfg, workers=16)
+    grads = make_grads(cfg, workers=16)
+    got = gpu_bwd(ssa, cfg, x, grads, budget=16)
+    hm = default_head_map(cfg.Hq, cfg.Hkv)
+    xn = {n: t.double().numpy() for n, t in x.items()}
+    idx, cnt = O.select_blocks(xn["q"], xn["k"], block=cfg.block, budget=16, n_sink=cfg.n_sink,
+                               n_local=cfg.n_local, head_map=hm)
+    assert np.array_equal(got["idx"].numpy(), idx), "selected blocks differ"
+    assert np.array_equal(got["cnt"].numpy(), cnt), "block counts differ"
+    say("[oracle] backward of both streams, 8 heads x 8192 rows")
+    dq, dk, dv = O.dual_attention_backward(xn["q"], xn["k"], xn["v"], idx,
+                                           grads["d_full"].double().numpy(),
+                                           grads["d_sparse"].double().numpy(), block=cfg.block,
+                                           scale=scale_for(cfg), head_map=hm)
+    for name, want in (("dq", dq), ("dk", dk), ("dv", dv)):
+        check_grad(name, to_np64(got[name]), want, "bf16")
+    for name, want in (("dk", dk), ("dv", dv)):
+        check_grad(f"{name} sink block", to_np64(got[name])[:, :, :cfg.block],
+                   want[:, :, :cfg.block], "bf16")
+
+
 def test_backward_full_budget_streams_agree(ssa):
     """Every causal block selected: a gradient fed to the sparse stream alone
     gives the same dq, dk, dv as the same gradient fed to the full stream."""

@@ -280,7 +280,26 @@ def test_pool_blocks_bit_exact(ssa):
 
 # ---------------------------------------------------------------- full-size workloads
 
-def sampled_compare(cfg, x, got, *, budget, heads, rows_per_head, seed, group_select=False):
+def row_loss_check(name, hf_gpu, hs_gpu, hf_ref, hs_ref):
+    """Alignment loss on sampled rows ("Bidirectional Attention Alignment":
+    both losses are the mean squared difference of the two streams): each
+    row's sum over d of (h_full - h_sparse)^2 from the GPU's outputs against
+    the oracle's, per row within the 2e-2 bar and summed over the rows within
+    the 5e-2 relative bar of the whole-problem comparisons."""
+    g = ((np.asarray(hf_gpu, np.float64) - np.asarray(hs_gpu, np.float64)) ** 2).sum(axis=-1)
+    w = ((np.asarray(hf_ref, np.float64) - np.asarray(hs_ref, np.float64)) ** 2).sum(axis=-1)
+    assert_close(f"row loss {name}", g, w, BF16_ABS)
+    if w.sum() > 1e-12:
+        rel = abs(g.sum() - w.sum()) / w.sum()
+        assert rel <= 5e-2, f"row loss {name}: relative error {rel:.3e} of the sampled sum"
+
+
+def sampled_compare(cfg, x, got, *, budget, heads, rows_per_head, seed, group_select=False,
+                    sparse=None):
+    """Every selected index, and sampled rows of the streams, delta and the
+    per-row alignment loss, against the oracle. `sparse`: the outputs of a
+    sparse-only call on the same inputs, whose h_sparse is checked on the
+    same rows."""
     xn = np_inputs(x)
     hm = default_head_map(cfg.Hq, cfg.Hkv)
     say(f"[oracle] selection for {cfg.name} budget {budget}")
@@ -289,18 +308,31 @@ def sampled_compare(cfg, x, got, *, budget, heads, rows_per_head, seed, group_se
                                        group_shared=group_select)
     assert np.array_equal(got["idx"].numpy(), ref_idx), "selected blocks differ"
     assert np.array_equal(got["cnt"].numpy(), ref_cnt), "block counts differ"
+    if sparse is not None:
+        assert np.array_equal(sparse["idx"].numpy(), ref_idx), "sparse-only: selected blocks differ"
+        assert np.array_equal(sparse["cnt"].numpy(), ref_cnt), "sparse-only: block counts differ"
+        assert "h_full" not in sparse
     rows = {bh: sample_rows(cfg.Nq, rows_per_head, seed + i) for i, bh in enumerate(heads)}
     say(f"[oracle] attention rows for {cfg.name} budget {budget}")
     res = O.dual_attention(xn["q"], xn["k"], xn["v"], ref_idx, block=cfg.block,
                            scale=scale_for(cfg), head_map=hm, rows=rows)
     for (b, h), (r, hf, hs, dl) in res.items():
-        assert_close(f"h_full[{b},{h}]", to_np64(got["h_full"][b, h, r]), hf, BF16_ABS, BF16_REL_L2)
-        assert_close(f"h_sparse[{b},{h}]", to_np64(got["h_sparse"][b, h, r]), hs, BF16_ABS, BF16_REL_L2)
+        gf, gs = to_np64(got["h_full"][b, h, r]), to_np64(got["h_sparse"][b, h, r])
+        assert_close(f"h_full[{b},{h}]", gf, hf, BF16_ABS, BF16_REL_L2)
+        assert_close(f"h_sparse[{b},{h}]", gs, hs, BF16_ABS, BF16_REL_L2)
         assert_close(f"delta[{b},{h}]", to_np64(got["delta"][b, h, r]), dl, BF16_DELTA_ABS)
-    # every row of every head: the streams coincide exactly where all causal
-    # blocks are selected, and delta is a probability
+        row_loss_check(f"[{b},{h}]", gf, gs, hf, hs)
+        if sparse is not None:
+            assert_close(f"h_sparse (sparse-only)[{b},{h}]", to_np64(sparse["h_sparse"][b, h, r]),
+                         hs, BF16_ABS, BF16_REL_L2)
+    # every row of every head: delta is a probability
     d = got["delta"]
     assert float(d.min()) >= 0.0 and float(d.max()) <= 1.0
+    # the loss kernel over the whole problem against the mean squared
+    # difference of the GPU's own outputs (float64 partials, float32 result)
+    ls, _, _, _ = O.align_loss(to_np64(got["h_full"]), to_np64(got["h_sparse"]))
+    assert abs(float(got["loss"][0]) - ls) <= 1e-6 * ls + 1e-12
+    assert float(got["loss"][1]) == float(got["loss"][0])
     return ref_idx
 
 
@@ -319,19 +351,19 @@ def test_full_size_gqa_8k_peaked(ssa):
     got = gpu_run(ssa, x, budget=cfg.budget)
     sampled_compare(cfg, x, got, budget=cfg.budget, heads=[(0, 0), (1, 13), (2, 22), (3, 31)],
                     rows_per_head=384, seed=20)
-    # loss over the whole problem against the oracle's loss on the GPU outputs
-    ls, _, _, _ = O.align_loss(to_np64(got["h_full"]), to_np64(got["h_sparse"]))
-    assert abs(float(got["loss"][0]) - ls) <= 1e-6 * ls + 1e-12
 
 
 @pytest.mark.parametrize("budget", [4, 8, 16, 32])
 def test_full_size_gqa_32k(ssa, budget):
+    """The 32K sweep at the benchmark's launch configuration, dual mode and
+    sparse-only (inference) mode on the same inputs."""
     cfg = CONFIGS["gqa_32k_sweep"].with_budget(budget)
     say(f"[parity] full size {cfg}")
     x = make_inputs(cfg, workers=16)
     got = gpu_run(ssa, x, budget=budget)
+    sp = gpu_run(ssa, x, budget=budget, sparse_only=True)
     sampled_compare(cfg, x, got, budget=budget, heads=[(0, 3), (0, 30)], rows_per_head=256,
-                    seed=30 + budget)
+                    seed=30 + budget, sparse=sp)
 
 
 def test_full_size_gqa_32k_group_select(ssa):
@@ -352,15 +384,21 @@ def test_full_size_paper_16k_b16(ssa):
     say(f"[parity] full size {cfg}")
     x = make_inputs(cfg, workers=16)
     got = gpu_run(ssa, x, budget=cfg.budget, block=16)
+    sp = gpu_run(ssa, x, budget=cfg.budget, block=16, sparse_only=True)
     sampled_compare(cfg, x, got, budget=cfg.budget, heads=[(0, 0), (0, 17)], rows_per_head=256,
-                    seed=91)
+                    seed=91, sparse=sp)
 
 
 def test_full_size_decode_64k(ssa):
+    """The 64K decode workload at the benchmark's launch configuration (the
+    caller's pooled-key table, 64 sequences), dual mode and sparse-only mode:
+    on 4 sampled sequences (all heads) every output and the alignment loss of
+    those sequences against the oracle; the loss kernel over all 64."""
     cfg = CONFIGS["gqa_decode_64k"]
     say(f"[parity] full size {cfg}")
     x = make_inputs(cfg, workers=16)
     got = gpu_run(ssa, x, budget=cfg.budget, k_pooled=True)
+    sp = gpu_run(ssa, x, budget=cfg.budget, k_pooled=True, sparse_only=True)
     hm = default_head_map(cfg.Hq, cfg.Hkv)
     seqs = [0, 17, 42, 63]
     xs = {k: v[seqs].float().numpy() for k, v in x.items()}
@@ -368,10 +406,21 @@ def test_full_size_decode_64k(ssa):
     assert np.array_equal(got["k_pooled"][seqs].numpy(), O.pool_blocks(xs["k"], 64))
     ref = O.ssa_forward(xs["q"], xs["k"], xs["v"], block=64, budget=cfg.budget, n_sink=1,
                         n_local=1, head_map=hm)
-    assert np.array_equal(got["idx"][seqs].numpy(), ref["idx"])
-    assert np.array_equal(got["cnt"][seqs].numpy(), ref["cnt"])
+    for tag, r in (("dual", got), ("sparse-only", sp)):
+        assert np.array_equal(r["idx"][seqs].numpy(), ref["idx"]), tag
+        assert np.array_equal(r["cnt"][seqs].numpy(), ref["cnt"]), tag
+        assert_close(f"h_sparse ({tag})", to_np64(r["h_sparse"][seqs]), ref["h_sparse"], BF16_ABS,
+                     BF16_REL_L2)
+    assert "h_full" not in sp
     assert_close("h_full", to_np64(got["h_full"][seqs]), ref["h_full"], BF16_ABS, BF16_REL_L2)
-    assert_close("h_sparse", to_np64(got["h_sparse"][seqs]), ref["h_sparse"], BF16_ABS, BF16_REL_L2)
     assert_close("delta", to_np64(got["delta"][seqs]), ref["delta"], BF16_DELTA_ABS)
+    # the alignment loss of the sampled sequences: the GPU outputs' mean
+    # squared difference against the oracle's loss on the same sequences
+    gh = to_np64(got["h_full"][seqs]) - to_np64(got["h_sparse"][seqs])
+    lg = float((gh * gh).mean())
+    assert abs(lg - ref["loss_sparsity"]) <= BF16_ABS
+    assert abs(lg - ref["loss_sparsity"]) <= 5e-2 * ref["loss_sparsity"], (lg, ref["loss_sparsity"])
+    row_loss_check("decode", to_np64(got["h_full"][seqs]), to_np64(got["h_sparse"][seqs]),
+                   ref["h_full"], ref["h_sparse"])
     ls, _, _, _ = O.align_loss(to_np64(got["h_full"]), to_np64(got["h_sparse"]))
     assert abs(float(got["loss"][0]) - ls) <= 1e-6 * ls + 1e-12

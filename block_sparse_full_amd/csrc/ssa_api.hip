@@ -6,6 +6,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/ssa.h"
 #include "ssa_common.h"
 #include "ssa_kernels.h"
@@ -213,6 +216,50 @@ ssa_status hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Scratch of ssa_align_loss_noalloc: the float64 partial sums of the loss
+// kernels, kLossPartials of them whatever the problem size. Each GPU that
+// loads the library holds its own copy until the process ends. Host code
+// never passes this name to a kernel (on the host it is only a stand-in for
+// the symbol): scratch_on() looks up each device's address once.
+static __device__ __align__(256) double scratch[ssa::kLossPartials];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the device that runs `stream` (the current
+// device for the null stream), looked up with that device current on the
+// first call for it.
+ssa_status scratch_on(void* stream, double** out) {
+  int dev = -1;
+  hipError_t e = stream != nullptr ? hipStreamGetDevice((hipStream_t)stream, &dev)
+                                   : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SSA_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SSA_ERR_UNSUPPORTED, "device %d is beyond the %d this library tracks", dev,
+                kMaxDevices);
+  void* addr = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (addr == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    addr = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (addr == nullptr) {
+      int cur = -1;
+      e = hipGetDevice(&cur);
+      if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+      if (e == hipSuccess) e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      const hipError_t e2 = (cur >= 0 && cur != dev) ? hipSetDevice(cur) : hipSuccess;
+      if (e != hipSuccess || addr == nullptr)
+        return fail(SSA_ERR_HIP, "address of the loss scratch on device %d: %s", dev,
+                    hipGetErrorString(e != hipSuccess ? e : hipErrorInvalidSymbol));
+      if (e2 != hipSuccess)
+        return fail(SSA_ERR_HIP, "restoring device %d: %s", cur, hipGetErrorString(e2));
+      g_scratch_addr[dev].store(addr, std::memory_order_release);
+    }
+  }
+  *out = (double*)addr;
+  return SSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -329,6 +376,26 @@ ssa_status ssa_align_loss(const ssa_problem* p, const void* h_full, const void* 
                                            grad_sparse, (double*)((char*)ws + L.loss),
                                            (hipStream_t)stream),
                     "align loss");
+}
+
+ssa_status ssa_align_loss_noalloc(const ssa_problem* p, const void* h_full,
+                                  const void* h_sparse, float* loss, void* grad_full,
+                                  void* grad_sparse, void* stream) {
+  Problem P;
+  ssa_status s = build(p, &P);
+  if (s != SSA_OK) return s;
+  if (h_full == nullptr || h_sparse == nullptr || loss == nullptr)
+    return fail(SSA_ERR_INVALID_ARG, "h_full, h_sparse or loss is NULL");
+  const long n = (long)P.d.B * P.d.Hq * P.d.Nq * P.d.D;
+  const size_t need = (size_t)ssa::align_loss_partials(n) * sizeof(double);
+  if (need > sizeof(scratch))
+    return fail(SSA_ERR_UNSUPPORTED, "the loss needs %zu bytes of scratch; the no-allocation "
+                "entry point holds %zu", need, sizeof(scratch));
+  double* part = nullptr;
+  if ((s = scratch_on(stream, &part)) != SSA_OK) return s;
+  return hip_status(ssa::launch_align_loss(h_full, h_sparse, P.bf16, n, loss, grad_full,
+                                           grad_sparse, part, (hipStream_t)stream),
+                    "align loss (no allocation)");
 }
 
 size_t ssa_bwd_workspace_bytes(const ssa_problem* p) {

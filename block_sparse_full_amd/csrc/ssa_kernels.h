@@ -58,6 +58,7 @@ hipError_t launch_attn_decode_bf16(const uint16_t* q, const uint16_t* k, const u
 hipError_t launch_align_loss(const void* hf, const void* hs, bool bf16, long n, float* loss,
                              void* gf, void* gs, double* partials, hipStream_t stream);
 constexpr int kLossPartials = 1024;
+long align_loss_partials(long n);   // float64 partials the loss kernels use for n elements
 
 // Backward pass (ssa_attn_backward.hip).
 int bwd_key_tiles(const Dims& d);   // 128-key tiles of the dK/dV kernel

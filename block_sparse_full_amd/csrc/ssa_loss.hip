@@ -95,12 +95,15 @@ __global__ __launch_bounds__(256) void loss_final_kernel(const double* __restric
   }
 }
 
+long align_loss_partials(long n) {
+  const long np = (n / 8 + 255) / 256;
+  return np < 1 ? 1 : np > kLossPartials ? kLossPartials : np;
+}
+
 hipError_t launch_align_loss(const void* hf, const void* hs, bool bf16, long n, float* loss,
                              void* gf, void* gs, double* partials, hipStream_t stream) {
   const long n8 = n / 8;
-  long np = (n8 + 255) / 256;
-  if (np > kLossPartials) np = kLossPartials;
-  if (np < 1) np = 1;
+  const long np = align_loss_partials(n);
   const double gscale = 2.0 / (double)n;
   if (bf16)
     hipLaunchKernelGGL(loss_partial_kernel<uint16_t>, dim3((unsigned)np), dim3(256), 0, stream,

@@ -28,7 +28,8 @@ SSA_SELECT_PER_HEAD, SSA_SELECT_GROUP, SSA_SELECT_TOKEN = 0, 1, 2
 STATUS = {0: "SSA_OK", 1: "SSA_ERR_INVALID_ARG", 2: "SSA_ERR_UNSUPPORTED",
           3: "SSA_ERR_WORKSPACE", 4: "SSA_ERR_HIP"}
 EXPORTS = ("ssa_workspace_bytes", "ssa_pool_blocks", "ssa_select_blocks", "ssa_attn_fwd",
-           "ssa_align_loss", "ssa_status_string", "ssa_last_error_message")
+           "ssa_align_loss", "ssa_align_loss_noalloc", "ssa_status_string",
+           "ssa_last_error_message")
 
 
 class SsaError(RuntimeError):
@@ -73,6 +74,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ssa_attn_fwd.restype = ctypes.c_int
     lib.ssa_align_loss.argtypes = [P, vp, vp, f32p, vp, vp, vp, sz, vp]
     lib.ssa_align_loss.restype = ctypes.c_int
+    lib.ssa_align_loss_noalloc.argtypes = [P, vp, vp, f32p, vp, vp, vp]
+    lib.ssa_align_loss_noalloc.restype = ctypes.c_int
     lib.ssa_bwd_workspace_bytes.argtypes = [P]
     lib.ssa_bwd_workspace_bytes.restype = sz
     lib.ssa_attn_bwd.argtypes = [P, vp, vp, vp, i32p, i32p, vp, vp, f32p, vp, vp, vp, vp, vp, vp,
@@ -274,6 +277,25 @@ def align_loss(p: Problem, h_full, h_sparse, *, want_grads: bool = False,
         ctypes.byref(c), _dev(h_full, "h_full", p.torch_dtype, shp),
         _dev(h_sparse, "h_sparse", p.torch_dtype, shp), loss.data_ptr(),
         _dev(gf, "grad_full"), _dev(gs, "grad_sparse"), wp, wn, _stream()))
+    return loss, gf, gs
+
+
+def align_loss_noalloc(p: Problem, h_full, h_sparse, *, want_grads: bool = False,
+                       loss: Optional[torch.Tensor] = None):
+    """align_loss through ssa_align_loss_noalloc: the library's own static
+    scratch instead of a workspace. Outputs are allocated here unless given."""
+    dev = h_full.device
+    shp = (p.B, p.Hq, p.Nq, p.D)
+    if loss is None:
+        loss = torch.empty(2, dtype=torch.float32, device=dev)
+    _dev(loss, "loss", torch.float32, (2,))
+    gf = torch.empty(shp, dtype=p.torch_dtype, device=dev) if want_grads else None
+    gs = torch.empty(shp, dtype=p.torch_dtype, device=dev) if want_grads else None
+    c, keep = p.to_c()
+    _check(load_library().ssa_align_loss_noalloc(
+        ctypes.byref(c), _dev(h_full, "h_full", p.torch_dtype, shp),
+        _dev(h_sparse, "h_sparse", p.torch_dtype, shp), loss.data_ptr(),
+        _dev(gf, "grad_full"), _dev(gs, "grad_sparse"), _stream()))
     return loss, gf, gs
 
 

@@ -188,6 +188,23 @@ ssa_status ssa_align_loss(const ssa_problem* p, const void* h_full,
                           void* grad_sparse, void* ws, size_t ws_bytes,
                           void* stream);
 
+/* ssa_align_loss for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels, results and arguments without the workspace. The
+ * float64 partial sums live in a static device array of the library, 8 KiB
+ * on each GPU that loads it (1024 partials, enough for any problem size),
+ * held until the process ends; its address is looked up on the first call
+ * on each device. Nothing is allocated and nothing needs clearing (every
+ * partial is written before it is read). Calls on one GPU share that array:
+ * calls that may overlap on one GPU (on different streams, or from different
+ * threads) race and must be serialised by the caller.
+ * Errors: as ssa_align_loss; SSA_ERR_HIP if the stream's device cannot be
+ * found, SSA_ERR_UNSUPPORTED for a device index of 64 or more. */
+ssa_status ssa_align_loss_noalloc(const ssa_problem* p, const void* h_full,
+                                  const void* h_sparse, float* loss,
+                                  void* grad_full, void* grad_sparse,
+                                  void* stream);
+
 /* Device workspace bytes needed by ssa_attn_bwd for problem p: per-row
  * statistics (16 bytes per query row) and, for SSA_BF16, the selection bits
  * of the dK/dV walk (2 bytes per q head, 128-key tile and 32-row step; 32

@@ -86,6 +86,8 @@ def test_null_pointers(lib):
     # delta without h_full (sparse-only mode has no dropped mass)
     assert lib.ssa_attn_fwd(ctypes.byref(c), 16, 16, 16, 16, 16, None, 16, 16, None, None, 0, None) == 1
     assert lib.ssa_align_loss(ctypes.byref(c), None, 16, 16, None, None, None, 0, None) == 1
+    assert lib.ssa_align_loss_noalloc(ctypes.byref(c), None, 16, 16, None, None, None) == 1
+    assert lib.ssa_align_loss_noalloc(ctypes.byref(c), 16, 16, None, None, None, None) == 1
     assert lib.ssa_pool_blocks(ctypes.byref(c), None, 2, 16, None) == 1
     assert lib.ssa_pool_blocks(ctypes.byref(c), 16, 0, 16, None) == 1
     assert lib.ssa_select_blocks(None, 16, 16, None, 16, 16, None, 0, None) == 1

@@ -353,7 +353,8 @@ ssa_status ssa_attn_fwd(const ssa_problem* p, const void* q, const void* k, cons
                       "attention (decode)");
   uint16_t* vt = (uint16_t*)(w + L.vt);
   int* queues = (int*)(w + L.queues);
-  hipError_t e = ssa::launch_transpose((const uint16_t*)v, vt, d.B * d.Hkv, d.Nk, d.D, queues, st);
+  hipError_t e = ssa::launch_transpose((const uint16_t*)v, vt, d.B * d.Hkv, d.Nk, d.D, queues,
+                                       ssa::prefill_vt_blk16(d, h_full == nullptr), st);
   if (e != hipSuccess) return hip_status(e, "transpose v");
   return hip_status(ssa::launch_attn_prefill_bf16((const uint16_t*)q, (const uint16_t*)k, vt, idx,
                                                   cnt, (uint16_t*)h_full, (uint16_t*)h_sparse,

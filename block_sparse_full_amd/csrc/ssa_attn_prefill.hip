@@ -1575,6 +1575,200 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
   }   // work items
 }
 
+// Sparse-only prefill with 16-token blocks (h_full == NULL, one list per
+// 16-row query block): only the selected keys are read and multiplied. A wave
+// owns one list (16 query rows) and walks its selected blocks two at a time
+// (32 keys), gathered straight from L2 into MFMA operand registers: no LDS,
+// no barriers, and exactly the algorithmic MFMA work of the sparse stream
+// ("SSA: Achieving Sparser Attention ...", section "Practical Implementation
+// of SSA": attention over the concatenated keys and values of the selected
+// blocks only).
+//
+// MFMA 16x16x32 bf16. S^T = K Q^T: the pair's 32 keys sit at positions
+// p = 0..15 (first block) and 16..31 (second); MFMA tile t reads, in row r,
+// the key at position 8*(r/4) + 4*t + r%4, so lane group g (lanes 16g ..
+// 16g+15) receives positions 8g .. 8g+7 across the two tiles: exactly the
+// eight keys of the PV B operand for k = 8g .. 8g+7, which are consecutive
+// keys of one block. V^T comes in the per-block layout [n/16][d][16] (made
+// by the V transpose for these calls), so the V^T operand of a block is 16
+// contiguous 32-byte rows: one 16-byte load per lane and d tile, whole cache
+// lines per wave. Lanes of rows r < 8 gather K from the first block, r >= 8
+// from the second. The diagonal block is masked per key (key > row gives
+// -inf); an odd count ends with a masked second half. Online softmax with
+// lazy rescaling as in the other kernels; each lane keeps partial row sums
+// over its keys, reduced over the four lanes of its query at the end.
+//
+// A workgroup is four consecutive lists in (b, kv head, query block, q head
+// of the group) order, so its waves share most of their blocks through L1
+// and L2 (the sink and diagonal blocks always).
+template <int D>
+__global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_sparse_gather_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ Vb, const int* __restrict__ idx, const int* __restrict__ cnt,
+    uint16_t* __restrict__ Hs, float* __restrict__ lse, Dims d, HeadMap hm) {
+  constexpr int NKS = D / 32;    // k-steps of QK^T
+  constexpr int NDT = D / 16;    // 16-wide d tiles of O^T
+  constexpr float kTau = 8.0f;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int n = lane & 15, g4 = lane >> 4;
+
+  // ---- which list
+  const int nlists = d.B * d.Hkv * d.nQB * d.G;
+  const int nwg = (nlists + 3) / 4;
+  const int li = 4 * xcd_remap(blockIdx.x, nwg) + wave;   // (b, g, qb, head of group) order
+  if (li >= nlists) return;
+  const int hi = li % d.G;
+  const int qb = (li / d.G) % d.nQB;
+  const int bg = li / (d.G * d.nQB);
+  const int b = bg / d.Hkv, g = bg - b * d.Hkv;
+  const int h = hm.q_of_kv[g * d.G + hi];
+  const int bh = b * d.Hq + h;
+  const int q0 = qb * 16;
+  const int qrow = q0 + n;
+  const size_t lrow = (size_t)bh * d.nQB + qb;
+  const int* list = idx + lrow * d.budget;
+  const int nsub = __builtin_amdgcn_readfirstlane(min(max(cnt[lrow], 0), d.budget));
+  auto sub_start = [&](int s) __attribute__((always_inline)) -> int {
+    return __builtin_amdgcn_readfirstlane(list[s]) * 16;
+  };
+
+  const float sl2 = d.scale_log2;
+  const uint16_t* kbase = K + ((size_t)(b * d.Hkv + g) * d.Nk) * D;
+  const uint16_t* vbase = Vb + ((size_t)(b * d.Hkv + g) * D) * d.Nk;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)((size_t)d.Nk * D * 2));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)((size_t)d.Nk * D * 2));
+  // per-lane byte offsets: K row of tiles 0 and 1 (key within its block, d
+  // chunk), V^T row (d) and key chunk within the block's [d][16] tile
+  const bool first_half = n < 8;
+  const int kin0 = (8 * (n >> 2) + (n & 3)) & 15;   // tile 0 key (tile 1: +4)
+  const uint32_t koff0 = (uint32_t)((kin0 * D + 8 * g4) * 2);
+  const uint32_t koff1 = (uint32_t)(((kin0 + 4) * D + 8 * g4) * 2);
+  const bool vfirst = g4 < 2;
+  const uint32_t voff_lane = (uint32_t)(n * 32 + (g4 & 1) * 16);
+
+  bf16x8_t qf[NKS];
+  {
+    const uint16_t* qp = Q + ((size_t)bh * d.Nq + qrow) * D + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8_t*)(qp + 32 * ks);
+  }
+
+  struct Frags { bf16x8_t k0[NKS], k1[NKS], v[NDT]; };
+  // a block starting at key s: K rows s*D*2 bytes in, V^T tile s*D*2 bytes in
+  auto load_pair = [&](Frags& f, int ka, int kb2) __attribute__((always_inline)) {
+    const uint32_t kb = (uint32_t)(first_half ? ka : kb2) * (uint32_t)(D * 2);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      f.k0[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
+          krs, kb + koff0 + 64u * ks, 0, 0));
+      f.k1[ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
+          krs, kb + koff1 + 64u * ks, 0, 0));
+    }
+    const uint32_t vk = (uint32_t)(vfirst ? ka : kb2) * (uint32_t)(D * 2) + voff_lane;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      f.v[dt] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
+          vrs, vk + 512u * dt, 0, 0));
+  };
+
+  f32x4_t o[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_sum = 0.f;
+
+  // one pair: blocks starting at keys ka and kb2; kb2 < 0: no second one
+  auto compute = [&](const Frags& f, int ka, int kb2) __attribute__((always_inline)) {
+    f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k0[ks], qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k1[ks], qf[ks], s1, 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    // keys past the row (the diagonal block) and a missing second half
+    if (ka + 15 > q0 || kb2 < 0 || kb2 + 15 > q0) {
+      const int kbase_l = vfirst ? ka : kb2;
+      const bool dead = !vfirst && kb2 < 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int key0 = kbase_l + 8 * (g4 & 1) + v;   // tile 0 key of this lane's value v
+        if (dead || key0 > qrow) s0[v] = -INFINITY;
+        if (dead || key0 + 4 > qrow) s1[v] = -INFINITY;
+      }
+    }
+    const float mx = fmaxf(max3f(s0[0], s0[1], s0[2]), max3f(s0[3], s1[0], max3f(s1[1], s1[2], s1[3])));
+    const float m_blk = quad_max(mx) * sl2;
+    if (__builtin_amdgcn_ballot_w64(m_blk > m_ref + kTau) != 0) {
+      const float m_new = fmaxf(m_ref, m_blk);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[i][v] *= alpha;
+      l_sum *= alpha;
+    }
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    uint32_t pw[4];
+    pw[0] = pack_bf16x2(fast_exp2(fmaf(s0[0], sl2, -m_use)), fast_exp2(fmaf(s0[1], sl2, -m_use)));
+    pw[1] = pack_bf16x2(fast_exp2(fmaf(s0[2], sl2, -m_use)), fast_exp2(fmaf(s0[3], sl2, -m_use)));
+    pw[2] = pack_bf16x2(fast_exp2(fmaf(s1[0], sl2, -m_use)), fast_exp2(fmaf(s1[1], sl2, -m_use)));
+    pw[3] = pack_bf16x2(fast_exp2(fmaf(s1[2], sl2, -m_use)), fast_exp2(fmaf(s1[3], sl2, -m_use)));
+    l_sum = add_bf16x2(pw[0], l_sum);
+    l_sum = add_bf16x2(pw[1], l_sum);
+    l_sum = add_bf16x2(pw[2], l_sum);
+    l_sum = add_bf16x2(pw[3], l_sum);
+    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.v[dt], pb, o[dt], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // pairs of blocks, the next pair's loads in flight during this one's
+  const int npairs = (nsub + 1) >> 1;
+  auto starts = [&](int i, int& ka, int& kb2) __attribute__((always_inline)) {
+    ka = sub_start(2 * i);
+    kb2 = 2 * i + 1 < nsub ? sub_start(2 * i + 1) : -1;
+  };
+  Frags fa, fb;
+  int ka = 0, kb2 = -1, na = 0, nb2 = -1;
+  if (npairs > 0) {
+    starts(0, ka, kb2);
+    load_pair(fa, ka, kb2 < 0 ? ka : kb2);
+  }
+  for (int i = 0; i < npairs; i += 2) {
+    if (i + 1 < npairs) {
+      starts(i + 1, na, nb2);
+      load_pair(fb, na, nb2 < 0 ? na : nb2);
+    }
+    compute(fa, ka, kb2);
+    if (i + 1 >= npairs) break;
+    if (i + 2 < npairs) {
+      starts(i + 2, ka, kb2);
+      load_pair(fa, ka, kb2 < 0 ? ka : kb2);
+    }
+    compute(fb, na, nb2);
+  }
+
+  const float lt = quad_sum(l_sum);
+  const float inv = 1.f / lt;
+  uint16_t* hp = Hs + ((size_t)bh * d.Nq + qrow) * D;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const uint32_t lo = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+    const uint32_t hi2 = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
+    *(uint2*)(hp + 16 * dt + 4 * g4) = make_uint2(lo, hi2);
+  }
+  if (lse != nullptr && g4 == 0) {
+    const size_t plane = (size_t)d.B * d.Hq * d.Nq;
+    lse[plane + (size_t)bh * d.Nq + qrow] = (m_ref + __log2f(lt)) * kLn2;
+  }
+}
+
 // Compute units of the current device (cached per device; threads that race
 // on the first call store the same value).
 static hipError_t compute_units(int* out) {
@@ -1611,6 +1805,18 @@ hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const 
       if (d.bs == 16) SSA_TOK_LAUNCH(64, 16); else SSA_TOK_LAUNCH(64, 64);
     }
 #undef SSA_TOK_LAUNCH
+    return hipGetLastError();
+  }
+  if (prefill_vt_blk16(d, hf == nullptr)) {
+    // sparse-only, 16-token per-block lists: gather only the selected keys
+    const int nlists = d.B * d.Hkv * d.nQB * d.G;
+    const int nwg = (nlists + 3) / 4;
+    if (d.D == 128)
+      hipLaunchKernelGGL((attn_sparse_gather_kernel<128>), dim3(nwg), dim3(256), 0, stream, q, k,
+                         vt, idx, cnt, hs, lse, d, hm);
+    else
+      hipLaunchKernelGGL((attn_sparse_gather_kernel<64>), dim3(nwg), dim3(256), 0, stream, q, k,
+                         vt, idx, cnt, hs, lse, d, hm);
     return hipGetLastError();
   }
   if (d.bs == 16 && d.D == 64 && d.G % 4 == 0 && hf != nullptr) {

@@ -39,8 +39,14 @@ inline size_t tok_kc_bytes(const Dims& d) {
 hipError_t launch_select_tok(const void* q, bool bf16, const float* kbar, double* kc, int* idx,
                              int* cnt, const Dims& d, const HeadMap& hm, hipStream_t stream);
 // Also zeroes the prefill work queues (kNumXcd counters) when queues != NULL.
+// blk16: the layout of prefill_vt_blk16 problems ([n/16][d][n%16] per head).
 hipError_t launch_transpose(const uint16_t* v, uint16_t* vt, int BH, int N, int D, int* queues,
-                            hipStream_t stream);
+                            bool blk16, hipStream_t stream);
+// Sparse-only prefill with 16-token per-block lists runs the gather kernel,
+// which reads V^T one 16-key block at a time: contiguous per block.
+inline bool prefill_vt_blk16(const Dims& d, bool sparse_only) {
+  return sparse_only && d.bs == 16 && !d.tok;
+}
 
 // queues: kNumXcd zeroed counters (see launch_transpose), or NULL for a
 // static workgroup-to-tile mapping.

@@ -498,7 +498,10 @@ hipError_t launch_select_tok(const void* q, bool bf16, const float* kbar, double
 }
 
 // ---------------------------------------------------------------- V transpose
-// vt[bh][d][n] = v[bh][n][d] for bf16, 64x64 tiles through LDS.
+// vt[bh][d][n] = v[bh][n][d] for bf16, 64x64 tiles through LDS; or, with
+// blk16, vt[bh][n/16][d][n%16]: the V^T of each 16-key block contiguous (D x
+// 16 keys), for the gather kernel of sparse-only 16-token blocks.
+template <bool BLK16>
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ v,
                                                         uint16_t* __restrict__ vt, int N, int D,
                                                         int* __restrict__ queues) {
@@ -513,13 +516,21 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   for (int r = ty; r < 64; r += 4) tile[r][tx] = src[(size_t)(n0 + r) * D + d0 + tx];
   __syncthreads();
-  for (int r = ty; r < 64; r += 4) dst[(size_t)(d0 + r) * N + n0 + tx] = tile[tx][r];
+  for (int r = ty; r < 64; r += 4) {
+    const int n = n0 + tx, dd = d0 + r;
+    const size_t o = BLK16 ? ((size_t)(n >> 4) * D + dd) * 16 + (n & 15) : (size_t)dd * N + n;
+    dst[o] = tile[tx][r];
+  }
 }
 
 hipError_t launch_transpose(const uint16_t* v, uint16_t* vt, int BH, int N, int D, int* queues,
-                            hipStream_t stream) {
-  hipLaunchKernelGGL(transpose_kernel, dim3(N / 64, D / 64, BH), dim3(256), 0, stream, v, vt,
-                     N, D, queues);
+                            bool blk16, hipStream_t stream) {
+  if (blk16)
+    hipLaunchKernelGGL(transpose_kernel<true>, dim3(N / 64, D / 64, BH), dim3(256), 0, stream, v,
+                       vt, N, D, queues);
+  else
+    hipLaunchKernelGGL(transpose_kernel<false>, dim3(N / 64, D / 64, BH), dim3(256), 0, stream, v,
+                       vt, N, D, queues);
   return hipGetLastError();
 }
 

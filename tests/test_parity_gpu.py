@@ -88,14 +88,18 @@ def test_decode_sparse_only_and_pooled_table(ssa):
     assert_close("sparse-only vs dual", to_np64(sp["h_sparse"]), to_np64(dual["h_sparse"]), 1e-2)
 
 
-def test_prefill_sparse_only_matches_dual_bitwise(ssa):
-    """Two q heads per kv head: both modes run the per-head kernel, whose
-    sparse-only walk is the first part of the dual walk."""
+def test_prefill_sparse_only_matches_dual(ssa):
+    """Two q heads per kv head: dual mode runs the per-head kernel, sparse-only
+    the gather kernel (a different summation order, so not bit for bit); both
+    match the oracle and each other."""
     cfg = CONFIGS["gqa_8k_peaked"].with_sizes(B=1, Hq=4, Hkv=2, N=1024, budget=4)
     x = make_inputs(cfg)
     dual = gpu_run(ssa, x, budget=4)
     sp = gpu_run(ssa, x, budget=4, sparse_only=True)
-    assert torch.equal(sp["h_sparse"], dual["h_sparse"])
+    ref = full_compare(cfg, x, dual, budget=4)
+    assert torch.equal(sp["idx"], dual["idx"])
+    assert_close("h_sparse (sparse-only)", to_np64(sp["h_sparse"]), ref["h_sparse"], BF16_ABS, BF16_REL_L2)
+    assert_close("sparse-only vs dual", to_np64(sp["h_sparse"]), to_np64(dual["h_sparse"]), 1e-2)
 
 
 def test_prefill_sparse_only_grouped_shape(ssa):
@@ -194,6 +198,38 @@ def test_block16_parity(ssa, name, kw, budget, n_sink, n_local, sparse):
                   sparse_only=sparse, block=16)
     full_compare(cfg, x, got, budget=budget, n_sink=n_sink, n_local=n_local, lse=not sparse,
                  sparse_only=sparse)
+
+
+# Sparse-only prefill with per-block lists (the gather kernel): 16- and
+# 64-token blocks, D 64 and 128, GQA 1:1 to 16:1 and 3:1 (workgroups whose
+# four lists span query blocks), odd list lengths, no forced blocks (the
+# diagonal may be missing), lists that cover every causal block, a head map,
+# 9 query tiles; h_sparse and the sparse lse against the oracle
+SPARSE_GATHER = [
+    ("paper_16k_b16", dict(Hq=16, Hkv=1, N=1024), 16, 1, 1, None),
+    ("paper_16k_b16", dict(Hq=4, Hkv=2, N=1024, D=128), 7, 1, 1, None),
+    ("paper_16k_b16", dict(Hq=3, Hkv=1, N=576, planted=False), 5, 0, 0, None),
+    ("paper_16k_b16", dict(B=2, Hq=8, Hkv=2, N=512), 40, 1, 1, None),
+    ("paper_16k_b16", dict(Hq=8, Hkv=2, N=1024), 9, 2, 2, [1, 0, 0, 1, 1, 0, 1, 0]),
+    ("gqa_8k_peaked", dict(B=2, Hq=8, Hkv=2, N=1024), 4, 1, 1, None),
+    ("gqa_8k_peaked", dict(B=1, Hq=4, Hkv=1, N=2048, D=64), 5, 0, 0, None),
+    ("gqa_8k_peaked", dict(B=1, Hq=3, Hkv=3, N=576, planted=False), 3, 1, 1, None),
+    ("gqa_8k_peaked", dict(B=1, Hq=4, Hkv=2, N=1024), 16, 1, 1, None),
+    ("mha_4k", dict(Hq=2, Hkv=2, N=640), 3, 0, 1, None),
+]
+
+
+@pytest.mark.parametrize("name,kw,budget,n_sink,n_local,hm", SPARSE_GATHER,
+                         ids=[f"gather-{i}" for i in range(len(SPARSE_GATHER))])
+def test_sparse_only_gather_parity(ssa, name, kw, budget, n_sink, n_local, hm):
+    cfg = CONFIGS[name].with_sizes(budget=budget, n_sink=n_sink, n_local=n_local, **kw)
+    say(f"[parity] sparse-only gather {cfg} head_map={hm}")
+    x = make_inputs(cfg, head_map=hm)
+    got = gpu_run(ssa, x, budget=budget, n_sink=n_sink, n_local=n_local, head_map=hm,
+                  want_lse=True, sparse_only=True, block=cfg.block)
+    assert "h_full" not in got
+    full_compare(cfg, x, got, budget=budget, n_sink=n_sink, n_local=n_local, head_map=hm,
+                 lse=True, sparse_only=True)
 
 
 def test_block16_group_select(ssa):

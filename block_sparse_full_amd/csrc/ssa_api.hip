@@ -40,7 +40,7 @@ struct Problem {
 };
 
 struct Layout {
-  size_t qbar, kbar, kc, vt, queues, partials, loss, total;
+  size_t qbar, kbar, kc, keys, vt, queues, partials, loss, total;
 };
 
 Layout layout_of(const Problem& P) {
@@ -53,6 +53,8 @@ Layout layout_of(const Problem& P) {
   off += align256((size_t)d.B * d.Hkv * d.nKB * d.D * sizeof(float));
   L.kc = off;   // per-token selection: float64 pooled keys, 16-block chunks
   if (d.tok) off += align256(ssa::tok_kc_bytes(d));
+  L.keys = off;   // decode: every candidate's orderable score key, per q head
+  if (P.decode) off += align256((size_t)d.B * d.Hq * d.nKB * sizeof(uint64_t));
   L.vt = off;
   if (P.bf16 && !P.decode) off += align256((size_t)d.B * d.Hkv * d.D * d.Nk * sizeof(uint16_t));
   L.queues = off;   // prefill work queues, zeroed by the V transpose of every call
@@ -322,7 +324,8 @@ ssa_status ssa_select_blocks(const ssa_problem* p, const void* q, const void* k,
     if (e != hipSuccess) return hip_status(e, "pool k");
     kbar = kb;
   }
-  return hip_status(ssa::launch_select(qbar, kbar, idx, cnt, d, P.hm, st), "select");
+  uint64_t* gkeys = P.decode ? (uint64_t*)(w + L.keys) : nullptr;
+  return hip_status(ssa::launch_select(qbar, kbar, idx, cnt, d, P.hm, gkeys, st), "select");
 }
 
 ssa_status ssa_attn_fwd(const ssa_problem* p, const void* q, const void* k, const void* v,

@@ -16,7 +16,7 @@ constexpr size_t kSelKeyBytes = 32 * 1024; // LDS for the selection keys
 // workgroup has kDecWaves waves.
 constexpr int kDecWaves = 4;
 constexpr int kDecWaveBlocks = 8;
-constexpr int kDecSparseParts = 4;         // workgroups per (b, kv head), sparse-only
+constexpr int kDecSparseParts = 2;         // workgroups per (b, kv head), sparse-only
 constexpr int kDecMaxGroup = 8;            // q heads per bf16 decode workgroup (larger groups split)
 
 inline int decode_splits(int nKB) {        // partial results per (b, q head), dual mode
@@ -27,8 +27,10 @@ inline int decode_partial_floats(int D) { return 2 * D + 4; }
 
 hipError_t launch_pool(const void* x, bool bf16, float* out, long nblk_total, int bs, int D,
                        hipStream_t stream);
+// gkeys: NULL (scores computed inside the selection kernel), or for decode a
+// [B, Hq, nKB] scratch that a wide scoring kernel fills first.
 hipError_t launch_select(const float* qbar, const float* kbar, int* idx, int* cnt,
-                         const Dims& d, const HeadMap& hm, hipStream_t stream);
+                         const Dims& d, const HeadMap& hm, uint64_t* gkeys, hipStream_t stream);
 // Per-token selection: float64 copy of the pooled keys in chunks of
 // kTokChunk blocks ([B*Hkv][chunk][D][kTokChunk]), read as scalar operands.
 constexpr int kTokChunk = 16;

@@ -124,7 +124,8 @@ __device__ __forceinline__ void wave_lds_fence() {
 
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar,
-    int* __restrict__ idx, int* __restrict__ cnt, Dims d, HeadMap hm, int hc) {
+    const uint64_t* __restrict__ gkeys, int* __restrict__ idx, int* __restrict__ cnt, Dims d,
+    HeadMap hm, int hc) {
   extern __shared__ __align__(16) unsigned char smem[];
   // layout: keys[hc or 1][nKB] u64 | qv[hc][D] f32
   uint64_t* keys = (uint64_t*)smem;
@@ -160,7 +161,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       qv[i] = qbar[((size_t)(b * d.Hq + h) * d.nQB + qb) * d.D + dd];
     }
     __syncthreads();
-    if (!take_all && !forced_only) {
+    if (!take_all && !forced_only && gkeys != nullptr) {
+      // keys scored by decode_score_kernel: copy the candidates' keys
+      const int rows = d.group_select ? 1 : nh;
+      for (int i = tid; i < rows * ncausal; i += kSelThreads) {
+        const int hh = i / ncausal, kb = i - hh * ncausal;
+        if (is_forced(kb, diag, d.n_sink, d.n_local)) continue;
+        const size_t krow = d.group_select ? (size_t)(b * d.Hkv + g)
+                                           : (size_t)(b * d.Hkv + g) * d.G + h0 + hh;
+        keys[(size_t)hh * d.nKB + kb] = gkeys[krow * d.nKB + kb];
+      }
+    } else if (!take_all && !forced_only) {
       // Scores of every candidate for the nh heads.
       for (int kb = tid; kb < ncausal; kb += kSelThreads) {
         if (is_forced(kb, diag, d.n_sink, d.n_local)) continue;
@@ -292,12 +303,89 @@ size_t select_smem_bytes(const Dims& d, int hc) {
   return (size_t)key_rows * d.nKB * sizeof(uint64_t) + (size_t)hc * d.D * sizeof(float);
 }
 
+// Decode scoring: one lane per candidate key block, 64 candidates per
+// workgroup, all q heads of the group (the single query of each head is its
+// block representation; its float32 values come from qbar as scalar
+// operands). The same float64 ascending-d dot products and orderable keys as
+// select_kernel's own scoring, written to gkeys [B, Hkv, G, nKB] (or the
+// group sum to [B, Hkv, nKB] with group-shared selection); forced and
+// non-causal blocks are not written. Spreading the pooled-key table over
+// B * Hkv * nKB / 64 workgroups keeps enough loads in flight to stream it at
+// HBM speed; select_kernel then runs the top-k on these keys.
+template <int D>
+__global__ __launch_bounds__(64) void decode_score_kernel(const float* __restrict__ qbar,
+                                                          const float* __restrict__ kbar,
+                                                          uint64_t* __restrict__ gkeys, Dims d,
+                                                          HeadMap hm) {
+  const int kb = blockIdx.x * 64 + (int)threadIdx.x;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int diag = row_block_diag(d, 0);
+  if (kb > diag || is_forced(kb, diag, d.n_sink, d.n_local)) return;
+  const float* kr = kbar + ((size_t)(b * d.Hkv + g) * d.nKB + kb) * D;
+  const size_t krow0 = (size_t)(b * d.Hkv + g);
+  double gsum = 0.0;
+  for (int hb = 0; hb < d.G; hb += 4) {
+    const float* qv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = hm.q_of_kv[g * d.G + min(hb + j, d.G - 1)];
+      qv[j] = qbar + (size_t)(b * d.Hq + h) * D;   // nQB == 1
+    }
+    double sc[4] = {0.0, 0.0, 0.0, 0.0};
+    // 16 floats of the row per step, the next step's loads in flight
+    auto load16 = [&](float4* f, int c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = *(const float4*)(kr + 16 * c + 4 * i);
+    };
+    auto fma16 = [&](const float4* f, int c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float kk[4] = {f[i].x, f[i].y, f[i].z, f[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double kv = (double)kk[e];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            sc[j] = __fma_rn((double)qv[j][16 * c + 4 * i + e], kv, sc[j]);
+        }
+      }
+    };
+    float4 fa[4], fb[4];
+    load16(fa, 0);
+#pragma unroll 1
+    for (int c = 0; c < D / 16; c += 2) {
+      load16(fb, c + 1);
+      fma16(fa, c);
+      if (c + 2 < D / 16) load16(fa, c + 2);
+      fma16(fb, c + 1);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (hb + j >= d.G) break;
+      if (d.group_select) gsum += sc[j];
+      else gkeys[(krow0 * d.G + hb + j) * d.nKB + kb] = orderable_key(sc[j]);
+    }
+  }
+  if (d.group_select) gkeys[krow0 * d.nKB + kb] = orderable_key(gsum);
+}
+
 hipError_t launch_select(const float* qbar, const float* kbar, int* idx, int* cnt,
-                         const Dims& d, const HeadMap& hm, hipStream_t stream) {
+                         const Dims& d, const HeadMap& hm, uint64_t* gkeys, hipStream_t stream) {
   const int hc = select_heads_per_pass(d);
   const size_t smem = select_smem_bytes(d, hc);
+  if (gkeys != nullptr) {
+    const dim3 grid((d.nKB + 63) / 64, d.Hkv, d.B);
+    if (d.D == 128)
+      hipLaunchKernelGGL(decode_score_kernel<128>, grid, dim3(64), 0, stream, qbar, kbar, gkeys,
+                         d, hm);
+    else
+      hipLaunchKernelGGL(decode_score_kernel<64>, grid, dim3(64), 0, stream, qbar, kbar, gkeys,
+                         d, hm);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(select_kernel, dim3(d.nQB, d.Hkv, d.B), dim3(kSelThreads), smem, stream,
-                     qbar, kbar, idx, cnt, d, hm, hc);
+                     qbar, kbar, gkeys, idx, cnt, d, hm, hc);
   return hipGetLastError();
 }
 

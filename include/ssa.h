@@ -30,7 +30,9 @@
  *   - Ownership: the caller owns every buffer; the library never allocates
  *     device or host memory. Scratch memory is the caller's workspace of
  *     ssa_workspace_bytes() bytes (ssa_bwd_workspace_bytes() for the
- *     backward; device memory, 256-byte aligned).
+ *     backward; device memory, 256-byte aligned). The one exception is
+ *     ssa_align_loss_noalloc, whose 8 KiB of partial sums are a static
+ *     device array of the library (one per GPU, loaded with the library).
  *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
  *     stream). Every call only enqueues kernels on it and returns without
  *     synchronising. Calls are reentrant; calls that share a workspace must

@@ -1601,8 +1601,9 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
 // A workgroup is four consecutive lists in (b, kv head, query block, q head
 // of the group) order, so its waves share most of their blocks through L1
 // and L2 (the sink and diagonal blocks always).
+constexpr int kGatherLists = 4;   // lists (waves) per workgroup
 template <int D>
-__global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_sparse_gather_kernel(
+__global__ __launch_bounds__(64 * kGatherLists) void attn_sparse_gather_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vb, const int* __restrict__ idx, const int* __restrict__ cnt,
     uint16_t* __restrict__ Hs, float* __restrict__ lse, Dims d, HeadMap hm) {
@@ -1615,8 +1616,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_sparse_gather_ker
 
   // ---- which list
   const int nlists = d.B * d.Hkv * d.nQB * d.G;
-  const int nwg = (nlists + 3) / 4;
-  const int li = 4 * xcd_remap(blockIdx.x, nwg) + wave;   // (b, g, qb, head of group) order
+  const int nwg = (nlists + kGatherLists - 1) / kGatherLists;
+  const int li = kGatherLists * xcd_remap(blockIdx.x, nwg) + wave;   // (b, g, qb, head) order
   if (li >= nlists) return;
   const int hi = li % d.G;
   const int qb = (li / d.G) % d.nQB;
@@ -1769,6 +1770,234 @@ __global__ __launch_bounds__(256, (D == 64 ? 3 : 2)) void attn_sparse_gather_ker
   }
 }
 
+// Sparse-only prefill, 16-token blocks, q heads per kv head a multiple of 4:
+// one workgroup = (b, kv head, 16-row query block, four q heads of the
+// group), one wave per head. The four heads' lists are merged into their
+// union (ascending, with a 4-bit mask of the heads that selected each block),
+// and the union's K rows and V^T tiles pass through LDS in chunks of CAP
+// blocks, each loaded once for the four heads (the heads of a group share
+// most blocks: the sink and the diagonal always). Small chunks (16 KB of LDS
+// at D 64) let five workgroups share a CU, whose loads and list set-up
+// overlap the others' MFMA work: measured faster than 8- and 16-block chunks
+// despite more odd-block padding. Per chunk each wave takes
+// its own selected blocks two at a time with the S^T / PV operand mapping of
+// attn_sparse_gather_kernel, reading the fragments from LDS; an odd block
+// left at the end of a chunk is paired with a masked half. Exactly the
+// selected keys enter the softmax; only that padding adds MFMA work.
+//
+// LDS layouts (16-byte chunks): K block slot s, key row r, logical chunk c at
+// position s*2D + r*(D/8) + (c ^ kf(r, s)); V^T block slot s, d row, key half
+// h at s*2D + 2*d + (h ^ ((d >> 3) & 1)). kf spreads the 16 rows one
+// ds_read_b128 phase reads (8 rows of each of the pair's two blocks) over
+// distinct bank groups whenever the two slots differ in parity.
+template <int D>
+__device__ __forceinline__ int kf16(int r, int s) {
+  if constexpr (D == 64) return ((r >> 1) & 7) ^ ((s & 1) << 1);
+  else return (r & 3) | ((r >> 1) & 4) | ((s & 1) << 3);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_sparse_union16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ Vb, const int* __restrict__ idx, const int* __restrict__ cnt,
+    uint16_t* __restrict__ Hs, float* __restrict__ lse, Dims d, HeadMap hm) {
+  constexpr int NKS = D / 32, NDT = D / 16, KCH = D / 8;
+  constexpr int CAP = D == 64 ? 4 : 2;             // union blocks per LDS chunk
+  constexpr int PCS = 2 * D;                      // 16-byte pieces per block tile
+  constexpr int kMaxWords = kMaxKeyBlocks / 32;
+  constexpr float kTau = 8.0f;
+  __shared__ __align__(16) uint16_t Ks[CAP * PCS * 8];
+  __shared__ __align__(16) uint16_t Vs[CAP * PCS * 8];
+  __shared__ uint32_t sel[4][kMaxWords];
+  __shared__ uint16_t ulist[kMaxKeyBlocks];
+  __shared__ int s_nu;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
+  const int n = lane & 15, g4 = lane >> 4;
+  const int ngrp = d.G / 4;
+  const int total = d.B * d.Hkv * ngrp * d.nQB;
+  const int lin = xcd_remap(blockIdx.x, total);   // (b, g, qb, head group) order
+  const int hg = lin % ngrp;
+  const int qb = (lin / ngrp) % d.nQB;
+  const int bg = lin / (ngrp * d.nQB);
+  const int b = bg / d.Hkv, g = bg - b * d.Hkv;
+  const int h = hm.q_of_kv[g * d.G + 4 * hg + wave];
+  const int bh = b * d.Hq + h;
+  const int diag = qb;
+  const int q0 = qb * 16, qrow = q0 + n;
+  const int nwords = (diag >> 5) + 1;
+
+  // ---- union of the four lists
+  for (int i = tid; i < 4 * kMaxWords; i += 256) (&sel[0][0])[i] = 0u;
+  __syncthreads();
+  {
+    const size_t lrow = (size_t)bh * d.nQB + qb;
+    const int ns = min(max(cnt[lrow], 0), d.budget);
+    for (int e = lane; e < ns; e += 64) {
+      const int kb = idx[lrow * d.budget + e];
+      if (kb >= 0 && kb <= diag) atomicOr(&sel[wave][kb >> 5], 1u << (kb & 31));
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // lane l owns words 2l and 2l+1 (kMaxWords <= 128)
+    uint32_t any[2], cntw = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int w = 2 * lane + j;
+      any[j] = w < nwords ? (sel[0][w] | sel[1][w] | sel[2][w] | sel[3][w]) : 0u;
+      cntw += __popc(any[j]);
+    }
+    int incl = (int)cntw;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    int pos = incl - (int)cntw;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int w = 2 * lane + j;
+      for (uint32_t bb = any[j]; bb != 0u; bb &= bb - 1u) {
+        const int bit = __builtin_ctz(bb);
+        uint32_t act = 0u;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) act |= ((sel[u][w] >> bit) & 1u) << u;
+        ulist[pos++] = (uint16_t)(((w << 5) + bit) | (act << 12));
+      }
+    }
+    if (lane == 63) s_nu = incl;
+  }
+  __syncthreads();
+  const int nu = s_nu;
+
+  // ---- per-wave state
+  bf16x8_t qf[NKS];
+  {
+    const uint16_t* qp = Q + ((size_t)bh * d.Nq + qrow) * D + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8_t*)(qp + 32 * ks);
+  }
+  f32x4_t o[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY, l_sum = 0.f;
+  const float sl2 = d.scale_log2;
+  const uint16_t* kbase = K + ((size_t)(b * d.Hkv + g) * d.Nk) * D;
+  const uint16_t* vbase = Vb + ((size_t)(b * d.Hkv + g) * D) * d.Nk;
+  const bool first_half = n < 8;
+  const int kin0 = (8 * (n >> 2) + (n & 3)) & 15;   // tile 0 key of this lane's row (tile 1: +4)
+  const bool vfirst = g4 < 2;
+
+  // one pair: blocks in LDS slots sa, sb (sb < 0: none) starting at keys ka, kb2
+  auto pair = [&](int sa, int sb, int ka, int kb2) __attribute__((always_inline)) {
+    const int sk = first_half ? sa : (sb < 0 ? sa : sb);
+    const int sv = vfirst ? sa : (sb < 0 ? sa : sb);
+    bf16x8_t k0[NKS], k1[NKS], vf[NDT];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int c = 4 * ks + g4;
+      k0[ks] = *(const bf16x8_t*)(Ks + (sk * PCS + kin0 * KCH + (c ^ kf16<D>(kin0, sk))) * 8);
+      k1[ks] = *(const bf16x8_t*)(Ks + (sk * PCS + (kin0 + 4) * KCH + (c ^ kf16<D>(kin0 + 4, sk))) * 8);
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int dd = 16 * dt + n;
+      vf[dt] = *(const bf16x8_t*)(Vs + (sv * PCS + 2 * dd + ((g4 & 1) ^ ((dd >> 3) & 1))) * 8);
+    }
+    f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[ks], qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[ks], qf[ks], s1, 0, 0, 0);
+    }
+    if (ka + 15 > q0 || kb2 < 0 || kb2 + 15 > q0) {
+      const int kbase_l = vfirst ? ka : kb2;
+      const bool dead = !vfirst && kb2 < 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int key0 = kbase_l + 8 * (g4 & 1) + v;
+        if (dead || key0 > qrow) s0[v] = -INFINITY;
+        if (dead || key0 + 4 > qrow) s1[v] = -INFINITY;
+      }
+    }
+    const float mx = fmaxf(max3f(s0[0], s0[1], s0[2]), max3f(s0[3], s1[0], max3f(s1[1], s1[2], s1[3])));
+    const float m_blk = quad_max(mx) * sl2;
+    if (__builtin_amdgcn_ballot_w64(m_blk > m_ref + kTau) != 0) {
+      const float m_new = fmaxf(m_ref, m_blk);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[i][v] *= alpha;
+      l_sum *= alpha;
+    }
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    uint32_t pw[4];
+    pw[0] = pack_bf16x2(fast_exp2(fmaf(s0[0], sl2, -m_use)), fast_exp2(fmaf(s0[1], sl2, -m_use)));
+    pw[1] = pack_bf16x2(fast_exp2(fmaf(s0[2], sl2, -m_use)), fast_exp2(fmaf(s0[3], sl2, -m_use)));
+    pw[2] = pack_bf16x2(fast_exp2(fmaf(s1[0], sl2, -m_use)), fast_exp2(fmaf(s1[1], sl2, -m_use)));
+    pw[3] = pack_bf16x2(fast_exp2(fmaf(s1[2], sl2, -m_use)), fast_exp2(fmaf(s1[3], sl2, -m_use)));
+    l_sum = add_bf16x2(pw[0], l_sum);
+    l_sum = add_bf16x2(pw[1], l_sum);
+    l_sum = add_bf16x2(pw[2], l_sum);
+    l_sum = add_bf16x2(pw[3], l_sum);
+    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pb, o[dt], 0, 0, 0);
+  };
+
+  for (int c0 = 0; c0 < nu; c0 += CAP) {
+    const int nc = min(CAP, nu - c0);
+    __syncthreads();   // every wave is done with the previous chunk's tiles
+    // copy the chunk: K rows and V^T tiles of nc blocks, 16 bytes per thread
+    for (int i = tid; i < nc * PCS; i += 256) {
+      const int s = i / PCS, rem = i - s * PCS;
+      const int kb = ulist[c0 + s] & 0xfff;
+      {
+        const int r = rem / KCH, p = rem - r * KCH;
+        const int c = p ^ kf16<D>(r, s);
+        *(uint4*)(Ks + i * 8) = *(const uint4*)(kbase + ((size_t)kb * 16 + r) * D + c * 8);
+      }
+      {
+        const int dd = rem >> 1, hh = (rem & 1) ^ ((dd >> 3) & 1);
+        *(uint4*)(Vs + i * 8) = *(const uint4*)(vbase + ((size_t)kb * D + dd) * 16 + hh * 8);
+      }
+    }
+    __syncthreads();
+    // this wave's blocks in the chunk, in pairs
+    const int e = c0 + lane;
+    const bool mine = lane < nc && ((ulist[e] >> (12 + wave)) & 1u);
+    uint64_t m = __builtin_amdgcn_ballot_w64(mine);
+    while (m != 0ull) {
+      const int sa = __builtin_ctzll(m);
+      m &= m - 1ull;
+      const int sb = m != 0ull ? __builtin_ctzll(m) : -1;
+      if (m != 0ull) m &= m - 1ull;
+      const int ka = (ulist[c0 + sa] & 0xfff) * 16;
+      const int kb2 = sb >= 0 ? (ulist[c0 + sb] & 0xfff) * 16 : -1;
+      pair(sa, sb, __builtin_amdgcn_readfirstlane(ka), __builtin_amdgcn_readfirstlane(kb2));
+    }
+  }
+
+  const float lt = quad_sum(l_sum);
+  const float inv = 1.f / lt;
+  uint16_t* hp = Hs + ((size_t)bh * d.Nq + qrow) * D;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const uint32_t lo = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+    const uint32_t hi2 = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
+    *(uint2*)(hp + 16 * dt + 4 * g4) = make_uint2(lo, hi2);
+  }
+  if (lse != nullptr && g4 == 0) {
+    const size_t plane = (size_t)d.B * d.Hq * d.Nq;
+    lse[plane + (size_t)bh * d.Nq + qrow] = (m_ref + __log2f(lt)) * kLn2;
+  }
+}
+
 // Compute units of the current device (cached per device; threads that race
 // on the first call store the same value).
 static hipError_t compute_units(int* out) {
@@ -1807,15 +2036,26 @@ hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const 
 #undef SSA_TOK_LAUNCH
     return hipGetLastError();
   }
+  if (prefill_vt_blk16(d, hf == nullptr) && d.G % 4 == 0) {
+    // sparse-only, 16-token per-block lists, four q heads per workgroup
+    const int total = d.B * d.Hkv * (d.G / 4) * d.nQB;
+    if (d.D == 128)
+      hipLaunchKernelGGL((attn_sparse_union16_kernel<128>), dim3(total), dim3(256), 0, stream, q,
+                         k, vt, idx, cnt, hs, lse, d, hm);
+    else
+      hipLaunchKernelGGL((attn_sparse_union16_kernel<64>), dim3(total), dim3(256), 0, stream, q,
+                         k, vt, idx, cnt, hs, lse, d, hm);
+    return hipGetLastError();
+  }
   if (prefill_vt_blk16(d, hf == nullptr)) {
     // sparse-only, 16-token per-block lists: gather only the selected keys
     const int nlists = d.B * d.Hkv * d.nQB * d.G;
-    const int nwg = (nlists + 3) / 4;
+    const int nwg = (nlists + kGatherLists - 1) / kGatherLists;
     if (d.D == 128)
-      hipLaunchKernelGGL((attn_sparse_gather_kernel<128>), dim3(nwg), dim3(256), 0, stream, q, k,
+      hipLaunchKernelGGL((attn_sparse_gather_kernel<128>), dim3(nwg), dim3(64 * kGatherLists), 0, stream, q, k,
                          vt, idx, cnt, hs, lse, d, hm);
     else
-      hipLaunchKernelGGL((attn_sparse_gather_kernel<64>), dim3(nwg), dim3(256), 0, stream, q, k,
+      hipLaunchKernelGGL((attn_sparse_gather_kernel<64>), dim3(nwg), dim3(64 * kGatherLists), 0, stream, q, k,
                          vt, idx, cnt, hs, lse, d, hm);
     return hipGetLastError();
   }

@@ -122,10 +122,95 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Top-k of one selection row by one wave: the free-th largest key by an
+// exact radix select over hk (8 bits per pass from the most significant byte,
+// histogram hw of 256 bins in LDS), then the ascending list of forced blocks
+// and picks (ties to the lower index) written to idx row `row` and its count.
+__device__ void select_row_wave(const uint64_t* hk, unsigned* hw, int* __restrict__ idx,
+                                int* __restrict__ cnt, size_t row, const Dims& d, int diag,
+                                int ncausal, int free_slots, bool take_all, bool forced_only) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes below
+  uint64_t thr = 0ull;   // keys above thr are taken
+  int k_eq = 0;          // and this many of the keys equal to thr
+  if (!take_all && !forced_only) {
+    uint64_t prefix = 0ull, pmask = 0ull;
+    int k = free_slots;
+    for (int pass = 0; pass < 8; ++pass) {
+      const int shift = 56 - 8 * pass;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hw[lane * 4 + j] = 0u;
+      wave_lds_fence();
+      for (int kb = lane; kb < ncausal; kb += 64) {
+        if (is_forced(kb, diag, d.n_sink, d.n_local)) continue;
+        const uint64_t key = hk[kb];
+        if ((key & pmask) == prefix) atomicAdd(&hw[(key >> shift) & 255u], 1u);
+      }
+      wave_lds_fence();
+      // lane l owns bins 255-4l .. 252-4l (descending order)
+      const int top = 255 - 4 * lane;
+      const int c0 = (int)hw[top], c1 = (int)hw[top - 1], c2 = (int)hw[top - 2],
+                c3 = (int)hw[top - 3];
+      const int csum = c0 + c1 + c2 + c3;
+      const int incl = wave_incl_scan(csum);
+      const int excl = incl - csum;
+      const bool mine = excl < k && k <= incl;
+      int bin = top, rest = k - excl, cbin = c0;
+      if (rest > c0) { rest -= c0; bin = top - 1; cbin = c1;
+        if (rest > c1) { rest -= c1; bin = top - 2; cbin = c2;
+          if (rest > c2) { rest -= c2; bin = top - 3; cbin = c3; } } }
+      const uint64_t ball = __builtin_amdgcn_ballot_w64(mine);
+      const int src = ball ? __builtin_ctzll(ball) : 0;   // ball != 0 always
+      const int sbin = __builtin_amdgcn_readlane(bin, src);
+      const int scnt = __builtin_amdgcn_readlane(cbin, src);
+      k = __builtin_amdgcn_readlane(rest, src);
+      prefix |= (uint64_t)sbin << shift;
+      pmask |= 0xFFull << shift;
+      wave_lds_fence();
+      // every remaining key of the chosen bin is taken: the selected keys
+      // are exactly those >= prefix, and the lower digits need no pass
+      if (scnt == k && prefix != 0ull) {
+        prefix -= 1ull;
+        k = 0;
+        break;
+      }
+    }
+    thr = prefix;
+    k_eq = k;
+  }
+  // ---- ascending compaction over the causal blocks, 64 at a time
+  int* out = idx + row * d.budget;
+  int n_out = 0, eq_seen = 0;
+  for (int base = 0; base < ncausal; base += 64) {
+    const int kb = base + lane;
+    const bool causal = kb < ncausal;
+    const bool forced = causal && is_forced(kb, diag, d.n_sink, d.n_local);
+    bool take = false, eq = false;
+    if (causal && !forced) {
+      if (take_all) {
+        take = true;
+      } else if (!forced_only) {
+        const uint64_t key = hk[kb];
+        take = key > thr;
+        eq = key == thr;
+      }
+    }
+    const uint64_t eq_ball = __builtin_amdgcn_ballot_w64(eq);
+    if (eq) take = (eq_seen + __popcll(eq_ball & lt_mask)) < k_eq;
+    eq_seen += __popcll(eq_ball);
+    const bool sel = forced || take;
+    const uint64_t sel_ball = __builtin_amdgcn_ballot_w64(sel);
+    const int pos = n_out + __popcll(sel_ball & lt_mask);
+    if (sel && pos < d.budget) out[pos] = kb;   // pos < budget always holds
+    n_out += __popcll(sel_ball);
+  }
+  for (int i = n_out + lane; i < d.budget; i += 64) out[i] = -1;
+  if (lane == 0) cnt[row] = min(n_out, d.budget);
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar,
-    const uint64_t* __restrict__ gkeys, int* __restrict__ idx, int* __restrict__ cnt, Dims d,
-    HeadMap hm, int hc) {
+    int* __restrict__ idx, int* __restrict__ cnt, Dims d, HeadMap hm, int hc) {
   extern __shared__ __align__(16) unsigned char smem[];
   // layout: keys[hc or 1][nKB] u64 | qv[hc][D] f32
   uint64_t* keys = (uint64_t*)smem;
@@ -161,17 +246,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       qv[i] = qbar[((size_t)(b * d.Hq + h) * d.nQB + qb) * d.D + dd];
     }
     __syncthreads();
-    if (!take_all && !forced_only && gkeys != nullptr) {
-      // keys scored by decode_score_kernel: copy the candidates' keys
-      const int rows = d.group_select ? 1 : nh;
-      for (int i = tid; i < rows * ncausal; i += kSelThreads) {
-        const int hh = i / ncausal, kb = i - hh * ncausal;
-        if (is_forced(kb, diag, d.n_sink, d.n_local)) continue;
-        const size_t krow = d.group_select ? (size_t)(b * d.Hkv + g)
-                                           : (size_t)(b * d.Hkv + g) * d.G + h0 + hh;
-        keys[(size_t)hh * d.nKB + kb] = gkeys[krow * d.nKB + kb];
-      }
-    } else if (!take_all && !forced_only) {
+    if (!take_all && !forced_only) {
       // Scores of every candidate for the nh heads.
       for (int kb = tid; kb < ncausal; kb += kSelThreads) {
         if (is_forced(kb, diag, d.n_sink, d.n_local)) continue;
@@ -209,83 +284,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     for (int hh = wave; hh < nh; hh += kSelWaves) {
       const int h = hm.q_of_kv[g * d.G + h0 + hh];
       const uint64_t* hk = keys + (size_t)(d.group_select ? 0 : hh) * d.nKB;
-      uint64_t thr = 0ull;   // keys above thr are taken
-      int k_eq = 0;          // and this many of the keys equal to thr
-      if (!take_all && !forced_only) {
-        unsigned* hw = hist[wave];
-        uint64_t prefix = 0ull, pmask = 0ull;
-        int k = free_slots;
-        for (int pass = 0; pass < 8; ++pass) {
-          const int shift = 56 - 8 * pass;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) hw[lane * 4 + j] = 0u;
-          wave_lds_fence();
-          for (int kb = lane; kb < ncausal; kb += 64) {
-            if (is_forced(kb, diag, d.n_sink, d.n_local)) continue;
-            const uint64_t key = hk[kb];
-            if ((key & pmask) == prefix) atomicAdd(&hw[(key >> shift) & 255u], 1u);
-          }
-          wave_lds_fence();
-          // lane l owns bins 255-4l .. 252-4l (descending order)
-          const int top = 255 - 4 * lane;
-          const int c0 = (int)hw[top], c1 = (int)hw[top - 1], c2 = (int)hw[top - 2],
-                    c3 = (int)hw[top - 3];
-          const int csum = c0 + c1 + c2 + c3;
-          const int incl = wave_incl_scan(csum);
-          const int excl = incl - csum;
-          const bool mine = excl < k && k <= incl;
-          int bin = top, rest = k - excl, cbin = c0;
-          if (rest > c0) { rest -= c0; bin = top - 1; cbin = c1;
-            if (rest > c1) { rest -= c1; bin = top - 2; cbin = c2;
-              if (rest > c2) { rest -= c2; bin = top - 3; cbin = c3; } } }
-          const uint64_t ball = __builtin_amdgcn_ballot_w64(mine);
-          const int src = ball ? __builtin_ctzll(ball) : 0;   // ball != 0 always
-          const int sbin = __builtin_amdgcn_readlane(bin, src);
-          const int scnt = __builtin_amdgcn_readlane(cbin, src);
-          k = __builtin_amdgcn_readlane(rest, src);
-          prefix |= (uint64_t)sbin << shift;
-          pmask |= 0xFFull << shift;
-          wave_lds_fence();
-          // every remaining key of the chosen bin is taken: the selected keys
-          // are exactly those >= prefix, and the lower digits need no pass
-          if (scnt == k && prefix != 0ull) {
-            prefix -= 1ull;
-            k = 0;
-            break;
-          }
-        }
-        thr = prefix;
-        k_eq = k;
-      }
-      // ---- ascending compaction over the causal blocks, 64 at a time
       const size_t row = (size_t)(b * d.Hq + h) * d.nQB + qb;
-      int* out = idx + row * d.budget;
-      int n_out = 0, eq_seen = 0;
-      for (int base = 0; base < ncausal; base += 64) {
-        const int kb = base + lane;
-        const bool causal = kb < ncausal;
-        const bool forced = causal && is_forced(kb, diag, d.n_sink, d.n_local);
-        bool take = false, eq = false;
-        if (causal && !forced) {
-          if (take_all) {
-            take = true;
-          } else if (!forced_only) {
-            const uint64_t key = hk[kb];
-            take = key > thr;
-            eq = key == thr;
-          }
-        }
-        const uint64_t eq_ball = __builtin_amdgcn_ballot_w64(eq);
-        if (eq) take = (eq_seen + __popcll(eq_ball & lt_mask)) < k_eq;
-        eq_seen += __popcll(eq_ball);
-        const bool sel = forced || take;
-        const uint64_t sel_ball = __builtin_amdgcn_ballot_w64(sel);
-        const int pos = n_out + __popcll(sel_ball & lt_mask);
-        if (sel && pos < d.budget) out[pos] = kb;   // pos < budget always holds
-        n_out += __popcll(sel_ball);
-      }
-      for (int i = n_out + lane; i < d.budget; i += 64) out[i] = -1;
-      if (lane == 0) cnt[row] = min(n_out, d.budget);
+      select_row_wave(hk, hist[wave], idx, cnt, row, d, diag, ncausal, free_slots, take_all,
+                      forced_only);
     }
   }
 }
@@ -310,8 +311,11 @@ size_t select_smem_bytes(const Dims& d, int hc) {
 // select_kernel's own scoring, written to gkeys [B, Hkv, G, nKB] (or the
 // group sum to [B, Hkv, nKB] with group-shared selection); forced and
 // non-causal blocks are not written. Spreading the pooled-key table over
-// B * Hkv * nKB / 64 workgroups keeps enough loads in flight to stream it at
-// HBM speed; select_kernel then runs the top-k on these keys.
+// B * Hkv * nKB / 64 workgroups keeps enough loads in flight to stream it;
+// each lane reads its own row 16 floats at a time with the next 16 in
+// flight. (Staging the rows through LDS for coalesced loads measured slower:
+// the LDS per workgroup, or the extra passes, cost more occupancy than the
+// scattered 16-byte loads cost bandwidth.)
 template <int D>
 __global__ __launch_bounds__(64) void decode_score_kernel(const float* __restrict__ qbar,
                                                           const float* __restrict__ kbar,
@@ -332,7 +336,6 @@ __global__ __launch_bounds__(64) void decode_score_kernel(const float* __restric
       qv[j] = qbar + (size_t)(b * d.Hq + h) * D;   // nQB == 1
     }
     double sc[4] = {0.0, 0.0, 0.0, 0.0};
-    // 16 floats of the row per step, the next step's loads in flight
     auto load16 = [&](float4* f, int c) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) f[i] = *(const float4*)(kr + 16 * c + 4 * i);
@@ -369,11 +372,41 @@ __global__ __launch_bounds__(64) void decode_score_kernel(const float* __restric
   if (d.group_select) gkeys[krow0 * d.nKB + kb] = orderable_key(gsum);
 }
 
+// Decode top-k: one wave per (b, q head) on the keys of decode_score_kernel
+// (copied to LDS), the same radix select and compaction as select_kernel.
+__global__ __launch_bounds__(64) void decode_select_kernel(const uint64_t* __restrict__ gkeys,
+                                                           int* __restrict__ idx,
+                                                           int* __restrict__ cnt, Dims d,
+                                                           HeadMap hm) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint64_t* keys = (uint64_t*)smem;   // [nKB]
+  __shared__ unsigned hist[256];
+  const int lane = (int)threadIdx.x;
+  const int hh = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int h = hm.q_of_kv[g * d.G + hh];
+  const int diag = row_block_diag(d, 0);
+  const int ncausal = diag + 1;
+  const int a_end = min(d.n_sink, ncausal);
+  const int l_begin = max(0, ncausal - d.n_local);
+  const int n_forced = a_end + (ncausal - l_begin) - max(0, a_end - l_begin);
+  const int n_cand = ncausal - n_forced;
+  const int free_slots = d.budget - n_forced;
+  const bool take_all = n_cand <= free_slots;
+  const bool forced_only = !take_all && free_slots <= 0;
+  if (!take_all && !forced_only) {
+    const size_t krow = d.group_select ? (size_t)(b * d.Hkv + g) : (size_t)(b * d.Hkv + g) * d.G + hh;
+    const uint64_t* src = gkeys + krow * d.nKB;
+    for (int kb = lane; kb < ncausal; kb += 64)
+      if (!is_forced(kb, diag, d.n_sink, d.n_local)) keys[kb] = src[kb];
+    wave_lds_fence();
+  }
+  select_row_wave(keys, hist, idx, cnt, (size_t)(b * d.Hq + h), d, diag, ncausal, free_slots,
+                  take_all, forced_only);
+}
+
 hipError_t launch_select(const float* qbar, const float* kbar, int* idx, int* cnt,
                          const Dims& d, const HeadMap& hm, uint64_t* gkeys, hipStream_t stream) {
-  const int hc = select_heads_per_pass(d);
-  const size_t smem = select_smem_bytes(d, hc);
-  if (gkeys != nullptr) {
+  if (gkeys != nullptr) {   // decode: wide scoring, then one wave per (b, q head)
     const dim3 grid((d.nKB + 63) / 64, d.Hkv, d.B);
     if (d.D == 128)
       hipLaunchKernelGGL(decode_score_kernel<128>, grid, dim3(64), 0, stream, qbar, kbar, gkeys,
@@ -383,9 +416,14 @@ hipError_t launch_select(const float* qbar, const float* kbar, int* idx, int* cn
                          d, hm);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_select_kernel, dim3(d.G, d.Hkv, d.B), dim3(64),
+                       (size_t)d.nKB * sizeof(uint64_t), stream, gkeys, idx, cnt, d, hm);
+    return hipGetLastError();
   }
+  const int hc = select_heads_per_pass(d);
+  const size_t smem = select_smem_bytes(d, hc);
   hipLaunchKernelGGL(select_kernel, dim3(d.nQB, d.Hkv, d.B), dim3(kSelThreads), smem, stream,
-                     qbar, kbar, gkeys, idx, cnt, d, hm, hc);
+                     qbar, kbar, idx, cnt, d, hm, hc);
   return hipGetLastError();
 }
 

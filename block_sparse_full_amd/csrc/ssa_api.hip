@@ -312,11 +312,10 @@ ssa_status ssa_select_blocks(const ssa_problem* p, const void* q, const void* k,
     return hip_status(ssa::launch_select_tok(q, P.bf16, kbar, (double*)(w + L.kc), idx, cnt, d,
                                              P.hm, st), "select (per token)");
   }
-  if (P.decode)  // the query is its own block representation
-    e = ssa::launch_pool(q, P.bf16, qbar, (long)d.B * d.Hq, 1, d.D, st);
-  else
+  if (!P.decode) {   // decode: the query is its own block representation
     e = ssa::launch_pool(q, P.bf16, qbar, (long)d.B * d.Hq * d.nQB, d.bs, d.D, st);
-  if (e != hipSuccess) return hip_status(e, "pool q");
+    if (e != hipSuccess) return hip_status(e, "pool q");
+  }
   const float* kbar = k_pooled;
   if (kbar == nullptr) {
     float* kb = (float*)(w + L.kbar);
@@ -324,8 +323,10 @@ ssa_status ssa_select_blocks(const ssa_problem* p, const void* q, const void* k,
     if (e != hipSuccess) return hip_status(e, "pool k");
     kbar = kb;
   }
-  uint64_t* gkeys = P.decode ? (uint64_t*)(w + L.keys) : nullptr;
-  return hip_status(ssa::launch_select(qbar, kbar, idx, cnt, d, P.hm, gkeys, st), "select");
+  if (P.decode)
+    return hip_status(ssa::launch_select_decode(q, P.bf16, kbar, idx, cnt, d, P.hm,
+                                                (uint64_t*)(w + L.keys), st), "select");
+  return hip_status(ssa::launch_select(qbar, kbar, idx, cnt, d, P.hm, st), "select");
 }
 
 ssa_status ssa_attn_fwd(const ssa_problem* p, const void* q, const void* k, const void* v,

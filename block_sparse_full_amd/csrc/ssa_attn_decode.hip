@@ -76,45 +76,7 @@ __global__ __launch_bounds__(256) void attn_decode_bf16_kernel(
   // ---- selection bitmaps of the group's heads
   for (int i = tid; i < GP * words; i += 256) bits[i] = 0u;
   __syncthreads();
-  for (int i = tid; i < G * d.budget; i += 256) {
-    const int n = i / d.budget, e = i - n * d.budget;
-    const int h = qmap[n];
-    const int c = cnt[b * d.Hq + h];
-    const int kb = idx[(size_t)(b * d.Hq + h) * d.budget + e];
-    if (e < c && kb >= 0 && kb < d.nKB) atomicOr(&bits[n * words + (kb >> 5)], 1u << (kb & 31));
-  }
-  __syncthreads();
-
-  // ---- the 64-key tiles this workgroup walks
-  int blk_begin, blk_count, blk_stride;
-  if (sparse_only) {
-    if (tid == 0) {
-      int nu = 0;
-      for (int w = 0; w < words; ++w) {
-        unsigned u = 0u;
-        for (int n = 0; n < G; ++n) u |= bits[n * words + w];
-        while (u) {
-          const int bit = __ffs(u) - 1;
-          u &= u - 1u;
-          const int t = (w * 32 + bit) * d.bs / kBlock;   // tile of that block
-          if (nu == 0 || ulist[nu - 1] != t) ulist[nu++] = t;
-        }
-      }
-      s_nunion = nu;
-    }
-    __syncthreads();
-    const int nu = s_nunion;
-    const int per = (nu + nsplit - 1) / nsplit;
-    blk_begin = split * per;
-    blk_count = max(0, min(per, nu - blk_begin));
-    blk_stride = kDecWaves;  // wave w takes entries w, w+4, ...
-  } else {
-    blk_begin = split * kDecWaves * kDecWaveBlocks;
-    blk_count = max(0, min(kDecWaves * kDecWaveBlocks, d.nT - blk_begin));
-    blk_stride = kDecWaves;
-  }
-
-  // ---- per-lane state
+  // ---- query fragments, in flight together with the idx/cnt loads below
   // QK^T layout (16x16x32): lane column n = lane & 15 is head n; rows
   // 4*(lane>>4) + r of key tile kt are its keys.
   const int n_col = lane & 15;
@@ -134,6 +96,72 @@ __global__ __launch_bounds__(256) void attn_decode_bf16_kernel(
       qf[ks] = v;
     }
   }
+  for (int i = tid; i < G * d.budget; i += 256) {
+    const int n = i / d.budget, e = i - n * d.budget;
+    const int h = qmap[n];
+    const int c = cnt[b * d.Hq + h];
+    const int kb = idx[(size_t)(b * d.Hq + h) * d.budget + e];
+    if (e < c && kb >= 0 && kb < d.nKB) atomicOr(&bits[n * words + (kb >> 5)], 1u << (kb & 31));
+  }
+  __syncthreads();
+
+  // ---- the 64-key tiles this workgroup walks
+  int blk_begin, blk_count, blk_stride;
+  if (sparse_only) {
+    // the union's tiles in ascending order, by wave 0: lane w takes tile
+    // word w (bit j: tile 32w + j selected by some head of the group), a
+    // wave prefix sum of the words' popcounts places each lane's tiles
+    if (wave == 0) {
+      const int twords = (d.nT + 31) >> 5;
+      int base = 0;
+      for (int w0 = 0; w0 < twords; w0 += 64) {
+        const int w = w0 + lane;
+        unsigned u = 0u;
+        if (w < twords) {
+          if (d.bs == kBlock) {
+            for (int n = 0; n < G; ++n) u |= bits[n * words + w];
+          } else {   // 16-token blocks: tile t is blocks 4t .. 4t+3
+            for (int i = 0; i < 4; ++i) {
+              const int bw = 4 * w + i;
+              if (bw >= words) break;
+              unsigned x = 0u;
+              for (int n = 0; n < G; ++n) x |= bits[n * words + bw];
+              x |= (x >> 1) | (x >> 2) | (x >> 3);   // bit 4j: block nibble j not empty
+              unsigned r = 0u;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) r |= ((x >> (4 * j)) & 1u) << j;
+              u |= r << (8 * i);
+            }
+          }
+        }
+        const int c = __popc(u);
+        int incl = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int o = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += o;
+        }
+        int pos = base + incl - c;
+        while (u) {
+          ulist[pos++] = w * 32 + __ffs(u) - 1;
+          u &= u - 1u;
+        }
+        base += __shfl(incl, 63, 64);
+      }
+      if (lane == 0) s_nunion = base;
+    }
+    __syncthreads();
+    const int nu = s_nunion;
+    const int per = (nu + nsplit - 1) / nsplit;
+    blk_begin = split * per;
+    blk_count = max(0, min(per, nu - blk_begin));
+    blk_stride = kDecWaves;  // wave w takes entries w, w+4, ...
+  } else {
+    blk_begin = split * kDecWaves * kDecWaveBlocks;
+    blk_count = max(0, min(kDecWaves * kDecWaveBlocks, d.nT - blk_begin));
+    blk_stride = kDecWaves;
+  }
+
   float m_run = -INFINITY, l_sel = 0.f, l_drop = 0.f;  // of head n_col (lane partials)
   // PV layout: lane owns d = 8*(lane % LPR) .. +7 and keys RPI*i + lane / LPR.
   const int pv_d0 = 8 * (lane % L::LPR);

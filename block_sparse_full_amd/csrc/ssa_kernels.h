@@ -27,10 +27,15 @@ inline int decode_partial_floats(int D) { return 2 * D + 4; }
 
 hipError_t launch_pool(const void* x, bool bf16, float* out, long nblk_total, int bs, int D,
                        hipStream_t stream);
-// gkeys: NULL (scores computed inside the selection kernel), or for decode a
-// [B, Hq, nKB] scratch that a wide scoring kernel fills first.
+// Prefill: pooled queries qbar, scores computed inside the selection kernel.
 hipError_t launch_select(const float* qbar, const float* kbar, int* idx, int* cnt,
-                         const Dims& d, const HeadMap& hm, uint64_t* gkeys, hipStream_t stream);
+                         const Dims& d, const HeadMap& hm, hipStream_t stream);
+// Decode: the query q itself (bf16 or float32) is scored by a wide kernel
+// into the [B, Hq, nKB] key scratch gkeys, then one wave per (b, q head)
+// selects.
+hipError_t launch_select_decode(const void* q, bool bf16, const float* kbar, int* idx, int* cnt,
+                                const Dims& d, const HeadMap& hm, uint64_t* gkeys,
+                                hipStream_t stream);
 // Per-token selection: float64 copy of the pooled keys in chunks of
 // kTokChunk blocks ([B*Hkv][chunk][D][kTokChunk]), read as scalar operands.
 constexpr int kTokChunk = 16;

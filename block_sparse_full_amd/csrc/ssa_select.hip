@@ -122,10 +122,114 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// Top-k of one selection row by one wave: the free-th largest key by an
-// exact radix select over hk (8 bits per pass from the most significant byte,
-// histogram hw of 256 bins in LDS), then the ascending list of forced blocks
-// and picks (ties to the lower index) written to idx row `row` and its count.
+// Gathers the candidate keys of a selection row for which in(key) holds into
+// hw (one slot each, ascending block order; slots past 64 are not written)
+// and returns how many there are. hw needs 768 bytes: 64 keys, 64 blocks.
+template <typename Pred>
+__device__ __forceinline__ int gather_few(const uint64_t* hk, unsigned* hw, const Dims& d,
+                                          int diag, int ncausal, uint64_t lt_mask, Pred in_set) {
+  const int lane = threadIdx.x & 63;
+  uint64_t* ck = (uint64_t*)hw;
+  int* cb = (int*)(ck + 64);
+  int n = 0;
+  for (int kb0 = 0; kb0 < ncausal; kb0 += 64 * 4) {
+    uint64_t v[4];   // the reads first: the slot writes below may alias hk
+    bool c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kb = kb0 + 64 * j + lane;
+      c[j] = kb < ncausal && !is_forced(kb, diag, d.n_sink, d.n_local);
+      v[j] = c[j] ? hk[kb] : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kb = kb0 + 64 * j + lane;
+      const bool in = c[j] && in_set(v[j]);
+      const uint64_t ball = __builtin_amdgcn_ballot_w64(in);
+      const int pos = n + __popcll(ball & lt_mask);
+      if (in && pos < 64) {
+        ck[pos] = v[j];
+        cb[pos] = kb;
+      }
+      n += __popcll(ball);
+    }
+  }
+  wave_lds_fence();
+  return n;
+}
+
+// Ranks the n <= 64 keys gather_few left in hw (larger key first, equal keys
+// by ascending block) and returns in thr the key of rank k - 1 (1 <= k <= n)
+// and in k_eq how many keys equal to it rank below k: taking every key above
+// thr and the first k_eq keys equal to it in block order takes exactly the k
+// highest-ranked keys.
+__device__ __forceinline__ void rank_few(const unsigned* hw, int n, int k, uint64_t& thr,
+                                         int& k_eq) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t* ck = (const uint64_t*)hw;
+  const int* cb = (const int*)(ck + 64);
+  const bool valid = lane < n;
+  const uint64_t mk = valid ? ck[lane] : 0ull;
+  const int mb = valid ? cb[lane] : 0;
+  // the other keys come from the lanes' registers (readlane), not LDS:
+  // no memory round trip per step
+  int rank = 0;
+  for (int j = 0; j < n; ++j) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)mk, j);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(mk >> 32), j);
+    const uint64_t ok = ((uint64_t)hi << 32) | lo;
+    const int ob = __builtin_amdgcn_readlane(mb, j);
+    rank += (int)(ok > mk) | ((int)(ok == mk) & (int)(ob < mb));
+  }
+  const uint64_t at = __builtin_amdgcn_ballot_w64(valid && rank == k - 1);
+  const int src = __builtin_ctzll(at);   // ranks are distinct: exactly one lane
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)mk, src);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(mk >> 32), src);
+  thr = ((uint64_t)hi << 32) | lo;
+  k_eq = __popcll(__builtin_amdgcn_ballot_w64(valid && mk == thr && rank < k));
+  wave_lds_fence();
+}
+
+// One 64-block step of the ascending compaction: block kb of this lane is
+// taken when forced, when its key is above thr, or when it equals thr and is
+// among the first k_eq such blocks; positions come from ballots.
+__device__ __forceinline__ void compact_step(int kb, bool causal, bool forced, uint64_t key,
+                                             bool take_all, bool forced_only, uint64_t thr,
+                                             int k_eq, uint64_t lt_mask, int* out, int budget,
+                                             int& n_out, int& eq_seen) {
+  const bool cand = causal && !forced;
+  bool take = false, eq = false;
+  if (cand) {
+    if (take_all) {
+      take = true;
+    } else if (!forced_only) {
+      take = key > thr;
+      eq = key == thr;
+    }
+  }
+  const uint64_t eq_ball = __builtin_amdgcn_ballot_w64(eq);
+  if (eq) take = (eq_seen + __popcll(eq_ball & lt_mask)) < k_eq;
+  eq_seen += __popcll(eq_ball);
+  const bool sel = forced || take;
+  const uint64_t sel_ball = __builtin_amdgcn_ballot_w64(sel);
+  const int pos = n_out + __popcll(sel_ball & lt_mask);
+  if (sel && pos < budget) out[pos] = kb;   // pos < budget always holds
+  n_out += __popcll(sel_ball);
+}
+
+// Top-k of one selection row by one wave, then the ascending list of forced
+// blocks and picks (ties to the lower index) written to idx row `row` and
+// its count. The free-th largest key (the threshold) is found in one of two
+// exact ways, both over hk with hw (1 KB of LDS) as scratch:
+// - free <= 64: each lane's largest candidate key; the free-th largest of
+//   those 64 bounds the threshold from below (the lanes ranked above it hold
+//   free distinct keys at least as large), so only the keys at or above it
+//   can be taken. When at most 64 keys are (the usual case: about 1.5 x free
+//   for random scores) they are gathered and ranked directly.
+// - otherwise a radix select, 8 bits per pass from the most significant
+//   byte (a 256-bin histogram per pass, wave prefix scans), until the bin
+//   that holds the threshold is taken whole or has at most 64 keys, which
+//   are then ranked directly.
 __device__ void select_row_wave(const uint64_t* hk, unsigned* hw, int* __restrict__ idx,
                                 int* __restrict__ cnt, size_t row, const Dims& d, int diag,
                                 int ncausal, int free_slots, bool take_all, bool forced_only) {
@@ -134,9 +238,42 @@ __device__ void select_row_wave(const uint64_t* hk, unsigned* hw, int* __restric
   uint64_t thr = 0ull;   // keys above thr are taken
   int k_eq = 0;          // and this many of the keys equal to thr
   if (!take_all && !forced_only) {
+    bool found = false;
+    if (free_slots <= 64) {
+      uint64_t lmax = 0ull;   // below every key of a finite score
+      for (int kb0 = 0; kb0 < ncausal; kb0 += 64 * 4) {
+        uint64_t v[4];   // four LDS reads in flight, then the maxima
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kb = kb0 + 64 * j + lane;
+          v[j] = (kb < ncausal && !is_forced(kb, diag, d.n_sink, d.n_local)) ? hk[kb] : 0ull;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lmax = v[j] > lmax ? v[j] : lmax;
+      }
+      int rank = 0;
+#pragma unroll
+      for (int j = 0; j < 64; ++j) {
+        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)lmax, j);
+        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(lmax >> 32), j);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        rank += (int)(o > lmax) | ((int)(o == lmax) & (int)(j < lane));
+      }
+      const uint64_t at = __builtin_amdgcn_ballot_w64(rank == free_slots - 1);
+      const int src = __builtin_ctzll(at);
+      const uint32_t t0_hi = __builtin_amdgcn_readlane((uint32_t)(lmax >> 32), src);
+      const uint32_t t0_lo = __builtin_amdgcn_readlane((uint32_t)lmax, src);
+      const uint64_t t0 = ((uint64_t)t0_hi << 32) | t0_lo;
+      const int n = gather_few(hk, hw, d, diag, ncausal, lt_mask,
+                               [t0](uint64_t key) { return key >= t0; });
+      if (n <= 64) {
+        rank_few(hw, n, free_slots, thr, k_eq);
+        found = true;
+      }
+    }
     uint64_t prefix = 0ull, pmask = 0ull;
     int k = free_slots;
-    for (int pass = 0; pass < 8; ++pass) {
+    for (int pass = 0; pass < 8 && !found; ++pass) {
       const int shift = 56 - 8 * pass;
 #pragma unroll
       for (int j = 0; j < 4; ++j) hw[lane * 4 + j] = 0u;
@@ -170,13 +307,20 @@ __device__ void select_row_wave(const uint64_t* hk, unsigned* hw, int* __restric
       // every remaining key of the chosen bin is taken: the selected keys
       // are exactly those >= prefix, and the lower digits need no pass
       if (scnt == k && prefix != 0ull) {
-        prefix -= 1ull;
-        k = 0;
-        break;
+        thr = prefix - 1ull;
+        k_eq = 0;
+        found = true;
+      } else if (scnt <= 64) {
+        const int n = gather_few(hk, hw, d, diag, ncausal, lt_mask,
+                                 [prefix, pmask](uint64_t key) { return (key & pmask) == prefix; });
+        rank_few(hw, n, k, thr, k_eq);
+        found = true;
       }
     }
-    thr = prefix;
-    k_eq = k;
+    if (!found) {   // eight passes: every remaining key equals prefix
+      thr = prefix;
+      k_eq = k;
+    }
   }
   // ---- ascending compaction over the causal blocks, 64 at a time
   int* out = idx + row * d.budget;
@@ -185,24 +329,9 @@ __device__ void select_row_wave(const uint64_t* hk, unsigned* hw, int* __restric
     const int kb = base + lane;
     const bool causal = kb < ncausal;
     const bool forced = causal && is_forced(kb, diag, d.n_sink, d.n_local);
-    bool take = false, eq = false;
-    if (causal && !forced) {
-      if (take_all) {
-        take = true;
-      } else if (!forced_only) {
-        const uint64_t key = hk[kb];
-        take = key > thr;
-        eq = key == thr;
-      }
-    }
-    const uint64_t eq_ball = __builtin_amdgcn_ballot_w64(eq);
-    if (eq) take = (eq_seen + __popcll(eq_ball & lt_mask)) < k_eq;
-    eq_seen += __popcll(eq_ball);
-    const bool sel = forced || take;
-    const uint64_t sel_ball = __builtin_amdgcn_ballot_w64(sel);
-    const int pos = n_out + __popcll(sel_ball & lt_mask);
-    if (sel && pos < d.budget) out[pos] = kb;   // pos < budget always holds
-    n_out += __popcll(sel_ball);
+    const uint64_t key = (causal && !forced && !take_all && !forced_only) ? hk[kb] : 0ull;
+    compact_step(kb, causal, forced, key, take_all, forced_only, thr, k_eq, lt_mask, out,
+                 d.budget, n_out, eq_seen);
   }
   for (int i = n_out + lane; i < d.budget; i += 64) out[i] = -1;
   if (lane == 0) cnt[row] = min(n_out, d.budget);
@@ -215,7 +344,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   // layout: keys[hc or 1][nKB] u64 | qv[hc][D] f32
   uint64_t* keys = (uint64_t*)smem;
   float* qv = (float*)(smem + (size_t)(d.group_select ? 1 : hc) * d.nKB * sizeof(uint64_t));
-  __shared__ unsigned hist[kSelWaves][256];
+  __shared__ __align__(16) unsigned hist[kSelWaves][256];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -306,18 +435,27 @@ size_t select_smem_bytes(const Dims& d, int hc) {
 
 // Decode scoring: one lane per candidate key block, 64 candidates per
 // workgroup, all q heads of the group (the single query of each head is its
-// block representation; its float32 values come from qbar as scalar
-// operands). The same float64 ascending-d dot products and orderable keys as
+// block representation: its values, read from q four at a time as scalar
+// operands and widened exactly to float32, are what pooling one token gives). The same float64 ascending-d dot products and orderable keys as
 // select_kernel's own scoring, written to gkeys [B, Hkv, G, nKB] (or the
 // group sum to [B, Hkv, nKB] with group-shared selection); forced and
 // non-causal blocks are not written. Spreading the pooled-key table over
 // B * Hkv * nKB / 64 workgroups keeps enough loads in flight to stream it;
-// each lane reads its own row 16 floats at a time with the next 16 in
-// flight. (Staging the rows through LDS for coalesced loads measured slower:
+// each lane reads its own row a whole 128-byte line (32 floats) at a time
+// with the next line in flight. Reading half lines let the L2 drop a line
+// between its two halves and fetch it twice (39 % more HBM reads than the
+// table). (Staging the rows through LDS for coalesced loads measured slower:
 // the LDS per workgroup, or the extra passes, cost more occupancy than the
 // scattered 16-byte loads cost bandwidth.)
-template <int D>
-__global__ __launch_bounds__(64) void decode_score_kernel(const float* __restrict__ qbar,
+__device__ __forceinline__ float4 q4_f32(const float* p) { return *(const float4*)p; }
+__device__ __forceinline__ float4 q4_f32(const uint16_t* p) {
+  const uint2 w = *(const uint2*)p;
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+}
+
+template <int D, typename QT>
+__global__ __launch_bounds__(64) void decode_score_kernel(const QT* __restrict__ q,
                                                           const float* __restrict__ kbar,
                                                           uint64_t* __restrict__ gkeys, Dims d,
                                                           HeadMap hm) {
@@ -329,38 +467,43 @@ __global__ __launch_bounds__(64) void decode_score_kernel(const float* __restric
   const size_t krow0 = (size_t)(b * d.Hkv + g);
   double gsum = 0.0;
   for (int hb = 0; hb < d.G; hb += 4) {
-    const float* qv[4];
+    const QT* qv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int h = hm.q_of_kv[g * d.G + min(hb + j, d.G - 1)];
-      qv[j] = qbar + (size_t)(b * d.Hq + h) * D;   // nQB == 1
+      qv[j] = q + (size_t)(b * d.Hq + h) * D;   // Nq == 1
     }
     double sc[4] = {0.0, 0.0, 0.0, 0.0};
-    auto load16 = [&](float4* f, int c) __attribute__((always_inline)) {
+    auto load32 = [&](float4* f, int c) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f[i] = *(const float4*)(kr + 16 * c + 4 * i);
+      for (int i = 0; i < 8; ++i) f[i] = *(const float4*)(kr + 32 * c + 4 * i);
     };
-    auto fma16 = [&](const float4* f, int c) __attribute__((always_inline)) {
+    auto fma32 = [&](const float4* f, int c) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 8; ++i) {
         const float kk[4] = {f[i].x, f[i].y, f[i].z, f[i].w};
+        float qq[4][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 t = q4_f32(qv[j] + 32 * c + 4 * i);
+          qq[j][0] = t.x; qq[j][1] = t.y; qq[j][2] = t.z; qq[j][3] = t.w;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const double kv = (double)kk[e];
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            sc[j] = __fma_rn((double)qv[j][16 * c + 4 * i + e], kv, sc[j]);
+          for (int j = 0; j < 4; ++j) sc[j] = __fma_rn((double)qq[j][e], kv, sc[j]);
         }
       }
     };
-    float4 fa[4], fb[4];
-    load16(fa, 0);
+    float4 fa[8], fb[8];
+    load32(fa, 0);
 #pragma unroll 1
-    for (int c = 0; c < D / 16; c += 2) {
-      load16(fb, c + 1);
-      fma16(fa, c);
-      if (c + 2 < D / 16) load16(fa, c + 2);
-      fma16(fb, c + 1);
+    for (int c = 0; c < D / 32; c += 2) {
+      load32(fb, c + 1);
+      fma32(fa, c);
+      if (c + 2 < D / 32) load32(fa, c + 2);
+      fma32(fb, c + 1);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -380,7 +523,7 @@ __global__ __launch_bounds__(64) void decode_select_kernel(const uint64_t* __res
                                                            HeadMap hm) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint64_t* keys = (uint64_t*)smem;   // [nKB]
-  __shared__ unsigned hist[256];
+  __shared__ __align__(16) unsigned hist[256];
   const int lane = (int)threadIdx.x;
   const int hh = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int h = hm.q_of_kv[g * d.G + hh];
@@ -393,33 +536,126 @@ __global__ __launch_bounds__(64) void decode_select_kernel(const uint64_t* __res
   const int free_slots = d.budget - n_forced;
   const bool take_all = n_cand <= free_slots;
   const bool forced_only = !take_all && free_slots <= 0;
+  const size_t row = (size_t)(b * d.Hq + h);
+  const size_t krow = d.group_select ? (size_t)(b * d.Hkv + g) : (size_t)(b * d.Hkv + g) * d.G + hh;
+  const uint64_t* src = gkeys + krow * d.nKB;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  if (!take_all && !forced_only && ncausal <= 64 * 16 && free_slots <= 64) {
+    // keys in registers (candidate kb = 64 j + lane): no LDS copy; the
+    // threshold from the lane-maximum bound and a direct ranking, as in
+    // select_row_wave
+    uint64_t key[16];
+    uint64_t lmax = 0ull;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int kb = 64 * j + lane;
+      key[j] = (kb < ncausal && !is_forced(kb, diag, d.n_sink, d.n_local)) ? src[kb] : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) lmax = key[j] > lmax ? key[j] : lmax;
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)lmax, j);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(lmax >> 32), j);
+      const uint64_t o = ((uint64_t)hi << 32) | lo;
+      rank += (int)(o > lmax) | ((int)(o == lmax) & (int)(j < lane));
+    }
+    const uint64_t at = __builtin_amdgcn_ballot_w64(rank == free_slots - 1);
+    const int src_lane = __builtin_ctzll(at);
+    const uint32_t t0_hi = __builtin_amdgcn_readlane((uint32_t)(lmax >> 32), src_lane);
+    const uint32_t t0_lo = __builtin_amdgcn_readlane((uint32_t)lmax, src_lane);
+    const uint64_t t0 = ((uint64_t)t0_hi << 32) | t0_lo;
+    uint64_t* ck = (uint64_t*)hist;
+    int* cb = (int*)(ck + 64);
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int kb = 64 * j + lane;
+      const bool in = kb < ncausal && !is_forced(kb, diag, d.n_sink, d.n_local) && key[j] >= t0;
+      const uint64_t ball = __builtin_amdgcn_ballot_w64(in);
+      const int pos = n + __popcll(ball & lt_mask);
+      if (in && pos < 64) {
+        ck[pos] = key[j];
+        cb[pos] = kb;
+      }
+      n += __popcll(ball);
+    }
+    wave_lds_fence();
+    if (n <= 64) {
+      uint64_t thr;
+      int k_eq;
+      rank_few(hist, n, free_slots, thr, k_eq);
+      int* out = idx + row * d.budget;
+      int n_out = 0, eq_seen = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (64 * j >= ncausal) break;
+        const int kb = 64 * j + lane;
+        const bool causal = kb < ncausal;
+        const bool forced = causal && is_forced(kb, diag, d.n_sink, d.n_local);
+        compact_step(kb, causal, forced, key[j], false, false, thr, k_eq, lt_mask, out,
+                     d.budget, n_out, eq_seen);
+      }
+      for (int i = n_out + lane; i < d.budget; i += 64) out[i] = -1;
+      if (lane == 0) cnt[row] = min(n_out, d.budget);
+      return;
+    }
+  }
   if (!take_all && !forced_only) {
-    const size_t krow = d.group_select ? (size_t)(b * d.Hkv + g) : (size_t)(b * d.Hkv + g) * d.G + hh;
-    const uint64_t* src = gkeys + krow * d.nKB;
-    for (int kb = lane; kb < ncausal; kb += 64)
-      if (!is_forced(kb, diag, d.n_sink, d.n_local)) keys[kb] = src[kb];
+    // all loads of a group of 16 in flight before the LDS writes (one at a
+    // time, each waiting for the last, took most of the kernel's time); the
+    // forced blocks' entries, never written by the scoring, are copied too
+    // and never read as candidates
+    for (int kb0 = 0; kb0 < ncausal; kb0 += 64 * 16) {
+      uint64_t v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int kb = kb0 + 64 * j + lane;
+        v[j] = kb < ncausal ? src[kb] : 0ull;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int kb = kb0 + 64 * j + lane;
+        if (kb < ncausal) keys[kb] = v[j];
+      }
+    }
     wave_lds_fence();
   }
-  select_row_wave(keys, hist, idx, cnt, (size_t)(b * d.Hq + h), d, diag, ncausal, free_slots,
-                  take_all, forced_only);
+  select_row_wave(keys, hist, idx, cnt, row, d, diag, ncausal, free_slots, take_all,
+                  forced_only);
+}
+
+hipError_t launch_select_decode(const void* q, bool bf16, const float* kbar, int* idx, int* cnt,
+                                const Dims& d, const HeadMap& hm, uint64_t* gkeys,
+                                hipStream_t stream) {
+  const dim3 grid((d.nKB + 63) / 64, d.Hkv, d.B);
+  if (bf16) {
+    const uint16_t* qq = (const uint16_t*)q;
+    if (d.D == 128)
+      hipLaunchKernelGGL((decode_score_kernel<128, uint16_t>), grid, dim3(64), 0, stream, qq,
+                         kbar, gkeys, d, hm);
+    else
+      hipLaunchKernelGGL((decode_score_kernel<64, uint16_t>), grid, dim3(64), 0, stream, qq,
+                         kbar, gkeys, d, hm);
+  } else {
+    const float* qq = (const float*)q;
+    if (d.D == 128)
+      hipLaunchKernelGGL((decode_score_kernel<128, float>), grid, dim3(64), 0, stream, qq, kbar,
+                         gkeys, d, hm);
+    else
+      hipLaunchKernelGGL((decode_score_kernel<64, float>), grid, dim3(64), 0, stream, qq, kbar,
+                         gkeys, d, hm);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_select_kernel, dim3(d.G, d.Hkv, d.B), dim3(64),
+                     (size_t)d.nKB * sizeof(uint64_t), stream, gkeys, idx, cnt, d, hm);
+  return hipGetLastError();
 }
 
 hipError_t launch_select(const float* qbar, const float* kbar, int* idx, int* cnt,
-                         const Dims& d, const HeadMap& hm, uint64_t* gkeys, hipStream_t stream) {
-  if (gkeys != nullptr) {   // decode: wide scoring, then one wave per (b, q head)
-    const dim3 grid((d.nKB + 63) / 64, d.Hkv, d.B);
-    if (d.D == 128)
-      hipLaunchKernelGGL(decode_score_kernel<128>, grid, dim3(64), 0, stream, qbar, kbar, gkeys,
-                         d, hm);
-    else
-      hipLaunchKernelGGL(decode_score_kernel<64>, grid, dim3(64), 0, stream, qbar, kbar, gkeys,
-                         d, hm);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_select_kernel, dim3(d.G, d.Hkv, d.B), dim3(64),
-                       (size_t)d.nKB * sizeof(uint64_t), stream, gkeys, idx, cnt, d, hm);
-    return hipGetLastError();
-  }
+                         const Dims& d, const HeadMap& hm, hipStream_t stream) {
   const int hc = select_heads_per_pass(d);
   const size_t smem = select_smem_bytes(d, hc);
   hipLaunchKernelGGL(select_kernel, dim3(d.nQB, d.Hkv, d.B), dim3(kSelThreads), smem, stream,

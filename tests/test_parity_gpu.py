@@ -289,6 +289,44 @@ def test_exact_ties_go_to_lower_index(ssa):
     full_compare(cfg, y, g2, budget=5)
 
 
+TIE_RUNS = [
+    # (case, Nq, N, block, patterns, budget)
+    ("decode_b64_few", 1, 65536, 64, 6, 32),
+    ("decode_b64_mid", 1, 65536, 64, 40, 32),
+    ("decode_b64_many", 1, 65536, 64, 300, 32),
+    ("prefill_b16_mid", 8192, 8192, 16, 40, 16),
+    ("prefill_b64_mid", 16384, 16384, 64, 12, 16),
+]
+
+
+@pytest.mark.parametrize("case", TIE_RUNS, ids=[c[0] for c in TIE_RUNS])
+def test_select_tie_runs(ssa, case):
+    """Every key block is a copy of one of a few random pattern blocks, so
+    the pooled scores come in runs of exactly equal values and the top-k
+    boundary falls inside a run: the selection must take the run's lowest
+    block indices, bit for bit as the oracle does. Few patterns leave runs of
+    hundreds of equal keys (radix passes down to the last byte); tens of
+    patterns leave runs of a few dozen (the direct ranking of at most 64
+    keys)."""
+    name, nq, n, bs, npat, budget = case
+    say(f"tie runs {name}: Nq {nq} N {n} block {bs} patterns {npat} budget {budget}")
+    r = np.random.default_rng(11 + npat)
+    D, Hq, Hkv = 128, 4, 1
+    pat = torch.from_numpy(r.standard_normal((npat, bs, D)).astype(np.float32)).to(torch.bfloat16)
+    ids = torch.from_numpy(r.integers(0, npat, size=n // bs))
+    k = pat[ids].reshape(1, Hkv, n, D).contiguous()
+    q = torch.from_numpy(r.standard_normal((1, Hq, nq, D)).astype(np.float32)).to(torch.bfloat16)
+    dev = torch.device("cuda:0")
+    qd, kd = q.to(dev), k.to(dev)
+    p = ssa.problem_for(qd, kd, budget=budget, block_size=bs)
+    idx, cnt = ssa.select_blocks(p, qd, kd)
+    torch.cuda.synchronize()
+    ri, rc = O.select_blocks(q.float().numpy(), k.float().numpy(), block=bs, budget=budget,
+                             n_sink=1, n_local=1, head_map=default_head_map(Hq, Hkv))
+    assert np.array_equal(cnt.cpu().numpy(), rc), "block counts differ"
+    assert np.array_equal(idx.cpu().numpy(), ri), "selected blocks differ"
+
+
 def test_loss_and_gradient_seeds(ssa):
     cfg = CONFIGS["gqa_8k_peaked"].with_sizes(B=1, Hq=4, Hkv=1, N=1024, budget=4)
     x = make_inputs(cfg)

@@ -216,6 +216,10 @@ SPARSE_GATHER = [
     ("gqa_8k_peaked", dict(B=1, Hq=3, Hkv=3, N=576, planted=False), 3, 1, 1, None),
     ("gqa_8k_peaked", dict(B=1, Hq=4, Hkv=2, N=1024), 16, 1, 1, None),
     ("mha_4k", dict(Hq=2, Hkv=2, N=640), 3, 0, 1, None),
+    # eight and sixteen q heads per workgroup
+    ("paper_16k_b16", dict(Hq=8, Hkv=1, N=1024), 12, 1, 1, None),
+    ("paper_16k_b16", dict(Hq=16, Hkv=1, N=1024, D=128), 16, 1, 1, None),
+    ("paper_16k_b16", dict(Hq=32, Hkv=2, N=512), 10, 1, 1, [i % 2 for i in range(32)]),
 ]
 
 

@@ -1352,7 +1352,18 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
   for (int tt = 0; tt < TPE; ++tt)
 #pragma unroll
     for (int k = 0; k < 16; ++k) pw[tt][k] = 0u;
-  float m_ref = -INFINITY, l_sel = 0.f, l_drop = 0.f;
+  float m_ref = -INFINITY;
+  // Row sums on the matrix cores: a 16x16x32 MFMA reads the P^T operand of a
+  // 32x32x16 k-step as its B operand (lane l: column l % 16, keys of k-group
+  // l / 16, i.e. query 16 * ((l / 16) % 2) + l % 16); its 0/1 A operand adds
+  // k-groups 0 and 2 into output row 0 and 1 and 3 into row 1. Lane n < 16
+  // so holds the sum of query n in register 0 and of query n + 16 in
+  // register 1: all weights in la4. The selected quarters' weights are added
+  // by dot2 chains, only on entries where some row of the wave selected one.
+  f32x4_t la4 = {0.f, 0.f, 0.f, 0.f};
+  float l_sel = 0.f;
+  const uint32_t one2 = (lane & 15) == ((lane >> 4) & 1) ? 0x3F803F80u : 0u;
+  const bf16x8_t ones_a = __builtin_bit_cast(bf16x8_t, make_uint4(one2, one2, one2, one2));
   const int pr = kperm32(c);
   const size_t plane = (size_t)d.B * d.Hq * d.Nq;
 
@@ -1370,10 +1381,9 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
     }
   };
 
-  // GEMM(e) = 8 MFMAs S(e) = K(e) Q^T plus 2 x 8 MFMAs O_all += V(e-1) P(e-1)
-  // and O_sel += V(e-1) P_sel(e-1) on the same V^T fragments.
   // GEMM(e) = per tile 8 MFMAs S = K Q^T, plus per tile of entry e-1 2 x 8
-  // MFMAs O_all += V P and O_sel += V P_sel on the same V^T fragments.
+  // MFMAs O_all += V P and O_sel += V P_sel on the same V^T fragments and 4
+  // small MFMAs adding P into the row sums la4.
   auto gemm = [&](auto stc) __attribute__((always_inline)) {
     constexpr int sk = decltype(stc)::value;
     constexpr int sv = (sk + NST - 1) % NST;
@@ -1432,10 +1442,11 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
           oa[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, oa[dt], 0, 0, 0);
           os[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, psb, os[dt], 0, 0, 0);
         }
+        la4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_a, pb, la4, 0, 0, 0);
       }
     // schedule: PF reads, then MFMAs interleaved with the remaining reads
     constexpr int NR = TPE * (RK + RV);
-    constexpr int NM = TPE * (2 * NKS + 8 * NDT);
+    constexpr int NM = TPE * (2 * NKS + 8 * NDT + 4);
     __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
 #pragma unroll
     for (int k = 0; k < NR - PF; ++k) {
@@ -1487,15 +1498,12 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
       for (int i = 0; i < NDT; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) { oa[i][v] *= alpha; os[i][v] *= alpha; }
+      // the sums of lane n < 16 belong to queries n and n + 16
+      const float alpha_hi = __shfl_xor(alpha, 16);
+      la4[0] *= alpha;
+      la4[1] *= alpha_hi;
       l_sel *= alpha;
-      l_drop *= alpha;
     }
-    // row sums per quarter (one dot2 chain each): all weights go to l_all,
-    // the row's selected quarters to l_sel; the dropped mass is their
-    // difference at the end
-    float qs[4 * TPE];
-#pragma unroll
-    for (int u = 0; u < 4 * TPE; ++u) qs[u] = 0.f;
 #pragma unroll
     for (int tt = 0; tt < TPE; ++tt)
 #pragma unroll
@@ -1506,18 +1514,25 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
         const float e1 = fast_exp2(fmaf(sc[tt][1][v + 1], sl2, -m_ref));
         pw[tt][v >> 1] = pack_bf16x2(a0, a1);
         pw[tt][8 + (v >> 1)] = pack_bf16x2(e0, e1);
-        qs[4 * tt + (v >> 3)] = add_bf16x2(pw[tt][v >> 1], qs[4 * tt + (v >> 3)]);
-        qs[4 * tt + 2 + (v >> 3)] = add_bf16x2(pw[tt][8 + (v >> 1)], qs[4 * tt + 2 + (v >> 3)]);
       }
-    float ls = 0.f, la = 0.f;
+    if (__builtin_amdgcn_ballot_w64(nibs != 0u) != 0) {
+      // per quarter dot2 chains; the row's selected quarters go to l_sel
+      float qs[4 * TPE];
 #pragma unroll
-    for (int u = 0; u < 4 * TPE; ++u) {
-      ls += ((nibs >> u) & 1u) ? qs[u] : 0.f;
-      la += qs[u];
+      for (int u = 0; u < 4 * TPE; ++u) qs[u] = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < TPE; ++tt)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          qs[4 * tt + (v >> 3)] = add_bf16x2(pw[tt][v >> 1], qs[4 * tt + (v >> 3)]);
+          qs[4 * tt + 2 + (v >> 3)] = add_bf16x2(pw[tt][8 + (v >> 1)], qs[4 * tt + 2 + (v >> 3)]);
+        }
+      float ls = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4 * TPE; ++u) ls += ((nibs >> u) & 1u) ? qs[u] : 0.f;
+      l_sel += ls;
     }
     qmask = nibs;
-    l_sel += ls;
-    l_drop += la;   // running sum of all weights; l_all - l_sel at the end
   };
   // Slots as in the kernel above: group A runs GEMM(t) in slot 2t and
   // softmax(t) in slot 2t+1, group B one slot later; each wave requests its
@@ -1560,8 +1575,10 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
   }
   if (group_a) slot_barrier();
   __builtin_amdgcn_s_waitcnt(0xF70);
+  const int sum_lane = lane & 15;   // holds this row's sum of all weights
+  const float lt_lo = __shfl(la4[0], sum_lane), lt_hi = __shfl(la4[1], sum_lane);
+  const float lt = c < 16 ? lt_lo : lt_hi;   // all weights
   const float ls_t = pair_sum(l_sel);
-  const float lt = pair_sum(l_drop);   // all weights
   const float ld_t = fmaxf(lt - ls_t, 0.f);
   store(Hs, os, 1.f / ls_t);
   store(Hf, oa, 1.f / lt);

@@ -997,7 +997,17 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
   uint32_t pw[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) pw[k] = 0u;
-  float m_ref = -INFINITY, l_sel = 0.f, l_drop = 0.f;
+  float m_ref = -INFINITY, l_sel = 0.f;
+  // row sums on the matrix cores, as in attn_prefill_bf16_pp16_kernel: lane
+  // n < 16 accumulates the weights of queries n and n + 16 in la4[0], la4[1]
+  f32x4_t la4 = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t one2 = (lane & 15) == ((lane >> 4) & 1) ? 0x3F803F80u : 0u;
+  const bf16x8_t ones_a = __builtin_bit_cast(bf16x8_t, make_uint4(one2, one2, one2, one2));
+  auto row_sum = [&]() __attribute__((always_inline)) {
+    const int sl = lane & 15;
+    const float lo = __shfl(la4[0], sl), hi = __shfl(la4[1], sl);
+    return c < 16 ? lo : hi;
+  };
   const int pr = kperm32(c);
   const size_t plane = (size_t)d.B * d.Hq * d.Nq;
 
@@ -1015,15 +1025,17 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
     }
   };
   auto snapshot = [&]() __attribute__((always_inline)) {
-    const float lt = pair_sum(l_sel);
+    l_sel = row_sum();
+    const float lt = l_sel;
     store(Hs, 1.f / lt);
     if (lse != nullptr && gl == 0)
       lse[plane + (size_t)bh * d.Nq + qrow] = (m_ref + __log2f(lt)) * kLn2;
   };
 
-  // GEMM(e) = 16 MFMAs S(e) = K(e) Q^T plus 16 MFMAs O += V(e-1) P(e-1),
-  // branch-free: an entry a head skips has S ignored and P = 0. The 32 LDS
-  // fragment reads are pipelined PF ahead of the MFMAs that use them.
+  // GEMM(e) = 16 MFMAs S(e) = K(e) Q^T plus 16 MFMAs O += V(e-1) P(e-1) and
+  // 4 small ones adding P(e-1) into the row sums, branch-free: an entry a head
+  // skips has S ignored and P = 0. The 32 LDS fragment reads are pipelined PF
+  // ahead of the MFMAs that use them.
   auto gemm = [&](auto stc) __attribute__((always_inline)) {
     constexpr int sk = decltype(stc)::value;
     constexpr int sv = (sk + NST - 1) % NST;
@@ -1058,6 +1070,7 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[2 * NKS + s * NDT + dt], pb, o[dt], 0, 0, 0);
+      la4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_a, pb, la4, 0, 0, 0);
     }
     // schedule: PF reads, then (1 MFMA, 1 read) pairs, then the last PF MFMAs
     __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
@@ -1066,7 +1079,7 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, PF + 4, 0);
   };
   // softmax(e): P(e) from S(e); the sparse snapshot is taken before the
   // first entry of the second part can rescale the accumulator.
@@ -1102,10 +1115,11 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
       for (int i = 0; i < NDT; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
-      l_sel *= alpha;
-      l_drop *= alpha;
+      const float alpha_hi = __shfl_xor(alpha, 16);
+      la4[0] *= alpha;
+      la4[1] *= alpha_hi;
+      l_sel *= alpha;   // the snapshot's sum, once taken
     }
-    float ls = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; v += 2) {
       const float a0 = fast_exp2(fmaf(s0[v], sl2, -m_ref));
@@ -1114,10 +1128,7 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
       const float e1 = fast_exp2(fmaf(s1[v + 1], sl2, -m_ref));
       pw[v >> 1] = pack_bf16x2(a0, a1);
       pw[8 + (v >> 1)] = pack_bf16x2(e0, e1);
-      ls = add_bf16x2(pw[v >> 1], ls);
-      ls = add_bf16x2(pw[8 + (v >> 1)], ls);
     }
-    if (e < nA) l_sel += ls; else l_drop += ls;
   };
   // Slots are opened by workgroup barriers. Group A runs GEMM(t) in slot 2t
   // and softmax(t) in slot 2t+1, group B one slot later; each wave requests
@@ -1174,9 +1185,9 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
   if (group_a) slot_barrier();
   __builtin_amdgcn_s_waitcnt(0xF70);
   if (!sparse_only) {
-    const float ls_t = pair_sum(l_sel);
-    const float ld_t = pair_sum(l_drop);
-    const float lt = ls_t + ld_t;
+    const float ls_t = l_sel;
+    const float lt = row_sum();
+    const float ld_t = fmaxf(lt - ls_t, 0.f);
     store(Hf, 1.f / lt);
     if (gl == 0) {
       if (delta != nullptr) delta[(size_t)bh * d.Nq + qrow] = ld_t / lt;

@@ -109,7 +109,7 @@ __device__ __forceinline__ void tile_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_
 // order: PF reads first, then alternating (MFMA, read) pairs, then the last
 // PF MFMAs; the reads run PF MFMAs ahead of their use instead of each MFMA
 // waiting for its own read.
-template <int N, int PF>
+template <int N, int PF, int XM = 0>
 __device__ __forceinline__ void pipeline_reads() {
   static_assert(PF <= N, "prefetch depth");
   __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);   // DS reads
@@ -118,7 +118,7 @@ __device__ __forceinline__ void pipeline_reads() {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, PF + XM, 0);   // and XM more MFMAs
 }
 
 // One workgroup = one (b, q head, 64-row query block); four waves of 16
@@ -557,7 +557,14 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_bf16_q16_kernel(
   f32x4_t oa[NDT], os[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) { oa[i] = f32x4_t{0.f, 0.f, 0.f, 0.f}; os[i] = oa[i]; }
-  float m_ref = -INFINITY, l_sel = 0.f, l_drop = 0.f;
+  float m_ref = -INFINITY;
+  // row sums on the matrix cores: with an all-ones A operand a 16x16x32 MFMA
+  // adds the 32 weights of each query column of a PV k-step, and every lane
+  // of that column gets the total (register 0 is read): la4 over all weights,
+  // ls4 over the selected ones
+  f32x4_t la4 = {0.f, 0.f, 0.f, 0.f}, ls4 = {0.f, 0.f, 0.f, 0.f};
+  const bf16x8_t ones16 = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u,
+                                                                  0x3F803F80u, 0x3F803F80u));
 
   auto store = [&](uint16_t* H, const f32x4_t* o, float inv) __attribute__((always_inline)) {
     uint16_t* hp = H + ((size_t)bh * d.Nq + qrow) * D;
@@ -569,7 +576,7 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_bf16_q16_kernel(
       *(uint2*)(hp + d0) = make_uint2(lo, hi2);
     }
   };
-  auto pv = [&](f32x4_t* o, const uint32_t* pwv) __attribute__((always_inline)) {
+  auto pv = [&](f32x4_t* o, const uint32_t* pwv, f32x4_t& lsum) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
     bf16x8_t fr[2 * NDT];
 #pragma unroll
@@ -586,8 +593,9 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_bf16_q16_kernel(
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[j * NDT + dt], pb, o[dt], 0, 0, 0);
+      lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones16, pb, lsum, 0, 0, 0);
     }
-    pipeline_reads<2 * NDT, kPrefetch>();
+    pipeline_reads<2 * NDT, kPrefetch, 2>();
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -652,12 +660,11 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_bf16_q16_kernel(
       for (int i = 0; i < NDT; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) { oa[i][v] *= alpha; os[i][v] *= alpha; }
-      l_sel *= alpha;
-      l_drop *= alpha;
+      la4[0] *= alpha;
+      ls4[0] *= alpha;
     }
     // such a row's logits are all -inf here: its weights come out 0
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    float ls = 0.f, ld = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const float p0 = fast_exp2(fmaf(s[kt][0], sl2, -m_use));
@@ -668,19 +675,14 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_bf16_q16_kernel(
       pw[2 * kt + 1] = pack_bf16x2(p2, p3);
       pws[2 * kt] = qsel[kt] ? pw[2 * kt] : 0u;
       pws[2 * kt + 1] = qsel[kt] ? pw[2 * kt + 1] : 0u;
-      float part = add_bf16x2(pw[2 * kt], 0.f);
-      part = add_bf16x2(pw[2 * kt + 1], part);
-      if (qsel[kt]) ls += part; else ld += part;
     }
-    l_sel += ls;
-    l_drop += ld;
     }
 
     wait_vm();
     __syncthreads();
     if (t_next >= 0) load_k(t_next);
-    if (!sparse_only) pv(oa, pw);
-    if (any_sel) pv(os, pws);
+    if (!sparse_only) pv(oa, pw, la4);
+    if (any_sel) pv(os, pws, ls4);
     wait_vm();
     __syncthreads();
     if (t_next >= 0) load_v(t_next);
@@ -699,13 +701,13 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_bf16_q16_kernel(
     t = t_next;
   }
   const size_t plane = (size_t)d.B * d.Hq * d.Nq;
-  const float ls_t = quad_sum(l_sel);
+  const float ls_t = ls4[0];
   store(Hs, os, 1.f / ls_t);
   if (lse != nullptr && g4 == 0)
     lse[plane + (size_t)bh * d.Nq + qrow] = (m_ref + __log2f(ls_t)) * kLn2;
   if (sparse_only) return;
-  const float ld_t = quad_sum(l_drop);
-  const float lt = ls_t + ld_t;
+  const float lt = la4[0];
+  const float ld_t = fmaxf(lt - ls_t, 0.f);
   store(Hf, oa, 1.f / lt);
   if (g4 == 0) {
     if (delta != nullptr) delta[(size_t)bh * d.Nq + qrow] = ld_t / lt;

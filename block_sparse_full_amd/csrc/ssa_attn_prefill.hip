@@ -238,7 +238,13 @@ __global__ __launch_bounds__(256, 4) void attn_prefill_bf16_kernel(
   f32x4_t o[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY, l_sel = 0.f, l_drop = 0.f;
+  float m_ref = -INFINITY, l_sel = 0.f;   // l_sel: the sum at the snapshot
+  // row sums on the matrix cores: with an all-ones A operand a 16x16x32 MFMA
+  // adds the 32 weights of each query column of a PV k-step, and every lane
+  // of that column gets the total (register 0 is read)
+  f32x4_t la4 = {0.f, 0.f, 0.f, 0.f};
+  const bf16x8_t ones16 = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u,
+                                                                  0x3F803F80u, 0x3F803F80u));
 
   auto store = [&](uint16_t* H, float inv) {
     uint16_t* hp = H + ((size_t)bh * d.Nq + qrow) * D;
@@ -251,7 +257,7 @@ __global__ __launch_bounds__(256, 4) void attn_prefill_bf16_kernel(
     }
   };
 
-  auto body = [&](int kb, bool selected, int kb_next) {
+  auto body = [&](int kb, int kb_next) {
     f32x4_t s[4];
     {
       // MFMA work runs at raised wave priority, so that a wave with its
@@ -296,10 +302,9 @@ __global__ __launch_bounds__(256, 4) void attn_prefill_bf16_kernel(
       for (int i = 0; i < NDT; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) o[i][v] *= alpha;
+      la4[0] *= alpha;
       l_sel *= alpha;
-      l_drop *= alpha;
     }
-    float ls = 0.f;
     uint32_t pw[8];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -309,10 +314,7 @@ __global__ __launch_bounds__(256, 4) void attn_prefill_bf16_kernel(
       const float p3 = fast_exp2(fmaf(s[kt][3], sl2, -m_ref));
       pw[2 * kt] = pack_bf16x2(p0, p1);
       pw[2 * kt + 1] = pack_bf16x2(p2, p3);
-      ls = add_bf16x2(pw[2 * kt], ls);
-      ls = add_bf16x2(pw[2 * kt + 1], ls);
     }
-    if (selected) l_sel += ls; else l_drop += ls;
 
     wait_vm();
     __syncthreads();
@@ -336,8 +338,9 @@ __global__ __launch_bounds__(256, 4) void attn_prefill_bf16_kernel(
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
           o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[j * NDT + dt], pb, o[dt], 0, 0, 0);
+        la4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones16, pb, la4, 0, 0, 0);
       }
-      pipeline_reads<2 * NDT, kPrefetch>();
+      pipeline_reads<2 * NDT, kPrefetch, 2>();
       __builtin_amdgcn_s_setprio(0);
     }
 
@@ -358,12 +361,13 @@ __global__ __launch_bounds__(256, 4) void attn_prefill_bf16_kernel(
   while (kb >= 0 && sel_cur) {
     bool sel_next = false;
     const int kb_next = next_block(sel_next);
-    body(kb, true, kb_next);
+    body(kb, kb_next);
     kb = kb_next;
     sel_cur = sel_next;
   }
   {
-    const float lt = quad_sum(l_sel);
+    l_sel = la4[0];
+    const float lt = l_sel;
     store(Hs, 1.f / lt);
     if (lse != nullptr && g4 == 0)
       lse[plane + (size_t)bh * d.Nq + qrow] = (m_ref + __log2f(lt)) * kLn2;
@@ -372,12 +376,12 @@ __global__ __launch_bounds__(256, 4) void attn_prefill_bf16_kernel(
   while (kb >= 0) {
     bool sel_next = false;
     const int kb_next = next_block(sel_next);
-    body(kb, false, kb_next);
+    body(kb, kb_next);
     kb = kb_next;
   }
-  const float ls_t = quad_sum(l_sel);
-  const float ld_t = quad_sum(l_drop);
-  const float lt = ls_t + ld_t;
+  const float ls_t = l_sel;
+  const float lt = la4[0];
+  const float ld_t = fmaxf(lt - ls_t, 0.f);
   store(Hf, 1.f / lt);
   if (g4 == 0) {
     if (delta != nullptr) delta[(size_t)bh * d.Nq + qrow] = ld_t / lt;

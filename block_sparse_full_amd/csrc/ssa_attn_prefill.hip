@@ -873,6 +873,13 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
     for (int w = tid; w < TILE / 8; w += 64 * NW) ((uint4*)vz)[w] = make_uint4(0u, 0u, 0u, 0u);
   }
   __syncthreads();
+  // the query fragments, in flight together with the idx/cnt loads below
+  bf16x8_t qf[NKS];
+  {
+    const uint16_t* qp = Q + ((size_t)bh * d.Nq + qrow) * D + 8 * gl;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8_t*)(qp + 16 * ks);
+  }
   for (int u = 0; u < HPW; ++u) {
     const int hu = hm.q_of_kv[g * d.G + hg * HPW + u];
     const size_t row = (size_t)(b * d.Hq + hu) * d.nQB + qb;
@@ -974,14 +981,9 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  bf16x8_t qf[NKS];
-  {
-    const uint16_t* qp = Q + ((size_t)bh * d.Nq + qrow) * D + 8 * gl;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8_t*)(qp + 16 * ks);
-  }
-  // the Q fragments land before any LDS copy is issued: the compiler does
-  // not count the copies, so it must see no load of its own outstanding
+  // the Q fragments (loaded with the lists above) have landed: the
+  // compiler does not count the LDS copies below, so it must see no load of
+  // its own outstanding
   __builtin_amdgcn_s_waitcnt(0xF70);
   // prologue = the copies of the virtual slots before slot 0: K(0..NST-2)
   // and V(0..NST-3), with V(0) standing in for the missing V(-1)

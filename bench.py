@@ -37,8 +37,8 @@ FP64_PEAK_TFLOPS = 78.6          # MI355X float64 vector FMA
 # sources they were taken on (the prefill file and the headers it includes);
 # any other source reports traffic as null.
 PREFILL_TRAFFIC = {
-    # 787651 KiB x 2.000 read + 531585 KiB x 1.000 written per dispatch
-    "745a63ea9a24e465d3f3b7ca55d0ac3410f5d3b3c96dc163a5c381981a045266": int(787651 * 2.0 * 1024 + 531585 * 1.0 * 1024),
+    # 783803 KiB x 2.000 read + 531995 KiB x 1.000 written per dispatch
+    "7b2862275a2c617bc7a7f10c5de8147d8cf8dfb2b56a8ae6e18c55743df578a1": int(783803 * 2.0 * 1024 + 531995 * 1.0 * 1024),
 }
 PREFILL_SRCS = [os.path.join(ROOT, "block_sparse_full_amd", "csrc", f)
                 for f in ("ssa_attn_prefill.hip", "ssa_device.h", "ssa_common.h")]

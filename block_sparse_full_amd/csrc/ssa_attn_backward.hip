@@ -492,12 +492,17 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // A: S and dP_f
+    // A: S and dP_f; the dP accumulators start at -D_r of their rows, so they
+    // end as dP - D_r
     f32x4_t sa[2][2], pf[2][2], ps[2][2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) sa[mb][nb] = pf[mb][nb] = ps[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < 2; ++nb) {
+        sa[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        pf[mb][nb] = FULL ? -df[mb] : sa[mb][nb];
+        ps[mb][nb] = sp ? -dd[mb] : sa[mb][nb];
+      }
     {
       constexpr int NR = (FULL ? 2 : 1) * 2 * KK;   // fragment reads
       bf16x8_t fr[NR];
@@ -555,12 +560,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
           if (FULL) {
             p = fast_exp2(fmaf(sa[mb][nb][r], sl2, -lf[mb][r]));
             p = keep ? p : 0.f;
-            dsv = p * (pf[mb][nb][r] - df[mb][r]);
+            dsv = p * pf[mb][nb][r];
           }
           if (sp) {
             q = fast_exp2(fmaf(sa[mb][nb][r], sl2, -ls[mb][r]));
             q = (keep && sel) ? q : 0.f;
-            dsv = fmaf(q, ps[mb][nb][r] - dd[mb][r], dsv);
+            dsv = fmaf(q, ps[mb][nb][r], dsv);
           }
           xf[nb][4 * mb + r] = p;
           xs[nb][4 * mb + r] = q;
@@ -841,11 +846,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
       const uint64_t rm = rowbits[(((size_t)bg * nKT + (t >> 2)) * nS + sw) * d.G * 4 + (size_t)hi * 4 + (t & 3)];
       rsel = (uint32_t)(rm >> (32 * (gq >> 1) + n));
     }
+    // the dP accumulators start at -D_r of their query (the lane's column)
     f32x4_t sa[2][2], pf[2][2], ps[2][2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) sa[mb][nb] = pf[mb][nb] = ps[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < 2; ++nb) {
+        sa[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        pf[mb][nb] = has_full ? f32x4_t{-dfv[nb], -dfv[nb], -dfv[nb], -dfv[nb]} : sa[mb][nb];
+        ps[mb][nb] = (has_sparse && sp) ? f32x4_t{-dsv_[nb], -dsv_[nb], -dsv_[nb], -dsv_[nb]} : sa[mb][nb];
+      }
     {
       bf16x8_t fr[4 * KK];   // K and V fragments, read ahead of their MFMAs
 #pragma unroll
@@ -893,12 +903,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
           if (has_full) {
             float p = fast_exp2(fmaf(sa[mb][nb][i], sl2, -lf[nb]));
             p = keep ? p : 0.f;
-            dsv = p * (pf[mb][nb][i] - dfv[nb]);
+            dsv = p * pf[mb][nb][i];
           }
           if (has_sparse && sp) {   // wave-uniform branch; the lane's own bit masks
             float q = fast_exp2(fmaf(sa[mb][nb][i], sl2, -ls[nb]));
             q = (keep && sel) ? q : 0.f;
-            dsv = fmaf(q, ps[mb][nb][i] - dsv_[nb], dsv);
+            dsv = fmaf(q, ps[mb][nb][i], dsv);
           }
           xd[nb][4 * mb + i] = dsv;
         }

@@ -1712,7 +1712,12 @@ __global__ __launch_bounds__(64 * kGatherLists) void attn_sparse_gather_kernel(
   f32x4_t o[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY, l_sum = 0.f;
+  float m_ref = -INFINITY;
+  // row sums on the matrix cores: with an all-ones A operand a 16x16x32 MFMA
+  // gives every lane of a query column the column's sum (register 0 is read)
+  f32x4_t l4 = {0.f, 0.f, 0.f, 0.f};
+  const bf16x8_t ones16 = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u,
+                                                                  0x3F803F80u, 0x3F803F80u));
 
   // one pair: blocks starting at keys ka and kb2; kb2 < 0: no second one
   auto compute = [&](const Frags& f, int ka, int kb2) __attribute__((always_inline)) {
@@ -1745,7 +1750,7 @@ __global__ __launch_bounds__(64 * kGatherLists) void attn_sparse_gather_kernel(
       for (int i = 0; i < NDT; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) o[i][v] *= alpha;
-      l_sum *= alpha;
+      l4[0] *= alpha;
     }
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
     uint32_t pw[4];
@@ -1753,15 +1758,12 @@ __global__ __launch_bounds__(64 * kGatherLists) void attn_sparse_gather_kernel(
     pw[1] = pack_bf16x2(fast_exp2(fmaf(s0[2], sl2, -m_use)), fast_exp2(fmaf(s0[3], sl2, -m_use)));
     pw[2] = pack_bf16x2(fast_exp2(fmaf(s1[0], sl2, -m_use)), fast_exp2(fmaf(s1[1], sl2, -m_use)));
     pw[3] = pack_bf16x2(fast_exp2(fmaf(s1[2], sl2, -m_use)), fast_exp2(fmaf(s1[3], sl2, -m_use)));
-    l_sum = add_bf16x2(pw[0], l_sum);
-    l_sum = add_bf16x2(pw[1], l_sum);
-    l_sum = add_bf16x2(pw[2], l_sum);
-    l_sum = add_bf16x2(pw[3], l_sum);
     const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.v[dt], pb, o[dt], 0, 0, 0);
+    l4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones16, pb, l4, 0, 0, 0);
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -1791,7 +1793,7 @@ __global__ __launch_bounds__(64 * kGatherLists) void attn_sparse_gather_kernel(
     compute(fb, na, nb2);
   }
 
-  const float lt = quad_sum(l_sum);
+  const float lt = l4[0];
   const float inv = 1.f / lt;
   uint16_t* hp = Hs + ((size_t)bh * d.Nq + qrow) * D;
 #pragma unroll
@@ -1918,7 +1920,12 @@ __global__ __launch_bounds__(256, 2) void attn_sparse_union16_kernel(
   f32x4_t o[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY, l_sum = 0.f;
+  float m_ref = -INFINITY;
+  // row sums on the matrix cores: with an all-ones A operand a 16x16x32 MFMA
+  // gives every lane of a query column the column's sum (register 0 is read)
+  f32x4_t l4 = {0.f, 0.f, 0.f, 0.f};
+  const bf16x8_t ones16 = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u,
+                                                                  0x3F803F80u, 0x3F803F80u));
   const float sl2 = d.scale_log2;
   const uint16_t* kbase = K + ((size_t)(b * d.Hkv + g) * d.Nk) * D;
   const uint16_t* vbase = Vb + ((size_t)(b * d.Hkv + g) * D) * d.Nk;
@@ -1968,7 +1975,7 @@ __global__ __launch_bounds__(256, 2) void attn_sparse_union16_kernel(
       for (int i = 0; i < NDT; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) o[i][v] *= alpha;
-      l_sum *= alpha;
+      l4[0] *= alpha;
     }
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
     uint32_t pw[4];
@@ -1976,14 +1983,11 @@ __global__ __launch_bounds__(256, 2) void attn_sparse_union16_kernel(
     pw[1] = pack_bf16x2(fast_exp2(fmaf(s0[2], sl2, -m_use)), fast_exp2(fmaf(s0[3], sl2, -m_use)));
     pw[2] = pack_bf16x2(fast_exp2(fmaf(s1[0], sl2, -m_use)), fast_exp2(fmaf(s1[1], sl2, -m_use)));
     pw[3] = pack_bf16x2(fast_exp2(fmaf(s1[2], sl2, -m_use)), fast_exp2(fmaf(s1[3], sl2, -m_use)));
-    l_sum = add_bf16x2(pw[0], l_sum);
-    l_sum = add_bf16x2(pw[1], l_sum);
-    l_sum = add_bf16x2(pw[2], l_sum);
-    l_sum = add_bf16x2(pw[3], l_sum);
     const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pb, o[dt], 0, 0, 0);
+    l4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones16, pb, l4, 0, 0, 0);
   };
 
   for (int c0 = 0; c0 < nu; c0 += CAP) {
@@ -2019,7 +2023,7 @@ __global__ __launch_bounds__(256, 2) void attn_sparse_union16_kernel(
     }
   }
 
-  const float lt = quad_sum(l_sum);
+  const float lt = l4[0];
   const float inv = 1.f / lt;
   uint16_t* hp = Hs + ((size_t)bh * d.Nq + qrow) * D;
 #pragma unroll

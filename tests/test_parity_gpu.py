@@ -300,6 +300,9 @@ TIE_RUNS = [
     ("decode_b64_many", 1, 65536, 64, 300, 32),
     ("prefill_b16_mid", 8192, 8192, 16, 40, 16),
     ("prefill_b64_mid", 16384, 16384, 64, 12, 16),
+    # more than 64 free slots: the radix select with the direct ranking of its last bin
+    ("decode_b64_free98", 1, 65536, 64, 40, 100),
+    ("prefill_b64_free88", 8192, 8192, 64, 400, 90),
 ]
 
 

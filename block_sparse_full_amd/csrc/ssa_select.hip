@@ -48,7 +48,18 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x,
   double acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0;
-  for (int tok = 0; tok < bs; ++tok) {
+  // eight tokens' loads in flight ahead of the ascending-order adds
+  int tok = 0;
+  for (; tok + 8 <= bs; tok += 8) {
+    float v[8][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) load8(src + (long)(tok + u) * D, v[u]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += (double)v[u][i];
+  }
+  for (; tok < bs; ++tok) {
     float v[8];
     load8(src + (long)tok * D, v);
 #pragma unroll

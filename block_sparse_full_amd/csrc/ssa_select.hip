@@ -91,14 +91,14 @@ hipError_t launch_pool(const void* x, bool bf16, float* out, long nblk_total, in
 // ---------------------------------------------------------------- selection
 // One workgroup (four waves) per (b, kv head, query row block). All threads
 // first score the causal candidate blocks of up to `hc` q heads of the group
-// at once (each pooled key row is read once for all of them) into LDS as
-// 64-bit orderable keys. Then each wave selects for one head on its own,
-// with no workgroup barrier: an exact radix select finds the free-th largest
-// key 8 bits at a time from the most significant byte (per-wave LDS
-// histogram, wave prefix scans); keys above it are taken and, among keys
-// equal to it, the lowest block indices fill the remaining slots. The
-// ascending index list is written by a ballot/popcount compaction over the
-// causal blocks in order.
+// (one candidate per lane, four heads per pass over its pooled key row; the
+// heads' pooled queries sit in LDS as float64 and reach the multiply-adds by
+// row broadcasts) into LDS as 64-bit orderable keys. Then each wave selects
+// for one head on its own, with no workgroup barrier (select_row_wave): the
+// keys that can be taken are bounded from below, gathered and ranked
+// directly, or an exact radix select finds the free-th largest key; keys
+// above it are taken and, among keys equal to it, the lowest block indices
+// fill the remaining slots.
 //
 // Group-shared selection (d.group_select): all G heads are scored in one
 // pass and only their sum is kept, added in the order of q_of_kv (ascending
@@ -131,6 +131,28 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
+}
+
+// The k-th largest (1 <= k <= 64) of the 64 lanes' values v, counting equal
+// values separately: the value of a lane with fewer than k values above it
+// and at least k at or above it. The values pass through hw (512 bytes of
+// LDS), where every lane reads all of them (same address in every lane).
+__device__ __forceinline__ uint64_t wave_kth_largest(uint64_t v, int k, unsigned* hw) {
+  const int lane = threadIdx.x & 63;
+  uint64_t* sv = (uint64_t*)hw;
+  sv[lane] = v;
+  wave_lds_fence();
+  int gt = 0, ge = 0;
+#pragma unroll
+  for (int j = 0; j < 64; j += 2) {
+    const ulonglong2 o = *(const ulonglong2*)(sv + j);
+    gt += (int)(o.x > v) + (int)(o.y > v);
+    ge += (int)(o.x >= v) + (int)(o.y >= v);
+  }
+  const uint64_t at = __builtin_amdgcn_ballot_w64(gt < k && k <= ge);
+  const uint64_t r = sv[__builtin_ctzll(at)];   // some lane always qualifies
+  wave_lds_fence();
+  return r;
 }
 
 // Gathers the candidate keys of a selection row for which in(key) holds into
@@ -169,35 +191,60 @@ __device__ __forceinline__ int gather_few(const uint64_t* hk, unsigned* hw, cons
   return n;
 }
 
-// Ranks the n <= 64 keys gather_few left in hw (larger key first, equal keys
-// by ascending block) and returns in thr the key of rank k - 1 (1 <= k <= n)
-// and in k_eq how many keys equal to it rank below k: taking every key above
-// thr and the first k_eq keys equal to it in block order takes exactly the k
-// highest-ranked keys.
-__device__ __forceinline__ void rank_few(const unsigned* hw, int n, int k, uint64_t& thr,
-                                         int& k_eq) {
+// Rank of this lane's entry among the n <= 64 keys gather_few left in hw
+// (larger key first, equal keys by ascending block; entries past n and
+// lanes >= n get meaningless ranks): each lane reads every entry (the same
+// address in all lanes, two per read).
+__device__ __forceinline__ int rank_few(const unsigned* hw, int n) {
   const int lane = threadIdx.x & 63;
   const uint64_t* ck = (const uint64_t*)hw;
   const int* cb = (const int*)(ck + 64);
-  const bool valid = lane < n;
-  const uint64_t mk = valid ? ck[lane] : 0ull;
-  const int mb = valid ? cb[lane] : 0;
-  // the other keys come from the lanes' registers (readlane), not LDS:
-  // no memory round trip per step
+  const uint64_t mk = ck[lane];
+  const int mb = cb[lane];
   int rank = 0;
-  for (int j = 0; j < n; ++j) {
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)mk, j);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(mk >> 32), j);
-    const uint64_t ok = ((uint64_t)hi << 32) | lo;
-    const int ob = __builtin_amdgcn_readlane(mb, j);
-    rank += (int)(ok > mk) | ((int)(ok == mk) & (int)(ob < mb));
+  for (int j = 0; j < n; j += 2) {   // entry n (when n is odd) is in bounds
+    const ulonglong2 o = *(const ulonglong2*)(ck + j);
+    const int2 ob = *(const int2*)(cb + j);
+    rank += (int)(o.x > mk) | ((int)(o.x == mk) & (int)(ob.x < mb));
+    if (j + 1 < n) rank += (int)(o.y > mk) | ((int)(o.y == mk) & (int)(ob.y < mb));
   }
+  return rank;
+}
+
+// From the ranks of the n gathered keys: thr, the key of rank k - 1
+// (1 <= k <= n), and k_eq, how many keys equal to it rank below k. Taking
+// every key above thr and the first k_eq keys equal to it in block order
+// takes exactly the k highest-ranked keys.
+__device__ __forceinline__ void threshold_of_ranks(const unsigned* hw, int n, int k, int rank,
+                                                   uint64_t& thr, int& k_eq) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t* ck = (const uint64_t*)hw;
+  const bool valid = lane < n;
+  const uint64_t mk = ck[lane];
   const uint64_t at = __builtin_amdgcn_ballot_w64(valid && rank == k - 1);
-  const int src = __builtin_ctzll(at);   // ranks are distinct: exactly one lane
-  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)mk, src);
-  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(mk >> 32), src);
-  thr = ((uint64_t)hi << 32) | lo;
+  thr = ck[__builtin_ctzll(at)];   // ranks are distinct: exactly one lane
   k_eq = __popcll(__builtin_amdgcn_ballot_w64(valid && mk == thr && rank < k));
+  wave_lds_fence();
+}
+
+// Writes a selection row whose free picks are the gathered entries (hw,
+// ascending block order) of the lanes in `picks`: the sink blocks, the
+// picks, then the local blocks, all ascending. Valid when candidates exist
+// between the sink and local ranges (so the two do not overlap) and exactly
+// free_slots entries are picked: the row is then full.
+__device__ __forceinline__ void write_picked_row(const unsigned* hw, uint64_t picks,
+                                                 int* __restrict__ out, int* __restrict__ cnt,
+                                                 size_t row, const Dims& d, int ncausal) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int* cb = (const int*)((const uint64_t*)hw + 64);
+  const int a_end = min(d.n_sink, ncausal);
+  const int l_begin = max(0, ncausal - d.n_local);
+  const int n_pick = __popcll(picks);
+  for (int i = lane; i < a_end; i += 64) out[i] = i;
+  if ((picks >> lane) & 1ull) out[a_end + __popcll(picks & lt_mask)] = cb[lane];
+  for (int i = lane; i < ncausal - l_begin; i += 64) out[a_end + n_pick + i] = l_begin + i;
+  if (lane == 0) cnt[row] = a_end + n_pick + (ncausal - l_begin);
   wave_lds_fence();
 }
 
@@ -230,13 +277,15 @@ __device__ __forceinline__ void compact_step(int kb, bool causal, bool forced, u
 
 // Top-k of one selection row by one wave, then the ascending list of forced
 // blocks and picks (ties to the lower index) written to idx row `row` and
-// its count. The free-th largest key (the threshold) is found in one of two
-// exact ways, both over hk with hw (1 KB of LDS) as scratch:
+// its count. The picks are found in one of two exact ways, both over hk
+// with hw (1 KB of LDS) as scratch:
 // - free <= 64: each lane's largest candidate key; the free-th largest of
-//   those 64 bounds the threshold from below (the lanes ranked above it hold
+//   those 64 bounds the threshold from below (the lanes at or above it hold
 //   free distinct keys at least as large), so only the keys at or above it
 //   can be taken. When at most 64 keys are (the usual case: about 1.5 x free
-//   for random scores) they are gathered and ranked directly.
+//   for random scores) they are gathered in block order and ranked
+//   directly; the picks are those ranked below free, written between the
+//   sink and local blocks with no second pass over the row.
 // - otherwise a radix select, 8 bits per pass from the most significant
 //   byte (a 256-bin histogram per pass, wave prefix scans), until the bin
 //   that holds the threshold is taken whole or has at most 64 keys, which
@@ -262,24 +311,14 @@ __device__ void select_row_wave(const uint64_t* hk, unsigned* hw, int* __restric
 #pragma unroll
         for (int j = 0; j < 4; ++j) lmax = v[j] > lmax ? v[j] : lmax;
       }
-      int rank = 0;
-#pragma unroll
-      for (int j = 0; j < 64; ++j) {
-        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)lmax, j);
-        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(lmax >> 32), j);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        rank += (int)(o > lmax) | ((int)(o == lmax) & (int)(j < lane));
-      }
-      const uint64_t at = __builtin_amdgcn_ballot_w64(rank == free_slots - 1);
-      const int src = __builtin_ctzll(at);
-      const uint32_t t0_hi = __builtin_amdgcn_readlane((uint32_t)(lmax >> 32), src);
-      const uint32_t t0_lo = __builtin_amdgcn_readlane((uint32_t)lmax, src);
-      const uint64_t t0 = ((uint64_t)t0_hi << 32) | t0_lo;
+      const uint64_t t0 = wave_kth_largest(lmax, free_slots, hw);
       const int n = gather_few(hk, hw, d, diag, ncausal, lt_mask,
                                [t0](uint64_t key) { return key >= t0; });
-      if (n <= 64) {
-        rank_few(hw, n, free_slots, thr, k_eq);
-        found = true;
+      if (n <= 64) {   // every key that can be taken is gathered: no scan
+        const int rank = rank_few(hw, n);
+        const uint64_t picks = __builtin_amdgcn_ballot_w64(lane < n && rank < free_slots);
+        write_picked_row(hw, picks, idx + row * d.budget, cnt, row, d, ncausal);
+        return;
       }
     }
     uint64_t prefix = 0ull, pmask = 0ull;
@@ -324,7 +363,7 @@ __device__ void select_row_wave(const uint64_t* hk, unsigned* hw, int* __restric
       } else if (scnt <= 64) {
         const int n = gather_few(hk, hw, d, diag, ncausal, lt_mask,
                                  [prefix, pmask](uint64_t key) { return (key & pmask) == prefix; });
-        rank_few(hw, n, k, thr, k_eq);
+        threshold_of_ranks(hw, n, k, rank_few(hw, n), thr, k_eq);
         found = true;
       }
     }
@@ -348,13 +387,82 @@ __device__ void select_row_wave(const uint64_t* hk, unsigned* hw, int* __restric
   if (lane == 0) cnt[row] = min(n_out, d.budget);
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(
+// Sixteen float64 multiply-adds of one step of four d for four heads:
+// sc[j] += q[j][d + e] * kv[e], e ascending. q holds the step's sixteen
+// query values, lane 4 e + j of each row of 16 lanes holding q[j][d + e]
+// (the same in all four rows); each multiply-add takes its query value from
+// that lane by a row broadcast (DPP row_newbcast), so the query needs no
+// scalar register and no per-lane copy. Every lane of the wave must be
+// active (a broadcast from an inactive lane reads nothing). The leading
+// wait states cover a VGPR or EXEC write just before the block (two and
+// five are required before a DPP read); inside the block each accumulator
+// is rewritten four instructions after its last use.
+template <int NOPS>
+__device__ __forceinline__ void fma16_bcast(double sc[4], double q, const double kv[4]) {
+  asm("s_nop %9\n\t"
+      "v_fmac_f64_dpp %0, %4, %5 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %1, %4, %5 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %2, %4, %5 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %3, %4, %5 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %4, %6 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %1, %4, %6 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %2, %4, %6 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %3, %4, %6 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %4, %7 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %1, %4, %7 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %2, %4, %7 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %3, %4, %7 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %0, %4, %8 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %1, %4, %8 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %2, %4, %8 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f64_dpp %3, %4, %8 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+      : "+v"(sc[0]), "+v"(sc[1]), "+v"(sc[2]), "+v"(sc[3])
+      : "v"(q), "v"(kv[0]), "v"(kv[1]), "v"(kv[2]), "v"(kv[3]), "i"(NOPS));
+}
+
+// Scores of the pooled key row kr (float32, D values) against four query
+// rows: float64 fused multiply-adds in ascending d into sc[j]. qs points at
+// this lane's slot of the four rows' step-major float64 copy in LDS
+// (qs[16 st] = q[j][4 st + e] for lane 4 e + j of its row). The key row is
+// read a whole 128-byte line (32 floats) at a time with the next line in
+// flight.
+template <int D>
+__device__ __forceinline__ void score_bcast(const float* __restrict__ kr, const double* qs,
+                                            double sc[4]) {
+  constexpr int NC = D / 32;
+  float4 f[2][8];
+  auto load32 = [&](float4* dst, int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = *(const float4*)(kr + 32 * c + 4 * i);
+  };
+  load32(f[0], 0);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (c + 1 < NC) load32(f[(c + 1) & 1], c + 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int st = 8 * c + i;
+      const double q = qs[16 * st];
+      const float4 k4 = f[c & 1][i];
+      const double kv[4] = {(double)k4.x, (double)k4.y, (double)k4.z, (double)k4.w};
+      if (st == 0)
+        fma16_bcast<4>(sc, q, kv);
+      else
+        fma16_bcast<1>(sc, q, kv);
+    }
+  }
+}
+
+// Four waves per SIMD (at most 128 VGPRs): the compiler's own choice of
+// 138 left three, 8 % slower.
+template <int D>
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar,
     int* __restrict__ idx, int* __restrict__ cnt, Dims d, HeadMap hm, int hc) {
   extern __shared__ __align__(16) unsigned char smem[];
-  // layout: keys[hc or 1][nKB] u64 | qv[hc][D] f32
+  // keys [hc, or 1 with group-shared selection][nKB] | qd [ceil(hc / 4)][D / 4][16]
   uint64_t* keys = (uint64_t*)smem;
-  float* qv = (float*)(smem + (size_t)(d.group_select ? 1 : hc) * d.nKB * sizeof(uint64_t));
+  double* qd = (double*)(smem + (size_t)(d.group_select ? 1 : hc) * d.nKB * sizeof(uint64_t));
   __shared__ __align__(16) unsigned hist[kSelWaves][256];
 
   const int tid = threadIdx.x;
@@ -365,7 +473,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int b = blockIdx.z;
   const int diag = row_block_diag(d, qb);
   const int ncausal = diag + 1;
-  const float* krow0 = kbar + ((size_t)(b * d.Hkv + g) * d.nKB) * d.D;
+  const float* krow0 = kbar + ((size_t)(b * d.Hkv + g) * d.nKB) * D;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes below
 
   // Forced set and slot count (identical for every head of the group).
@@ -379,43 +487,48 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
   for (int h0 = 0; h0 < d.G; h0 += hc) {
     const int nh = min(hc, d.G - h0);
-    __syncthreads();
-    for (int i = tid; i < nh * d.D; i += kSelThreads) {
-      const int hh = i / d.D, dd = i % d.D;
-      const int h = hm.q_of_kv[g * d.G + h0 + hh];
-      qv[i] = qbar[((size_t)(b * d.Hq + h) * d.nQB + qb) * d.D + dd];
-    }
-    __syncthreads();
+    if (h0 > 0) __syncthreads();   // the last pass's selections are done with keys
     if (!take_all && !forced_only) {
-      // Scores of every candidate for the nh heads.
-      for (int kb = tid; kb < ncausal; kb += kSelThreads) {
-        if (is_forced(kb, diag, d.n_sink, d.n_local)) continue;
-        const float* kr = krow0 + (size_t)kb * d.D;
+      // The nh heads' pooled queries widened to float64 in LDS, step-major
+      // (heads padded to a multiple of four with copies of the last).
+      const int nhp = (nh + 3) & ~3;
+      for (int i = tid; i < nhp * D; i += kSelThreads) {
+        const int hj = i / D, dd = i % D;
+        const int h = hm.q_of_kv[g * d.G + h0 + min(hj, nh - 1)];
+        qd[((hj >> 2) * (D / 4) + (dd >> 2)) * 16 + (dd & 3) * 4 + (hj & 3)] =
+            (double)qbar[((size_t)(b * d.Hq + h) * d.nQB + qb) * D + dd];
+      }
+      __syncthreads();
+      // Scores of every candidate for the nh heads, one candidate per lane;
+      // the loop is wave-uniform (past the causal range a lane scores the
+      // last causal block and keeps nothing) so every lane stays active for
+      // the row broadcasts.
+      for (int base = wave * 64; base < ncausal; base += kSelThreads) {
+        const int kb = base + lane;
+        const bool ok = kb < ncausal && !is_forced(kb, diag, d.n_sink, d.n_local);
+        const float* kr = krow0 + (size_t)min(kb, ncausal - 1) * D;
         double gsum = 0.0;
         for (int hb = 0; hb < nh; hb += 4) {
+          // the row through an offset the compiler cannot see is zero: its
+          // loads and widening stay in this loop rather than being hoisted
+          // out of it as live values for every d
+          int z;
+          asm("v_mov_b32 %0, 0" : "=v"(z) : "s"(hb));
           double sc[4] = {0.0, 0.0, 0.0, 0.0};
-          for (int dd = 0; dd < d.D; dd += 4) {
-            const float4 k4 = *(const float4*)(kr + dd);
-            const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const double kv = (double)kk[e];
+          score_bcast<D>(kr + z, qd + (hb >> 2) * (D / 4) * 16 + (lane & 15), sc);
+          if (ok) {
+            if (d.group_select) {
 #pragma unroll
               for (int j = 0; j < 4; ++j)
-                if (hb + j < nh) sc[j] = __fma_rn((double)qv[(hb + j) * d.D + dd + e], kv, sc[j]);
+                if (hb + j < nh) gsum += sc[j];
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                if (hb + j < nh) keys[(size_t)(hb + j) * d.nKB + kb] = orderable_key(sc[j]);
             }
           }
-          if (d.group_select) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (hb + j < nh) gsum += sc[j];
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (hb + j < nh) keys[(size_t)(hb + j) * d.nKB + kb] = orderable_key(sc[j]);
-          }
         }
-        if (d.group_select) keys[kb] = orderable_key(gsum);
+        if (d.group_select && ok) keys[kb] = orderable_key(gsum);
       }
     }
     __syncthreads();
@@ -441,14 +554,16 @@ int select_heads_per_pass(const Dims& d) {
 
 size_t select_smem_bytes(const Dims& d, int hc) {
   const int key_rows = d.group_select ? 1 : hc;
-  return (size_t)key_rows * d.nKB * sizeof(uint64_t) + (size_t)hc * d.D * sizeof(float);
+  return (size_t)key_rows * d.nKB * sizeof(uint64_t) +
+         (size_t)((hc + 3) / 4) * 4 * d.D * sizeof(double);
 }
 
 // Decode scoring: one lane per candidate key block, 64 candidates per
 // workgroup, all q heads of the group (the single query of each head is its
 // block representation: its values, read from q four at a time as scalar
-// operands and widened exactly to float32, are what pooling one token gives). The same float64 ascending-d dot products and orderable keys as
-// select_kernel's own scoring, written to gkeys [B, Hkv, G, nKB] (or the
+// operands and widened exactly, are what pooling one token gives). The same
+// float64 ascending-d dot products and orderable keys as select_kernel's
+// own scoring, written to gkeys [B, Hkv, G, nKB] (or the
 // group sum to [B, Hkv, nKB] with group-shared selection); forced and
 // non-causal blocks are not written. Spreading the pooled-key table over
 // B * Hkv * nKB / 64 workgroups keeps enough loads in flight to stream it;
@@ -458,11 +573,55 @@ size_t select_smem_bytes(const Dims& d, int hc) {
 // table). (Staging the rows through LDS for coalesced loads measured slower:
 // the LDS per workgroup, or the extra passes, cost more occupancy than the
 // scattered 16-byte loads cost bandwidth.)
-__device__ __forceinline__ float4 q4_f32(const float* p) { return *(const float4*)p; }
-__device__ __forceinline__ float4 q4_f32(const uint16_t* p) {
+
+// Four query values widened exactly to float64 (float32 or bfloat16).
+__device__ __forceinline__ void q4_f64(const float* p, double o[4]) {
+  const float4 f = *(const float4*)p;
+  o[0] = (double)f.x; o[1] = (double)f.y; o[2] = (double)f.z; o[3] = (double)f.w;
+}
+__device__ __forceinline__ void q4_f64(const uint16_t* p, double o[4]) {
   const uint2 w = *(const uint2*)p;
-  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
-                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+  o[0] = (double)__uint_as_float(w.x << 16);
+  o[1] = (double)__uint_as_float(w.x & 0xFFFF0000u);
+  o[2] = (double)__uint_as_float(w.y << 16);
+  o[3] = (double)__uint_as_float(w.y & 0xFFFF0000u);
+}
+
+// Scores of one pooled key row kr (float32, D values) against four query
+// rows qv[j] (wave-uniform addresses: scalar loads): float64 fused
+// multiply-adds in ascending d into sc[j]. The key row is read a whole
+// 128-byte line (32 floats) at a time with the next line in flight.
+template <int D, typename QT>
+__device__ __forceinline__ void score4(const float* __restrict__ kr, const QT* const qv[4],
+                                       double sc[4]) {
+  auto load32 = [&](float4* f, int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = *(const float4*)(kr + 32 * c + 4 * i);
+  };
+  auto fma32 = [&](const float4* f, int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float kk[4] = {f[i].x, f[i].y, f[i].z, f[i].w};
+      double qq[4][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) q4_f64(qv[j] + 32 * c + 4 * i, qq[j]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double kv = (double)kk[e];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc[j] = __fma_rn(qq[j][e], kv, sc[j]);
+      }
+    }
+  };
+  float4 fa[8], fb[8];
+  load32(fa, 0);
+#pragma unroll 1
+  for (int c = 0; c < D / 32; c += 2) {
+    load32(fb, c + 1);
+    fma32(fa, c);
+    if (c + 2 < D / 32) load32(fa, c + 2);
+    fma32(fb, c + 1);
+  }
 }
 
 template <int D, typename QT>
@@ -485,37 +644,7 @@ __global__ __launch_bounds__(64) void decode_score_kernel(const QT* __restrict__
       qv[j] = q + (size_t)(b * d.Hq + h) * D;   // Nq == 1
     }
     double sc[4] = {0.0, 0.0, 0.0, 0.0};
-    auto load32 = [&](float4* f, int c) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = *(const float4*)(kr + 32 * c + 4 * i);
-    };
-    auto fma32 = [&](const float4* f, int c) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float kk[4] = {f[i].x, f[i].y, f[i].z, f[i].w};
-        float qq[4][4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 t = q4_f32(qv[j] + 32 * c + 4 * i);
-          qq[j][0] = t.x; qq[j][1] = t.y; qq[j][2] = t.z; qq[j][3] = t.w;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const double kv = (double)kk[e];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sc[j] = __fma_rn((double)qq[j][e], kv, sc[j]);
-        }
-      }
-    };
-    float4 fa[8], fb[8];
-    load32(fa, 0);
-#pragma unroll 1
-    for (int c = 0; c < D / 32; c += 2) {
-      load32(fb, c + 1);
-      fma32(fa, c);
-      if (c + 2 < D / 32) load32(fa, c + 2);
-      fma32(fb, c + 1);
-    }
+    score4<D>(kr, qv, sc);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (hb + j >= d.G) break;
@@ -564,19 +693,7 @@ __global__ __launch_bounds__(64) void decode_select_kernel(const uint64_t* __res
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) lmax = key[j] > lmax ? key[j] : lmax;
-    int rank = 0;
-#pragma unroll
-    for (int j = 0; j < 64; ++j) {
-      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)lmax, j);
-      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(lmax >> 32), j);
-      const uint64_t o = ((uint64_t)hi << 32) | lo;
-      rank += (int)(o > lmax) | ((int)(o == lmax) & (int)(j < lane));
-    }
-    const uint64_t at = __builtin_amdgcn_ballot_w64(rank == free_slots - 1);
-    const int src_lane = __builtin_ctzll(at);
-    const uint32_t t0_hi = __builtin_amdgcn_readlane((uint32_t)(lmax >> 32), src_lane);
-    const uint32_t t0_lo = __builtin_amdgcn_readlane((uint32_t)lmax, src_lane);
-    const uint64_t t0 = ((uint64_t)t0_hi << 32) | t0_lo;
+    const uint64_t t0 = wave_kth_largest(lmax, free_slots, hist);
     uint64_t* ck = (uint64_t*)hist;
     int* cb = (int*)(ck + 64);
     int n = 0;
@@ -593,23 +710,10 @@ __global__ __launch_bounds__(64) void decode_select_kernel(const uint64_t* __res
       n += __popcll(ball);
     }
     wave_lds_fence();
-    if (n <= 64) {
-      uint64_t thr;
-      int k_eq;
-      rank_few(hist, n, free_slots, thr, k_eq);
-      int* out = idx + row * d.budget;
-      int n_out = 0, eq_seen = 0;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (64 * j >= ncausal) break;
-        const int kb = 64 * j + lane;
-        const bool causal = kb < ncausal;
-        const bool forced = causal && is_forced(kb, diag, d.n_sink, d.n_local);
-        compact_step(kb, causal, forced, key[j], false, false, thr, k_eq, lt_mask, out,
-                     d.budget, n_out, eq_seen);
-      }
-      for (int i = n_out + lane; i < d.budget; i += 64) out[i] = -1;
-      if (lane == 0) cnt[row] = min(n_out, d.budget);
+    if (n <= 64) {   // every key that can be taken is gathered
+      const int rank = rank_few(hist, n);
+      const uint64_t picks = __builtin_amdgcn_ballot_w64(lane < n && rank < free_slots);
+      write_picked_row(hist, picks, idx + row * d.budget, cnt, row, d, ncausal);
       return;
     }
   }
@@ -669,8 +773,13 @@ hipError_t launch_select(const float* qbar, const float* kbar, int* idx, int* cn
                          const Dims& d, const HeadMap& hm, hipStream_t stream) {
   const int hc = select_heads_per_pass(d);
   const size_t smem = select_smem_bytes(d, hc);
-  hipLaunchKernelGGL(select_kernel, dim3(d.nQB, d.Hkv, d.B), dim3(kSelThreads), smem, stream,
-                     qbar, kbar, idx, cnt, d, hm, hc);
+  const dim3 grid(d.nQB, d.Hkv, d.B);
+  if (d.D == 128)
+    hipLaunchKernelGGL(select_kernel<128>, grid, dim3(kSelThreads), smem, stream, qbar, kbar, idx,
+                       cnt, d, hm, hc);
+  else
+    hipLaunchKernelGGL(select_kernel<64>, grid, dim3(kSelThreads), smem, stream, qbar, kbar, idx,
+                       cnt, d, hm, hc);
   return hipGetLastError();
 }
 

@@ -40,7 +40,7 @@ struct Problem {
 };
 
 struct Layout {
-  size_t qbar, kbar, kc, keys, vt, queues, partials, loss, total;
+  size_t qbar, kbar, kc, keys, vt, kn, queues, partials, loss, total;
 };
 
 Layout layout_of(const Problem& P) {
@@ -57,6 +57,8 @@ Layout layout_of(const Problem& P) {
   if (P.decode) off += align256((size_t)d.B * d.Hq * d.nKB * sizeof(uint64_t));
   L.vt = off;
   if (P.bf16 && !P.decode) off += align256((size_t)d.B * d.Hkv * d.D * d.Nk * sizeof(uint16_t));
+  L.kn = off;   // largest key norm per 64-key block, written by the V transpose
+  if (P.bf16 && !P.decode) off += align256((size_t)d.B * d.Hkv * (d.Nk / 64) * sizeof(float));
   L.queues = off;   // prefill work queues, zeroed by the V transpose of every call
   if (P.bf16 && !P.decode) off += align256((size_t)ssa::kNumXcd * ssa::kQueueStride * sizeof(int));
   L.partials = off;
@@ -357,12 +359,14 @@ ssa_status ssa_attn_fwd(const ssa_problem* p, const void* q, const void* k, cons
                       "attention (decode)");
   uint16_t* vt = (uint16_t*)(w + L.vt);
   int* queues = (int*)(w + L.queues);
+  float* kn = ssa::prefill_key_norms(d, h_full == nullptr) ? (float*)(w + L.kn) : nullptr;
   hipError_t e = ssa::launch_transpose((const uint16_t*)v, vt, d.B * d.Hkv, d.Nk, d.D, queues,
-                                       ssa::prefill_vt_blk16(d, h_full == nullptr), st);
+                                       ssa::prefill_vt_blk16(d, h_full == nullptr),
+                                       (const uint16_t*)k, kn, st);
   if (e != hipSuccess) return hip_status(e, "transpose v");
   return hip_status(ssa::launch_attn_prefill_bf16((const uint16_t*)q, (const uint16_t*)k, vt, idx,
                                                   cnt, (uint16_t*)h_full, (uint16_t*)h_sparse,
-                                                  delta, lse, queues, d, P.hm, st),
+                                                  delta, lse, queues, kn, d, P.hm, st),
                     "attention (prefill)");
 }
 

@@ -802,7 +802,8 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vt, const int* __restrict__ idx, const int* __restrict__ cnt,
     uint16_t* __restrict__ Hf, uint16_t* __restrict__ Hs, float* __restrict__ delta,
-    float* __restrict__ lse, int* __restrict__ queues, Dims d, HeadMap hm) {
+    float* __restrict__ lse, int* __restrict__ queues, const float* __restrict__ kn, Dims d,
+    HeadMap hm) {
   constexpr int HPW = 4;
   constexpr int NW = 8;
   constexpr int KSPR = D / 8;
@@ -811,14 +812,21 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
   constexpr int NDT = D / 32;
   constexpr int TILE = kBlock * D;
   constexpr int LPH = (TILE / 8) / (64 * NW);   // buffer loads per half tile (K or V) per wave
-  constexpr float kTau = 8.0f;
+  // rescale slack 2^24 (P <= 2^24: no float32 or bfloat16 range concern for
+  // up to 2^18 keys): wide enough for the norm bound below to spare most
+  // blocks their maximum when queries and keys have unit-variance entries
+  constexpr float kTau = 24.0f;
   constexpr int kMaxWords = kMaxKeyBlocks / 32;
   // one LDS object per stage, always addressed with a compile-time stage,
   // so copies into one stage and reads of another are known not to alias
   __shared__ __align__(16) uint16_t K0[TILE], K1[TILE], K2[TILE], K3[NST > 3 ? TILE : 8];
   __shared__ __align__(16) uint16_t V0[TILE], V1[TILE], V2[TILE], V3[NST > 3 ? TILE : 8];
   __shared__ uint32_t sel_mask[HPW][kMaxWords];
-  __shared__ uint16_t list[2 * kMaxKeyBlocks];
+  // walk list entries: key block (bits 0-11), the heads that compute it
+  // (bits 12-15), the block's largest key norm rounded up to bfloat16 (bits
+  // 16-31)
+  __shared__ uint32_t list[2 * kMaxKeyBlocks];
+  __shared__ float knl[kMaxKeyBlocks];   // largest key norm of each causal block
   __shared__ int scan_u[kMaxWords], scan_c[kMaxWords];
   __shared__ int counts[2];
 
@@ -889,6 +897,10 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
       if (kb >= 0 && kb <= diag) atomicOr(&sel_mask[u][kb >> 5], 1u << (kb & 31));
     }
   }
+  {
+    const float* knr = kn + (size_t)(b * d.Hkv + g) * (d.Nk / kBlock);
+    for (int kb = tid; kb <= diag; kb += 64 * NW) knl[kb] = knr[kb];
+  }
   __syncthreads();
   uint32_t wu = 0u, wc = 0u;
   if (tid < nwords) {
@@ -921,13 +933,19 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
     uint32_t m[HPW];
 #pragma unroll
     for (int u = 0; u < HPW; ++u) m[u] = sel_mask[u][tid];
+    // a norm rounded up to bfloat16 stays an upper bound (NaN becomes +inf)
+    auto kn_bits = [&](int kb) __attribute__((always_inline)) {
+      const uint32_t x = min(__float_as_uint(knl[kb]), 0x7F800000u);
+      return (x + 0xFFFFu) & 0xFFFF0000u;
+    };
     int pos = scan_u[tid];
     for (uint32_t bb = wu; bb != 0u; bb &= bb - 1u) {
       const int bit = __builtin_ctz(bb);
       uint32_t act = 0u;
 #pragma unroll
       for (int u = 0; u < HPW; ++u) act |= ((m[u] >> bit) & 1u) << u;
-      list[pos++] = (uint16_t)(((tid << 5) + bit) | (act << 12));
+      const int kb = (tid << 5) + bit;
+      list[pos++] = (uint32_t)kb | (act << 12) | kn_bits(kb);
     }
     pos = nA + scan_c[tid];
     for (uint32_t bb = wc; bb != 0u; bb &= bb - 1u) {
@@ -935,7 +953,8 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
       uint32_t act = 0u;
 #pragma unroll
       for (int u = 0; u < HPW; ++u) act |= (((m[u] >> bit) & 1u) ^ 1u) << u;
-      list[pos++] = (uint16_t)(((tid << 5) + bit) | (act << 12));
+      const int kb = (tid << 5) + bit;
+      list[pos++] = (uint32_t)kb | (act << 12) | kn_bits(kb);
     }
   }
   __syncthreads();
@@ -951,6 +970,9 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
   };
   auto entry_act = [&](int e) __attribute__((always_inline)) {
     return ((__builtin_amdgcn_readfirstlane((int)list[e]) >> (12 + hs)) & 1) != 0;
+  };
+  auto entry_kn = [&](int e) __attribute__((always_inline)) {
+    return __uint_as_float((uint32_t)__builtin_amdgcn_readfirstlane((int)list[e]) & 0xFFFF0000u);
   };
   // copies past the end of the list repeat its last block (or block 0):
   // every slot issues the same number of copies, so the waits are static
@@ -985,6 +1007,23 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
   // compiler does not count the LDS copies below, so it must see no load of
   // its own outstanding
   __builtin_amdgcn_s_waitcnt(0xF70);
+  // Bound on this row's scaled logits against a key block: |q| sl2 times
+  // the block's largest key norm, raised by 2^-10 (far above the float32
+  // rounding of the dot products and norms). A block whose bound is at most
+  // m_ref + kTau cannot trigger a rescale, so its maximum is not needed.
+  float qsq = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const uint4 u = __builtin_bit_cast(uint4, qf[ks]);
+    const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xFFFF0000u);
+      qsq = fmaf(lo, lo, qsq);
+      qsq = fmaf(hi, hi, qsq);
+    }
+  }
+  const float qbound = sqrtf(pair_sum(qsq)) * sl2 * (1.f + 0x1p-10f);
   // prologue = the copies of the virtual slots before slot 0: K(0..NST-2)
   // and V(0..NST-3), with V(0) standing in for the missing V(-1)
   load_k(I0{}, 0);
@@ -1107,14 +1146,19 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
         if (key0 + 32 > qq) s1[v] = -INFINITY;
       }
     }
-    // two chains of three-input maxima: 17 VALU operations for the 32 logits
-    float mx0 = -INFINITY, mx1 = -INFINITY;
+    // the block maximum only when some row's bound allows a rescale (always
+    // for a row's first block, and for a NaN bound): two chains of
+    // three-input maxima, 17 VALU operations for the 32 logits
+    float m_blk = -INFINITY;
+    if (__builtin_amdgcn_ballot_w64(!(qbound * entry_kn(e) <= m_ref + kTau)) != 0) {
+      float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 16; v += 2) {
-      mx0 = max3f(mx0, s0[v], s1[v]);
-      mx1 = max3f(mx1, s0[v + 1], s1[v + 1]);
+      for (int v = 0; v < 16; v += 2) {
+        mx0 = max3f(mx0, s0[v], s1[v]);
+        mx1 = max3f(mx1, s0[v + 1], s1[v + 1]);
+      }
+      m_blk = pair_max(fmaxf(mx0, mx1)) * sl2;
     }
-    const float m_blk = pair_max(fmaxf(mx0, mx1)) * sl2;
     if (__builtin_amdgcn_ballot_w64(m_blk > m_ref + kTau) != 0) {
       const float m_new = fmaxf(m_ref, m_blk);
       const float alpha = fast_exp2(m_ref - m_new);
@@ -2061,8 +2105,8 @@ static hipError_t compute_units(int* out) {
 
 hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* vt,
                                     const int* idx, const int* cnt, uint16_t* hf, uint16_t* hs,
-                                    float* delta, float* lse, int* queues, const Dims& d,
-                                    const HeadMap& hm, hipStream_t stream) {
+                                    float* delta, float* lse, int* queues, const float* kn,
+                                    const Dims& d, const HeadMap& hm, hipStream_t stream) {
   if (d.tok) {   // per-token lists
     const int tiles = d.B * d.Hq * d.nQT;
 #define SSA_TOK_LAUNCH(DD, TT)                                                                  \
@@ -2137,8 +2181,9 @@ hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const 
       if (e != hipSuccess) return e;
       grid = std::min(groups, cus);
     }
+    if (kn == nullptr) return hipErrorInvalidValue;   // prefill_key_norms holds here
     hipLaunchKernelGGL((attn_prefill_bf16_pp_kernel<128, 3>), dim3(grid), dim3(512), 0, stream,
-                       q, k, vt, idx, cnt, hf, hs, delta, lse, dyn ? queues : nullptr, d, hm);
+                       q, k, vt, idx, cnt, hf, hs, delta, lse, dyn ? queues : nullptr, kn, d, hm);
     return hipGetLastError();
   }
   const int total = d.B * d.Hq * d.nQB;

@@ -45,10 +45,18 @@ inline size_t tok_kc_bytes(const Dims& d) {
 }
 hipError_t launch_select_tok(const void* q, bool bf16, const float* kbar, double* kc, int* idx,
                              int* cnt, const Dims& d, const HeadMap& hm, hipStream_t stream);
-// Also zeroes the prefill work queues (kNumXcd counters) when queues != NULL.
+// Also zeroes the prefill work queues (kNumXcd counters) when queues != NULL,
+// and when kn != NULL writes kn[bh][n / 64], the largest L2 norm of the 64
+// keys of each block of k ([BH, N, D] bf16), for prefill_key_norms.
 // blk16: the layout of prefill_vt_blk16 problems ([n/16][d][n%16] per head).
 hipError_t launch_transpose(const uint16_t* v, uint16_t* vt, int BH, int N, int D, int* queues,
-                            bool blk16, hipStream_t stream);
+                            bool blk16, const uint16_t* k, float* kn, hipStream_t stream);
+// The grouped dual-stream prefill kernel bounds each key block's logits by
+// its queries' norms times the block's largest key norm (from the transpose)
+// and skips the block maximum when the bound cannot trigger a rescale.
+inline bool prefill_key_norms(const Dims& d, bool sparse_only) {
+  return d.D == 128 && d.G % 4 == 0 && !sparse_only && !d.tok && d.bs != 16;
+}
 // Sparse-only prefill with 16-token per-block lists runs the gather kernel,
 // which reads V^T one 16-key block at a time: contiguous per block.
 inline bool prefill_vt_blk16(const Dims& d, bool sparse_only) {
@@ -57,10 +65,11 @@ inline bool prefill_vt_blk16(const Dims& d, bool sparse_only) {
 
 // queues: kNumXcd zeroed counters (see launch_transpose), or NULL for a
 // static workgroup-to-tile mapping.
+// kn: the transpose's key-block norms when prefill_key_norms(d, hf == NULL).
 hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* vt,
                                     const int* idx, const int* cnt, uint16_t* hf, uint16_t* hs,
-                                    float* delta, float* lse, int* queues, const Dims& d,
-                                    const HeadMap& hm, hipStream_t stream);
+                                    float* delta, float* lse, int* queues, const float* kn,
+                                    const Dims& d, const HeadMap& hm, hipStream_t stream);
 hipError_t launch_attn_rows_f32(const float* q, const float* k, const float* v, const int* idx,
                                 const int* cnt, float* hf, float* hs, float* delta, float* lse,
                                 const Dims& d, const HeadMap& hm, hipStream_t stream);

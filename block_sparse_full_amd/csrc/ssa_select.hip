@@ -986,8 +986,38 @@ hipError_t launch_select_tok(const void* q, bool bf16, const float* kbar, double
 template <bool BLK16>
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ v,
                                                         uint16_t* __restrict__ vt, int N, int D,
-                                                        int* __restrict__ queues) {
+                                                        int* __restrict__ queues,
+                                                        const uint16_t* __restrict__ k,
+                                                        float* __restrict__ kn) {
   __shared__ uint16_t tile[64][66];
+  if (kn != nullptr && blockIdx.y == 0) {
+    // The largest key norm of this 64-key block: four threads per key, each
+    // summing squares over a quarter of the 16-byte chunks, then maxima over
+    // the wave's 16 keys and the four waves.
+    __shared__ float wmax[4];
+    const int key = threadIdx.x >> 2, part = threadIdx.x & 3;
+    const uint16_t* kr = k + (blockIdx.z * (size_t)N + blockIdx.x * 64 + key) * D;
+    float ss = 0.f;
+    for (int c = part; c < D / 8; c += 4) {
+      const uint4 u = *(const uint4*)(kr + 8 * c);
+      const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xFFFF0000u);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
+    }
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+#pragma unroll
+    for (int off = 4; off < 64; off <<= 1) ss = fmaxf(ss, __shfl_xor(ss, off));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      kn[blockIdx.z * (size_t)(N / 64) + blockIdx.x] =
+          sqrtf(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
+  }
   if (queues != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 &&
       threadIdx.x < kNumXcd)
     queues[threadIdx.x * kQueueStride] = 0;
@@ -1006,13 +1036,13 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
 }
 
 hipError_t launch_transpose(const uint16_t* v, uint16_t* vt, int BH, int N, int D, int* queues,
-                            bool blk16, hipStream_t stream) {
+                            bool blk16, const uint16_t* k, float* kn, hipStream_t stream) {
   if (blk16)
     hipLaunchKernelGGL(transpose_kernel<true>, dim3(N / 64, D / 64, BH), dim3(256), 0, stream, v,
-                       vt, N, D, queues);
+                       vt, N, D, queues, k, kn);
   else
     hipLaunchKernelGGL(transpose_kernel<false>, dim3(N / 64, D / 64, BH), dim3(256), 0, stream, v,
-                       vt, N, D, queues);
+                       vt, N, D, queues, k, kn);
   return hipGetLastError();
 }
 

@@ -97,9 +97,11 @@ def test_workspace_checks(lib):
     from block_sparse_full_amd.ssa import workspace_bytes
     p = _p()
     need = workspace_bytes(p)
-    # pooled Q + pooled K + transposed V + prefill work queues (8 counters on
-    # 256-byte lines) + loss partials, each 256-byte aligned
-    expect = 8 * 64 * 128 * 4 + 2 * 64 * 128 * 4 + 2 * 128 * 4096 * 2 + 8 * 256 + 1024 * 8
+    # pooled Q + pooled K + transposed V + key-block norms (2 x 64 floats,
+    # 512 bytes) + prefill work queues (8 counters on 256-byte lines) + loss
+    # partials, each 256-byte aligned
+    expect = (8 * 64 * 128 * 4 + 2 * 64 * 128 * 4 + 2 * 128 * 4096 * 2 + 512 + 8 * 256
+              + 1024 * 8)
     assert need == expect
     c, keep = p.to_c()
     st = lib.ssa_align_loss(ctypes.byref(c), 16, 16, 16, None, None, 4096, need - 256, None)

@@ -1268,7 +1268,8 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vt, const int* __restrict__ idx, const int* __restrict__ cnt,
     uint16_t* __restrict__ Hf, uint16_t* __restrict__ Hs, float* __restrict__ delta,
-    float* __restrict__ lse, int* __restrict__ queues, Dims d, HeadMap hm) {
+    float* __restrict__ lse, int* __restrict__ queues, const float* __restrict__ kn, Dims d,
+    HeadMap hm) {
   constexpr int D = 64;
   constexpr int HPW = 4;
   constexpr int NW = 8;
@@ -1278,7 +1279,8 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
   constexpr int NDT = D / 32;
   constexpr int TILE = kBlock * D;
   constexpr int LPH = (TILE / 8) / (64 * NW);   // buffer loads per half tile (K or V) per wave
-  constexpr float kTau = 8.0f;
+  // rescale slack 2^24, as in the kernel above, for the key-norm bound
+  constexpr float kTau = 24.0f;
   constexpr int kWords16 = kMaxKeyBlocks / 32;
   static_assert(LPH == 1, "copy shape");
   // each stage holds TPE consecutive 64-key tiles (one list entry)
@@ -1287,6 +1289,7 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
   __shared__ __align__(16) uint16_t V0[TPE * TILE], V1[TPE * TILE], V2[TPE * TILE],
       V3[NST > 3 ? TPE * TILE : 8];
   __shared__ uint32_t sel16[HPW][4][kWords16];   // per head and 16-row query block
+  __shared__ float knl[kMaxKeyBlocks];           // largest key norm of each causal tile
 
   const int ngrp = d.G / HPW;
   const int total = d.B * d.Hkv * ngrp * d.nQT;
@@ -1348,6 +1351,10 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
       }
     }
   }
+  {
+    const float* knr = kn + (size_t)(b * d.Hkv + g) * (d.Nk / kBlock);
+    for (int t = tid; t < ntiles; t += 64 * NW) knl[t] = knr[t];
+  }
   __syncthreads();
   (void)nwords16;
 
@@ -1392,6 +1399,20 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
   // the Q fragments land before any LDS copy is issued: the compiler does
   // not count the copies, so it must see no load of its own outstanding
   __builtin_amdgcn_s_waitcnt(0xF70);
+  // bound on this row's scaled logits against a tile (the kernel above)
+  float qsq = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const uint4 u = __builtin_bit_cast(uint4, qf[ks]);
+    const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xFFFF0000u);
+      qsq = fmaf(lo, lo, qsq);
+      qsq = fmaf(hi, hi, qsq);
+    }
+  }
+  const float qbound = sqrtf(pair_sum(qsq)) * sl2 * (1.f + 0x1p-10f);
   // prologue = the copies of the virtual slots before slot 0: K(0..NST-2)
   // and V(0..NST-3), with V(0) standing in for the missing V(-1)
   load_k_e(I0{}, 0);
@@ -1544,15 +1565,22 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
         }
       }
     }
-    float mx0 = -INFINITY, mx1 = -INFINITY;
+    // the entry's maximum only when some row's bound allows a rescale
+    float knb = 0.f;
 #pragma unroll
-    for (int tt = 0; tt < TPE; ++tt)
+    for (int tt = 0; tt < TPE; ++tt) knb = fmaxf(knb, knl[tile_c(TPE * e + tt)]);
+    float m_blk = -INFINITY;
+    if (__builtin_amdgcn_ballot_w64(!(qbound * knb <= m_ref + kTau)) != 0) {
+      float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        mx0 = max3f(mx0, sc[tt][0][v], sc[tt][1][v]);
-        mx1 = max3f(mx1, sc[tt][0][v + 1], sc[tt][1][v + 1]);
-      }
-    const float m_blk = pair_max(fmaxf(mx0, mx1)) * sl2;
+      for (int tt = 0; tt < TPE; ++tt)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          mx0 = max3f(mx0, sc[tt][0][v], sc[tt][1][v]);
+          mx1 = max3f(mx1, sc[tt][0][v + 1], sc[tt][1][v + 1]);
+        }
+      m_blk = pair_max(fmaxf(mx0, mx1)) * sl2;
+    }
     if (__builtin_amdgcn_ballot_w64(m_blk > m_ref + kTau) != 0) {
       const float m_new = fmaxf(m_ref, m_blk);
       const float alpha = fast_exp2(m_ref - m_new);
@@ -2154,8 +2182,9 @@ hipError_t launch_attn_prefill_bf16(const uint16_t* q, const uint16_t* k, const 
       if (e != hipSuccess) return e;
       grid = std::min(groups, cus);
     }
+    if (kn == nullptr) return hipErrorInvalidValue;   // prefill_key_norms holds here
     hipLaunchKernelGGL((attn_prefill_bf16_pp16_kernel<3, 2>), dim3(grid), dim3(512), 0, stream,
-                       q, k, vt, idx, cnt, hf, hs, delta, lse, dyn ? queues : nullptr, d, hm);
+                       q, k, vt, idx, cnt, hf, hs, delta, lse, dyn ? queues : nullptr, kn, d, hm);
     return hipGetLastError();
   }
   if (d.bs == 16) {

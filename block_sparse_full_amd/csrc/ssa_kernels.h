@@ -51,11 +51,13 @@ hipError_t launch_select_tok(const void* q, bool bf16, const float* kbar, double
 // blk16: the layout of prefill_vt_blk16 problems ([n/16][d][n%16] per head).
 hipError_t launch_transpose(const uint16_t* v, uint16_t* vt, int BH, int N, int D, int* queues,
                             bool blk16, const uint16_t* k, float* kn, hipStream_t stream);
-// The grouped dual-stream prefill kernel bounds each key block's logits by
-// its queries' norms times the block's largest key norm (from the transpose)
-// and skips the block maximum when the bound cannot trigger a rescale.
+// The grouped dual-stream prefill kernels bound each key block's logits by
+// their queries' norms times the block's largest key norm (from the
+// transpose) and skip the block maximum when the bound cannot trigger a
+// rescale.
 inline bool prefill_key_norms(const Dims& d, bool sparse_only) {
-  return d.D == 128 && d.G % 4 == 0 && !sparse_only && !d.tok && d.bs != 16;
+  return d.G % 4 == 0 && !sparse_only && !d.tok &&
+         ((d.D == 128 && d.bs != 16) || (d.D == 64 && d.bs == 16));
 }
 // Sparse-only prefill with 16-token per-block lists runs the gather kernel,
 // which reads V^T one 16-key block at a time: contiguous per block.

@@ -37,8 +37,8 @@ FP64_PEAK_TFLOPS = 78.6          # MI355X float64 vector FMA
 # sources they were taken on (the prefill file and the headers it includes);
 # any other source reports traffic as null.
 PREFILL_TRAFFIC = {
-    # 783732 KiB x 2.000 read + 532014 KiB x 1.000 written per dispatch
-    "6384fedc840a4ff94d5c60c1437b910ec8095b02ed5b5b000c4014aedede90c4": int(783732 * 2.0 * 1024 + 532014 * 1.0 * 1024),
+    # 784307 KiB x 2.000 read + 531629 KiB x 1.000 written per dispatch
+    "333950fc0fcd7e4e2bc1a7298931bd47a96d3904aa7b2b9b17e36a99321064cc": int(784307 * 2.0 * 1024 + 531629 * 1.0 * 1024),
 }
 PREFILL_SRCS = [os.path.join(ROOT, "block_sparse_full_amd", "csrc", f)
                 for f in ("ssa_attn_prefill.hip", "ssa_device.h", "ssa_common.h")]

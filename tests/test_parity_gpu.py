@@ -200,6 +200,34 @@ def test_block16_parity(ssa, name, kw, budget, n_sink, n_local, sparse):
                  sparse_only=sparse)
 
 
+# Large and growing logits: queries scaled by 4 and keys by a ramp from 1 at
+# the first position to 8 at the last, so a row's block maxima climb along
+# the walk by far more than the 2^24 rescale slack (logit standard deviation
+# from about 6 to 46 in log2 units). The grouped kernels' key-norm bound can
+# then no longer rule out a rescale: they compute the block maxima and
+# rescale many times. The selection favours the late, large blocks, so the
+# selected stream's weights stay within float32 range of the row maximum
+# (the 16-token kernel keeps one running maximum for both streams).
+LARGE_LOGITS = [
+    ("gqa_8k_peaked", dict(B=1, Hq=8, Hkv=2, N=2048), 6, 1, 1, 64),   # D 128, 64-token blocks
+    ("paper_16k_b16", dict(Hq=8, Hkv=2, N=2048), 16, 1, 1, 16),       # D 64, 16-token blocks
+]
+
+
+@pytest.mark.parametrize("name,kw,budget,n_sink,n_local,block", LARGE_LOGITS,
+                         ids=["grouped-d128", "grouped-b16"])
+def test_large_logits_parity(ssa, name, kw, budget, n_sink, n_local, block):
+    cfg = CONFIGS[name].with_sizes(budget=budget, n_sink=n_sink, n_local=n_local, **kw)
+    say(f"[parity] large logits {cfg}")
+    x = make_inputs(cfg)
+    ramp = torch.linspace(1.0, 8.0, cfg.N).view(1, 1, cfg.N, 1)
+    x["q"] = x["q"] * 4
+    x["k"] = (x["k"].float() * ramp).to(x["k"].dtype)
+    got = gpu_run(ssa, x, budget=budget, n_sink=n_sink, n_local=n_local, want_lse=True,
+                  block=block)
+    full_compare(cfg, x, got, budget=budget, n_sink=n_sink, n_local=n_local, lse=True)
+
+
 # Sparse-only prefill with per-block lists (the gather kernel): 16- and
 # 64-token blocks, D 64 and 128, GQA 1:1 to 16:1 and 3:1 (workgroups whose
 # four lists span query blocks), odd list lengths, no forced blocks (the

@@ -828,6 +828,7 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
   __shared__ uint32_t list[2 * kMaxKeyBlocks];
   __shared__ float knl[kMaxKeyBlocks];   // largest key norm of each causal block
   __shared__ int scan_u[kMaxWords], scan_c[kMaxWords];
+  __shared__ uint32_t word_u[kMaxWords], word_c[kMaxWords];
   __shared__ int counts[2];
 
   const int ngrp = d.G / HPW;
@@ -902,60 +903,56 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
     for (int kb = tid; kb <= diag; kb += 64 * NW) knl[kb] = knr[kb];
   }
   __syncthreads();
-  uint32_t wu = 0u, wc = 0u;
+  // per 32-block word: the union (wu) and complement (wc) bits, their
+  // counts, exclusive prefix sums by wave 0 (64 words per step), then one
+  // thread per causal block writes its entries at its prefix position
   if (tid < nwords) {
     const uint32_t lim = (tid == nwords - 1) ? (0xffffffffu >> (31 - (diag & 31))) : 0xffffffffu;
     uint32_t any = 0u, all = 0xffffffffu;
 #pragma unroll
     for (int u = 0; u < HPW; ++u) { any |= sel_mask[u][tid]; all &= sel_mask[u][tid]; }
-    wu = any & lim;
-    wc = sparse_only ? 0u : (~all & lim);
+    const uint32_t wu = any & lim;
+    const uint32_t wc = sparse_only ? 0u : (~all & lim);
+    word_u[tid] = wu;
+    word_c[tid] = wc;
     scan_u[tid] = __popc(wu);
     scan_c[tid] = __popc(wc);
   }
   __syncthreads();
-  if (tid == 0) {
-    int su = 0, sc = 0;
-    for (int w = 0; w < nwords; ++w) {
-      const int pu = scan_u[w], pc = scan_c[w];
-      scan_u[w] = su; scan_c[w] = sc;
-      su += pu; sc += pc;
+  if (wave == 0) {
+    int cu = 0, cc = 0;   // carried totals of earlier 64-word steps
+    for (int w0 = 0; w0 < nwords; w0 += 64) {
+      const int w = w0 + lane;
+      const int pu = w < nwords ? scan_u[w] : 0, pc = w < nwords ? scan_c[w] : 0;
+      int iu = pu, ic = pc;   // inclusive wave scans
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int ou = __shfl_up(iu, off, 64), oc = __shfl_up(ic, off, 64);
+        if (lane >= off) { iu += ou; ic += oc; }
+      }
+      if (w < nwords) { scan_u[w] = cu + iu - pu; scan_c[w] = cc + ic - pc; }
+      cu += __shfl(iu, 63, 64);
+      cc += __shfl(ic, 63, 64);
     }
-    counts[0] = su;
-    counts[1] = sc;
+    if (lane == 0) { counts[0] = cu; counts[1] = cc; }
   }
   __syncthreads();
   const int nA = __builtin_amdgcn_readfirstlane(counts[0]);
   const int nB = __builtin_amdgcn_readfirstlane(counts[1]);
   const int n = nA + nB;
-  __syncthreads();
-  if (tid < nwords) {
-    uint32_t m[HPW];
+  for (int kb = tid; kb <= diag; kb += 64 * NW) {
+    const int w = kb >> 5, bit = kb & 31;
+    const uint32_t below = (1u << bit) - 1u;
+    const uint32_t wu = word_u[w], wc = word_c[w];
+    uint32_t mine = 0u;   // the heads that selected kb
 #pragma unroll
-    for (int u = 0; u < HPW; ++u) m[u] = sel_mask[u][tid];
+    for (int u = 0; u < HPW; ++u) mine |= ((sel_mask[u][w] >> bit) & 1u) << u;
     // a norm rounded up to bfloat16 stays an upper bound (NaN becomes +inf)
-    auto kn_bits = [&](int kb) __attribute__((always_inline)) {
-      const uint32_t x = min(__float_as_uint(knl[kb]), 0x7F800000u);
-      return (x + 0xFFFFu) & 0xFFFF0000u;
-    };
-    int pos = scan_u[tid];
-    for (uint32_t bb = wu; bb != 0u; bb &= bb - 1u) {
-      const int bit = __builtin_ctz(bb);
-      uint32_t act = 0u;
-#pragma unroll
-      for (int u = 0; u < HPW; ++u) act |= ((m[u] >> bit) & 1u) << u;
-      const int kb = (tid << 5) + bit;
-      list[pos++] = (uint32_t)kb | (act << 12) | kn_bits(kb);
-    }
-    pos = nA + scan_c[tid];
-    for (uint32_t bb = wc; bb != 0u; bb &= bb - 1u) {
-      const int bit = __builtin_ctz(bb);
-      uint32_t act = 0u;
-#pragma unroll
-      for (int u = 0; u < HPW; ++u) act |= (((m[u] >> bit) & 1u) ^ 1u) << u;
-      const int kb = (tid << 5) + bit;
-      list[pos++] = (uint32_t)kb | (act << 12) | kn_bits(kb);
-    }
+    const uint32_t knb = (min(__float_as_uint(knl[kb]), 0x7F800000u) + 0xFFFFu) & 0xFFFF0000u;
+    if ((wu >> bit) & 1u)
+      list[scan_u[w] + __popc(wu & below)] = (uint32_t)kb | (mine << 12) | knb;
+    if ((wc >> bit) & 1u)
+      list[nA + scan_c[w] + __popc(wc & below)] = (uint32_t)kb | ((mine ^ 0xFu) << 12) | knb;
   }
   __syncthreads();
 

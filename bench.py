@@ -37,8 +37,8 @@ FP64_PEAK_TFLOPS = 78.6          # MI355X float64 vector FMA
 # sources they were taken on (the prefill file and the headers it includes);
 # any other source reports traffic as null.
 PREFILL_TRAFFIC = {
-    # 784307 KiB x 2.000 read + 531629 KiB x 1.000 written per dispatch
-    "333950fc0fcd7e4e2bc1a7298931bd47a96d3904aa7b2b9b17e36a99321064cc": int(784307 * 2.0 * 1024 + 531629 * 1.0 * 1024),
+    # 783211 KiB x 2.000 read + 531583 KiB x 1.000 written per dispatch
+    "27525f210fb06339dd9014fbe001590c626d176111f4135cf4775976434d137b": int(783211 * 2.0 * 1024 + 531583 * 1.0 * 1024),
 }
 PREFILL_SRCS = [os.path.join(ROOT, "block_sparse_full_amd", "csrc", f)
                 for f in ("ssa_attn_prefill.hip", "ssa_device.h", "ssa_common.h")]

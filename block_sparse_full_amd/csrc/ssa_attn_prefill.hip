@@ -771,11 +771,12 @@ __device__ __forceinline__ void tile_to_lds_asm(i32x4_t rsrc, uint32_t tile_off,
 // wave w takes rows 32*(w/4) .. +31 of head w%4, so each SIMD holds one wave
 // of group A (waves 0-3) and one of group B (waves 4-7).
 //
-// Walk: list entries [0, nA) are the union of the four heads' selected
-// blocks, [nA, n) the causal blocks not selected by all four, both
-// ascending; a head computes an entry of the first part when it selected it
-// and of the second part when it did not. Each head thus sees exactly its
-// selected blocks, a snapshot (h_sparse), then its other causal blocks.
+// Walk: one list for the four heads, each entry marking the heads that
+// compute it, built so that each head sees exactly its selected blocks, a
+// snapshot (h_sparse), then its other causal blocks; blocks selected by
+// only some of the heads are walked twice (once for the heads that selected
+// them, once for the others) unless their heads fit the snapshot order
+// (details where the list is built).
 //
 // Ping-pong: time is cut into slots separated by workgroup barriers; in
 // slot 2e group A runs GEMM(e) = QK^T(e) + PV(e-1) while group B runs
@@ -817,6 +818,7 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
   // blocks their maximum when queries and keys have unit-variance entries
   constexpr float kTau = 24.0f;
   constexpr int kMaxWords = kMaxKeyBlocks / 32;
+  constexpr int kParts = 5;
   // one LDS object per stage, always addressed with a compile-time stage,
   // so copies into one stage and reads of another are known not to alias
   __shared__ __align__(16) uint16_t K0[TILE], K1[TILE], K2[TILE], K3[NST > 3 ? TILE : 8];
@@ -827,9 +829,13 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
   // 16-31)
   __shared__ uint32_t list[2 * kMaxKeyBlocks];
   __shared__ float knl[kMaxKeyBlocks];   // largest key norm of each causal block
-  __shared__ int scan_u[kMaxWords], scan_c[kMaxWords];
-  __shared__ uint32_t word_u[kMaxWords], word_c[kMaxWords];
-  __shared__ int counts[2];
+  // walk-list parts (below): per 32-block word the part's bits and the
+  // exclusive prefix of their counts
+  __shared__ uint32_t word_p[kParts][kMaxWords];
+  __shared__ int scan_p[kParts][kMaxWords];
+  __shared__ int counts[kParts];
+  __shared__ int snap_at[HPW];   // the entry before which each head takes its snapshot
+  __shared__ int mask_hist[16];  // causal blocks per selection pattern of the four heads
 
   const int ngrp = d.G / HPW;
   const int total = d.B * d.Hkv * ngrp * d.nQB;
@@ -876,6 +882,7 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
   // ---- walk list
   const int nwords = (diag >> 5) + 1;
   for (int w = tid; w < HPW * kMaxWords; w += 64 * NW) (&sel_mask[0][0])[w] = 0u;
+  if (tid < 16) mask_hist[tid] = 0;
   {
     // GEMM(0) multiplies the V stage of the (absent) entry -1 by P = 0
     uint16_t* vz = (NST - 1) == 1 ? V1 : (NST - 1) == 2 ? V2 : V3;
@@ -903,56 +910,148 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
     for (int kb = tid; kb <= diag; kb += 64 * NW) knl[kb] = knr[kb];
   }
   __syncthreads();
-  // per 32-block word: the union (wu) and complement (wc) bits, their
-  // counts, exclusive prefix sums by wave 0 (64 words per step), then one
-  // thread per causal block writes its entries at its prefix position
+  // The walk list. m(kb) is the set of the four heads that selected causal
+  // block kb. Every head must meet its selected blocks, then take its
+  // snapshot (h_sparse), then meet its other causal blocks. With the heads
+  // in an order p0..p3 that snapshot last to first (p3 first), the list is
+  //   part 0: blocks with m = all four, and blocks whose m is partial and
+  //           not one of the chain sets below (the heads in m compute them);
+  //   part 1: m = {p0, p1, p2}; part 2: m = {p0, p1}; part 3: m = {p0}
+  //           (every head computes these: selected by the heads that have
+  //           not yet taken their snapshot, unselected for those that have);
+  //   part 4: m = {} and the partial blocks of part 0 again (the heads not
+  //           in m compute them),
+  // each part in ascending block order; p3 takes its snapshot before part
+  // 1, p2 before part 2, p1 before part 3, p0 before part 4. A partial block
+  // whose m is a chain set is walked once instead of twice; the order p is
+  // the one of the 24 that puts the most causal blocks on the chain. In
+  // sparse-only mode there is no part 4 and no chain: every partial block
+  // stays in part 0.
   if (tid < nwords) {
     const uint32_t lim = (tid == nwords - 1) ? (0xffffffffu >> (31 - (diag & 31))) : 0xffffffffu;
     uint32_t any = 0u, all = 0xffffffffu;
 #pragma unroll
     for (int u = 0; u < HPW; ++u) { any |= sel_mask[u][tid]; all &= sel_mask[u][tid]; }
-    const uint32_t wu = any & lim;
-    const uint32_t wc = sparse_only ? 0u : (~all & lim);
-    word_u[tid] = wu;
-    word_c[tid] = wc;
-    scan_u[tid] = __popc(wu);
-    scan_c[tid] = __popc(wc);
+    for (uint32_t part = any & ~all & lim; part != 0u; part &= part - 1u) {
+      const int bit = __builtin_ctz(part);
+      int m = 0;
+#pragma unroll
+      for (int u = 0; u < HPW; ++u) m |= (int)((sel_mask[u][tid] >> bit) & 1u) << u;
+      atomicAdd(&mask_hist[m], 1);
+    }
   }
   __syncthreads();
   if (wave == 0) {
-    int cu = 0, cc = 0;   // carried totals of earlier 64-word steps
+    // lane l < 24 scores the l-th head order: p0 is the (l / 6)-th head,
+    // p1 the ((l % 6) / 2)-th of the three left, p2 the (l % 2)-th of the
+    // two left, p3 the last one
+    auto kth_bit = [](uint32_t m, int k) __attribute__((always_inline)) {
+      for (int i = 0; i < k; ++i) m &= m - 1u;
+      return (int)__builtin_ctz(m);
+    };
+    int p[4];
+    {
+      const int l = lane % 24;
+      uint32_t rem = 0xFu;
+      p[0] = kth_bit(rem, l / 6);
+      rem &= ~(1u << p[0]);
+      p[1] = kth_bit(rem, (l % 6) / 2);
+      rem &= ~(1u << p[1]);
+      p[2] = kth_bit(rem, l % 2);
+      rem &= ~(1u << p[2]);
+      p[3] = (int)__builtin_ctz(rem);
+    }
+    const int c1 = 1 << p[0], c2 = c1 | (1 << p[1]), c3 = c2 | (1 << p[2]);
+    const int score = lane < 24 ? mask_hist[c1] + mask_hist[c2] + mask_hist[c3] : -1;
+    int best = score;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) best = max(best, __shfl_xor(best, off, 64));
+    const uint64_t win = __builtin_amdgcn_ballot_w64(score == best);
+    const int wl = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(win));
+    const int pw0 = __shfl(p[0], wl, 64), pw1 = __shfl(p[1], wl, 64);
+    const int pw2 = __shfl(p[2], wl, 64), pw3 = __shfl(p[3], wl, 64);
+    // chain sets as 4-bit masks; none in sparse-only mode (16 matches no m)
+    const uint32_t ch1 = sparse_only ? 16u : (1u << pw0);
+    const uint32_t ch2 = sparse_only ? 16u : ch1 | (1u << pw1);
+    const uint32_t ch3 = sparse_only ? 16u : ch2 | (1u << pw2);
+    // bits of the blocks whose m equals the 4-bit set c
+    auto eq = [&](uint32_t c, const uint32_t s4[HPW]) __attribute__((always_inline)) {
+      if (c > 15u) return 0u;
+      uint32_t r = 0xffffffffu;
+#pragma unroll
+      for (int u = 0; u < HPW; ++u) r &= ((c >> u) & 1u) ? s4[u] : ~s4[u];
+      return r;
+    };
+    int carry[kParts] = {0, 0, 0, 0, 0};
     for (int w0 = 0; w0 < nwords; w0 += 64) {
       const int w = w0 + lane;
-      const int pu = w < nwords ? scan_u[w] : 0, pc = w < nwords ? scan_c[w] : 0;
-      int iu = pu, ic = pc;   // inclusive wave scans
+      uint32_t pm[kParts] = {0u, 0u, 0u, 0u, 0u};
+      if (w < nwords) {
+        const uint32_t lim = (w == nwords - 1) ? (0xffffffffu >> (31 - (diag & 31))) : 0xffffffffu;
+        uint32_t s4[HPW];
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int ou = __shfl_up(iu, off, 64), oc = __shfl_up(ic, off, 64);
-        if (lane >= off) { iu += ou; ic += oc; }
+        for (int u = 0; u < HPW; ++u) s4[u] = sel_mask[u][w];
+        const uint32_t any = (s4[0] | s4[1] | s4[2] | s4[3]) & lim;
+        const uint32_t all = s4[0] & s4[1] & s4[2] & s4[3] & lim;
+        const uint32_t e1 = eq(ch3, s4) & lim, e2 = eq(ch2, s4) & lim, e3 = eq(ch1, s4) & lim;
+        const uint32_t chain = e1 | e2 | e3;
+        pm[0] = any & ~chain;
+        pm[1] = e1;
+        pm[2] = e2;
+        pm[3] = e3;
+        pm[4] = sparse_only ? 0u : (~all & lim & ~chain);
       }
-      if (w < nwords) { scan_u[w] = cu + iu - pu; scan_c[w] = cc + ic - pc; }
-      cu += __shfl(iu, 63, 64);
-      cc += __shfl(ic, 63, 64);
+#pragma unroll
+      for (int k = 0; k < kParts; ++k) {
+        const int pc = __popc(pm[k]);
+        int inc = pc;   // inclusive wave scan
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int o = __shfl_up(inc, off, 64);
+          if (lane >= off) inc += o;
+        }
+        if (w < nwords) { word_p[k][w] = pm[k]; scan_p[k][w] = carry[k] + inc - pc; }
+        carry[k] += __shfl(inc, 63, 64);
+      }
     }
-    if (lane == 0) { counts[0] = cu; counts[1] = cc; }
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < kParts; ++k) counts[k] = carry[k];
+      const int s1 = carry[0], s2 = s1 + carry[1], s3 = s2 + carry[2], s4 = s3 + carry[3];
+      snap_at[pw3] = s1;
+      snap_at[pw2] = s2;
+      snap_at[pw1] = s3;
+      snap_at[pw0] = s4;
+    }
   }
   __syncthreads();
-  const int nA = __builtin_amdgcn_readfirstlane(counts[0]);
-  const int nB = __builtin_amdgcn_readfirstlane(counts[1]);
-  const int n = nA + nB;
+  int part_base[kParts];
+  {
+    int acc = 0;
+#pragma unroll
+    for (int k = 0; k < kParts; ++k) {
+      part_base[k] = acc;
+      acc += __builtin_amdgcn_readfirstlane(counts[k]);
+    }
+  }
+  const int n = part_base[kParts - 1] + __builtin_amdgcn_readfirstlane(counts[kParts - 1]);
+  const int n_snap = __builtin_amdgcn_readfirstlane(snap_at[hs]);
   for (int kb = tid; kb <= diag; kb += 64 * NW) {
     const int w = kb >> 5, bit = kb & 31;
     const uint32_t below = (1u << bit) - 1u;
-    const uint32_t wu = word_u[w], wc = word_c[w];
     uint32_t mine = 0u;   // the heads that selected kb
 #pragma unroll
     for (int u = 0; u < HPW; ++u) mine |= ((sel_mask[u][w] >> bit) & 1u) << u;
     // a norm rounded up to bfloat16 stays an upper bound (NaN becomes +inf)
     const uint32_t knb = (min(__float_as_uint(knl[kb]), 0x7F800000u) + 0xFFFFu) & 0xFFFF0000u;
-    if ((wu >> bit) & 1u)
-      list[scan_u[w] + __popc(wu & below)] = (uint32_t)kb | (mine << 12) | knb;
-    if ((wc >> bit) & 1u)
-      list[nA + scan_c[w] + __popc(wc & below)] = (uint32_t)kb | ((mine ^ 0xFu) << 12) | knb;
+#pragma unroll
+    for (int k = 0; k < kParts; ++k) {
+      const uint32_t wk = word_p[k][w];
+      if ((wk >> bit) & 1u) {
+        const uint32_t act = k == 0 ? mine : k == 4 ? (mine ^ 0xFu) : 0xFu;
+        list[part_base[k] + scan_p[k][w] + __popc(wk & below)] = (uint32_t)kb | (act << 12) | knb;
+      }
+    }
   }
   __syncthreads();
 
@@ -1128,7 +1227,7 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
   // softmax(e): P(e) from S(e); the sparse snapshot is taken before the
   // first entry of the second part can rescale the accumulator.
   auto softmax = [&](int e) __attribute__((always_inline)) {
-    if (e == nA) snapshot();
+    if (e == n_snap) snapshot();
     if (e >= n || !entry_act(e)) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) pw[k] = 0u;

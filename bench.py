@@ -37,8 +37,8 @@ FP64_PEAK_TFLOPS = 78.6          # MI355X float64 vector FMA
 # sources they were taken on (the prefill file and the headers it includes);
 # any other source reports traffic as null.
 PREFILL_TRAFFIC = {
-    # 783211 KiB x 2.000 read + 531583 KiB x 1.000 written per dispatch
-    "27525f210fb06339dd9014fbe001590c626d176111f4135cf4775976434d137b": int(783211 * 2.0 * 1024 + 531583 * 1.0 * 1024),
+    # 776830 KiB x 2.000 read + 531677 KiB x 1.000 written per dispatch
+    "ed6da421050c2b33fd5ff653bc6e4adcace251241bc6353e745f521eb5d4f508": int(776830 * 2.0 * 1024 + 531677 * 1.0 * 1024),
 }
 PREFILL_SRCS = [os.path.join(ROOT, "block_sparse_full_amd", "csrc", f)
                 for f in ("ssa_attn_prefill.hip", "ssa_device.h", "ssa_common.h")]

@@ -271,6 +271,92 @@ def test_block16_group_select(ssa):
     full_compare(cfg, x, got, budget=16, lse=True, group_select=True)
 
 
+# ---------------------------------------------------------------- hand-built lists
+
+def pattern_lists(B, Hq, Hkv, nqb, seed, head_map):
+    """Per-head block lists whose selection patterns over the four heads of a
+    work group cover every subset: blocks chosen by nested head sets (the
+    runs the grouped kernel walks once), arbitrary partial sets, no head and
+    all heads. Block 0 and the diagonal block are in every list (so every row
+    has a selected key). Returns idx [B, Hq, nqb, budget] (ascending, padded
+    with -1) and cnt."""
+    G = Hq // Hkv
+    heads = [[h for h in range(Hq) if head_map[h] == g] for g in range(Hkv)]
+    lists = {}
+    for b in range(B):
+        for g in range(Hkv):
+            for hg in range(G // 4):
+                hs = heads[g][4 * hg:4 * hg + 4]
+                for qb in range(nqb):
+                    rng = np.random.default_rng([seed, b, g, hg, qb])
+                    perm = rng.permutation(4)
+                    chain = [1 << perm[0], (1 << perm[0]) | (1 << perm[1]),
+                             (1 << perm[0]) | (1 << perm[1]) | (1 << perm[2])]
+                    masks = {0: 15, qb: 15}
+                    for kb in range(1, qb):
+                        r = rng.random()
+                        if qb % 7 == 3:        # only all-or-none patterns
+                            masks[kb] = 15 if r < 0.3 else 0
+                        elif r < 0.4:
+                            masks[kb] = chain[int(rng.integers(3))]
+                        elif r < 0.7:
+                            masks[kb] = int(rng.integers(1, 15))
+                        elif r < 0.85:
+                            masks[kb] = 0
+                        else:
+                            masks[kb] = 15
+                    for u, h in enumerate(hs):
+                        lists[(b, h, qb)] = sorted(kb for kb, m in masks.items() if (m >> u) & 1)
+    budget = max(len(v) for v in lists.values())
+    idx = np.full((B, Hq, nqb, budget), -1, dtype=np.int32)
+    cnt = np.zeros((B, Hq, nqb), dtype=np.int32)
+    for (b, h, qb), l in lists.items():
+        idx[b, h, qb, :len(l)] = l
+        cnt[b, h, qb] = len(l)
+    return idx, cnt
+
+
+WALK = [
+    ("gqa_8k_peaked", dict(B=1, Hq=8, Hkv=2, N=2048), None),             # 64 items: queues
+    ("gqa_8k_peaked", dict(B=2, Hq=16, Hkv=2, N=2112, planted=False),    # 132 items: static
+     [h % 2 for h in range(16)]),                                        # interleaved kv heads
+]
+
+
+@pytest.mark.parametrize("name,kw,hm", WALK, ids=["queues", "static_g8_headmap"])
+def test_walk_patterns_parity(ssa, name, kw, hm):
+    """The grouped D 128 kernel's walk list (per-head snapshot positions, a
+    chosen head order, blocks walked once or twice by their selection
+    pattern) on lists built to hit every pattern, dual and sparse-only, in
+    full against the oracle's attention over the same lists."""
+    cfg = CONFIGS[name].with_sizes(**kw)
+    x = make_inputs(cfg)
+    head_map = hm if hm is not None else default_head_map(cfg.Hq, cfg.Hkv)
+    nqb = cfg.N // cfg.block
+    idx, cnt = pattern_lists(cfg.B, cfg.Hq, cfg.Hkv, nqb, 7, head_map)
+    budget = idx.shape[-1]
+    say(f"walk patterns {name} {kw} budget {budget}")
+    dev = torch.device("cuda:0")
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    p = ssa.problem_for(q, k, budget=budget, n_sink=1, n_local=1, head_map=head_map)
+    di, dc = torch.from_numpy(idx).to(dev), torch.from_numpy(cnt).to(dev)
+    out = ssa.attn_fwd(p, q, k, v, di, dc)
+    sp = ssa.attn_fwd(p, q, k, v, di, dc, sparse_only=True)
+    torch.cuda.synchronize()
+    xn = np_inputs(x)
+    ref = O.dual_attention(xn["q"], xn["k"], xn["v"], idx, block=cfg.block,
+                           scale=scale_for(cfg), head_map=head_map)
+    want = {n: np.zeros((cfg.B, cfg.Hq, cfg.N) + ((cfg.D,) if n != "delta" else ()))
+            for n in ("h_full", "h_sparse", "delta")}
+    for (b, h), (r, hf, hs_, dl) in ref.items():
+        want["h_full"][b, h, r], want["h_sparse"][b, h, r], want["delta"][b, h, r] = hf, hs_, dl
+    assert_close("h_full", to_np64(out["h_full"]), want["h_full"], BF16_ABS, BF16_REL_L2)
+    assert_close("h_sparse", to_np64(out["h_sparse"]), want["h_sparse"], BF16_ABS, BF16_REL_L2)
+    assert_close("delta", to_np64(out["delta"]), want["delta"], BF16_DELTA_ABS)
+    assert_close("h_sparse (sparse-only)", to_np64(sp["h_sparse"]), want["h_sparse"], BF16_ABS,
+                 BF16_REL_L2)
+
+
 DETERMINISM = [
     ("gqa_8k_peaked", dict(B=1, Hq=8, Hkv=2, N=2048, budget=6), dict()),
     ("paper_16k_b16", dict(Hq=8, Hkv=2, N=2048, budget=16), dict(block=16)),

@@ -189,13 +189,26 @@ __global__ __launch_bounds__(256, 4) void attn_prefill_bf16_kernel(
   };
   auto kchunk = [&](int row, int ch) { return kswz<KSPR>(row, ch); };
 
+  // Q^T operand: lane holds Q[qrow][32ks + 8g4 .. +7] (in flight with the
+  // list loads below)
+  bf16x8_t qf[NKS];
+  {
+    const uint16_t* qp = Q + ((size_t)bh * d.Nq + qrow) * D + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8_t*)(qp + 32 * ks);
+  }
+  // the count and the first 256 entries are read side by side (entries past
+  // the count are read and ignored)
   const int* my_idx = idx + ((size_t)bh * d.nQB + qb) * d.budget;
-  const int n_sel =
-      __builtin_amdgcn_readfirstlane(min(max(cnt[(size_t)bh * d.nQB + qb], 0), d.budget));
+  const int c_raw = cnt[(size_t)bh * d.nQB + qb];
+  const int kb_first = tid < d.budget ? my_idx[tid] : -1;
   const int nwords = (diag >> 5) + 1;
   for (int w = tid; w < nwords; w += 256) sel_mask[w] = 0u;
   __syncthreads();
-  for (int e = tid; e < n_sel; e += 256) {
+  const int n_sel = __builtin_amdgcn_readfirstlane(min(max(c_raw, 0), d.budget));
+  if (tid < n_sel && kb_first >= 0 && kb_first <= diag)
+    atomicOr(&sel_mask[kb_first >> 5], 1u << (kb_first & 31));
+  for (int e = tid + 256; e < n_sel; e += 256) {
     const int kb = my_idx[e];
     if (kb >= 0 && kb <= diag) atomicOr(&sel_mask[kb >> 5], 1u << (kb & 31));
   }
@@ -228,13 +241,6 @@ __global__ __launch_bounds__(256, 4) void attn_prefill_bf16_kernel(
     }
   };
 
-  // Q^T operand: lane holds Q[qrow][32ks + 8g4 .. +7].
-  bf16x8_t qf[NKS];
-  {
-    const uint16_t* qp = Q + ((size_t)bh * d.Nq + qrow) * D + 8 * g4;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8_t*)(qp + 32 * ks);
-  }
   f32x4_t o[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -473,15 +479,16 @@ __global__ __launch_bounds__(256, 3) void attn_prefill_bf16_q16_kernel(
   if constexpr (TOK == 0) {
     for (int w = tid; w < 4 * kWords16; w += 256) (&sel16[0][0])[w] = 0u;
     __syncthreads();
-    for (int u = 0; u < 4; ++u) {
+    // one thread per (query block, list entry): all list loads in flight
+    // at once (entries past the count are read and ignored)
+    for (int t = tid; t < 4 * d.budget; t += 256) {
+      const int u = t / d.budget, e = t - u * d.budget;
       const size_t row = (size_t)bh * d.nQB + 4 * qt + u;
-      const int ns = min(max(cnt[row], 0), d.budget);
-      for (int e = tid; e < ns; e += 256) {
-        const int kb = idx[row * d.budget + e];
-        if (kb >= 0 && kb <= 4 * qt + u) {
-          atomicOr(&sel16[u][kb >> 5], 1u << (kb & 31));
-          if (sparse_only) atomicOr(&tiles[kb >> 7], 1u << ((kb >> 2) & 31));
-        }
+      const int ns = cnt[row];
+      const int kb = idx[row * d.budget + e];
+      if (e < ns && kb >= 0 && kb <= 4 * qt + u) {
+        atomicOr(&sel16[u][kb >> 5], 1u << (kb & 31));
+        if (sparse_only) atomicOr(&tiles[kb >> 7], 1u << ((kb >> 2) & 31));
       }
     }
   } else {
@@ -1436,20 +1443,25 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp16_kernel(
     for (int w = tid; w < TPE * TILE / 8; w += 64 * NW) ((uint4*)vz)[w] = make_uint4(0u, 0u, 0u, 0u);
   }
   __syncthreads();
-  for (int u = 0; u < HPW; ++u) {
-    const int hu = hm.q_of_kv[g * d.G + hg * HPW + u];
-    for (int qs = 0; qs < 4; ++qs) {
-      const size_t row = (size_t)(b * d.Hq + hu) * d.nQB + 4 * qt + qs;
-      const int ns = min(max(cnt[row], 0), d.budget);
-      for (int e = tid; e < ns; e += 64 * NW) {
-        const int kb = idx[row * d.budget + e];
-        if (kb >= 0 && kb <= 4 * qt + qs) atomicOr(&sel16[u][qs][kb >> 5], 1u << (kb & 31));
-      }
-    }
-  }
   {
     const float* knr = kn + (size_t)(b * d.Hkv + g) * (d.Nk / kBlock);
     for (int t = tid; t < ntiles; t += 64 * NW) knl[t] = knr[t];
+  }
+  {
+    // one thread per (head, query block, list entry): every list load is in
+    // flight at once (entries past the count are read and ignored)
+    int hq[HPW];
+#pragma unroll
+    for (int u = 0; u < HPW; ++u) hq[u] = hm.q_of_kv[g * d.G + hg * HPW + u];
+    for (int t = tid; t < HPW * 4 * d.budget; t += 64 * NW) {
+      const int l = t / d.budget, e = t - l * d.budget;
+      const int u = l >> 2, qs = l & 3;
+      const int hu = u == 0 ? hq[0] : u == 1 ? hq[1] : u == 2 ? hq[2] : hq[3];
+      const size_t row = (size_t)(b * d.Hq + hu) * d.nQB + 4 * qt + qs;
+      const int ns = cnt[row];
+      const int kb = idx[row * d.budget + e];
+      if (e < ns && kb >= 0 && kb <= 4 * qt + qs) atomicOr(&sel16[u][qs][kb >> 5], 1u << (kb & 31));
+    }
   }
   __syncthreads();
   (void)nwords16;

@@ -1071,12 +1071,6 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
   auto entry_kb = [&](int e) __attribute__((always_inline)) {
     return __builtin_amdgcn_readfirstlane((int)list[e]) & 0xfff;
   };
-  auto entry_act = [&](int e) __attribute__((always_inline)) {
-    return ((__builtin_amdgcn_readfirstlane((int)list[e]) >> (12 + hs)) & 1) != 0;
-  };
-  auto entry_kn = [&](int e) __attribute__((always_inline)) {
-    return __uint_as_float((uint32_t)__builtin_amdgcn_readfirstlane((int)list[e]) & 0xFFFF0000u);
-  };
   // copies past the end of the list repeat its last block (or block 0):
   // every slot issues the same number of copies, so the waits are static
   auto entry_kb_c = [&](int e) __attribute__((always_inline)) {
@@ -1232,15 +1226,16 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, PF + 4, 0);
   };
   // softmax(e): P(e) from S(e); the sparse snapshot is taken before the
-  // first entry of the second part can rescale the accumulator.
-  auto softmax = [&](int e) __attribute__((always_inline)) {
+  // first entry a head computes past its selected blocks. w is list entry
+  // e's word (read before the slot opened).
+  auto softmax = [&](int e, uint32_t w) __attribute__((always_inline)) {
     if (e == n_snap) snapshot();
-    if (e >= n || !entry_act(e)) {
+    if (e >= n || ((w >> (12 + hs)) & 1u) == 0u) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) pw[k] = 0u;
       return;
     }
-    const int kb = entry_kb(e);
+    const int kb = (int)(w & 0xfffu);
     if (kb == diag) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -1253,7 +1248,7 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
     // for a row's first block, and for a NaN bound): two chains of
     // three-input maxima, 17 VALU operations for the 32 logits
     float m_blk = -INFINITY;
-    if (__builtin_amdgcn_ballot_w64(!(qbound * entry_kn(e) <= m_ref + kTau)) != 0) {
+    if (__builtin_amdgcn_ballot_w64(!(qbound * __uint_as_float(w & 0xFFFF0000u) <= m_ref + kTau)) != 0) {
       float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 16; v += 2) {
@@ -1322,9 +1317,17 @@ __global__ __launch_bounds__(512, 2) void attn_prefill_bf16_pp_kernel(
     __builtin_amdgcn_s_setprio(0);
     issue_tiles(stc, kbk, kbv);
     slot_barrier();
-    kbk = entry_kb_c(t + NST);
-    kbv = entry_kb_c(t + NST - 1);
-    softmax(t);
+    // the blocks of the next copies and entry t's word: three LDS reads in
+    // flight together, one wait
+    const int nl = max(n - 1, 0);
+    const uint32_t wk = list[min(t + NST, nl)], wv = list[min(t + NST - 1, nl)];
+    const uint32_t we = list[min(t, nl)];
+    // (with an empty list, n = 0 in sparse-only mode, the copies read a
+    // stale word: any block index is in bounds or clipped by the buffer's
+    // range check, and nothing reads those stages)
+    kbk = __builtin_amdgcn_readfirstlane((int)wk) & 0xfff;
+    kbv = __builtin_amdgcn_readfirstlane((int)wv) & 0xfff;
+    softmax(t, (uint32_t)__builtin_amdgcn_readfirstlane((int)we));
   };
   for (int t = 0; t <= n; t += NST) {
     slots(I0{}, t);

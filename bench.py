@@ -37,8 +37,8 @@ FP64_PEAK_TFLOPS = 78.6          # MI355X float64 vector FMA
 # sources they were taken on (the prefill file and the headers it includes);
 # any other source reports traffic as null.
 PREFILL_TRAFFIC = {
-    # 776830 KiB x 2.000 read + 531677 KiB x 1.000 written per dispatch
-    "ed6da421050c2b33fd5ff653bc6e4adcace251241bc6353e745f521eb5d4f508": int(776830 * 2.0 * 1024 + 531677 * 1.0 * 1024),
+    # 778032 KiB x 2.000 read + 531942 KiB x 1.000 written per dispatch
+    "f64bb4b72ff93a8230594bf1988387fff3206c33c9c756faad6e08e397fdb4e4": int(778032 * 2.0 * 1024 + 531942 * 1.0 * 1024),
 }
 PREFILL_SRCS = [os.path.join(ROOT, "block_sparse_full_amd", "csrc", f)
                 for f in ("ssa_attn_prefill.hip", "ssa_device.h", "ssa_common.h")]

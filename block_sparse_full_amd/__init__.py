@@ -8,4 +8,4 @@ from .ssa import (SSA_BF16, SSA_F32, SSA_SELECT_GROUP, SSA_SELECT_PER_HEAD, SSA_
                   align_loss, align_loss_noalloc, alloc_bwd_workspace, alloc_workspace,
                   attn_bwd, attn_fwd,
                   bwd_workspace_bytes, dual_attention, load_library, pool_blocks, problem_for,
-                  select_blocks, workspace_bytes)
+                  select_blocks, set_attn_timing_events, workspace_bytes)

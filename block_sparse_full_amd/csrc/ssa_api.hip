@@ -16,6 +16,8 @@
 namespace {
 
 thread_local char g_err[512] = "";
+// the caller's event pair of ssa_set_attn_timing_events (NULL: no timing)
+hipEvent_t g_timing_start = nullptr, g_timing_stop = nullptr;
 
 ssa_status fail(ssa_status s, const char* fmt, ...) {
   va_list ap;
@@ -364,10 +366,23 @@ ssa_status ssa_attn_fwd(const ssa_problem* p, const void* q, const void* k, cons
                                        ssa::prefill_vt_blk16(d, h_full == nullptr),
                                        (const uint16_t*)k, kn, st);
   if (e != hipSuccess) return hip_status(e, "transpose v");
-  return hip_status(ssa::launch_attn_prefill_bf16((const uint16_t*)q, (const uint16_t*)k, vt, idx,
-                                                  cnt, (uint16_t*)h_full, (uint16_t*)h_sparse,
-                                                  delta, lse, queues, kn, d, P.hm, st),
-                    "attention (prefill)");
+  if (g_timing_start != nullptr && (e = hipEventRecord(g_timing_start, st)) != hipSuccess)
+    return hip_status(e, "timing event (start)");
+  e = ssa::launch_attn_prefill_bf16((const uint16_t*)q, (const uint16_t*)k, vt, idx, cnt,
+                                    (uint16_t*)h_full, (uint16_t*)h_sparse, delta, lse, queues,
+                                    kn, d, P.hm, st);
+  if (e != hipSuccess) return hip_status(e, "attention (prefill)");
+  if (g_timing_stop != nullptr && (e = hipEventRecord(g_timing_stop, st)) != hipSuccess)
+    return hip_status(e, "timing event (stop)");
+  return SSA_OK;
+}
+
+ssa_status ssa_set_attn_timing_events(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(SSA_ERR_INVALID_ARG, "timing events: give both or neither");
+  g_timing_start = (hipEvent_t)start;
+  g_timing_stop = (hipEvent_t)stop;
+  return ok();
 }
 
 ssa_status ssa_align_loss(const ssa_problem* p, const void* h_full, const void* h_sparse,

@@ -28,8 +28,8 @@ SSA_SELECT_PER_HEAD, SSA_SELECT_GROUP, SSA_SELECT_TOKEN = 0, 1, 2
 STATUS = {0: "SSA_OK", 1: "SSA_ERR_INVALID_ARG", 2: "SSA_ERR_UNSUPPORTED",
           3: "SSA_ERR_WORKSPACE", 4: "SSA_ERR_HIP"}
 EXPORTS = ("ssa_workspace_bytes", "ssa_pool_blocks", "ssa_select_blocks", "ssa_attn_fwd",
-           "ssa_align_loss", "ssa_align_loss_noalloc", "ssa_status_string",
-           "ssa_last_error_message")
+           "ssa_align_loss", "ssa_align_loss_noalloc", "ssa_set_attn_timing_events",
+           "ssa_status_string", "ssa_last_error_message")
 
 
 class SsaError(RuntimeError):
@@ -76,6 +76,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ssa_align_loss.restype = ctypes.c_int
     lib.ssa_align_loss_noalloc.argtypes = [P, vp, vp, f32p, vp, vp, vp]
     lib.ssa_align_loss_noalloc.restype = ctypes.c_int
+    lib.ssa_set_attn_timing_events.argtypes = [vp, vp]
+    lib.ssa_set_attn_timing_events.restype = ctypes.c_int
     lib.ssa_bwd_workspace_bytes.argtypes = [P]
     lib.ssa_bwd_workspace_bytes.restype = sz
     lib.ssa_attn_bwd.argtypes = [P, vp, vp, vp, i32p, i32p, vp, vp, f32p, vp, vp, vp, vp, vp, vp,
@@ -258,6 +260,20 @@ def attn_fwd(p: Problem, q, k, v, idx, cnt, *, sparse_only: bool = False, want_d
         _dev(o.get("delta") if not sparse_only else None, "delta", torch.float32),
         _dev(o.get("lse"), "lse", torch.float32), wp, wn, _stream()))
     return o
+
+
+def set_attn_timing_events(start=None, stop=None) -> None:
+    """Record torch.cuda.Event `start` / `stop` around the attention kernel of
+    every following bf16 prefill attn_fwd (the V transpose before it stays
+    outside the pair); no arguments clears the hook. The events must have been
+    recorded once (torch creates them on first use)."""
+    if (start is None) != (stop is None):
+        raise ValueError("give both events or neither")
+    h0 = None if start is None else ctypes.c_void_p(start.cuda_event)
+    h1 = None if stop is None else ctypes.c_void_p(stop.cuda_event)
+    if start is not None and (not h0.value or not h1.value):
+        raise ValueError("record the events once before passing them")
+    _check(load_library().ssa_set_attn_timing_events(h0, h1))
 
 
 def align_loss(p: Problem, h_full, h_sparse, *, want_grads: bool = False,

@@ -257,6 +257,19 @@ ssa_status ssa_attn_bwd(const ssa_problem* p, const void* q, const void* k,
                         const void* d_sparse, void* dq, void* dk, void* dv,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* Measurement hook, for callers that time the attention kernel of a prefill
+ * call on its own (a benchmark's roofline): while set, every bf16 prefill
+ * ssa_attn_fwd records `start` on its stream immediately before launching
+ * the attention kernel and `stop` immediately after it, so that the pair
+ * brackets that one kernel and not the V transpose launched before it.
+ *   start, stop : hipEvent_t handles (passed as void*), created and owned by
+ *                 the caller, both non-NULL; NULL, NULL clears the hook
+ * The setting is process-wide and not synchronised: set it from the thread
+ * that issues the calls, with no call in flight on another thread. Decode and
+ * float32 calls ignore it. Errors: SSA_ERR_INVALID_ARG when exactly one of
+ * the two is NULL (the previous setting is kept). */
+ssa_status ssa_set_attn_timing_events(void* start, void* stop);
+
 /* Static text of a status code. */
 const char* ssa_status_string(ssa_status s);
 

@@ -199,3 +199,13 @@ def test_backward_workspace_size(lib):
     assert _bwd(lib, c, ws=4096 + 8, wn=need) == 3   # not 256-byte aligned
     f32 = _p(dtype=0)
     assert bwd_workspace_bytes(f32) == stats        # float32 path keeps statistics only
+
+
+def test_timing_hook_arguments(lib):
+    """The measurement hook takes both event handles or neither; one alone is
+    rejected (no device work is involved in setting it)."""
+    assert lib.ssa_set_attn_timing_events(ctypes.c_void_p(16), None) == 1
+    assert "both" in lib.ssa_last_error_message().decode()
+    assert lib.ssa_set_attn_timing_events(None, ctypes.c_void_p(16)) == 1
+    assert lib.ssa_set_attn_timing_events(None, None) == 0
+    assert lib.ssa_last_error_message().decode() == ""

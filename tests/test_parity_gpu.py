@@ -357,6 +357,43 @@ def test_walk_patterns_parity(ssa, name, kw, hm):
                  BF16_REL_L2)
 
 
+def test_attention_timing_hook(ssa):
+    """Events handed to ssa_set_attn_timing_events bracket the attention
+    kernel of a grouped prefill call: recorded after the V transpose, inside
+    the call's own bracket; outputs are unchanged; clearing stops them."""
+    cfg = CONFIGS["gqa_8k_peaked"].with_sizes(B=1, Hq=8, Hkv=2, N=4096)
+    x = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    p = ssa.problem_for(q, k, budget=8, n_sink=1, n_local=1)
+    ws = ssa.alloc_workspace(p, dev)
+    idx, cnt = ssa.select_blocks(p, q, k, ws=ws)
+    ref = ssa.attn_fwd(p, q, k, v, idx, cnt, ws=ws)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    ssa.set_attn_timing_events(ev[1], ev[2])
+    try:
+        ev[0].record()
+        out = ssa.attn_fwd(p, q, k, v, idx, cnt, ws=ws)
+        ev[3].record()
+    finally:
+        ssa.set_attn_timing_events()
+    torch.cuda.synchronize()
+    call_ms, kern_ms = ev[0].elapsed_time(ev[3]), ev[1].elapsed_time(ev[2])
+    say(f"call {call_ms:.4f} ms, attention kernel {kern_ms:.4f} ms")
+    assert 0.0 < kern_ms <= call_ms
+    assert ev[0].elapsed_time(ev[1]) >= 0.0 and ev[2].elapsed_time(ev[3]) >= 0.0
+    for n in ("h_full", "h_sparse", "delta"):
+        assert torch.equal(out[n], ref[n]), n
+    # cleared: a later call leaves the events where they were
+    before = ev[1].elapsed_time(ev[2])
+    ssa.attn_fwd(p, q, k, v, idx, cnt, ws=ws)
+    torch.cuda.synchronize()
+    assert ev[1].elapsed_time(ev[2]) == before
+
+
 DETERMINISM = [
     ("gqa_8k_peaked", dict(B=1, Hq=8, Hkv=2, N=2048, budget=6), dict()),
     ("paper_16k_b16", dict(Hq=8, Hkv=2, N=2048, budget=16), dict(block=16)),
